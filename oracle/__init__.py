@@ -1,0 +1,183 @@
+"""Float64 CPU oracle for the LittleBit factorized binary linear forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP
+library never calls it, and it shares no code with the HIP library.
+
+Sources (the web pages this method is taken from; cited by short name):
+
+* [LB2 column] physicalainews.jp, "LittleBit-2: sub-1-bit LLM quantization
+  (2026)".  Ch. 1 defines the effective bit width of a LittleBit layer
+  (one formula without and one with the residual path); Ch. 2 describes
+  the binary low-rank factors and the Joint-ITQ rotation.
+* [LB news] aifrontier.co.jp, "Samsung LittleBit: 13B to 0.84 GB".  Sec. 1
+  has the model-size table; Sec. 2 ("how it works") says the weight matrix
+  is approximated by the product of two binarised (+-1) low-rank factors,
+  with three learnable FP16 scales (row h, column g, latent l), that the
+  residual path is a second factorisation whose output is added at
+  inference, and that inference is two small binary matrix products plus
+  elementwise scaling.
+
+Readings where the pages are silent (each one is also listed in the
+design notes):
+
+* polarity: bit 1 is +1 and bit 0 is -1;
+* canonical packing: each row of S_U (b x s) and of S_V (a x s) is packed
+  along s, 32 entries per uint32, entry k in bit k % 32 of word k // 32;
+  bits past s are ignored;
+* orientation: a is the input width and b the output width, W is b x a and
+  W ~= diag(h) S_U diag(l) S_V^T diag(g);
+* residual: both paths read the same x, have fully independent
+  (S_U, S_V, h, g, l) and are summed;
+* no bias (the bit count of [LB2 column] Ch. 1 has no bias term).
+
+Every function here is pinned by tests that do not re-type it: brute-force
+loops on tiny inputs, closed forms, invariants, hand-worked fixtures under
+``tests/golden/`` and the model sizes printed in [LB news] Sec. 1.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "unpack_signs", "pack_signs", "num_bits", "eff_bits", "rank_for_bpw",
+    "forward", "forward_path", "dense_weight", "combine", "stack_units",
+]
+
+
+# --------------------------------------------------------------------------
+# Sign bits
+# --------------------------------------------------------------------------
+def unpack_signs(words, s: int) -> np.ndarray:
+    """Canonical words (rows x ceil(s/32) uint32) -> +-1 int8 matrix (rows x s).
+
+    [LB news] Sec. 2: the factors are binarised to +-1 and stored as bits.
+    Bits past ``s`` in the last word are ignored.
+    """
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    rows = words.shape[0]
+    out = np.empty((rows, s), dtype=np.int8)
+    for k in range(s):
+        bit = (words[:, k // 32] >> np.uint32(k % 32)) & np.uint32(1)
+        out[:, k] = np.where(bit == 1, 1, -1)
+    return out
+
+
+def pack_signs(S) -> np.ndarray:
+    """+-1 matrix (rows x s) -> canonical words (rows x ceil(s/32) uint32).
+
+    Padding bits are zero.  Inverse of :func:`unpack_signs`.
+    """
+    S = np.asarray(S)
+    rows, s = S.shape
+    words = np.zeros((rows, (s + 31) // 32), dtype=np.uint32)
+    for k in range(s):
+        one = (S[:, k] > 0).astype(np.uint32)
+        words[:, k // 32] |= one << np.uint32(k % 32)
+    return words
+
+
+# --------------------------------------------------------------------------
+# Bit accounting ([LB2 column] Ch. 1)
+# --------------------------------------------------------------------------
+def num_bits(a: int, b: int, s: int, residual: bool) -> int:
+    """Storage bits of one layer: s*(a+b+16) + 16*(a+b) per path.
+
+    [LB2 column] Ch. 1 gives the single-path count and the residual count,
+    which doubles every term.  a = input width, b = output width, s = rank.
+    """
+    paths = 2 if residual else 1
+    return paths * (s * (a + b + 16) + 16 * (a + b))
+
+
+def eff_bits(a: int, b: int, s: int, residual: bool) -> Fraction:
+    """Effective bits per weight, exactly: num_bits / (a*b) ([LB2 column] Ch. 1)."""
+    return Fraction(num_bits(a, b, s, residual), a * b)
+
+
+def rank_for_bpw(a: int, b: int, bpw, residual: bool) -> int:
+    """Largest rank s whose effective bit width does not exceed ``bpw``.
+
+    Solves the bit count of [LB2 column] Ch. 1 for s in exact rationals and
+    takes the floor.  Raises ValueError when even s = 0 exceeds the budget.
+    """
+    bpw = Fraction(bpw)
+    paths = 2 if residual else 1
+    budget = bpw * a * b - 16 * paths * (a + b)
+    if budget < 0:
+        raise ValueError("bit budget too small for the scale vectors alone")
+    return int(budget // (paths * (a + b + 16)))
+
+
+# --------------------------------------------------------------------------
+# Forward
+# --------------------------------------------------------------------------
+def _f64(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float16).astype(np.float64)
+
+
+def forward_path(x, path: dict) -> np.ndarray:
+    """One path: h * (S_U (l * (S_V^T (g * x)))), rows of x independent.
+
+    [LB news] Sec. 2: two small binary matrix products and elementwise
+    scaling with the column scale g, latent scale l and row scale h.
+    ``x`` is (M x a) fp16; the result is float64 (M x b), not rounded.
+    """
+    s = path["s"]
+    S_U = unpack_signs(path["su"], s).astype(np.float64)   # b x s
+    S_V = unpack_signs(path["sv"], s).astype(np.float64)   # a x s
+    x = _f64(x)
+    z = x * _f64(path["g"])[None, :]          # column scale
+    t = z @ S_V                               # first binary product
+    w = t * _f64(path["l"])[None, :]          # latent scale
+    u = w @ S_U.T                             # second binary product
+    return u * _f64(path["h"])[None, :]       # row scale
+
+
+def forward(x, paths) -> np.ndarray:
+    """Layer output in float64: the sum of its paths ([LB news] Sec. 2, residual)."""
+    y = None
+    for p in paths:
+        v = forward_path(x, p)
+        y = v if y is None else y + v
+    return y
+
+
+def dense_weight(paths) -> np.ndarray:
+    """Dense W (b x a) = sum_p diag(h) S_U diag(l) S_V^T diag(g), float64."""
+    W = None
+    for p in paths:
+        s = p["s"]
+        S_U = unpack_signs(p["su"], s).astype(np.float64)
+        S_V = unpack_signs(p["sv"], s).astype(np.float64)
+        Wp = (_f64(p["h"])[:, None] * S_U) @ (_f64(p["l"])[:, None] * (S_V * _f64(p["g"])[:, None]).T)
+        W = Wp if W is None else W + Wp
+    return W
+
+
+# --------------------------------------------------------------------------
+# Stack wiring (not on the pages: linear stand-ins for the parts of a
+# transformer block that are not LittleBit layers)
+# --------------------------------------------------------------------------
+def combine(ys, c: float) -> np.ndarray:
+    """fp16(c * sum(ys)) computed in float64 from fp16 producer outputs."""
+    acc = None
+    for y in ys:
+        v = _f64(y)
+        acc = v if acc is None else acc + v
+    return (float(c) * acc).astype(np.float16)
+
+
+def stack_units(kind: str, n_layers: int) -> list:
+    """Unit sizes of a stack: matrices in one unit share one input.
+
+    ``mlp``: per layer [gate, up], [down].  ``block``: per layer
+    [q, k, v], [o], [gate, up], [down].  A unit's input is the previous
+    unit's outputs summed and scaled by kappa / sqrt(n_prev) (the first
+    unit reads the stack input); the stack output is the last unit's
+    combine.
+    """
+    per = {"mlp": [2, 1], "block": [3, 1, 2, 1]}[kind]
+    return per * int(n_layers)
