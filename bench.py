@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the LittleBit linear forward on one MI355X.
+
+One step = one forward sweep of the whole workload (every matrix of the
+stack, chained as a transformer would chain them) on one batch of
+synthetic input already resident in HBM.  The default workload is the
+Llama2-70B MLP stack at 0.1 bits per weight with the residual path
+(80 blocks x gate, up 8192->28672 and down 28672->8192, rank 302, M = 1).
+
+Prints one JSON line.  value = algorithmic bytes of one sweep (sign bits,
+fp16 scales, fp16 activations in and out of every matrix) / time per
+step, in GB/s.  The oracle (float64 numpy) is timed on the host cores on
+a bounded sample of the same workload as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lb_synth  # noqa: E402
+
+METRIC = ("LittleBit linear fwd: µs/layer + achieved HBM GB/s vs 8 TB/s at batch 1; "
+          "M=128 TFLOP/s")
+HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_bytes(wl: dict, M: int) -> int:
+    tot = 0
+    for sp in wl["layers"]:
+        P = 2 if sp["residual"] else 1
+        a, b, s = sp["a"], sp["b"], sp["s"]
+        tot += P * s * (a + b) // 8          # sign bits (P*s*(a+b) is a multiple of 8 here)
+        tot += 2 * P * (a + b + s)           # fp16 h, g, l
+        tot += 2 * M * (a + b)               # fp16 input and output rows
+    return tot
+
+
+def algorithmic_flops(wl: dict, M: int) -> int:
+    tot = 0
+    for sp in wl["layers"]:
+        P = 2 if sp["residual"] else 1
+        tot += 2 * M * P * sp["s"] * (sp["a"] + sp["b"])
+    return tot
+
+
+def build(lbm, wl):
+    layers, t0 = [], time.time()
+    for sp in wl["layers"]:
+        layers.append(lbm.Layer.from_paths(lb_synth.workload_layer_inputs(sp)))
+    P = 2 if wl["layers"][0]["residual"] else 1
+    stack = lbm.Stack(layers, wl["units"], lb_synth.kappa(P))
+    return stack, time.time() - t0
+
+
+def time_steps(torch, stack, x, y, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        stack.forward(x, y, None, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        stack.forward(x, y, None, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(wl: dict, M: int, budget_s: float) -> dict:
+    """Time the float64 oracle on a bounded sample of the workload's layers."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    x = lb_synth.activations(M, wl["layers"][0]["a"], seed=wl["seed"])
+    done_bytes, done_layers, t_used = 0, 0, 0.0
+    one = {"layers": None}
+    for sp in wl["layers"]:
+        paths = lb_synth.workload_layer_inputs(sp)
+        xin = x if x.shape[1] == sp["a"] else lb_synth.activations(M, sp["a"], seed=sp["block"])
+        t0 = time.perf_counter()
+        oracle.forward(xin, paths)
+        t_used += time.perf_counter() - t0
+        one["layers"] = [sp]
+        done_bytes += algorithmic_bytes(one, M)
+        done_layers += 1
+        if t_used >= budget_s:
+            break
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done_layers} of {len(wl['layers'])} matrices, M={M}, "
+                      f"float64 numpy incl. bit unpack, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama70b_mlp_stack", choices=sorted(lb_synth.WORKLOADS))
+    ap.add_argument("--blocks", type=int, default=None)
+    ap.add_argument("--mode", type=int, default=0, help="0 auto, 1 per-layer kernels, 2 persistent")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="llama7b_full_stack_M128",
+                    help="extra workload measured in the same run ('' to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the layer's multi-GPU split is described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import binary_rank_gemv_littlebitlinear_amd as lbm
+    assert torch.cuda.is_available(), "no GPU visible"
+    lbm.load_library()
+
+    def measure(name, blocks, with_cpu):
+        wl = lb_synth.workload(name, blocks)
+        M = wl["M"]
+        print(f"[bench] building {name} ({len(wl['layers'])} matrices, M={M})", file=sys.stderr, flush=True)
+        stack, t_build = build(lbm, wl)
+        stack.set_mode(args.mode)
+        x = torch.from_numpy(lb_synth.activations(M, wl["layers"][0]["a"], seed=wl["seed"])).cuda()
+        y = torch.empty((M, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+        print(f"[bench] built in {t_build:.1f} s; timing {args.steps} steps", file=sys.stderr, flush=True)
+        ms, wall_ms = time_steps(torch, stack, x, y, args.steps, args.warmup)
+        nbytes, flops = algorithmic_bytes(wl, M), algorithmic_flops(wl, M)
+        res = {"wl": wl, "M": M, "ms": ms, "wall_ms": wall_ms, "bytes": nbytes, "flops": flops}
+        if with_cpu:
+            print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+            res["cpu"] = cpu_baseline(wl, M, args.cpu_budget)
+        stack.close()
+        torch.cuda.synchronize()
+        return res
+
+    r = measure(args.workload, args.blocks, not args.no_cpu_baseline)
+    wl, M, ms = r["wl"], r["M"], r["ms"]
+    gbs = r["bytes"] / (ms * 1e-3) / 1e9
+    tflops = r["flops"] / (ms * 1e-3) / 1e12
+    batch1 = M < 64
+    out = {
+        "metric": METRIC,
+        "value": round(gbs if batch1 else tflops, 3),
+        "unit": "GB/s" if batch1 else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl["name"], "M": M, "blocks": wl["blocks"],
+                   "matrices": len(wl["layers"]), "s": sorted({sp["s"] for sp in wl["layers"]}),
+                   "residual": wl["layers"][0]["residual"], "parallelism": "single GPU"},
+        "us_per_layer": round(ms * 1e3 / wl["blocks"], 4),
+        "tokens_per_s_equiv": round(M / (ms * 1e-3), 1),
+        "algorithmic_bytes_per_step": r["bytes"],
+        "roofline": {"bound": "hbm" if batch1 else "mfma",
+                     "achieved": round(gbs if batch1 else tflops, 3),
+                     "peak": HBM_PEAK_GBS if batch1 else MFMA_FP16_PEAK_TFLOPS,
+                     "unit": "GB/s" if batch1 else "TFLOP/s",
+                     "frac": round((gbs / HBM_PEAK_GBS) if batch1 else (tflops / MFMA_FP16_PEAK_TFLOPS), 4),
+                     "traffic": None,
+                     "kernel": "whole sweep (stream events around each step)"},
+    }
+    if "cpu" in r:
+        out["cpu_baseline"] = r["cpu"]
+    if args.secondary and args.secondary != args.workload:
+        s2 = measure(args.secondary, None, False)
+        ms2 = s2["ms"]
+        out["secondary"] = {"workload": args.secondary, "M": s2["M"], "ms_per_step": round(ms2, 5),
+                            "us_per_layer": round(ms2 * 1e3 / s2["wl"]["blocks"], 3),
+                            "TFLOP/s": round(s2["flops"] / (ms2 * 1e-3) / 1e12, 3),
+                            "mfma_frac": round(s2["flops"] / (ms2 * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                            "GB/s": round(s2["bytes"] / (ms2 * 1e-3) / 1e9, 2),
+                            "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

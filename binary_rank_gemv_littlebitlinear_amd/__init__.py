@@ -1,0 +1,283 @@
+"""Python binding of the LittleBit linear-forward C ABI (``include/lb.h``).
+
+Argument marshalling only: every step of the forward runs in the HIP
+library ``liblb.so`` built next to this file.  There is no fallback: if
+the library is missing, loading fails loudly.  torch is used for device
+memory and streams only (tensors are passed as raw pointers).
+
+Functions keep the C names (``lb_create``, ``lb_pack_signs``, ...);
+``Layer`` and ``Stack`` are thin owners that call them.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblb.so")
+
+LB_OK, LB_EINVAL, LB_ENOMEM, LB_EHIP, LB_ENOTREADY, LB_EUNSUPPORTED, LB_ETIMEOUT = 0, -1, -2, -3, -4, -5, -6
+
+
+class LBError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblb.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run python -m binary_rank_gemv_littlebitlinear_amd.build)")
+    lib = C.CDLL(path)
+    vp, i64, i32, u64 = C.c_void_p, C.c_int64, C.c_int, C.c_uint64
+    P = C.POINTER
+    sig = {
+        "lb_create": ([i64, i64, i64, i32, P(vp)], i32),
+        "lb_pack_signs": ([vp, i32, vp, vp], i32),
+        "lb_set_scales": ([vp, i32, vp, vp, vp], i32),
+        "lb_forward": ([vp, vp, vp, i64, vp], i32),
+        "lb_unpack_signs": ([vp, i32, vp, vp], i32),
+        "lb_layer_shape": ([vp, P(i64), P(i64), P(i64), P(i32)], i32),
+        "lb_destroy": ([vp], i32),
+        "lb_forward_stage1": ([vp, vp, vp, i64, vp], i32),
+        "lb_forward_stage2": ([vp, vp, vp, i64, vp], i32),
+        "lb_eff_bits": ([i64, i64, i64, i32, P(u64), P(u64)], i32),
+        "lb_rank_for_bpw": ([i64, i64, u64, u64, i32, P(i64)], i32),
+        "lb_stack_create": ([vp, i32, vp, i32, C.c_float, P(vp)], i32),
+        "lb_stack_forward": ([vp, vp, vp, vp, i64, vp], i32),
+        "lb_stack_trace_elems": ([vp, i64, P(i64)], i32),
+        "lb_stack_set_mode": ([vp, i32], i32),
+        "lb_stack_destroy": ([vp], i32),
+        "lb_status_str": ([i32], C.c_char_p),
+        "lb_last_error": ([], C.c_char_p),
+        "lb_version": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
+            "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
+            "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
+            "lb_stack_trace_elems", "lb_stack_set_mode", "lb_stack_destroy", "lb_status_str",
+            "lb_last_error", "lb_version")
+
+
+def _status_name(st: int) -> str:
+    names = {0: "LB_OK", -1: "LB_EINVAL", -2: "LB_ENOMEM", -3: "LB_EHIP", -4: "LB_ENOTREADY",
+             -5: "LB_EUNSUPPORTED", -6: "LB_ETIMEOUT"}
+    return names.get(st, f"status {st}")
+
+
+def _check(st: int):
+    if st != LB_OK:
+        msg = load_library().lb_last_error().decode(errors="replace")
+        raise LBError(st, msg)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a torch tensor / raw int / None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return torch.cuda.current_stream().cuda_stream
+        except Exception:
+            pass
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _host(arr, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(arr)
+    if a.dtype != dtype:
+        a = np.ascontiguousarray(a.view(dtype) if a.dtype.itemsize == np.dtype(dtype).itemsize else a.astype(dtype))
+    return a
+
+
+# ------------------------------------------------------------ raw calls
+def lb_create(a: int, b: int, s: int, residual: bool) -> int:
+    out = C.c_void_p()
+    _check(load_library().lb_create(a, b, s, int(bool(residual)), C.byref(out)))
+    return out.value
+
+
+def lb_pack_signs(layer: int, path: int, su_words, sv_words):
+    su = _host(su_words, np.uint32)
+    sv = _host(sv_words, np.uint32)
+    _check(load_library().lb_pack_signs(layer, path, su.ctypes.data, sv.ctypes.data))
+
+
+def lb_set_scales(layer: int, path: int, h, g, l):
+    hh = _host(np.asarray(h, np.float16), np.uint16)
+    gg = _host(np.asarray(g, np.float16), np.uint16)
+    ll = _host(np.asarray(l, np.float16), np.uint16)
+    _check(load_library().lb_set_scales(layer, path, hh.ctypes.data, gg.ctypes.data, ll.ctypes.data))
+
+
+def lb_forward(layer: int, x, y, M: int, stream=None):
+    _check(load_library().lb_forward(layer, _ptr(x), _ptr(y), int(M), _stream(stream)))
+
+
+def lb_forward_stage1(layer: int, x, w, M: int, stream=None):
+    _check(load_library().lb_forward_stage1(layer, _ptr(x), _ptr(w), int(M), _stream(stream)))
+
+
+def lb_forward_stage2(layer: int, w, y, M: int, stream=None):
+    _check(load_library().lb_forward_stage2(layer, _ptr(w), _ptr(y), int(M), _stream(stream)))
+
+
+def lb_unpack_signs(layer: int, path: int):
+    a, b, s, _ = lb_layer_shape(layer)
+    wk = (s + 31) // 32
+    su = np.zeros((b, wk), np.uint32)
+    sv = np.zeros((a, wk), np.uint32)
+    _check(load_library().lb_unpack_signs(layer, path, su.ctypes.data, sv.ctypes.data))
+    return su, sv
+
+
+def lb_layer_shape(layer: int):
+    a, b, s, r = C.c_int64(), C.c_int64(), C.c_int64(), C.c_int()
+    _check(load_library().lb_layer_shape(layer, C.byref(a), C.byref(b), C.byref(s), C.byref(r)))
+    return a.value, b.value, s.value, bool(r.value)
+
+
+def lb_destroy(layer: int):
+    _check(load_library().lb_destroy(layer))
+
+
+def lb_eff_bits(a: int, b: int, s: int, residual: bool):
+    n, d = C.c_uint64(), C.c_uint64()
+    _check(load_library().lb_eff_bits(a, b, s, int(bool(residual)), C.byref(n), C.byref(d)))
+    return n.value, d.value
+
+
+def lb_rank_for_bpw(a: int, b: int, bpw_num: int, bpw_den: int, residual: bool) -> int:
+    s = C.c_int64()
+    _check(load_library().lb_rank_for_bpw(a, b, bpw_num, bpw_den, int(bool(residual)), C.byref(s)))
+    return s.value
+
+
+def lb_stack_create(layers, unit_sizes, kappa: float) -> int:
+    arr = (C.c_void_p * len(layers))(*layers)
+    us = np.ascontiguousarray(unit_sizes, dtype=np.int32)
+    out = C.c_void_p()
+    _check(load_library().lb_stack_create(C.cast(arr, C.c_void_p), len(layers), us.ctypes.data,
+                                          len(us), float(kappa), C.byref(out)))
+    return out.value
+
+
+def lb_stack_forward(stack: int, x0, y, trace, M: int, stream=None):
+    _check(load_library().lb_stack_forward(stack, _ptr(x0), _ptr(y), _ptr(trace), int(M),
+                                           _stream(stream)))
+
+
+def lb_stack_trace_elems(stack: int, M: int) -> int:
+    n = C.c_int64()
+    _check(load_library().lb_stack_trace_elems(stack, int(M), C.byref(n)))
+    return n.value
+
+
+def lb_stack_set_mode(stack: int, mode: int):
+    _check(load_library().lb_stack_set_mode(stack, int(mode)))
+
+
+def lb_stack_destroy(stack: int):
+    _check(load_library().lb_stack_destroy(stack))
+
+
+# --------------------------------------------------------------- owners
+class Layer:
+    """Owner of one lb_layer handle."""
+
+    def __init__(self, a: int, b: int, s: int, residual: bool):
+        self.a, self.b, self.s, self.residual = a, b, s, bool(residual)
+        self.handle = lb_create(a, b, s, residual)
+
+    @classmethod
+    def from_paths(cls, paths):
+        p0 = paths[0]
+        L = cls(p0["a"], p0["b"], p0["s"], len(paths) == 2)
+        for i, p in enumerate(paths):
+            lb_pack_signs(L.handle, i, p["su"], p["sv"])
+            lb_set_scales(L.handle, i, p["h"], p["g"], p["l"])
+        return L
+
+    def forward(self, x, y, M=None, stream=None):
+        lb_forward(self.handle, x, y, x.shape[0] if M is None else M, stream)
+
+    def close(self):
+        if self.handle:
+            lb_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Stack:
+    """Owner of one lb_stack handle (keeps its layers alive)."""
+
+    def __init__(self, layers, unit_sizes, kappa: float):
+        self.layers = list(layers)
+        self.unit_sizes = list(unit_sizes)
+        self.handle = lb_stack_create([L.handle for L in self.layers], self.unit_sizes, kappa)
+
+    def forward(self, x0, y, trace=None, M=None, stream=None):
+        lb_stack_forward(self.handle, x0, y, trace, x0.shape[0] if M is None else M, stream)
+
+    def trace_elems(self, M: int) -> int:
+        return lb_stack_trace_elems(self.handle, M)
+
+    def set_mode(self, mode: int):
+        lb_stack_set_mode(self.handle, mode)
+
+    def close(self):
+        if self.handle:
+            lb_stack_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lb_status_str(status: int) -> str:
+    return load_library().lb_status_str(int(status)).decode()
+
+
+def lb_last_error() -> str:
+    return load_library().lb_last_error().decode(errors="replace")
+
+
+def lb_version() -> int:
+    return load_library().lb_version()

@@ -1,0 +1,165 @@
+/*
+ * lb.h -- C ABI of the LittleBit factorized binary linear forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by short name throughout the library):
+ *   [LB2 column] physicalainews.jp, "LittleBit-2: sub-1-bit LLM
+ *                quantization (2026)".  Ch. 1: effective bit width of a
+ *                layer, single path and residual.
+ *   [LB news]    aifrontier.co.jp, "Samsung LittleBit: 13B to 0.84 GB".
+ *                Sec. 2: W is approximated by two binarised (+-1) low-rank
+ *                factors with FP16 row scale h, column scale g and latent
+ *                scale l; a residual path is a second factorisation added
+ *                at inference; inference is two small binary matrix
+ *                products plus elementwise scaling.
+ *
+ * The layer computes, for every row x of an M x a input,
+ *
+ *     y = sum_p  h_p * ( S_U,p ( l_p * ( S_V,p^T ( g_p * x ) ) ) )
+ *
+ * with S_U,p in {+-1}^(b x s), S_V,p in {+-1}^(a x s), h_p (b), g_p (a),
+ * l_p (s) in fp16, p = 0 only, or p = 0, 1 when residual.  a is the input
+ * width and b the output width.  Accumulation is fp32; y is rounded once
+ * to fp16 (round to nearest even).
+ *
+ * Conventions
+ *   - Every call returns lb_status; the library never aborts or exits.
+ *     lb_last_error() returns a thread-local text for the last failure.
+ *   - Sign words ("canonical layout"): a factor with `rows` rows is given
+ *     as rows x ceil(s/32) uint32 words, row-major; entry k of a row is
+ *     bit (k % 32) of word (k / 32); bit 1 means +1 and bit 0 means -1.
+ *     Bits past s are ignored.
+ *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16).
+ *   - Host inputs are copied before the call returns; the caller may free
+ *     them at once.  The library owns every device buffer it allocates.
+ *   - Device pointers (x, y) are caller-owned, contiguous, row-major and
+ *     16-byte aligned, and x must not overlap y.
+ *   - Forward calls are asynchronous on the given hipStream_t (passed as
+ *     void*, NULL = the null stream), make no allocation and no host
+ *     synchronisation.  Calls that use one layer or stack must be ordered
+ *     on one stream: they share the object's device workspace.
+ */
+#ifndef LB_H
+#define LB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lb_layer lb_layer; /* opaque, library-owned */
+typedef struct lb_stack lb_stack; /* opaque, library-owned */
+
+typedef enum {
+  LB_OK = 0,
+  LB_EINVAL = -1,        /* bad argument (null pointer, size, path, overlap) */
+  LB_ENOMEM = -2,        /* device or host allocation failed */
+  LB_EHIP = -3,          /* a HIP runtime call failed (text in lb_last_error) */
+  LB_ENOTREADY = -4,     /* forward before signs and scales of every path */
+  LB_EUNSUPPORTED = -5,  /* valid request the library cannot run here */
+  LB_ETIMEOUT = -6       /* a device-side wait gave up (watchdog) */
+} lb_status;
+
+/* ---------------------------------------------------------------- layers */
+
+/* Create a layer with input width a, output width b, rank s, and one
+ * path (residual = 0) or two (residual = 1), on the current HIP device.
+ * [LB2 column] Ch. 1 names a, b, s and residual; [LB news] Sec. 2 the
+ * structure.  a, b, s >= 1 and a, b, s <= 2^24.  Allocates the device
+ * storage for signs, scales and workspace.  *out is set on success only. */
+lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb_layer **out);
+
+/* Set the sign factors of one path (0, or 1 when residual) from host
+ * canonical words: su is b x ceil(s/32), sv is a x ceil(s/32).  The words
+ * are re-laid out for the device and copied synchronously; bit-exact. */
+lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, const uint32_t *sv);
+
+/* Set the fp16 scales of one path from host arrays: h (b values, row /
+ * output scale), g (a values, column / input scale), l (s values, latent
+ * scale), [LB news] Sec. 2.  Copied synchronously. */
+lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t *g,
+                        const uint16_t *l);
+
+/* y[M x b] = layer(x[M x a]); x, y are device fp16.  M = 0 is a no-op.
+ * M < 64 runs the wave-level binary GEMV path (sign-flip identity on
+ * packed bits); M >= 64 runs the fp16 MFMA path, in which the latent
+ * vector t is rounded once to fp16 before the second product.
+ * Returns LB_ENOTREADY unless every path has signs and scales. */
+lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
+
+/* Read the device signs of one path back into canonical words (padding
+ * bits zero).  Bit-exact inverse of lb_pack_signs; synchronous. */
+lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, uint32_t *sv);
+
+/* Shape queries. */
+lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, int64_t *s, int *residual);
+
+lb_status lb_destroy(lb_layer *L);
+
+/* ------------------------------------------------------- split stages */
+/* The two halves of lb_forward, for callers that keep the latent vector
+ * (the pages note that factorised K/V projections let a cache hold the
+ * latent instead of the full width, [LB news] Sec. 4).
+ * stage1: w[M x P*s] (fp32, device) = l_p * S_V,p^T (g_p * x), path-major
+ *         (columns p*s .. p*s+s-1 belong to path p).
+ * stage2: y[M x b] (fp16) = sum_p h_p * S_U,p w_p.  Any M >= 0. */
+lb_status lb_forward_stage1(const lb_layer *L, const void *x, float *w, int64_t M, void *stream);
+lb_status lb_forward_stage2(const lb_layer *L, const float *w, void *y, int64_t M, void *stream);
+
+/* ---------------------------------------------------------- bit count */
+/* Exact effective bits per weight of [LB2 column] Ch. 1:
+ *   num_bits = P * (s*(a+b+16) + 16*(a+b)),  den = a*b,  P = 1 or 2.
+ * Pure host arithmetic.  LB_EINVAL on overflow or a non-positive size. */
+lb_status lb_eff_bits(int64_t a, int64_t b, int64_t s, int residual, uint64_t *num_bits,
+                      uint64_t *den);
+
+/* Largest rank s >= 0 with eff_bits(a, b, s, residual) <= bpw_num/bpw_den
+ * (the same formula solved for s, floor).  LB_EINVAL when the scale
+ * vectors alone exceed the budget. */
+lb_status lb_rank_for_bpw(int64_t a, int64_t b, uint64_t bpw_num, uint64_t bpw_den, int residual,
+                          int64_t *s);
+
+/* -------------------------------------------------------------- stacks */
+/* A stack is an ordered list of layers grouped into units: the layers of
+ * one unit read the same input and have the same a and b; unit u+1 has
+ * a = unit u's b.  Unit 0 reads the stack input x0.  Unit u+1 reads
+ * fp16(kappa / sqrt(n_u) * sum of unit u's outputs), computed in fp32 from
+ * the fp16 outputs, where n_u is unit u's layer count; the stack output
+ * is the same combine of the last unit.  (The transformer parts between
+ * LittleBit layers are not LittleBit layers; these linear stand-ins keep
+ * the activations O(1).)  E.g. a Llama MLP stack has units [gate, up],
+ * [down] per block.  Layers stay owned by the caller and must outlive the
+ * stack; their signs and scales must be set before lb_stack_create.      */
+lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *unit_sizes,
+                          int n_units, float kappa, lb_stack **out);
+
+/* Run the whole stack on device fp16 x0 [M x a_0] into y [M x b_last].
+ * trace, when not NULL, receives every layer's fp16 output followed by
+ * every unit's fp16 input, each M rows, in stack order (size from
+ * lb_stack_trace_elems).  M < 64 runs one persistent cooperative launch
+ * for the whole sweep when the device can co-schedule it, else (and for
+ * M >= 64) the per-layer kernels in order. */
+lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
+                           void *stream);
+
+/* Number of fp16 elements lb_stack_forward writes to trace for M rows. */
+lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t *elems);
+
+/* Select the execution mode of lb_stack_forward: 0 = automatic, 1 = per
+ * layer kernels only, 2 = persistent only (LB_EUNSUPPORTED if impossible). */
+lb_status lb_stack_set_mode(lb_stack *S, int mode);
+
+lb_status lb_stack_destroy(lb_stack *S);
+
+/* ---------------------------------------------------------- diagnostics */
+const char *lb_status_str(lb_status st);
+const char *lb_last_error(void);
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LB_H */

@@ -40,7 +40,7 @@ def _rng(*key: int) -> np.random.Generator:
 def random_sign_words(rng: np.random.Generator, rows: int, s: int) -> np.ndarray:
     """Uniform random canonical sign words, padding bits cleared."""
     w = words_per_row(s)
-    words = rng.integers(0, 1 << 32, size=(rows, w), dtype=np.uint64).astype(np.uint32)
+    words = rng.integers(0, 1 << 32, size=(rows, w), dtype=np.uint32)
     tail = s % 32
     if tail:
         words[:, -1] &= np.uint32((1 << tail) - 1)
@@ -94,3 +94,40 @@ def kappa(paths: int) -> float:
     wiring scales each combine by kappa = (P * (13/12)^3) ** -0.5.
     """
     return float((paths * (13.0 / 12.0) ** 3) ** -0.5)
+
+
+# ---------------------------------------------------------------------------
+# Workloads: layer shapes of the measured configurations (Llama2-7B and
+# Llama2-70B linear layers at the stated bits per weight).  Pure data.
+# ---------------------------------------------------------------------------
+WORKLOADS = {
+    # name: (seed, M, per-block [(a, b, s, residual)], per-block unit sizes, blocks)
+    "tiny_256": (0, 1, [(256, 256, 32, False)], [1], 1),
+    "llama7b_attn_proj_4096": (1, 1, [(4096, 4096, 86, True)], [1], 1),
+    "llama7b_mlp_stack": (2, 1, [(4096, 11008, 133, True), (4096, 11008, 133, True),
+                                 (11008, 4096, 133, True)], [2, 1], 32),
+    "llama70b_mlp_stack": (3, 1, [(8192, 28672, 302, True), (8192, 28672, 302, True),
+                                  (28672, 8192, 302, True)], [2, 1], 80),
+    "llama7b_full_stack_M128": (4, 128, [(4096, 4096, 290, True)] * 4 +
+                                [(4096, 11008, 431, True), (4096, 11008, 431, True),
+                                 (11008, 4096, 431, True)], [3, 1, 2, 1], 32),
+}
+
+
+def workload(name: str, blocks: int | None = None) -> dict:
+    """Shapes, unit sizes, M and seed of a workload (optionally fewer blocks)."""
+    seed, M, per, units, nb = WORKLOADS[name]
+    nb = nb if blocks is None else int(blocks)
+    layers = []
+    for blk in range(nb):
+        for mi, (a, b, s, res) in enumerate(per):
+            layers.append({"a": a, "b": b, "s": s, "residual": res, "block": blk,
+                           "matrix": mi, "seed": seed})
+    return {"name": name, "seed": seed, "M": M, "layers": layers, "units": list(units) * nb,
+            "blocks": nb, "per_block": len(per)}
+
+
+def workload_layer_inputs(spec: dict) -> list:
+    """Paths of one layer of a workload: stream (seed, block, matrix, path)."""
+    return layer_inputs(spec["a"], spec["b"], spec["s"], spec["residual"], spec["seed"],
+                        spec["block"], spec["matrix"])

@@ -1,0 +1,118 @@
+"""GPU parity of stacks (chained layers) through the C ABI.
+
+Parity is teacher-forced per layer: each layer's fp16 output in the trace
+is compared with the float64 oracle applied to the fp16 input the GPU
+actually fed it, so errors do not compound along the chain.  Each unit
+input is checked against the combine of the previous unit's fp16 outputs
+(fp16 of kappa/sqrt(n) * sum, computed in float64) to within one fp16 ulp.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import lb_synth
+import oracle
+from tests import lbtest
+from tests.lbtest import assert_parity, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lbm():
+    lbtest.torch_dev()
+    return lbtest.ensure_built()
+
+
+def build_stack(lbm, name, blocks=None, keep_paths=True):
+    wl = lb_synth.workload(name, blocks)
+    layers, paths = [], []
+    for spec in wl["layers"]:
+        p = lb_synth.workload_layer_inputs(spec)
+        layers.append(lbm.Layer.from_paths(p))
+        paths.append(p if keep_paths else None)
+    P = 2 if wl["layers"][0]["residual"] else 1
+    S = lbm.Stack(layers, wl["units"], lb_synth.kappa(P))
+    return wl, S, paths
+
+
+def run_stack(lbm, wl, S, M, mode=0):
+    torch = lbtest.torch_dev()
+    a0 = wl["layers"][0]["a"]
+    b_last = wl["layers"][-1]["b"]
+    x0 = lb_synth.activations(M, a0, seed=wl["seed"])
+    xd = lbtest.to_dev(x0)
+    y = torch.empty((M, b_last), dtype=torch.float16, device="cuda")
+    tr = torch.empty(S.trace_elems(M), dtype=torch.float16, device="cuda")
+    S.set_mode(mode)
+    S.forward(xd, y, tr)
+    torch.cuda.synchronize()
+    return x0, y.cpu().numpy(), tr.cpu().numpy()
+
+
+def split_trace(wl, tr, M):
+    Ys, Xs, off = [], [], 0
+    for spec in wl["layers"]:
+        Ys.append(tr[off:off + M * spec["b"]].reshape(M, spec["b"]))
+        off += M * spec["b"]
+    ub = np.cumsum([0] + wl["units"][:-1])
+    for u, b0 in enumerate(ub):
+        a = wl["layers"][b0]["a"]
+        Xs.append(tr[off:off + M * a].reshape(M, a))
+        off += M * a
+    assert off == tr.size
+    return Ys, Xs, ub
+
+
+def check_combine(got, ys, c):
+    """got == fp16(c * sum ys) within one fp16 ulp (float64 reference)."""
+    ref = oracle.combine(ys, c).astype(np.float64)
+    g = got.astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert (np.abs(g - ref) <= ulp).all(), float(np.max(np.abs(g - ref) / ulp))
+
+
+def check_stack(wl, paths, x0, y, tr, M, sample=None):
+    Ys, Xs, ub = split_trace(wl, tr, M)
+    kap = lb_synth.kappa(2 if wl["layers"][0]["residual"] else 1)
+    assert np.array_equal(Xs[0], x0)
+    units = wl["units"]
+    idx = list(range(len(wl["layers"]))) if sample is None else sample
+    unit_of = np.repeat(np.arange(len(units)), units)
+    for li in idx:
+        u = unit_of[li]
+        say(f"[check] layer {li} (unit {u})")
+        p = paths[li] if paths[li] is not None else lb_synth.workload_layer_inputs(wl["layers"][li])
+        assert_parity(Ys[li], oracle.forward(Xs[u], p), f"layer {li}")
+    for u in range(1, len(units)):
+        prev = list(range(ub[u - 1], ub[u - 1] + units[u - 1]))
+        check_combine(Xs[u], [Ys[i] for i in prev], kap / math.sqrt(units[u - 1]))
+    last = list(range(ub[-1], ub[-1] + units[-1]))
+    check_combine(y, [Ys[i] for i in last], kap / math.sqrt(units[-1]))
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_mlp_stack_two_blocks(lbm, M):
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    say(f"[case] mlp stack 2 blocks M={M}")
+    x0, y, tr = run_stack(lbm, wl, S, M)
+    check_stack(wl, paths, x0, y, tr, M)
+
+
+def test_full_block_stack_M128(lbm):
+    wl, S, paths = build_stack(lbm, "llama7b_full_stack_M128", blocks=1)
+    say("[case] full block stack M=128")
+    x0, y, tr = run_stack(lbm, wl, S, 128)
+    check_stack(wl, paths, x0, y, tr, 128)
+
+
+def test_stack_without_trace_matches_trace_run(lbm):
+    torch = lbtest.torch_dev()
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    x0, y, tr = run_stack(lbm, wl, S, 1)
+    xd = lbtest.to_dev(x0)
+    y2 = torch.empty_like(torch.from_numpy(y)).cuda()
+    S.forward(xd, y2, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
