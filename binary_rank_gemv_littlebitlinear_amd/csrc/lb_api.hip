@@ -107,12 +107,63 @@ void transpose32(uint32_t m[32]) {
     }
   }
 }
+
+// m2 of one path (see lb_internal.h): bit (16q + r) of mask i of row tile
+// tau = S_U[16 tau + r, q*Q + i].  32 x 32 bit transposes turn rows of
+// canonical words into per-column 32-row fields.
+void build_m2(const Layer &Ly, int path, const uint32_t *su, std::vector<uint64_t> &m2) {
+  const int64_t b = Ly.b, s = Ly.s, Wk = Ly.Wk, Q = Ly.Q, Qp = Ly.Qp, T = Ly.T16b;
+  m2.assign((size_t)T * Qp, 0);
+  uint32_t blk[32];
+  for (int64_t R = 0; R < (b + 31) / 32; ++R) {
+    for (int64_t C = 0; C < Wk; ++C) {
+      const uint32_t msk = tail_mask(s, C);
+      for (int e = 0; e < 32; ++e) {
+        const int64_t j = 32 * R + e;
+        blk[e] = j < b ? (su[j * Wk + C] & msk) : 0u;
+      }
+      transpose32(blk);  // blk[kk] bit e = S_U[32R + e, 32C + kk]
+      for (int kk = 0; kk < 32; ++kk) {
+        const int64_t k = 32 * C + kk;
+        if (k >= s) break;
+        const int64_t q = k / Q, i = k - q * Q;
+        const int64_t t0 = 2 * R;
+        m2[(size_t)t0 * Qp + i] |= (uint64_t)(blk[kk] & 0xffffu) << (16 * q);
+        if (t0 + 1 < T) m2[(size_t)(t0 + 1) * Qp + i] |= (uint64_t)(blk[kk] >> 16) << (16 * q);
+      }
+    }
+  }
+}
+
+// m1 of all paths: bit (16q + cc) of mask i of (row tile tau, column tile
+// kap) = S_V[16 tau + 4q + i, latent column 16 kap + cc], c = p*s + k.
+void build_m1(const Layer &Ly, std::vector<uint64_t> &m1) {
+  const int64_t a = Ly.a, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L, NCT = Ly.NCT;
+  m1.assign((size_t)Ly.T16a * NCT * 4, 0);
+  std::vector<uint64_t> cat((size_t)(Lc + 63) / 64 + 1);
+  for (int64_t i = 0; i < a; ++i) {
+    std::fill(cat.begin(), cat.end(), 0);
+    for (int p = 0; p < Ly.P; ++p) {
+      const uint32_t *row = Ly.sv_host[p].data() + i * Wk;
+      for (int64_t w = 0; w < Wk; ++w) {
+        const uint64_t v = row[w] & tail_mask(s, w);
+        const int64_t off = p * s + 32 * w;
+        cat[off / 64] |= v << (off % 64);
+        if (off % 64 > 32) cat[off / 64 + 1] |= v >> (64 - off % 64);
+      }
+    }
+    const int64_t tau = i / 16, q = (i % 16) / 4, i4 = i % 4;
+    for (int64_t kap = 0; kap < NCT; ++kap) {
+      const int64_t off = 16 * kap;
+      uint64_t f = cat[off / 64] >> (off % 64);
+      if (off % 64 > 48) f |= cat[off / 64 + 1] << (64 - off % 64);
+      m1[(size_t)(tau * NCT + kap) * 4 + i4] |= (f & 0xffffu) << (16 * q);
+    }
+  }
+}
 }  // namespace
 
-struct lb_layer {
-  Layer ly;
-  DevCtx *dev = nullptr;
-};
+static inline DevCtx *ctx_of(const lb_layer *L) { return static_cast<DevCtx *>(L->ctx); }
 
 // --------------------------------------------------------- workspace need
 static size_t layer_ws_need(const Layer &Ly, const DeviceInfo &dev) {
@@ -145,12 +196,16 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
   Layer &Ly = L->ly;
   Ly.a = a; Ly.b = b; Ly.s = s; Ly.P = residual ? 2 : 1; Ly.device = device;
   Ly.L = Ly.P * s; Ly.R1 = (a + 31) / 32; Ly.Wk = (s + 31) / 32;
-  L->dev = dc;
+  Ly.T16a = (a + 15) / 16; Ly.T16b = (b + 15) / 16; Ly.NCT = (Ly.L + 15) / 16;
+  Ly.Q = (s + 3) / 4; Ly.Qp = (Ly.Q + 3) / 4 * 4;
+  L->ctx = dc;
   struct Alloc { void **p; size_t n; };
   Alloc allocs[] = {
       {(void **)&Ly.sv1, (size_t)Ly.R1 * Ly.L * 4}, {(void **)&Ly.su2, (size_t)Ly.P * Ly.Wk * b * 4},
       {(void **)&Ly.h, (size_t)Ly.P * b * 2},       {(void **)&Ly.g, (size_t)Ly.P * a * 2},
-      {(void **)&Ly.l, (size_t)Ly.P * s * 2}};
+      {(void **)&Ly.l, (size_t)Ly.P * s * 2},
+      {(void **)&Ly.m1, (size_t)Ly.T16a * Ly.NCT * 4 * 8},
+      {(void **)&Ly.m2, (size_t)Ly.P * Ly.T16b * Ly.Qp * 8}};
   for (auto &al : allocs) {
     hipError_t e = hipMalloc(al.p, al.n);
     if (e != hipSuccess) {
@@ -176,7 +231,7 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   if (!L) return LB_OK;
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
-  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l};
+  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.m1, Ly.m2};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   delete L;
@@ -232,6 +287,21 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
       }
     }
     LB_HIP(hipMemcpy(Ly.sv1, v1.data(), v1.size() * 4, hipMemcpyHostToDevice));
+  }
+  // lane-mask layouts
+  {
+    std::vector<uint64_t> m2;
+    build_m2(Ly, path, su, m2);
+    LB_HIP(hipMemcpy(Ly.m2 + (size_t)path * Ly.T16b * Ly.Qp, m2.data(), m2.size() * 8,
+                     hipMemcpyHostToDevice));
+    Ly.sv_host[path].assign(sv, sv + (size_t)a * Wk);
+    bool all = true;
+    for (int p = 0; p < Ly.P; ++p) all = all && !Ly.sv_host[p].empty();
+    if (all) {
+      std::vector<uint64_t> m1;
+      build_m1(Ly, m1);
+      LB_HIP(hipMemcpy(Ly.m1, m1.data(), m1.size() * 8, hipMemcpyHostToDevice));
+    }
   }
   Ly.signs_set[path] = true;
   return LB_OK;
@@ -296,7 +366,7 @@ static lb_status check_io(const Layer &Ly, const void *x, const void *y, int64_t
 static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
                               hipStream_t st) {
   const Layer &Ly = L->ly;
-  DevCtx *dc = L->dev;
+  DevCtx *dc = ctx_of(L);
   if (M < 64) {
     const int nch = wave_nchunk(Ly, M, dc->info);
     float *part = reinterpret_cast<float *>(dc->ws);
@@ -330,7 +400,7 @@ extern "C" lb_status lb_forward_stage1(const lb_layer *L, const void *x, float *
   lb_status st = check_io(Ly, x, w, M, "lb_forward_stage1");
   if (st != LB_OK || M == 0) return st;
   DeviceGuard dg(Ly.device);
-  DevCtx *dc = L->dev;
+  DevCtx *dc = ctx_of(L);
   // Rows in blocks of 63 so the partial buffer stays within the workspace.
   for (int64_t m0 = 0; m0 < M; m0 += 63) {
     const int64_t Mc = (M - m0) < 63 ? (M - m0) : 63;
@@ -496,6 +566,18 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
   return LB_OK;
 }
 
+extern "C" lb_status lb_stack_check(lb_stack *S) {
+  if (!S) return fail(LB_EINVAL, "lb_stack_check: NULL stack");
+  DeviceGuard dg(S->device);
+  LB_HIP(hipDeviceSynchronize());
+  if (S->persist) {
+    std::string msg;
+    lb_status st = persist_check(S->persist, &msg);
+    if (st != LB_OK) return fail(st, msg);
+  }
+  return LB_OK;
+}
+
 extern "C" lb_status lb_stack_destroy(lb_stack *S) {
   if (!S) return LB_OK;
   DeviceGuard dg(S->device);
@@ -541,10 +623,14 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     for (int u = 0; u < U; ++u) { tX[u] = p; p += M * S->layers[S->unit_begin[u]]->ly.a; }
   }
   const bool can_persist = S->persist && M <= persist_max_rows();
-  if (S->mode == 2 && !can_persist) return fail(LB_EUNSUPPORTED, "lb_stack_forward: persistent mode cannot run this M");
+  if (S->mode == 2 && !can_persist)
+    return fail(LB_EUNSUPPORTED, "lb_stack_forward: persistent mode cannot run this M");
   if (can_persist && S->mode != 1) {
-    return persist_run(S->persist, (const uint16_t *)x0, (uint16_t *)y, trace ? tY.data() : nullptr,
-                       trace ? tX.data() : nullptr, M, st);
+    std::string msg;
+    lb_status ps = persist_run(S->persist, (const uint16_t *)x0, (uint16_t *)y, (uint16_t *)trace, M,
+                               st, &msg);
+    if (ps != LB_OK) return fail(ps, msg);
+    return LB_OK;
   }
   lb_status rs = stack_reserve(S, M);
   if (rs != LB_OK) return rs;

@@ -20,10 +20,30 @@
 //
 // Padding bits (i >= a in the last row group of sv1, k >= s in the last
 // word of su2) are zero, so they contribute nothing.
+//
+// Lane-mask layouts for the wave-level kernels.  A 64-bit mask holds one
+// bit per lane of a 64-lane wave; the kernels turn it into a per-lane
+// predicate and add a broadcast value in the lanes whose bit is set
+// (sign-flip identity).  Lanes are split 16 x 4: lane = 16*q + r.
+//
+//   T16a = ceil(a / 16), T16b = ceil(b / 16) row tiles of 16 rows
+//   NCT  = ceil(L / 16)  column tiles of 16 latent columns
+//   Q    = ceil(s / 4),  Qp = Q rounded up to a multiple of 4
+//
+//   m1[(tau * NCT + kap) * 4 + i]          (uint64, T16a x NCT x 4)
+//       bit (16 q + cc) = S_V[16 tau + 4 q + i, column 16 kap + cc]
+//       (columns of the concatenated latent c = p*s + k; lane 16q+cc of
+//       the first product accumulates column 16kap+cc over rows 4q+i).
+//   m2[((p * T16b + tau) * Qp) + i]         (uint64, P x T16b x Qp)
+//       bit (16 q + r) = S_U,p[16 tau + r, q*Q + i]   (0 if q*Q+i >= s)
+//       (lane 16q+r of the second product accumulates row 16tau+r over
+//       the latent quarter q).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <vector>
 
 #include "../../include/lb.h"
 
@@ -48,6 +68,12 @@ struct Layer {
   uint16_t *h = nullptr;    // P * b
   uint16_t *g = nullptr;    // P * a
   uint16_t *l = nullptr;    // P * s
+  int64_t T16a = 0, T16b = 0, NCT = 0, Q = 0, Qp = 0;
+  uint64_t *m1 = nullptr;   // T16a * NCT * 4
+  uint64_t *m2 = nullptr;   // P * T16b * Qp
+  // host copies of the canonical S_V words of each path, kept until every
+  // path is packed (m1 interleaves the paths' columns)
+  std::vector<uint32_t> sv_host[2];
   // workspace: stage-1 partials / latent vectors, sized at create time
   float *ws = nullptr;
   size_t ws_bytes = 0;
@@ -57,6 +83,17 @@ struct Layer {
     return true;
   }
 };
+
+}  // namespace lbi
+
+// The C ABI's opaque layer handle.
+struct lb_layer {
+  lbi::Layer ly;
+  void *ctx = nullptr;  // the device context (workspace owner)
+  void *plan = nullptr; // single-layer persistent plan (M = 1), may be null
+};
+
+namespace lbi {
 
 // ------------------------------------------------------------- launchers
 // All return hipError_t of the launch (no synchronisation).

@@ -1,11 +1,10 @@
 // Persistent whole-stack sweep for decode-sized M (one cooperative launch).
 #pragma once
 
+#include <string>
 #include <vector>
 
 #include "lb_internal.h"
-
-struct lb_layer;
 
 namespace lbi {
 
@@ -18,7 +17,11 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
                         PersistPlan **out);
 void persist_free(PersistPlan *p);
 int64_t persist_max_rows();
-lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *const *traceY,
-                      uint16_t *const *traceX, int64_t M, hipStream_t st);
+// Launch the sweep for M rows (M <= persist_max_rows()).  trace, when not
+// null, receives every layer's output then every unit's input (M = 1).
+lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace, int64_t M,
+                      hipStream_t st, std::string *msg);
+// Synchronise and report a device-side wait timeout of an earlier launch.
+lb_status persist_check(PersistPlan *p, std::string *msg);
 
 }  // namespace lbi

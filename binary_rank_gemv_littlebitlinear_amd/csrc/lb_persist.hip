@@ -1,21 +1,597 @@
-// Persistent whole-stack sweep (not yet available: every stack runs the
-// per-layer kernels).
+// Persistent whole-stack sweep for one decode row (M = 1).
+//
+// [LB news] Sec. 2: each layer is two small binary products with
+// elementwise scales; the residual path is a second factorisation whose
+// output is added.  A stack chains layers (units of layers that share an
+// input, combined in fp32 and rounded to fp16 between units).
+//
+// One launch of G = #CU workgroups (one per CU) runs the whole sweep as
+// U + 1 phases.  Workgroup w owns a fixed set of 16-row tiles of every
+// width, so the second product of unit u-1 (rows j), the combine and the
+// first product of unit u (rows i = j) are local to the workgroup:
+//
+//   phase 0     : X_0 rows -> partial t of unit 0 over own rows
+//   phase u     : t_{u-1} -> y rows of unit u-1 -> combine -> X_u rows
+//                 -> partial t of unit u over own rows
+//   phase U     : t_{U-1} -> y rows -> final combine -> output rows
+//
+// Between phases the partial latent vectors of all workgroups are
+// all-reduced (reduce-scatter over slices, then broadcast), with flag
+// words that carry a generation number.  Every exchanged word is written
+// and read with device-coherent (sc1) relaxed atomics; a store's
+// completion (s_waitcnt) precedes the flag that publishes it.  All waits
+// are bounded: on timeout a device error word is set, every workgroup
+// leaves, and the host returns LB_ETIMEOUT.
+//
+// Products use the sign-flip identity  sum_i s_i v_i = 2 sum_{bit} v_i -
+// sum_i v_i  with 64-bit lane masks (one bit per lane of a wave): each
+// mask becomes a lane predicate (v_cndmask on an SGPR pair) and the
+// broadcast value is added where the bit is set.  Mask layouts m1 / m2
+// are described in lb_internal.h.
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
 #include "lb_persist.h"
 
 namespace lbi {
 
-struct PersistPlan {};
+constexpr int kThreads = 512;           // 8 waves
+constexpr int kWaves = kThreads / 64;
+constexpr int kTMax = 8;                // row tiles per workgroup and width
+constexpr int kKMax = 16;               // column tiles per wave in the first product
+constexpr int kMaxUnitLayers = 8;
+constexpr int kLuMax = 4096;            // latent columns per unit
+constexpr long kSpin = 4000000;         // polls before a wait gives up
 
-lb_status persist_build(const std::vector<lb_layer *> &, const std::vector<int> &,
-                        const std::vector<int> &, float, int, PersistPlan **out) {
-  *out = nullptr;
-  return LB_EUNSUPPORTED;
+typedef __attribute__((address_space(4))) const uint64_t cmask_t;
+
+struct PLayer {
+  const uint64_t *m1, *m2;
+  const uint16_t *h, *g, *l;
+  int a, b, s, P, Q, Qp, NCT, L, T16a, T16b;
+  int col0, ct0;     // first latent column / column tile within the unit
+  int64_t trace_y;   // element offset of this layer's output in the trace, -1 if none
+};
+
+struct PUnit {
+  int first, n;
+  int a, b;
+  int Lu, nct;
+  float c_out;       // kappa / sqrt(n): combine of this unit's outputs
+  int64_t trace_x;   // element offset of this unit's input in the trace
+};
+
+struct PArgs {
+  const PUnit *units;
+  const PLayer *layers;
+  int nunits;
+  const uint16_t *x0;
+  uint16_t *y;
+  uint16_t *trace;   // may be null
+  unsigned gen_base;
+  float *xpart;      // [G][G][spw_max] partial slices (transposed)
+  float *xT;         // [kLuMax] reduced latent
+  unsigned *flag1;   // [G]
+  unsigned *flag2;   // [G]
+  unsigned *err;
+  int spw_max;
+};
+
+struct PersistPlan {
+  int device = 0;
+  int G = 0;
+  int nunits = 0, nlayers = 0;
+  size_t lds = 0;
+  PUnit *d_units = nullptr;
+  PLayer *d_layers = nullptr;
+  std::vector<PUnit> h_units;
+  std::vector<PLayer> h_layers;
+  float *xpart = nullptr, *xT = nullptr;
+  unsigned *flags = nullptr;  // flag1 [G], flag2 [G], err [64]
+  int spw_max = 0;
+  unsigned gen = 0;
+  bool broken = false;
+};
+
+// ----------------------------------------------------------- primitives
+__device__ __forceinline__ float h2f(uint16_t v) { return __half2float(__ushort_as_half(v)); }
+__device__ __forceinline__ uint16_t f2h(float v) { return __half_as_ushort(__float2half_rn(v)); }
+__device__ __forceinline__ unsigned ld_u(unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-void persist_free(PersistPlan *p) { delete p; }
-int64_t persist_max_rows() { return 0; }
-lb_status persist_run(PersistPlan *, const uint16_t *, uint16_t *, uint16_t *const *,
-                      uint16_t *const *, int64_t, hipStream_t) {
-  return LB_EUNSUPPORTED;
+__device__ __forceinline__ void st_u(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_f(float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool reached(unsigned v, unsigned gen) { return (int)(v - gen) >= 0; }
+
+// Tiles [t0, t1) of a width with `tiles` 16-row tiles owned by workgroup w.
+__device__ __forceinline__ void my_tiles(int tiles, int G, int w, int &t0, int &t1) {
+  t0 = (int)(((long)tiles * w) / G);
+  t1 = (int)(((long)tiles * (w + 1)) / G);
+}
+
+// Wait until flags[0..n) all reached gen (threads < n poll one flag each).
+// Returns false on timeout or device error.
+__device__ bool wait_flags(unsigned *flags, int n, unsigned gen, unsigned *err) {
+  long spins = 0;
+  while (true) {
+    int ok = 1;
+    if ((int)threadIdx.x < n) ok = reached(ld_u(&flags[threadIdx.x]), gen);
+    if (__syncthreads_and(ok)) return true;
+    if (++spins > kSpin) {
+      if (threadIdx.x == 0) atomicOr(err, 1u);
+      return false;
+    }
+    if (spins > 64) __builtin_amdgcn_s_sleep(1);
+    const int bad = (threadIdx.x == 0) ? (int)ld_u(err) : 0;
+    if (__syncthreads_or(bad)) return false;
+  }
+}
+
+// -------------------------------------------------------- the exchange
+// part (LDS, Lu floats) of every workgroup -> T (LDS, Lu floats) = sum.
+// Slice m (columns m*spw ..) is reduced by workgroup m in fixed order.
+__device__ bool exchange(const float *part, float *T, float *red, int Lu, unsigned gen,
+                         const PArgs &A) {
+  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+  const int spw = (Lu + G - 1) / G;
+  for (int c = t; c < Lu; c += kThreads) {
+    const int m = c / spw, j = c - m * spw;
+    st_f(&A.xpart[((size_t)m * G + w) * A.spw_max + j], part[c]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0) st_u(&A.flag1[w], gen);
+  if (w * spw < Lu) {
+    if (!wait_flags(A.flag1, G, gen, A.err)) return false;
+    const int nj = (Lu - w * spw) < spw ? (Lu - w * spw) : spw;
+    for (int j = 0; j < nj; ++j)
+      red[j * kThreads + t] = t < G ? ld_f(&A.xpart[((size_t)w * G + t) * A.spw_max + j]) : 0.f;
+    __syncthreads();
+    for (int st = kThreads / 2; st > 0; st >>= 1) {
+      if (t < st)
+        for (int j = 0; j < nj; ++j) red[j * kThreads + t] += red[j * kThreads + t + st];
+      __syncthreads();
+    }
+    if (t < nj) st_f(&A.xT[w * spw + t], red[t * kThreads]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0) st_u(&A.flag2[w], gen);
+  }
+  const int nsl = (Lu + spw - 1) / spw;
+  if (!wait_flags(A.flag2, nsl, gen, A.err)) return false;
+  for (int c = t; c < Lu; c += kThreads) T[c] = ld_f(&A.xT[c]);
+  __syncthreads();
+  return true;
+}
+
+// ------------------------------------------------------ LDS arrangement
+struct Lds {
+  float *xs;     // [16*kTMax] fp32 copy of this workgroup's input rows (fp16 values)
+  float *z;      // [kMaxUnitLayers*2][16*kTMax]  g * x per layer and path
+  float *zsum;   // [kMaxUnitLayers*2]
+  float *part;   // [kLuMax]
+  float *T;      // [kLuMax] reduced t, then w = l*t
+  float *wq;     // [kLuMax + pad] quarter-major w per layer and path
+  float *wsum;   // [kMaxUnitLayers*2]
+  float *ysum;   // [16*kTMax] combine accumulator
+  float *red;    // [kWaves][2][kTMax][64] (aliases the exchange scratch)
+  int *wq_off;   // [kMaxUnitLayers*2] float offset of each (layer, path) block in wq
+};
+
+__device__ float block_sum(float v, float *scratch) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float tot = 0.f;
+  for (int i = 0; i < kWaves; ++i) tot += scratch[i];
+  __syncthreads();
+  return tot;
+}
+
+// ----------------------------------------------------------- products
+// First product of unit U over row tiles [t0, t1) of width a:
+// part[col] = 2 * sum_{rows, bit} z - sum_rows z   for every latent column.
+__device__ void first_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &S) {
+  const int nt = t1 - t0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4, cc = lane & 15;
+  // z = g * x per layer and path, and its sums
+  for (int m = 0; m < U.n; ++m) {
+    const PLayer &Ly = A.layers[U.first + m];
+    for (int p = 0; p < Ly.P; ++p) {
+      float *z = S.z + (m * 2 + p) * 16 * kTMax;
+      float v = 0.f;
+      for (int r = threadIdx.x; r < 16 * nt; r += kThreads) {
+        const int i = 16 * t0 + r;
+        const float zi = i < U.a ? h2f(Ly.g[(size_t)p * Ly.a + i]) * S.xs[r] : 0.f;
+        z[r] = zi;
+        v += zi;
+      }
+      v = block_sum(v, S.red);
+      if (threadIdx.x == 0) S.zsum[m * 2 + p] = v;
+    }
+  }
+  __syncthreads();
+  // column tiles round-robin over waves; per tile: layer, mask base, z offset
+  const uint64_t *mb[kKMax];
+  int mstride[kKMax], zoff[kKMax], lidx[kKMax], colb[kKMax];
+#pragma unroll
+  for (int k = 0; k < kKMax; ++k) {
+    const int kap_u = wave + k * kWaves;
+    lidx[k] = -1; mb[k] = nullptr; mstride[k] = 0; zoff[k] = 0; colb[k] = 0;
+    if (kap_u < U.nct) {
+      int m = 0;
+      while (m + 1 < U.n && A.layers[U.first + m + 1].ct0 <= kap_u) ++m;
+      const PLayer &Ly = A.layers[U.first + m];
+      const int kap = kap_u - Ly.ct0;
+      const int col = 16 * kap + cc;
+      const int p = (col >= Ly.s && col < Ly.L) ? 1 : 0;
+      lidx[k] = m;
+      mb[k] = Ly.m1 + ((size_t)t0 * Ly.NCT + kap) * 4;
+      mstride[k] = Ly.NCT * 4;
+      zoff[k] = (m * 2 + p) * 16 * kTMax + 4 * q;
+      colb[k] = Ly.col0 + 16 * kap;
+    }
+  }
+  float acc[kKMax];
+#pragma unroll
+  for (int k = 0; k < kKMax; ++k) acc[k] = 0.f;
+  for (int t = 0; t < nt; ++t) {
+#pragma unroll
+    for (int k = 0; k < kKMax; ++k) {
+      if (lidx[k] >= 0) {
+        const float4 zv = *reinterpret_cast<const float4 *>(S.z + zoff[k] + 16 * t);
+        cmask_t *mk = (cmask_t *)(mb[k] + (size_t)t * mstride[k]);
+        const uint64_t k0 = mk[0], k1 = mk[1], k2 = mk[2], k3 = mk[3];
+        float a0 = acc[k];
+        a0 += __builtin_amdgcn_inverse_ballot_w64(k0) ? zv.x : 0.f;
+        a0 += __builtin_amdgcn_inverse_ballot_w64(k1) ? zv.y : 0.f;
+        a0 += __builtin_amdgcn_inverse_ballot_w64(k2) ? zv.z : 0.f;
+        a0 += __builtin_amdgcn_inverse_ballot_w64(k3) ? zv.w : 0.f;
+        acc[k] = a0;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kKMax; ++k) {
+    float v = acc[k];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (lidx[k] >= 0 && q == 0) {
+      const PLayer &Ly = A.layers[U.first + lidx[k]];
+      const int col = colb[k] - Ly.col0 + cc;
+      if (col < Ly.L) {
+        const int p = col < Ly.s ? 0 : 1;
+        S.part[colb[k] + cc] = 2.f * v - S.zsum[lidx[k] * 2 + p];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// After the exchange: w = l * t per layer/path in quarter-major layout
+// wq[(q * Qp) + i] = w[q*Q + i] (0 past s), and the sums of w.
+__device__ void prepare_w(const PArgs &A, const PUnit &U, Lds &S) {
+  int off = 0;
+  for (int m = 0; m < U.n; ++m) {
+    const PLayer &Ly = A.layers[U.first + m];
+    for (int p = 0; p < Ly.P; ++p) {
+      if (threadIdx.x == 0) S.wq_off[m * 2 + p] = off;
+      float *wq = S.wq + off;
+      float v = 0.f;
+      for (int e = threadIdx.x; e < 4 * Ly.Qp; e += kThreads) {
+        const int q = e / Ly.Qp, i = e - q * Ly.Qp;
+        const int k = q * Ly.Q + i;
+        float wv = 0.f;
+        if (i < Ly.Q && k < Ly.s) wv = h2f(Ly.l[(size_t)p * Ly.s + k]) * S.T[Ly.col0 + p * Ly.s + k];
+        wq[e] = wv;
+        v += wv;
+      }
+      v = block_sum(v, S.red);
+      if (threadIdx.x == 0) S.wsum[m * 2 + p] = v;
+      off += 4 * Ly.Qp;
+    }
+  }
+  __syncthreads();
+}
+
+// Second product of unit U over row tiles [t0, t1) of width b; outputs
+// each layer's fp16 y and accumulates the combine in S.ysum.
+__device__ void second_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &S) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  for (int r = threadIdx.x; r < 16 * kTMax; r += kThreads) S.ysum[r] = 0.f;
+  for (int tb = t0; tb < t1; tb += kTMax) {
+    const int nt = (t1 - tb) < kTMax ? (t1 - tb) : kTMax;
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &Ly = A.layers[U.first + m];
+      const int nchunk = Ly.Qp / 4;          // chunks of 4 masks per path
+      const int total = Ly.P * nchunk;
+      float acc[2][kTMax];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int t = 0; t < kTMax; ++t) acc[p][t] = 0.f;
+      for (int ch = wave; ch < total; ch += kWaves) {
+        const int p = ch / nchunk, i0 = (ch - p * nchunk) * 4;
+        const float4 wv = *reinterpret_cast<const float4 *>(S.wq + S.wq_off[m * 2 + p] + q * Ly.Qp + i0);
+        cmask_t *base = (cmask_t *)(Ly.m2 + ((size_t)p * Ly.T16b + tb) * Ly.Qp + i0);
+#pragma unroll
+        for (int t = 0; t < kTMax; ++t) {
+          if (t < nt) {
+            cmask_t *mk = base + (size_t)t * Ly.Qp;
+            const uint64_t k0 = mk[0], k1 = mk[1], k2 = mk[2], k3 = mk[3];
+            float a0 = p == 0 ? acc[0][t] : acc[1][t];
+            a0 += __builtin_amdgcn_inverse_ballot_w64(k0) ? wv.x : 0.f;
+            a0 += __builtin_amdgcn_inverse_ballot_w64(k1) ? wv.y : 0.f;
+            a0 += __builtin_amdgcn_inverse_ballot_w64(k2) ? wv.z : 0.f;
+            a0 += __builtin_amdgcn_inverse_ballot_w64(k3) ? wv.w : 0.f;
+            if (p == 0) acc[0][t] = a0; else acc[1][t] = a0;
+          }
+        }
+      }
+      // cross-wave reduction
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int t = 0; t < kTMax; ++t)
+          S.red[((wave * 2 + p) * kTMax + t) * 64 + lane] = acc[p][t];
+      __syncthreads();
+      for (int e = threadIdx.x; e < 16 * nt; e += kThreads) {
+        const int t = e >> 4, r = e & 15;
+        const int j = 16 * (tb + t) + r;
+        float yv = 0.f;
+        for (int p = 0; p < Ly.P; ++p) {
+          float sacc = 0.f;
+          for (int wv2 = 0; wv2 < kWaves; ++wv2)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) sacc += S.red[((wv2 * 2 + p) * kTMax + t) * 64 + 16 * qq + r];
+          const float u = 2.f * sacc - S.wsum[m * 2 + p];
+          if (j < U.b) yv += h2f(Ly.h[(size_t)p * Ly.b + j]) * u;
+        }
+        if (j < U.b) {
+          const uint16_t y16 = f2h(yv);
+          if (A.trace && Ly.trace_y >= 0) A.trace[Ly.trace_y + j] = y16;
+          S.ysum[16 * (tb - t0 + t) + r] += h2f(y16);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+}
+
+// --------------------------------------------------------------- kernel
+__global__ void __launch_bounds__(kThreads)
+k_persist(PArgs A) {
+  extern __shared__ __align__(16) float smem[];
+  Lds S;
+  {
+    float *p = smem;
+    S.xs = p; p += 16 * kTMax * 8;  // up to 8 batches of tiles
+    S.z = p; p += kMaxUnitLayers * 2 * 16 * kTMax;
+    S.zsum = p; p += kMaxUnitLayers * 2;
+    S.wsum = p; p += kMaxUnitLayers * 2;
+    S.wq_off = reinterpret_cast<int *>(p); p += kMaxUnitLayers * 2;
+    S.part = p; p += kLuMax;
+    S.T = p; p += kLuMax;
+    S.wq = p; p += kLuMax + 64 * kMaxUnitLayers;
+    S.ysum = p; p += 16 * kTMax * 8;
+    S.red = p;  // kWaves*2*kTMax*64 floats, also >= 16*kThreads for the exchange
+  }
+  const int G = gridDim.x, w = blockIdx.x;
+  const int U = A.nunits;
+  for (int ph = 0; ph <= U; ++ph) {
+    {
+      const int bad = (threadIdx.x == 0) ? (int)ld_u(A.err) : 0;
+      if (__syncthreads_or(bad)) return;
+    }
+    // ---- input rows of this phase: width = units[ph].a (or last b)
+    int t0, t1;
+    if (ph == 0) {
+      const PUnit &U0 = A.units[0];
+      my_tiles((U0.a + 15) / 16, G, w, t0, t1);
+      for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
+        const int i = 16 * t0 + r;
+        const uint16_t v = i < U0.a ? A.x0[i] : (uint16_t)0;
+        S.xs[r] = h2f(v);
+        if (A.trace && U0.trace_x >= 0 && i < U0.a) A.trace[U0.trace_x + i] = v;
+      }
+      __syncthreads();
+    } else {
+      const PUnit &Up = A.units[ph - 1];
+      my_tiles((Up.b + 15) / 16, G, w, t0, t1);
+      if (t1 - t0 > kTMax * 8) { if (threadIdx.x == 0) atomicOr(A.err, 2u); return; }
+      prepare_w(A, Up, S);
+      second_product(A, Up, t0, t1, S);
+      // combine: X = fp16(c * sum y)
+      for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
+        const int j = 16 * t0 + r;
+        const uint16_t v = f2h(Up.c_out * S.ysum[r]);
+        S.xs[r] = j < Up.b ? h2f(v) : 0.f;
+        if (j < Up.b) {
+          if (ph == U) {
+            A.y[j] = v;
+          } else if (A.trace && A.units[ph].trace_x >= 0) {
+            A.trace[A.units[ph].trace_x + j] = v;
+          }
+        }
+      }
+      __syncthreads();
+      if (ph == U) break;
+    }
+    // ---- first product of unit ph and the exchange
+    const PUnit &Uc = A.units[ph];
+    if (t1 - t0 > kTMax) { if (threadIdx.x == 0) atomicOr(A.err, 2u); return; }
+    first_product(A, Uc, t0, t1, S);
+    if (!exchange(S.part, S.T, S.red, Uc.Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
+  }
+}
+
+// ------------------------------------------------------------------ host
+static size_t lds_bytes() {
+  size_t f = 16 * kTMax * 8 + kMaxUnitLayers * 2 * 16 * kTMax + kMaxUnitLayers * 2 * 3 + kLuMax * 2 +
+             kLuMax + 64 * kMaxUnitLayers + 16 * kTMax * 8;
+  size_t red = (size_t)kWaves * 2 * kTMax * 64;
+  const size_t red_x = (size_t)16 * kThreads;
+  if (red_x > red) red = red_x;
+  return (f + red) * sizeof(float) + 256;
+}
+
+int64_t persist_max_rows() { return 1; }
+
+lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector<int> &unit_begin,
+                        const std::vector<int> &unit_size, float kappa, int device,
+                        PersistPlan **out) {
+  *out = nullptr;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return LB_EHIP;
+  const int G = prop.multiProcessorCount;
+  if (G < 1 || G > kThreads) return LB_EUNSUPPORTED;
+  PersistPlan *P = new PersistPlan();
+  P->device = device;
+  P->G = G;
+  P->nunits = (int)unit_begin.size();
+  P->nlayers = (int)layers.size();
+  int64_t ty = 0;
+  for (auto *Lr : layers) ty += Lr->ly.b;
+  int64_t tx = ty;
+  int spw_max = 1;
+  for (int u = 0; u < P->nunits; ++u) {
+    PUnit U{};
+    U.first = unit_begin[u];
+    U.n = unit_size[u];
+    const Layer &L0 = layers[U.first]->ly;
+    U.a = (int)L0.a;
+    U.b = (int)L0.b;
+    U.c_out = kappa / std::sqrt((float)U.n);
+    U.trace_x = tx;
+    tx += U.a;
+    int col = 0, ct = 0;
+    int64_t yoff = 0;
+    for (int i = 0; i < U.first; ++i) yoff += layers[i]->ly.b;
+    if (U.n > kMaxUnitLayers) { delete P; return LB_EUNSUPPORTED; }
+    for (int m = 0; m < U.n; ++m) {
+      const Layer &Ly = layers[U.first + m]->ly;
+      if (Ly.P > 2) { delete P; return LB_EUNSUPPORTED; }
+      PLayer D{};
+      D.m1 = Ly.m1; D.m2 = Ly.m2; D.h = Ly.h; D.g = Ly.g; D.l = Ly.l;
+      D.a = (int)Ly.a; D.b = (int)Ly.b; D.s = (int)Ly.s; D.P = Ly.P;
+      D.Q = (int)Ly.Q; D.Qp = (int)Ly.Qp; D.NCT = (int)Ly.NCT; D.L = (int)Ly.L;
+      D.T16a = (int)Ly.T16a; D.T16b = (int)Ly.T16b;
+      D.col0 = col; D.ct0 = ct;
+      D.trace_y = yoff;
+      yoff += Ly.b;
+      col += (int)Ly.L;
+      ct += (int)Ly.NCT;
+      P->h_layers.push_back(D);
+    }
+    U.Lu = col;
+    U.nct = ct;
+    if (U.Lu > kLuMax || (U.nct + kWaves - 1) / kWaves > kKMax) { delete P; return LB_EUNSUPPORTED; }
+    // row tiles per workgroup must fit the per-phase buffers
+    const int ta = ((U.a + 15) / 16 + G - 1) / G, tb = ((U.b + 15) / 16 + G - 1) / G;
+    if (ta > kTMax || tb > kTMax) { delete P; return LB_EUNSUPPORTED; }
+    // wq capacity: sum over layers/paths of 4*Qp
+    int wq = 0;
+    for (int m = 0; m < U.n; ++m) wq += layers[U.first + m]->ly.P * 4 * (int)layers[U.first + m]->ly.Qp;
+    if (wq > kLuMax + 64 * kMaxUnitLayers) { delete P; return LB_EUNSUPPORTED; }
+    const int spw = (U.Lu + G - 1) / G;
+    if (spw > 16) { delete P; return LB_EUNSUPPORTED; }
+    if (spw > spw_max) spw_max = spw;
+    P->h_units.push_back(U);
+  }
+  // units must chain
+  for (int u = 1; u < P->nunits; ++u)
+    if (P->h_units[u].a != P->h_units[u - 1].b) { delete P; return LB_EINVAL; }
+  P->spw_max = spw_max;
+  P->lds = lds_bytes();
+  if (P->lds > (size_t)prop.sharedMemPerBlock) { delete P; return LB_EUNSUPPORTED; }
+  bool ok = hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
+            hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
+            hipMalloc(&P->xpart, sizeof(float) * (size_t)G * G * spw_max) == hipSuccess &&
+            hipMalloc(&P->xT, sizeof(float) * kLuMax) == hipSuccess &&
+            hipMalloc(&P->flags, sizeof(unsigned) * (2 * (size_t)G + 64)) == hipSuccess;
+  ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits, hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers, hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemset(P->flags, 0, sizeof(unsigned) * (2 * (size_t)G + 64)) == hipSuccess;
+  ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)P->lds) == hipSuccess;
+  int occ = 0;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_persist, kThreads, P->lds) == hipSuccess;
+  if (!ok || occ < 1) {
+    persist_free(P);
+    return ok ? LB_EUNSUPPORTED : LB_EHIP;
+  }
+  *out = P;
+  return LB_OK;
+}
+
+void persist_free(PersistPlan *p) {
+  if (!p) return;
+  if (p->d_units) (void)hipFree(p->d_units);
+  if (p->d_layers) (void)hipFree(p->d_layers);
+  if (p->xpart) (void)hipFree(p->xpart);
+  if (p->xT) (void)hipFree(p->xT);
+  if (p->flags) (void)hipFree(p->flags);
+  delete p;
+}
+
+lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace,
+                      int64_t M, hipStream_t st, std::string *msg) {
+  if (M != 1) return LB_EUNSUPPORTED;
+  if (p->broken) {
+    // a previous launch timed out: reset the flags before reuse
+    if (hipMemset(p->flags, 0, sizeof(unsigned) * (2 * (size_t)p->G + 64)) != hipSuccess) return LB_EHIP;
+    p->gen = 0;
+    p->broken = false;
+  }
+  PArgs A{};
+  A.units = p->d_units;
+  A.layers = p->d_layers;
+  A.nunits = p->nunits;
+  A.x0 = x0;
+  A.y = y;
+  A.trace = trace;
+  A.gen_base = p->gen;
+  A.xpart = p->xpart;
+  A.xT = p->xT;
+  A.flag1 = p->flags;
+  A.flag2 = p->flags + p->G;
+  A.err = p->flags + 2 * p->G;
+  A.spw_max = p->spw_max;
+  hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    if (msg) *msg = std::string("persistent launch: ") + hipGetErrorString(e);
+    return LB_EHIP;
+  }
+  p->gen += (unsigned)p->nunits;
+  return LB_OK;
+}
+
+lb_status persist_check(PersistPlan *p, std::string *msg) {
+  unsigned e = 0;
+  if (hipMemcpy(&e, p->flags + 2 * p->G, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+    return LB_EHIP;
+  if (e) {
+    p->broken = true;
+    if (msg) *msg = "persistent sweep: a device-side wait timed out (err=" + std::to_string(e) + ")";
+    return LB_ETIMEOUT;
+  }
+  return LB_OK;
 }
 
 }  // namespace lbi

@@ -146,6 +146,11 @@ lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, in
 /* Number of fp16 elements lb_stack_forward writes to trace for M rows. */
 lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t *elems);
 
+/* Synchronise the device and report whether any earlier persistent sweep
+ * of this stack gave up a device-side wait (LB_ETIMEOUT; the stack resets
+ * its synchronisation words before the next sweep).  LB_OK otherwise. */
+lb_status lb_stack_check(lb_stack *S);
+
 /* Select the execution mode of lb_stack_forward: 0 = automatic, 1 = per
  * layer kernels only, 2 = persistent only (LB_EUNSUPPORTED if impossible). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);

@@ -191,9 +191,9 @@ def test_error_codes(lbm):
     with pytest.raises(lbm.LBError) as ei:
         lbm.lb_pack_signs(L.handle, 2, p0["su"], p0["sv"])
     assert ei.value.status == lbm.LB_EINVAL
-    big = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
-    with pytest.raises(lbm.LBError) as ei:   # y overlaps x
-        lbm.lb_forward(L.handle, big, big[1:], 1)
+    big = torch.zeros((4, 64), dtype=torch.float16, device="cuda").view(-1)
+    with pytest.raises(lbm.LBError) as ei:   # y (64 bytes in) overlaps x's first row
+        lbm.lb_forward(L.handle, big, big[32:], 1)
     assert ei.value.status == lbm.LB_EINVAL
     with pytest.raises(lbm.LBError) as ei:   # misaligned x
         lbm.lb_forward(L.handle, x.data_ptr() + 2, y, 1)

@@ -116,3 +116,58 @@ def test_stack_without_trace_matches_trace_run(lbm):
     S.forward(xd, y2, None)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
+
+
+def _odd_stack(lbm, seed=5):
+    """A small stack with widths that are not multiples of 16."""
+    shapes = [(100, 37, 5), (100, 37, 5), (37, 70, 33), (70, 100, 17), (70, 100, 17)]
+    units = [2, 1, 2]
+    layers, paths = [], []
+    for i, (a, b, s) in enumerate(shapes):
+        p = lb_synth.layer_inputs(a, b, s, True, seed=seed, layer=i)
+        for q in p:
+            q["a"], q["b"], q["s"] = a, b, s
+        layers.append(lbm.Layer.from_paths(p))
+        paths.append(p)
+    wl = {"name": "odd", "seed": seed, "M": 1, "units": units,
+          "layers": [{"a": a, "b": b, "s": s, "residual": True} for (a, b, s) in shapes]}
+    return wl, lbm.Stack(layers, units, lb_synth.kappa(2)), paths
+
+
+@pytest.mark.parametrize("name,blocks", [("llama7b_mlp_stack", 3), ("llama70b_mlp_stack", 2),
+                                         ("llama7b_attn_proj_4096", 1), ("tiny_256", 1)])
+def test_persistent_sweep_parity(lbm, name, blocks):
+    wl, S, paths = build_stack(lbm, name, blocks=blocks)
+    say(f"[case] persistent sweep {name} blocks={blocks}")
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    check_stack(wl, paths, x0, y, tr, 1)
+    # the per-layer kernels reach the same result within the parity bar
+    _, y1, _ = run_stack(lbm, wl, S, 1, mode=1)
+    assert_parity(y.astype(np.float64), y1.astype(np.float64), "persistent vs per-layer")
+
+
+def test_persistent_odd_widths(lbm):
+    wl, S, paths = _odd_stack(lbm)
+    say("[case] persistent odd widths")
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    check_stack(wl, paths, x0, y, tr, 1)
+
+
+def test_persistent_repeated_and_deterministic(lbm):
+    """Many launches in a row (generation counters advance) give bitwise
+    identical outputs, with and without the trace."""
+    torch = lbtest.torch_dev()
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=4)
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    xd = lbtest.to_dev(x0)
+    outs = []
+    for _ in range(20):
+        y2 = torch.empty((1, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+        S.forward(xd, y2, None)
+        outs.append(y2)
+    torch.cuda.synchronize()
+    S.check()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), y.view(np.uint16))
