@@ -58,6 +58,7 @@ def load_library(path: str = LIB_PATH):
         "lb_stack_trace_elems": ([vp, i64, P(i64)], i32),
         "lb_stack_set_mode": ([vp, i32], i32),
         "lb_stack_check": ([vp], i32),
+        "lb_stack_timeline": ([vp, vp, i64, P(i64)], i32),
         "lb_stack_destroy": ([vp], i32),
         "lb_status_str": ([i32], C.c_char_p),
         "lb_last_error": ([], C.c_char_p),
@@ -74,7 +75,7 @@ def load_library(path: str = LIB_PATH):
 EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
-            "lb_stack_trace_elems", "lb_stack_set_mode", "lb_stack_check", "lb_stack_destroy", "lb_status_str",
+            "lb_stack_trace_elems", "lb_stack_set_mode", "lb_stack_check", "lb_stack_timeline", "lb_stack_destroy", "lb_status_str",
             "lb_last_error", "lb_version")
 
 
@@ -209,6 +210,12 @@ def lb_stack_set_mode(stack: int, mode: int):
 
 def lb_stack_check(stack: int):
     _check(load_library().lb_stack_check(stack))
+
+
+def lb_stack_timeline(stack: int, buf=None, capacity: int = 0) -> int:
+    n = C.c_int64()
+    _check(load_library().lb_stack_timeline(stack, _ptr(buf), int(capacity), C.byref(n)))
+    return n.value
 
 
 def lb_stack_destroy(stack: int):

@@ -108,59 +108,6 @@ void transpose32(uint32_t m[32]) {
   }
 }
 
-// m2 of one path (see lb_internal.h): bit (16q + r) of mask i of row tile
-// tau = S_U[16 tau + r, q*Q + i].  32 x 32 bit transposes turn rows of
-// canonical words into per-column 32-row fields.
-void build_m2(const Layer &Ly, int path, const uint32_t *su, std::vector<uint64_t> &m2) {
-  const int64_t b = Ly.b, s = Ly.s, Wk = Ly.Wk, Q = Ly.Q, Qp = Ly.Qp, T = Ly.T16b;
-  m2.assign((size_t)T * Qp, 0);
-  uint32_t blk[32];
-  for (int64_t R = 0; R < (b + 31) / 32; ++R) {
-    for (int64_t C = 0; C < Wk; ++C) {
-      const uint32_t msk = tail_mask(s, C);
-      for (int e = 0; e < 32; ++e) {
-        const int64_t j = 32 * R + e;
-        blk[e] = j < b ? (su[j * Wk + C] & msk) : 0u;
-      }
-      transpose32(blk);  // blk[kk] bit e = S_U[32R + e, 32C + kk]
-      for (int kk = 0; kk < 32; ++kk) {
-        const int64_t k = 32 * C + kk;
-        if (k >= s) break;
-        const int64_t q = k / Q, i = k - q * Q;
-        const int64_t t0 = 2 * R;
-        m2[(size_t)t0 * Qp + i] |= (uint64_t)(blk[kk] & 0xffffu) << (16 * q);
-        if (t0 + 1 < T) m2[(size_t)(t0 + 1) * Qp + i] |= (uint64_t)(blk[kk] >> 16) << (16 * q);
-      }
-    }
-  }
-}
-
-// m1 of all paths: bit (16q + cc) of mask i of (row tile tau, column tile
-// kap) = S_V[16 tau + 4q + i, latent column 16 kap + cc], c = p*s + k.
-void build_m1(const Layer &Ly, std::vector<uint64_t> &m1) {
-  const int64_t a = Ly.a, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L, NCT = Ly.NCT;
-  m1.assign((size_t)Ly.T16a * NCT * 4, 0);
-  std::vector<uint64_t> cat((size_t)(Lc + 63) / 64 + 1);
-  for (int64_t i = 0; i < a; ++i) {
-    std::fill(cat.begin(), cat.end(), 0);
-    for (int p = 0; p < Ly.P; ++p) {
-      const uint32_t *row = Ly.sv_host[p].data() + i * Wk;
-      for (int64_t w = 0; w < Wk; ++w) {
-        const uint64_t v = row[w] & tail_mask(s, w);
-        const int64_t off = p * s + 32 * w;
-        cat[off / 64] |= v << (off % 64);
-        if (off % 64 > 32) cat[off / 64 + 1] |= v >> (64 - off % 64);
-      }
-    }
-    const int64_t tau = i / 16, q = (i % 16) / 4, i4 = i % 4;
-    for (int64_t kap = 0; kap < NCT; ++kap) {
-      const int64_t off = 16 * kap;
-      uint64_t f = cat[off / 64] >> (off % 64);
-      if (off % 64 > 48) f |= cat[off / 64 + 1] << (64 - off % 64);
-      m1[(size_t)(tau * NCT + kap) * 4 + i4] |= (f & 0xffffu) << (16 * q);
-    }
-  }
-}
 }  // namespace
 
 static inline DevCtx *ctx_of(const lb_layer *L) { return static_cast<DevCtx *>(L->ctx); }
@@ -196,16 +143,21 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
   Layer &Ly = L->ly;
   Ly.a = a; Ly.b = b; Ly.s = s; Ly.P = residual ? 2 : 1; Ly.device = device;
   Ly.L = Ly.P * s; Ly.R1 = (a + 31) / 32; Ly.Wk = (s + 31) / 32;
-  Ly.T16a = (a + 15) / 16; Ly.T16b = (b + 15) / 16; Ly.NCT = (Ly.L + 15) / 16;
-  Ly.Q = (s + 3) / 4; Ly.Qp = (Ly.Q + 3) / 4 * 4;
+  Ly.T16a = (a + 15) / 16; Ly.T16b = (b + 15) / 16;
+  Ly.a16 = Ly.T16a * 16; Ly.b16 = Ly.T16b * 16; Ly.s8 = (s + 7) / 8 * 8;
+  Ly.Lp = (Ly.L + 7) / 8 * 8;
   L->ctx = dc;
   struct Alloc { void **p; size_t n; };
   Alloc allocs[] = {
-      {(void **)&Ly.sv1, (size_t)Ly.R1 * Ly.L * 4}, {(void **)&Ly.su2, (size_t)Ly.P * Ly.Wk * b * 4},
-      {(void **)&Ly.h, (size_t)Ly.P * b * 2},       {(void **)&Ly.g, (size_t)Ly.P * a * 2},
-      {(void **)&Ly.l, (size_t)Ly.P * s * 2},
-      {(void **)&Ly.m1, (size_t)Ly.T16a * Ly.NCT * 4 * 8},
-      {(void **)&Ly.m2, (size_t)Ly.P * Ly.T16b * Ly.Qp * 8}};
+      {(void **)&Ly.sv1, (size_t)Ly.R1 * Ly.L * 4},
+      {(void **)&Ly.su2, (size_t)Ly.P * Ly.Wk * Ly.b16 * 4},
+      {(void **)&Ly.h, (size_t)Ly.P * Ly.b16 * 2},
+      {(void **)&Ly.g, (size_t)Ly.P * Ly.a16 * 2},
+      {(void **)&Ly.l, (size_t)Ly.P * Ly.s8 * 2},
+      {(void **)&Ly.sv16, (size_t)Ly.T16a * Ly.Lp * 2},
+      {(void **)&Ly.su2t, (size_t)Ly.T16b * Ly.P * Ly.Wk * 16 * 4},
+      {(void **)&Ly.ht, (size_t)Ly.T16b * Ly.P * 16 * 2},
+      {(void **)&Ly.gt, (size_t)Ly.T16a * Ly.P * 16 * 2}};
   for (auto &al : allocs) {
     hipError_t e = hipMalloc(al.p, al.n);
     if (e != hipSuccess) {
@@ -231,7 +183,7 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   if (!L) return LB_OK;
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
-  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.m1, Ly.m2};
+  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   delete L;
@@ -254,20 +206,32 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
   if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_pack_signs: path out of range");
   DeviceGuard dg(Ly.device);
   const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L;
-  // S_U: su2[(p*Wk + q)*b + j] = su[j*Wk + q] (padding masked)
+  // S_U: su2[(p*Wk + q)*b16 + j] = su[j*Wk + q] (padding masked, rows >= b zero)
+  const int64_t b16 = Ly.b16;
   std::vector<uint32_t> u2;
   std::vector<uint32_t> v1;
+  std::vector<uint16_t> v16;
   try {
-    u2.resize((size_t)Wk * b);
+    u2.assign((size_t)Wk * b16, 0u);
     v1.resize((size_t)Ly.R1 * Lc);
+    v16.assign((size_t)Ly.T16a * Ly.Lp, 0);
   } catch (...) {
     return fail(LB_ENOMEM, "lb_pack_signs: host allocation");
   }
   for (int64_t q = 0; q < Wk; ++q) {
     const uint32_t msk = tail_mask(s, q);
-    for (int64_t j = 0; j < b; ++j) u2[(size_t)q * b + j] = su[j * Wk + q] & msk;
+    for (int64_t j = 0; j < b; ++j) u2[(size_t)q * b16 + j] = su[j * Wk + q] & msk;
   }
-  LB_HIP(hipMemcpy(Ly.su2 + (size_t)path * Wk * b, u2.data(), u2.size() * 4, hipMemcpyHostToDevice));
+  LB_HIP(hipMemcpy(Ly.su2 + (size_t)path * Wk * b16, u2.data(), u2.size() * 4, hipMemcpyHostToDevice));
+  {
+    // tile-major: for tile tau, this path's Wk x 16 words are one 64*Wk-byte run
+    std::vector<uint32_t> u2t((size_t)Ly.T16b * Wk * 16);
+    for (int64_t tau = 0; tau < Ly.T16b; ++tau)
+      for (int64_t q = 0; q < Wk; ++q)
+        for (int r = 0; r < 16; ++r) u2t[((size_t)tau * Wk + q) * 16 + r] = u2[(size_t)q * b16 + 16 * tau + r];
+    LB_HIP(hipMemcpy2D(Ly.su2t + (size_t)path * Wk * 16, (size_t)Ly.P * Wk * 16 * 4, u2t.data(),
+                       (size_t)Wk * 16 * 4, (size_t)Wk * 16 * 4, (size_t)Ly.T16b, hipMemcpyHostToDevice));
+  }
   // S_V: 32 x 32 bit transposes.  Block (row group r, word q) -> columns
   // p*s + 32q + kk of row group r.
   {
@@ -287,21 +251,11 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
       }
     }
     LB_HIP(hipMemcpy(Ly.sv1, v1.data(), v1.size() * 4, hipMemcpyHostToDevice));
-  }
-  // lane-mask layouts
-  {
-    std::vector<uint64_t> m2;
-    build_m2(Ly, path, su, m2);
-    LB_HIP(hipMemcpy(Ly.m2 + (size_t)path * Ly.T16b * Ly.Qp, m2.data(), m2.size() * 8,
-                     hipMemcpyHostToDevice));
-    Ly.sv_host[path].assign(sv, sv + (size_t)a * Wk);
-    bool all = true;
-    for (int p = 0; p < Ly.P; ++p) all = all && !Ly.sv_host[p].empty();
-    if (all) {
-      std::vector<uint64_t> m1;
-      build_m1(Ly, m1);
-      LB_HIP(hipMemcpy(Ly.m1, m1.data(), m1.size() * 8, hipMemcpyHostToDevice));
-    }
+    // sv16[gi*Lp + c]: the 16-row halves of the sv1 words
+    for (int64_t gi = 0; gi < Ly.T16a; ++gi)
+      for (int64_t c = 0; c < Lc; ++c)
+        v16[(size_t)gi * Ly.Lp + c] = (uint16_t)(v1[(size_t)(gi / 2) * Lc + c] >> (16 * (gi % 2)));
+    LB_HIP(hipMemcpy(Ly.sv16, v16.data(), v16.size() * 2, hipMemcpyHostToDevice));
   }
   Ly.signs_set[path] = true;
   return LB_OK;
@@ -313,11 +267,11 @@ extern "C" lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, 
   if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_unpack_signs: path out of range");
   DeviceGuard dg(Ly.device);
   const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L;
-  std::vector<uint32_t> u2((size_t)Wk * b), v1((size_t)Ly.R1 * Lc);
-  LB_HIP(hipMemcpy(u2.data(), Ly.su2 + (size_t)path * Wk * b, u2.size() * 4, hipMemcpyDeviceToHost));
+  std::vector<uint32_t> u2((size_t)Wk * Ly.b16), v1((size_t)Ly.R1 * Lc);
+  LB_HIP(hipMemcpy(u2.data(), Ly.su2 + (size_t)path * Wk * Ly.b16, u2.size() * 4, hipMemcpyDeviceToHost));
   LB_HIP(hipMemcpy(v1.data(), Ly.sv1, v1.size() * 4, hipMemcpyDeviceToHost));
   for (int64_t j = 0; j < b; ++j)
-    for (int64_t q = 0; q < Wk; ++q) su[j * Wk + q] = u2[(size_t)q * b + j];
+    for (int64_t q = 0; q < Wk; ++q) su[j * Wk + q] = u2[(size_t)q * Ly.b16 + j];
   uint32_t blk[32];
   for (int64_t r = 0; r < Ly.R1; ++r) {
     for (int64_t q = 0; q < Wk; ++q) {
@@ -339,9 +293,19 @@ extern "C" lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, con
   Layer &Ly = L->ly;
   if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_set_scales: path out of range");
   DeviceGuard dg(Ly.device);
-  LB_HIP(hipMemcpy(Ly.h + (size_t)path * Ly.b, h, Ly.b * 2, hipMemcpyHostToDevice));
-  LB_HIP(hipMemcpy(Ly.g + (size_t)path * Ly.a, g, Ly.a * 2, hipMemcpyHostToDevice));
-  LB_HIP(hipMemcpy(Ly.l + (size_t)path * Ly.s, l, Ly.s * 2, hipMemcpyHostToDevice));
+  LB_HIP(hipMemcpy(Ly.h + (size_t)path * Ly.b16, h, Ly.b * 2, hipMemcpyHostToDevice));
+  LB_HIP(hipMemcpy(Ly.g + (size_t)path * Ly.a16, g, Ly.a * 2, hipMemcpyHostToDevice));
+  LB_HIP(hipMemcpy(Ly.l + (size_t)path * Ly.s8, l, Ly.s * 2, hipMemcpyHostToDevice));
+  {
+    // tile-major copies of h and g: 16 values per (tile, path), zero padded
+    std::vector<uint16_t> hb((size_t)Ly.T16b * 16, 0), gb((size_t)Ly.T16a * 16, 0);
+    std::memcpy(hb.data(), h, Ly.b * 2);
+    std::memcpy(gb.data(), g, Ly.a * 2);
+    LB_HIP(hipMemcpy2D(Ly.ht + (size_t)path * 16, (size_t)Ly.P * 16 * 2, hb.data(), 32, 32,
+                       (size_t)Ly.T16b, hipMemcpyHostToDevice));
+    LB_HIP(hipMemcpy2D(Ly.gt + (size_t)path * 16, (size_t)Ly.P * 16 * 2, gb.data(), 32, 32,
+                       (size_t)Ly.T16a, hipMemcpyHostToDevice));
+  }
   Ly.scales_set[path] = true;
   return LB_OK;
 }
@@ -563,6 +527,17 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     return st;
   }
   *out = S;
+  return LB_OK;
+}
+
+extern "C" lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed) {
+  if (!S) return fail(LB_EINVAL, "lb_stack_timeline: NULL stack");
+  if (!S->persist) return fail(LB_EUNSUPPORTED, "lb_stack_timeline: no persistent plan");
+  const int64_t need = (int64_t)persist_grid(S->persist) * persist_phases(S->persist) * 4;
+  if (needed) *needed = need;
+  if (buf && capacity < need) return fail(LB_EINVAL, "lb_stack_timeline: buffer too small");
+  if (((uintptr_t)buf) & 7) return fail(LB_EINVAL, "lb_stack_timeline: buffer not 8-byte aligned");
+  persist_set_timeline(S->persist, (uint64_t *)buf);
   return LB_OK;
 }
 

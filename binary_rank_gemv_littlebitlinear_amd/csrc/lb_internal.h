@@ -13,31 +13,25 @@
 //       Column-major bits over the input index: lane c of a wave reads
 //       its own column's word, so a wave's load of one row group is one
 //       contiguous, coalesced 4*64-byte segment.
-//   su2[(p*Wk + q) * b + j]        (uint32, P*Wk x b)
+//   su2[(p*Wk + q) * b16 + j]      (uint32, P*Wk x b16, b16 = b rounded up to 16)
 //       bit (k % 32) = S_U,p[j, 32 q + bit].  Row j's words of one path
-//       are b apart, so lane j of a wave reads consecutive addresses.
-//   h[p*b + j], g[p*a + i], l[p*s + k]   (fp16 bit patterns)
+//       are b16 apart, so lane j of a wave reads consecutive addresses, and
+//       the words of 16-row tiles start on 64-byte boundaries.
+//   sv16[gi * Lp + c]              (uint16, T16a x Lp, Lp = L rounded up to 8)
+//       bit (i % 16) = S_V,p[i, k] for i = 16 gi + bit, c = p*s + k: the
+//       first product's bits by 16-row groups, so a workgroup owning whole
+//       16-row tiles reads one contiguous, 16-byte aligned block.
+//   h[p*b16 + j], g[p*a16 + i], l[p*s8 + k]   (fp16 bit patterns; padded
+//       per-path pitches, s8 = s rounded up to 8, zero padding)
 //
-// Padding bits (i >= a in the last row group of sv1, k >= s in the last
-// word of su2) are zero, so they contribute nothing.
+// Tile-major copies for the persistent sweep, where a workgroup owns whole
+// 16-row tiles and stages them into LDS as one contiguous block each:
+//   su2t[((tau * P + p) * Wk + q) * 16 + r]   (uint32) = su2 word q, path p,
+//       row 16 tau + r
+//   ht[(tau * P + p) * 16 + r] = h[p*b16 + 16 tau + r]   (fp16)
+//   gt[(tau * P + p) * 16 + r] = g[p*a16 + 16 tau + r]   (fp16)
 //
-// Lane-mask layouts for the wave-level kernels.  A 64-bit mask holds one
-// bit per lane of a 64-lane wave; the kernels turn it into a per-lane
-// predicate and add a broadcast value in the lanes whose bit is set
-// (sign-flip identity).  Lanes are split 16 x 4: lane = 16*q + r.
-//
-//   T16a = ceil(a / 16), T16b = ceil(b / 16) row tiles of 16 rows
-//   NCT  = ceil(L / 16)  column tiles of 16 latent columns
-//   Q    = ceil(s / 4),  Qp = Q rounded up to a multiple of 4
-//
-//   m1[(tau * NCT + kap) * 4 + i]          (uint64, T16a x NCT x 4)
-//       bit (16 q + cc) = S_V[16 tau + 4 q + i, column 16 kap + cc]
-//       (columns of the concatenated latent c = p*s + k; lane 16q+cc of
-//       the first product accumulates column 16kap+cc over rows 4q+i).
-//   m2[((p * T16b + tau) * Qp) + i]         (uint64, P x T16b x Qp)
-//       bit (16 q + r) = S_U,p[16 tau + r, q*Q + i]   (0 if q*Q+i >= s)
-//       (lane 16q+r of the second product accumulates row 16tau+r over
-//       the latent quarter q).
+// Padding bits and padding scales are zero, so they contribute nothing.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,16 +58,15 @@ struct Layer {
   bool signs_set[2] = {false, false};
   bool scales_set[2] = {false, false};
   uint32_t *sv1 = nullptr;  // R1 * L words
-  uint32_t *su2 = nullptr;  // P * Wk * b words
-  uint16_t *h = nullptr;    // P * b
-  uint16_t *g = nullptr;    // P * a
-  uint16_t *l = nullptr;    // P * s
-  int64_t T16a = 0, T16b = 0, NCT = 0, Q = 0, Qp = 0;
-  uint64_t *m1 = nullptr;   // T16a * NCT * 4
-  uint64_t *m2 = nullptr;   // P * T16b * Qp
-  // host copies of the canonical S_V words of each path, kept until every
-  // path is packed (m1 interleaves the paths' columns)
-  std::vector<uint32_t> sv_host[2];
+  uint32_t *su2 = nullptr;  // P * Wk * b16 words
+  uint16_t *h = nullptr;    // P * b16
+  uint16_t *g = nullptr;    // P * a16
+  uint16_t *l = nullptr;    // P * s8
+  int64_t a16 = 0, b16 = 0, s8 = 0, Lp = 0, T16a = 0, T16b = 0;
+  uint16_t *sv16 = nullptr; // T16a * Lp
+  uint32_t *su2t = nullptr; // T16b * P * Wk * 16
+  uint16_t *ht = nullptr;   // T16b * P * 16
+  uint16_t *gt = nullptr;   // T16a * P * 16
   // workspace: stage-1 partials / latent vectors, sized at create time
   float *ws = nullptr;
   size_t ws_bytes = 0;

@@ -86,8 +86,8 @@ __device__ __forceinline__ void mma_step(const uint16_t (*As)[BK + kPadK],
 // multiple of BK.
 __global__ void __launch_bounds__(kMfmaThreads)
 k_mfma_stage1(const uint16_t *__restrict__ x, int64_t M, const uint32_t *__restrict__ sv1,
-              const uint16_t *__restrict__ g, int64_t a, int64_t s, int64_t L, int64_t kper,
-              float *__restrict__ part) {
+              const uint16_t *__restrict__ g, int64_t a, int64_t a16, int64_t s, int64_t L,
+              int64_t kper, float *__restrict__ part) {
   __shared__ __align__(16) uint16_t As[BM][BK + kPadK];
   __shared__ __align__(16) uint16_t Bs[BN][BK + kPadK];
   const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
@@ -113,7 +113,7 @@ k_mfma_stage1(const uint16_t *__restrict__ x, int64_t M, const uint32_t *__restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int64_t i = k0 + bk + e;
-          const uint16_t gv = i < a ? g[p * a + i] : (uint16_t)0;
+          const uint16_t gv = i < a ? g[p * a16 + i] : (uint16_t)0;
           const uint32_t bit = (wd >> (bk + e)) & 1u;
           v[e] = bit ? gv : (uint16_t)(gv ^ 0x8000u);
           if (i >= a) v[e] = 0;
@@ -165,8 +165,8 @@ __global__ void k_mfma_reduce(const float *__restrict__ part, int nsplit, int64_
 __global__ void __launch_bounds__(kMfmaThreads)
 k_mfma_stage2(const uint16_t *__restrict__ T16, int64_t M, int64_t s_pad,
               const uint32_t *__restrict__ su2, const uint16_t *__restrict__ l,
-              const uint16_t *__restrict__ h, int64_t b, int64_t s, int64_t Wk, int P,
-              uint16_t *__restrict__ y) {
+              const uint16_t *__restrict__ h, int64_t b, int64_t b16, int64_t s, int64_t s8,
+              int64_t Wk, int P, uint16_t *__restrict__ y) {
   __shared__ __align__(16) uint16_t As[BM][BK + kPadK];
   __shared__ __align__(16) uint16_t Bs[BN][BK + kPadK];
   const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
@@ -188,11 +188,11 @@ k_mfma_stage2(const uint16_t *__restrict__ T16, int64_t M, int64_t s_pad,
       {
         uint16_t v[8];
         if (j < b) {
-          const uint32_t wd = su2[(p * Wk + (k0 >> 5)) * b + j];
+          const uint32_t wd = su2[(p * Wk + (k0 >> 5)) * b16 + j];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int64_t k = k0 + bk + e;
-            const uint16_t lv = k < s ? l[p * s + k] : (uint16_t)0;
+            const uint16_t lv = k < s ? l[p * s8 + k] : (uint16_t)0;
             const uint32_t bit = (wd >> (bk + e)) & 1u;
             v[e] = k < s ? (bit ? lv : (uint16_t)(lv ^ 0x8000u)) : (uint16_t)0;
           }
@@ -224,7 +224,7 @@ k_mfma_stage2(const uint16_t *__restrict__ T16, int64_t M, int64_t s_pad,
         const int64_t c = n0 + wn * 32 + ni * 16 + (lane & 15);
         if (m < M && c < b) {
           float v = mh2f(h[c]) * acc[0][mi][ni][r];
-          if (P > 1) v += mh2f(h[b + c]) * acc[1][mi][ni][r];
+          if (P > 1) v += mh2f(h[b16 + c]) * acc[1][mi][ni][r];
           y[m * b + c] = mf2h(v);
         }
       }
@@ -260,7 +260,7 @@ hipError_t launch_mfma_forward(const Layer &Ly, const uint16_t *x, uint16_t *y, 
         reinterpret_cast<char *>(ws) + (size_t)16 * Mc * Ly.L * sizeof(float));
     dim3 g1((unsigned)((Ly.L + BN - 1) / BN), (unsigned)((Mc + BM - 1) / BM), (unsigned)nsr);
     hipLaunchKernelGGL(k_mfma_stage1, g1, dim3(kMfmaThreads), 0, st, x + mb * Ly.a, Mc, Ly.sv1,
-                       Ly.g, Ly.a, Ly.s, Ly.L, kper, part);
+                       Ly.g, Ly.a, Ly.a16, Ly.s, Ly.L, kper, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nT = (int64_t)Ly.P * Mc * s_pad;
@@ -270,7 +270,7 @@ hipError_t launch_mfma_forward(const Layer &Ly, const uint16_t *x, uint16_t *y, 
     if (e != hipSuccess) return e;
     dim3 g2((unsigned)((Ly.b + BN - 1) / BN), (unsigned)((Mc + BM - 1) / BM));
     hipLaunchKernelGGL(k_mfma_stage2, g2, dim3(kMfmaThreads), 0, st, T16, Mc, s_pad, Ly.su2, Ly.l,
-                       Ly.h, Ly.b, Ly.s, Ly.Wk, Ly.P, y + mb * Ly.b);
+                       Ly.h, Ly.b, Ly.b16, Ly.s, Ly.s8, Ly.Wk, Ly.P, y + mb * Ly.b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -21,6 +21,10 @@ int64_t persist_max_rows();
 // null, receives every layer's output then every unit's input (M = 1).
 lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace, int64_t M,
                       hipStream_t st, std::string *msg);
+// Diagnostics: per-phase device timestamps of every workgroup.
+void persist_set_timeline(PersistPlan *p, uint64_t *buf);
+int persist_grid(const PersistPlan *p);
+int persist_phases(const PersistPlan *p);
 // Synchronise and report a device-side wait timeout of an earlier launch.
 lb_status persist_check(PersistPlan *p, std::string *msg);
 

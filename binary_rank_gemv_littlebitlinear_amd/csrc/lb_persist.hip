@@ -3,31 +3,40 @@
 // [LB news] Sec. 2: each layer is two small binary products with
 // elementwise scales; the residual path is a second factorisation whose
 // output is added.  A stack chains layers (units of layers that share an
-// input, combined in fp32 and rounded to fp16 between units).
+// input; unit outputs are combined in fp32 and rounded to fp16).
 //
 // One launch of G = #CU workgroups (one per CU) runs the whole sweep as
-// U + 1 phases.  Workgroup w owns a fixed set of 16-row tiles of every
-// width, so the second product of unit u-1 (rows j), the combine and the
-// first product of unit u (rows i = j) are local to the workgroup:
+// U + 1 phases.  Workgroup w owns fixed 16-row tiles of every width, so
+// the second product of unit u-1 (rows j), the combine and the first
+// product of unit u (rows i = j) stay inside the workgroup:
 //
-//   phase 0     : X_0 rows -> partial t of unit 0 over own rows
-//   phase u     : t_{u-1} -> y rows of unit u-1 -> combine -> X_u rows
-//                 -> partial t of unit u over own rows
-//   phase U     : t_{U-1} -> y rows -> final combine -> output rows
+//   phase 0 : X_0 rows -> partial t of unit 0 over own rows
+//   phase u : t_{u-1} -> y rows of unit u-1 -> combine -> X_u rows
+//             -> partial t of unit u over own rows
+//   phase U : t_{U-1} -> y rows -> final combine -> output rows
 //
-// Between phases the partial latent vectors of all workgroups are
-// all-reduced (reduce-scatter over slices, then broadcast), with flag
-// words that carry a generation number.  Every exchanged word is written
-// and read with device-coherent (sc1) relaxed atomics; a store's
-// completion (s_waitcnt) precedes the flag that publishes it.  All waits
-// are bounded: on timeout a device error word is set, every workgroup
-// leaves, and the host returns LB_ETIMEOUT.
+// Products.  With S in {+-1}, sum_i s_i v_i is evaluated four signs at a
+// time: for every group of four values a 16-entry table holds all sixteen
+// signed sums, and each 4-bit nibble of a sign word selects one entry.  A
+// wave reads at most 16 distinct entries of one table per lookup, which
+// the LDS serves without bank conflicts.  The first product's tables are
+// built from z = g * x over the workgroup's own rows; the second
+// product's tables from w = l * t.
 //
-// Products use the sign-flip identity  sum_i s_i v_i = 2 sum_{bit} v_i -
-// sum_i v_i  with 64-bit lane masks (one bit per lane of a wave): each
-// mask becomes a lane predicate (v_cndmask on an SGPR pair) and the
-// broadcast value is added where the bit is set.  Mask layouts m1 / m2
-// are described in lb_internal.h.
+// Memory.  The sign bits and scales a workgroup needs in a phase form a
+// few contiguous blocks (layouts in lb_internal.h).  Waves 4-7 copy them
+// into LDS with LDS-DMA loads while waves 0-3 run the previous phase's
+// exchange, so HBM latency overlaps the device-wide synchronisation.
+//
+// Exchange.  Partial latent vectors (one per workgroup) are all-reduced
+// between phases: each workgroup stores its partials contiguously and
+// raises a flag; workgroup r sums the 8-column slice r over all
+// workgroups in a fixed order and raises a second flag; everyone reads the
+// reduced vector.  Exchanged words are written and read with relaxed
+// device-coherent (sc1) atomics, a store's completion (s_waitcnt) comes
+// before the flag that publishes it, and flags carry a generation number.
+// Every wait is bounded: on timeout a device error word is set, all
+// workgroups leave, and lb_stack_check returns LB_ETIMEOUT.
 #include <hip/hip_fp16.h>
 
 #include <cmath>
@@ -38,30 +47,32 @@
 
 namespace lbi {
 
-constexpr int kThreads = 512;           // 8 waves
+constexpr int kThreads = 512;  // 8 waves: 0-3 exchange, 4-7 prefetch
 constexpr int kWaves = kThreads / 64;
-constexpr int kTMax = 8;                // row tiles per workgroup and width
-constexpr int kKMax = 16;               // column tiles per wave in the first product
+constexpr int kXThreads = 256;  // threads that touch exchange memory
+constexpr int kTMax = 8;        // 16-row tiles per workgroup and width
 constexpr int kMaxUnitLayers = 8;
-constexpr int kLuMax = 4096;            // latent columns per unit
-constexpr long kSpin = 4000000;         // polls before a wait gives up
-
-typedef __attribute__((address_space(4))) const uint64_t cmask_t;
+constexpr int kLuMax = 2048;    // latent columns per unit
+constexpr int kStgBytes = 56 * 1024;
+constexpr int kTab2Floats = 10240;
+constexpr int kTab1Floats = 4096;
+constexpr long kSpin = 4000000;  // polls before a wait gives up
+constexpr int kFlagStride = 64;  // flags 256 bytes apart (separate lines and channels)
 
 struct PLayer {
-  const uint64_t *m1, *m2;
-  const uint16_t *h, *g, *l;
-  int a, b, s, P, Q, Qp, NCT, L, T16a, T16b;
-  int col0, ct0;     // first latent column / column tile within the unit
-  int64_t trace_y;   // element offset of this layer's output in the trace, -1 if none
+  const uint32_t *su2t;
+  const uint16_t *sv16, *ht, *gt, *l;
+  int a, b, s, P, L, Lp, Wk, a16, b16, s8;
+  int col0;         // first latent column within the unit
+  int64_t trace_y;  // element offset of this layer's output in the trace
 };
 
 struct PUnit {
   int first, n;
   int a, b;
-  int Lu, nct;
-  float c_out;       // kappa / sqrt(n): combine of this unit's outputs
-  int64_t trace_x;   // element offset of this unit's input in the trace
+  int Lu;
+  float c_out;      // kappa / sqrt(n): combine of this unit's outputs
+  int64_t trace_x;  // element offset of this unit's input in the trace
 };
 
 struct PArgs {
@@ -70,14 +81,14 @@ struct PArgs {
   int nunits;
   const uint16_t *x0;
   uint16_t *y;
-  uint16_t *trace;   // may be null
+  uint16_t *trace;  // may be null
   unsigned gen_base;
-  float *xpart;      // [G][G][spw_max] partial slices (transposed)
-  float *xT;         // [kLuMax] reduced latent
-  unsigned *flag1;   // [G]
-  unsigned *flag2;   // [G]
+  float *xpart;     // [G][kLuMax] partials
+  float *xT;        // [kLuMax] reduced latent
+  unsigned *flag1;  // [G] flags, kFlagStride words apart
+  unsigned *flag2;  // [kLuMax / 8] flags, kFlagStride words apart
   unsigned *err;
-  int spw_max;
+  uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
 };
 
 struct PersistPlan {
@@ -90,10 +101,10 @@ struct PersistPlan {
   std::vector<PUnit> h_units;
   std::vector<PLayer> h_layers;
   float *xpart = nullptr, *xT = nullptr;
-  unsigned *flags = nullptr;  // flag1 [G], flag2 [G], err [64]
-  int spw_max = 0;
+  unsigned *flags = nullptr;  // flag1 [G], flag2 [kLuMax/8], err [64]
   unsigned gen = 0;
   bool broken = false;
+  uint64_t *timeline = nullptr;
 };
 
 // ----------------------------------------------------------- primitives
@@ -112,342 +123,431 @@ __device__ __forceinline__ void st_f(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool reached(unsigned v, unsigned gen) { return (int)(v - gen) >= 0; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// Tiles [t0, t1) of a width with `tiles` 16-row tiles owned by workgroup w.
+// 16-row tiles [t0, t1) owned by workgroup w out of `tiles`.
 __device__ __forceinline__ void my_tiles(int tiles, int G, int w, int &t0, int &t1) {
   t0 = (int)(((long)tiles * w) / G);
   t1 = (int)(((long)tiles * (w + 1)) / G);
 }
 
-// Wait until flags[0..n) all reached gen (threads < n poll one flag each).
-// Returns false on timeout or device error.
-__device__ bool wait_flags(unsigned *flags, int n, unsigned gen, unsigned *err) {
-  long spins = 0;
-  while (true) {
-    int ok = 1;
-    if ((int)threadIdx.x < n) ok = reached(ld_u(&flags[threadIdx.x]), gen);
-    if (__syncthreads_and(ok)) return true;
-    if (++spins > kSpin) {
-      if (threadIdx.x == 0) atomicOr(err, 1u);
-      return false;
-    }
-    if (spins > 64) __builtin_amdgcn_s_sleep(1);
-    const int bad = (threadIdx.x == 0) ? (int)ld_u(err) : 0;
-    if (__syncthreads_or(bad)) return false;
-  }
+// Block-wide AND through LDS only (waits on LDS, never on global memory).
+__device__ __forceinline__ bool block_all(bool ok, int *flags8) {
+  const int wok = __all(ok);
+  if ((threadIdx.x & 63) == 0) flags8[wave_id()] = wok;
+  __syncthreads();
+  int r = 1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r &= flags8[i];
+  __syncthreads();
+  return r != 0;
 }
 
-// -------------------------------------------------------- the exchange
-// part (LDS, Lu floats) of every workgroup -> T (LDS, Lu floats) = sum.
-// Slice m (columns m*spw ..) is reduced by workgroup m in fixed order.
-__device__ bool exchange(const float *part, float *T, float *red, int Lu, unsigned gen,
-                         const PArgs &A) {
-  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
-  const int spw = (Lu + G - 1) / G;
-  for (int c = t; c < Lu; c += kThreads) {
-    const int m = c / spw, j = c - m * spw;
-    st_f(&A.xpart[((size_t)m * G + w) * A.spw_max + j], part[c]);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t == 0) st_u(&A.flag1[w], gen);
-  if (w * spw < Lu) {
-    if (!wait_flags(A.flag1, G, gen, A.err)) return false;
-    const int nj = (Lu - w * spw) < spw ? (Lu - w * spw) : spw;
-    for (int j = 0; j < nj; ++j)
-      red[j * kThreads + t] = t < G ? ld_f(&A.xpart[((size_t)w * G + t) * A.spw_max + j]) : 0.f;
-    __syncthreads();
-    for (int st = kThreads / 2; st > 0; st >>= 1) {
-      if (t < st)
-        for (int j = 0; j < nj; ++j) red[j * kThreads + t] += red[j * kThreads + t + st];
-      __syncthreads();
+// Wait until flags[0..n) reached gen; threads < kXThreads poll.
+__device__ bool wait_flags(unsigned *flags, int n, unsigned gen, unsigned *err, int *flags8) {
+  long spins = 0;
+  while (true) {
+    bool ok = true;
+    if ((int)threadIdx.x < kXThreads)
+      for (int i = threadIdx.x; i < n; i += kXThreads)
+        ok = ok && reached(ld_u(&flags[(size_t)i * kFlagStride]), gen);
+    if (block_all(ok, flags8)) return true;
+    if ((++spins & 63) == 0) {
+      const bool bad = threadIdx.x == 0 && ld_u(err) != 0;
+      if (!block_all(!bad, flags8)) return false;
+      if (spins > kSpin) {
+        if (threadIdx.x == 0) atomicOr(err, 1u);
+        return false;
+      }
     }
-    if (t < nj) st_f(&A.xT[w * spw + t], red[t * kThreads]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t == 0) st_u(&A.flag2[w], gen);
   }
-  const int nsl = (Lu + spw - 1) / spw;
-  if (!wait_flags(A.flag2, nsl, gen, A.err)) return false;
-  for (int c = t; c < Lu; c += kThreads) T[c] = ld_f(&A.xT[c]);
-  __syncthreads();
-  return true;
 }
 
 // ------------------------------------------------------ LDS arrangement
 struct Lds {
-  float *xs;     // [16*kTMax] fp32 copy of this workgroup's input rows (fp16 values)
-  float *z;      // [kMaxUnitLayers*2][16*kTMax]  g * x per layer and path
-  float *zsum;   // [kMaxUnitLayers*2]
-  float *part;   // [kLuMax]
-  float *T;      // [kLuMax] reduced t, then w = l*t
-  float *wq;     // [kLuMax + pad] quarter-major w per layer and path
-  float *wsum;   // [kMaxUnitLayers*2]
-  float *ysum;   // [16*kTMax] combine accumulator
-  float *red;    // [kWaves][2][kTMax][64] (aliases the exchange scratch)
-  int *wq_off;   // [kMaxUnitLayers*2] float offset of each (layer, path) block in wq
+  unsigned char *stg;  // kStgBytes staged bits and scales of the phase
+  float *tab2;         // kTab2Floats second-product tables
+  float *tab1;         // kTab1Floats first-product tables
+  float *part;         // kLuMax
+  float *T;            // kLuMax
+  float *acc2;         // kMaxUnitLayers * 2 * 16 * kTMax
+  float *xs;           // 16 * kTMax input rows (fp16 values as fp32)
+  float *red;          // 8 * kXThreads exchange scratch
+  int *flags8;         // kWaves
 };
 
-__device__ float block_sum(float v, float *scratch) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float tot = 0.f;
-  for (int i = 0; i < kWaves; ++i) tot += scratch[i];
-  __syncthreads();
-  return tot;
+// Offsets of the staged blocks of one phase (identical in every wave).
+struct Stage {
+  // second product of unit ph-1
+  int s2_off[kMaxUnitLayers];  // uint32 [nt][P][Wk][16]
+  int h_off[kMaxUnitLayers];   // fp16  [nt][P][16]
+  int l_off[kMaxUnitLayers];   // fp16  [P][s8]
+  // first product of unit ph
+  int s1_off[kMaxUnitLayers];  // uint16 [nt][Lp]
+  int g_off[kMaxUnitLayers];   // fp16  [nt][P][16]
+};
+
+// Lay out the blocks of phase ph for tiles [t0, t1) and copy them into
+// LDS with LDS-DMA loads (16 bytes per lane, 1 KB per wave instruction);
+// the instructions of all blocks go round-robin to waves 4-7.
+__device__ void stage_phase(const PArgs &A, int ph, int t0, int t1, unsigned char *stg, Stage &S) {
+  const int nt = t1 - t0;
+  int off = 0, kglob = 0;
+  const int pw = wave_id() - 4;  // prefetch wave index 0..3
+  const int lane = threadIdx.x & 63;
+  auto copy = [&](const void *src, int dst, int nbytes) {
+    const int units = nbytes / 16;
+    const int nch = (units + 63) / 64;
+    for (int c = 0; c < nch; ++c, ++kglob) {
+      if (pw < 0 || (kglob & 3) != pw) continue;
+      const int u = c * 64 + lane;
+      if (u < units)
+        __builtin_amdgcn_global_load_lds((const char *)src + (size_t)u * 16, stg + dst + c * 1024, 16,
+                                         0, 0);
+    }
+  };
+  if (ph > 0) {
+    const PUnit &U = A.units[ph - 1];
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &Ly = A.layers[U.first + m];
+      S.s2_off[m] = off;
+      copy(Ly.su2t + (size_t)t0 * Ly.P * Ly.Wk * 16, off, nt * Ly.P * Ly.Wk * 64);
+      off += nt * Ly.P * Ly.Wk * 64;
+      S.h_off[m] = off;
+      copy(Ly.ht + (size_t)t0 * Ly.P * 16, off, nt * Ly.P * 32);
+      off += nt * Ly.P * 32;
+      S.l_off[m] = off;
+      copy(Ly.l, off, Ly.P * Ly.s8 * 2);
+      off += Ly.P * Ly.s8 * 2;
+    }
+  }
+  if (ph < A.nunits) {
+    const PUnit &U = A.units[ph];
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &Ly = A.layers[U.first + m];
+      S.s1_off[m] = off;
+      copy(Ly.sv16 + (size_t)t0 * Ly.Lp, off, nt * Ly.Lp * 2);
+      off += nt * Ly.Lp * 2;
+      S.g_off[m] = off;
+      copy(Ly.gt + (size_t)t0 * Ly.P * 16, off, nt * Ly.P * 32);
+      off += nt * Ly.P * 32;
+    }
+  }
+}
+
+// Entries lo + 4*hi (lo = 0..3) of the table over (v0, v1, v2, v3), entry
+// e = sum_j (bit j of e ? v_j : -v_j), summed as ((+-v0 +- v1) + (+-v2 +- v3)).
+__device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float v2, float v3,
+                                           int hi) {
+  const float hs = ((hi & 1) ? v2 : -v2) + ((hi & 2) ? v3 : -v3);
+  float4 e;
+  e.x = (-v0 - v1) + hs;
+  e.y = (v0 - v1) + hs;
+  e.z = (-v0 + v1) + hs;
+  e.w = (v0 + v1) + hs;
+  *reinterpret_cast<float4 *>(tab + 4 * hi) = e;
 }
 
 // ----------------------------------------------------------- products
-// First product of unit U over row tiles [t0, t1) of width a:
-// part[col] = 2 * sum_{rows, bit} z - sum_rows z   for every latent column.
-__device__ void first_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &S) {
-  const int nt = t1 - t0;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = lane >> 4, cc = lane & 15;
-  // z = g * x per layer and path, and its sums
-  for (int m = 0; m < U.n; ++m) {
-    const PLayer &Ly = A.layers[U.first + m];
-    for (int p = 0; p < Ly.P; ++p) {
-      float *z = S.z + (m * 2 + p) * 16 * kTMax;
-      float v = 0.f;
-      for (int r = threadIdx.x; r < 16 * nt; r += kThreads) {
-        const int i = 16 * t0 + r;
-        const float zi = i < U.a ? h2f(Ly.g[(size_t)p * Ly.a + i]) * S.xs[r] : 0.f;
-        z[r] = zi;
-        v += zi;
-      }
-      v = block_sum(v, S.red);
-      if (threadIdx.x == 0) S.zsum[m * 2 + p] = v;
-    }
-  }
-  __syncthreads();
-  // column tiles round-robin over waves; per tile: layer, mask base, z offset
-  const uint64_t *mb[kKMax];
-  int mstride[kKMax], zoff[kKMax], lidx[kKMax], colb[kKMax];
-#pragma unroll
-  for (int k = 0; k < kKMax; ++k) {
-    const int kap_u = wave + k * kWaves;
-    lidx[k] = -1; mb[k] = nullptr; mstride[k] = 0; zoff[k] = 0; colb[k] = 0;
-    if (kap_u < U.nct) {
-      int m = 0;
-      while (m + 1 < U.n && A.layers[U.first + m + 1].ct0 <= kap_u) ++m;
-      const PLayer &Ly = A.layers[U.first + m];
-      const int kap = kap_u - Ly.ct0;
-      const int col = 16 * kap + cc;
-      const int p = (col >= Ly.s && col < Ly.L) ? 1 : 0;
-      lidx[k] = m;
-      mb[k] = Ly.m1 + ((size_t)t0 * Ly.NCT + kap) * 4;
-      mstride[k] = Ly.NCT * 4;
-      zoff[k] = (m * 2 + p) * 16 * kTMax + 4 * q;
-      colb[k] = Ly.col0 + 16 * kap;
-    }
-  }
-  float acc[kKMax];
-#pragma unroll
-  for (int k = 0; k < kKMax; ++k) acc[k] = 0.f;
-  for (int t = 0; t < nt; ++t) {
-#pragma unroll
-    for (int k = 0; k < kKMax; ++k) {
-      if (lidx[k] >= 0) {
-        const float4 zv = *reinterpret_cast<const float4 *>(S.z + zoff[k] + 16 * t);
-        cmask_t *mk = (cmask_t *)(mb[k] + (size_t)t * mstride[k]);
-        const uint64_t k0 = mk[0], k1 = mk[1], k2 = mk[2], k3 = mk[3];
-        float a0 = acc[k];
-        a0 += __builtin_amdgcn_inverse_ballot_w64(k0) ? zv.x : 0.f;
-        a0 += __builtin_amdgcn_inverse_ballot_w64(k1) ? zv.y : 0.f;
-        a0 += __builtin_amdgcn_inverse_ballot_w64(k2) ? zv.z : 0.f;
-        a0 += __builtin_amdgcn_inverse_ballot_w64(k3) ? zv.w : 0.f;
-        acc[k] = a0;
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kKMax; ++k) {
-    float v = acc[k];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (lidx[k] >= 0 && q == 0) {
-      const PLayer &Ly = A.layers[U.first + lidx[k]];
-      const int col = colb[k] - Ly.col0 + cc;
-      if (col < Ly.L) {
-        const int p = col < Ly.s ? 0 : 1;
-        S.part[colb[k] + cc] = 2.f * v - S.zsum[lidx[k] * 2 + p];
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// After the exchange: w = l * t per layer/path in quarter-major layout
-// wq[(q * Qp) + i] = w[q*Q + i] (0 past s), and the sums of w.
-__device__ void prepare_w(const PArgs &A, const PUnit &U, Lds &S) {
-  int off = 0;
-  for (int m = 0; m < U.n; ++m) {
-    const PLayer &Ly = A.layers[U.first + m];
-    for (int p = 0; p < Ly.P; ++p) {
-      if (threadIdx.x == 0) S.wq_off[m * 2 + p] = off;
-      float *wq = S.wq + off;
-      float v = 0.f;
-      for (int e = threadIdx.x; e < 4 * Ly.Qp; e += kThreads) {
-        const int q = e / Ly.Qp, i = e - q * Ly.Qp;
-        const int k = q * Ly.Q + i;
-        float wv = 0.f;
-        if (i < Ly.Q && k < Ly.s) wv = h2f(Ly.l[(size_t)p * Ly.s + k]) * S.T[Ly.col0 + p * Ly.s + k];
-        wq[e] = wv;
-        v += wv;
-      }
-      v = block_sum(v, S.red);
-      if (threadIdx.x == 0) S.wsum[m * 2 + p] = v;
-      off += 4 * Ly.Qp;
-    }
-  }
-  __syncthreads();
-}
-
-// Second product of unit U over row tiles [t0, t1) of width b; outputs
-// each layer's fp16 y and accumulates the combine in S.ysum.
-__device__ void second_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &S) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = lane >> 4;
-  for (int r = threadIdx.x; r < 16 * kTMax; r += kThreads) S.ysum[r] = 0.f;
-  for (int tb = t0; tb < t1; tb += kTMax) {
-    const int nt = (t1 - tb) < kTMax ? (t1 - tb) : kTMax;
+// Second product of unit U over the workgroup's rows (tiles [t0, t1)):
+// every layer's fp16 outputs (trace), their combine into xs, and the
+// output rows on the last phase.
+__device__ void second_product(const PArgs &A, const PUnit &U, int ph, int t0, int t1, Lds &L,
+                               const Stage &S) {
+  const int nt = t1 - t0, rows = 16 * nt;
+  int tbase[kMaxUnitLayers * 2];
+  int ntask = 0;
+  {
+    int toff = 0;
     for (int m = 0; m < U.n; ++m) {
       const PLayer &Ly = A.layers[U.first + m];
-      const int nchunk = Ly.Qp / 4;          // chunks of 4 masks per path
-      const int total = Ly.P * nchunk;
-      float acc[2][kTMax];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int t = 0; t < kTMax; ++t) acc[p][t] = 0.f;
-      for (int ch = wave; ch < total; ch += kWaves) {
-        const int p = ch / nchunk, i0 = (ch - p * nchunk) * 4;
-        const float4 wv = *reinterpret_cast<const float4 *>(S.wq + S.wq_off[m * 2 + p] + q * Ly.Qp + i0);
-        cmask_t *base = (cmask_t *)(Ly.m2 + ((size_t)p * Ly.T16b + tb) * Ly.Qp + i0);
-#pragma unroll
-        for (int t = 0; t < kTMax; ++t) {
-          if (t < nt) {
-            cmask_t *mk = base + (size_t)t * Ly.Qp;
-            const uint64_t k0 = mk[0], k1 = mk[1], k2 = mk[2], k3 = mk[3];
-            float a0 = p == 0 ? acc[0][t] : acc[1][t];
-            a0 += __builtin_amdgcn_inverse_ballot_w64(k0) ? wv.x : 0.f;
-            a0 += __builtin_amdgcn_inverse_ballot_w64(k1) ? wv.y : 0.f;
-            a0 += __builtin_amdgcn_inverse_ballot_w64(k2) ? wv.z : 0.f;
-            a0 += __builtin_amdgcn_inverse_ballot_w64(k3) ? wv.w : 0.f;
-            if (p == 0) acc[0][t] = a0; else acc[1][t] = a0;
-          }
+      for (int p = 0; p < 2; ++p) {
+        tbase[m * 2 + p] = toff;
+        if (p < Ly.P) {
+          toff += Ly.Wk * 8 * 16;
+          ntask += Ly.Wk * 8 * 4;
         }
       }
-      // cross-wave reduction
+    }
+  }
+  // tables from w = l * t: task = (layer, path, group, hi)
+  for (int task = threadIdx.x; task < ntask; task += kThreads) {
+    int rem = task, m = 0, p = 0;
+    while (true) {
+      const int per = A.layers[U.first + m].Wk * 8 * 4;
+      if (rem < per) break;
+      rem -= per;
+      if (++p == A.layers[U.first + m].P) { p = 0; ++m; }
+    }
+    const PLayer &Ly = A.layers[U.first + m];
+    const int grp = rem >> 2, hi = rem & 3;
+    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + S.l_off[m]) + p * Ly.s8;
+    float v[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * grp + j;
+      v[j] = k < Ly.s ? h2f(lv[k]) * L.T[Ly.col0 + p * Ly.s + k] : 0.f;
+    }
+    table_quad(L.tab2 + tbase[m * 2 + p] + grp * 16, v[0], v[1], v[2], v[3], hi);
+  }
+  __syncthreads();
+  // lookups: task = (layer, path, row); lpt lanes of a task split the words
+  if (rows > 0) {
+    const int ntk = U.n * 2 * rows;
+    int lpt = 1;
+    while (lpt < 64 && ntk * lpt * 2 <= kThreads) lpt *= 2;
+    const int sub = threadIdx.x & (lpt - 1);
+    for (int tk0 = 0; tk0 < ntk; tk0 += kThreads / lpt) {
+      const int tk = tk0 + (int)threadIdx.x / lpt;
+      const int r = tk % rows, mp = tk / rows, m = mp >> 1, p = mp & 1;
+      float acc = 0.f;
+      if (tk < ntk && p < A.layers[U.first + m].P) {
+        const PLayer &Ly = A.layers[U.first + m];
+        const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + S.s2_off[m]) +
+                             ((size_t)((r >> 4) * Ly.P + p) * Ly.Wk) * 16 + (r & 15);
+        const float *tb = L.tab2 + tbase[m * 2 + p];
+        for (int q = sub; q < Ly.Wk; q += lpt) {
+          const uint32_t wd = wb[q * 16];
+          const float *tq = tb + q * 128;
 #pragma unroll
-        for (int t = 0; t < kTMax; ++t)
-          S.red[((wave * 2 + p) * kTMax + t) * 64 + lane] = acc[p][t];
-      __syncthreads();
-      for (int e = threadIdx.x; e < 16 * nt; e += kThreads) {
-        const int t = e >> 4, r = e & 15;
-        const int j = 16 * (tb + t) + r;
-        float yv = 0.f;
-        for (int p = 0; p < Ly.P; ++p) {
-          float sacc = 0.f;
-          for (int wv2 = 0; wv2 < kWaves; ++wv2)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) sacc += S.red[((wv2 * 2 + p) * kTMax + t) * 64 + 16 * qq + r];
-          const float u = 2.f * sacc - S.wsum[m * 2 + p];
-          if (j < U.b) yv += h2f(Ly.h[(size_t)p * Ly.b + j]) * u;
-        }
-        if (j < U.b) {
-          const uint16_t y16 = f2h(yv);
-          if (A.trace && Ly.trace_y >= 0) A.trace[Ly.trace_y + j] = y16;
-          S.ysum[16 * (tb - t0 + t) + r] += h2f(y16);
+          for (int n = 0; n < 8; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
         }
       }
-      __syncthreads();
+      for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      if (sub == 0 && tk < ntk) L.acc2[mp * (16 * kTMax) + r] = acc;
     }
   }
   __syncthreads();
+  // epilogue: y per layer, combine, output
+  for (int r = threadIdx.x; r < rows; r += kThreads) {
+    const int j = 16 * t0 + r;
+    float ys = 0.f;
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &Ly = A.layers[U.first + m];
+      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + S.h_off[m]);
+      float yv = 0.f;
+      for (int p = 0; p < Ly.P; ++p)
+        yv += h2f(hv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.acc2[(m * 2 + p) * (16 * kTMax) + r];
+      const uint16_t y16 = f2h(yv);
+      if (j < U.b && A.trace) A.trace[Ly.trace_y + j] = y16;
+      ys += h2f(y16);
+    }
+    const uint16_t xv = f2h(U.c_out * ys);
+    L.xs[r] = j < U.b ? h2f(xv) : 0.f;
+    if (j < U.b) {
+      if (ph == A.nunits)
+        A.y[j] = xv;
+      else if (A.trace)
+        A.trace[A.units[ph].trace_x + j] = xv;
+    }
+  }
+  __syncthreads();
+}
+
+// First product of unit U over the workgroup's rows: part[col] for every
+// latent column of every layer of the unit.
+__device__ void first_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &L,
+                              const Stage &S) {
+  const int nt = t1 - t0, rows = 16 * nt, quads = 4 * nt;
+  if (nt == 0) {
+    for (int c = threadIdx.x; c < U.Lu; c += kThreads) L.part[c] = 0.f;
+    __syncthreads();
+    return;
+  }
+  int tbase[kMaxUnitLayers * 2];
+  int ntask = 0;
+  {
+    int toff = 0;
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &Ly = A.layers[U.first + m];
+      for (int p = 0; p < 2; ++p) {
+        tbase[m * 2 + p] = toff;
+        if (p < Ly.P) {
+          toff += quads * 16;
+          ntask += quads * 4;
+        }
+      }
+    }
+  }
+  // tables from z = g * x: task = (layer, path, quad, hi)
+  for (int task = threadIdx.x; task < ntask; task += kThreads) {
+    const int per = quads * 4;
+    int mp_lin = task / per;
+    const int rem = task - mp_lin * per;
+    int m = 0;
+    while (mp_lin >= A.layers[U.first + m].P) { mp_lin -= A.layers[U.first + m].P; ++m; }
+    const int p = mp_lin;
+    const PLayer &Ly = A.layers[U.first + m];
+    const int qd = rem >> 2, hi = rem & 3;
+    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + S.g_off[m]);
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * qd + j;
+      v[j] = h2f(gv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.xs[r];
+    }
+    table_quad(L.tab1 + tbase[m * 2 + p] + qd * 16, v[0], v[1], v[2], v[3], hi);
+  }
+  __syncthreads();
+  int lpt = 1;
+  while (lpt < 64 && lpt < nt && U.Lu * lpt * 2 <= kThreads) lpt *= 2;
+  const int sub = threadIdx.x & (lpt - 1);
+  for (int c0 = 0; c0 < U.Lu; c0 += kThreads / lpt) {
+    const int c = c0 + (int)threadIdx.x / lpt;
+    float acc = 0.f;
+    if (c < U.Lu) {
+      int m = 0;
+      while (m + 1 < U.n && A.layers[U.first + m + 1].col0 <= c) ++m;
+      const PLayer &Ly = A.layers[U.first + m];
+      const int cl = c - Ly.col0;
+      const int p = cl < Ly.s ? 0 : 1;
+      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + S.s1_off[m]) + cl;
+      const float *tb = L.tab1 + tbase[m * 2 + p];
+      for (int gi = sub; gi < nt; gi += lpt) {
+        const uint32_t wd = bits[gi * Ly.Lp];
+        const float *tq = tb + gi * 64;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
+      }
+    }
+    for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
+    if (sub == 0 && c < U.Lu) L.part[c] = acc;
+  }
+  __syncthreads();
+}
+
+// -------------------------------------------------------- the exchange
+// part (LDS, Lu floats) of every workgroup -> T (LDS) = their sum.  Only
+// threads < kXThreads touch global memory; the others (the prefetch
+// waves) only join the barriers.  Every step issues all of its loads
+// before using any of them, so each step costs one memory round trip.
+constexpr int kXLoads = kLuMax / kXThreads;  // per-thread loads of one step
+
+__device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A) {
+  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+  const bool xw = t < kXThreads;
+  const int nsl = (Lu + 7) / 8;
+  if (xw) {
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k) {
+      const int c = t + k * kXThreads;
+      if (c < nsl * 8) st_f(&A.xpart[(size_t)w * kLuMax + c], c < Lu ? L.part[c] : 0.f);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  if (t == 0) st_u(&A.flag1[(size_t)w * kFlagStride], gen);
+  if (w < nsl) {
+    if (!wait_flags(A.flag1, G, gen, A.err, L.flags8)) return false;
+    for (int r = w; r < nsl; r += G) {
+      // lane t of load k reads element e = 256 k + t of the (producer, j)
+      // grid: 8 lanes cover one producer's 32 contiguous bytes.  Thread t
+      // sums column j = t % 8 over its producers in fixed order.
+      if (xw) {
+        float vals[kXLoads];
+#pragma unroll
+        for (int k = 0; k < kXLoads; ++k) {
+          const int e = t + k * kXThreads;
+          vals[k] = e < G * 8 ? ld_f(&A.xpart[(size_t)(e >> 3) * kLuMax + 8 * r + (e & 7)]) : 0.f;
+        }
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < kXLoads; ++k) v += vals[k];
+        L.red[t] = v;
+      }
+      __syncthreads();
+      for (int st = kXThreads / 2; st >= 8; st >>= 1) {
+        if (t < st) L.red[t] += L.red[t + st];
+        __syncthreads();
+      }
+      if (t < 8) st_f(&A.xT[8 * r + t], L.red[t]);
+      if (xw) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t == 0) st_u(&A.flag2[(size_t)r * kFlagStride], gen);
+    }
+  }
+  if (!wait_flags(A.flag2, nsl, gen, A.err, L.flags8)) return false;
+  if (xw) {
+    float vals[kXLoads];
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k) {
+      const int c = t + k * kXThreads;
+      vals[k] = c < Lu ? ld_f(&A.xT[c]) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k) {
+      const int c = t + k * kXThreads;
+      if (c < Lu) L.T[c] = vals[k];
+    }
+  }
+  __syncthreads();
+  return true;
 }
 
 // --------------------------------------------------------------- kernel
+__device__ __forceinline__ int phase_width(const PArgs &A, int ph) {
+  return ph == 0 ? A.units[0].a : A.units[ph - 1].b;
+}
+
 __global__ void __launch_bounds__(kThreads)
 k_persist(PArgs A) {
-  extern __shared__ __align__(16) float smem[];
-  Lds S;
+  extern __shared__ __align__(16) unsigned char smem[];
+  Lds L;
   {
-    float *p = smem;
-    S.xs = p; p += 16 * kTMax * 8;  // up to 8 batches of tiles
-    S.z = p; p += kMaxUnitLayers * 2 * 16 * kTMax;
-    S.zsum = p; p += kMaxUnitLayers * 2;
-    S.wsum = p; p += kMaxUnitLayers * 2;
-    S.wq_off = reinterpret_cast<int *>(p); p += kMaxUnitLayers * 2;
-    S.part = p; p += kLuMax;
-    S.T = p; p += kLuMax;
-    S.wq = p; p += kLuMax + 64 * kMaxUnitLayers;
-    S.ysum = p; p += 16 * kTMax * 8;
-    S.red = p;  // kWaves*2*kTMax*64 floats, also >= 16*kThreads for the exchange
+    unsigned char *p = smem;
+    L.stg = p; p += kStgBytes;
+    L.tab2 = reinterpret_cast<float *>(p); p += kTab2Floats * 4;
+    L.tab1 = reinterpret_cast<float *>(p); p += kTab1Floats * 4;
+    L.part = reinterpret_cast<float *>(p); p += kLuMax * 4;
+    L.T = reinterpret_cast<float *>(p); p += kLuMax * 4;
+    L.acc2 = reinterpret_cast<float *>(p); p += kMaxUnitLayers * 2 * 16 * kTMax * 4;
+    L.xs = reinterpret_cast<float *>(p); p += 16 * kTMax * 4;
+    L.red = reinterpret_cast<float *>(p); p += 8 * kXThreads * 4;
+    L.flags8 = reinterpret_cast<int *>(p);
   }
   const int G = gridDim.x, w = blockIdx.x;
   const int U = A.nunits;
+  uint64_t *tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * 4 : nullptr;
+  Stage S;
+  int t0, t1;
+  my_tiles((phase_width(A, 0) + 15) / 16, G, w, t0, t1);
+  stage_phase(A, 0, t0, t1, L.stg, S);
   for (int ph = 0; ph <= U; ++ph) {
+    if (wave_id() >= 4) __builtin_amdgcn_s_waitcnt(0);  // this phase's staged blocks landed
+    __syncthreads();
+    if (tl && threadIdx.x == 0) tl[ph * 4 + 0] = __builtin_amdgcn_s_memrealtime();
     {
-      const int bad = (threadIdx.x == 0) ? (int)ld_u(A.err) : 0;
-      if (__syncthreads_or(bad)) return;
+      const bool bad = threadIdx.x == 0 && ld_u(A.err) != 0;
+      if (!block_all(!bad, L.flags8)) return;
     }
-    // ---- input rows of this phase: width = units[ph].a (or last b)
-    int t0, t1;
     if (ph == 0) {
-      const PUnit &U0 = A.units[0];
-      my_tiles((U0.a + 15) / 16, G, w, t0, t1);
       for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
         const int i = 16 * t0 + r;
-        const uint16_t v = i < U0.a ? A.x0[i] : (uint16_t)0;
-        S.xs[r] = h2f(v);
-        if (A.trace && U0.trace_x >= 0 && i < U0.a) A.trace[U0.trace_x + i] = v;
+        const uint16_t v = i < A.units[0].a ? A.x0[i] : (uint16_t)0;
+        L.xs[r] = h2f(v);
+        if (A.trace && i < A.units[0].a) A.trace[A.units[0].trace_x + i] = v;
       }
       __syncthreads();
     } else {
-      const PUnit &Up = A.units[ph - 1];
-      my_tiles((Up.b + 15) / 16, G, w, t0, t1);
-      if (t1 - t0 > kTMax * 8) { if (threadIdx.x == 0) atomicOr(A.err, 2u); return; }
-      prepare_w(A, Up, S);
-      second_product(A, Up, t0, t1, S);
-      // combine: X = fp16(c * sum y)
-      for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
-        const int j = 16 * t0 + r;
-        const uint16_t v = f2h(Up.c_out * S.ysum[r]);
-        S.xs[r] = j < Up.b ? h2f(v) : 0.f;
-        if (j < Up.b) {
-          if (ph == U) {
-            A.y[j] = v;
-          } else if (A.trace && A.units[ph].trace_x >= 0) {
-            A.trace[A.units[ph].trace_x + j] = v;
-          }
-        }
-      }
-      __syncthreads();
+      second_product(A, A.units[ph - 1], ph, t0, t1, L, S);
+      if (tl && threadIdx.x == 0) tl[ph * 4 + 1] = __builtin_amdgcn_s_memrealtime();
       if (ph == U) break;
     }
-    // ---- first product of unit ph and the exchange
-    const PUnit &Uc = A.units[ph];
-    if (t1 - t0 > kTMax) { if (threadIdx.x == 0) atomicOr(A.err, 2u); return; }
-    first_product(A, Uc, t0, t1, S);
-    if (!exchange(S.part, S.T, S.red, Uc.Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
+    first_product(A, A.units[ph], t0, t1, L, S);
+    if (tl && threadIdx.x == 0) tl[ph * 4 + 2] = __builtin_amdgcn_s_memrealtime();
+    // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
+    my_tiles((phase_width(A, ph + 1) + 15) / 16, G, w, t0, t1);
+    stage_phase(A, ph + 1, t0, t1, L.stg, S);
+    if (!exchange(L, A.units[ph].Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
+    if (tl && threadIdx.x == 0) tl[ph * 4 + 3] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
 // ------------------------------------------------------------------ host
 static size_t lds_bytes() {
-  size_t f = 16 * kTMax * 8 + kMaxUnitLayers * 2 * 16 * kTMax + kMaxUnitLayers * 2 * 3 + kLuMax * 2 +
-             kLuMax + 64 * kMaxUnitLayers + 16 * kTMax * 8;
-  size_t red = (size_t)kWaves * 2 * kTMax * 64;
-  const size_t red_x = (size_t)16 * kThreads;
-  if (red_x > red) red = red_x;
-  return (f + red) * sizeof(float) + 256;
+  return (size_t)kStgBytes + (size_t)(kTab2Floats + kTab1Floats + 2 * kLuMax +
+                                      kMaxUnitLayers * 2 * 16 * kTMax + 16 * kTMax +
+                                      8 * kXThreads + kWaves) * 4 + 64;
 }
 
 int64_t persist_max_rows() { return 1; }
@@ -459,78 +559,91 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return LB_EHIP;
   const int G = prop.multiProcessorCount;
-  if (G < 1 || G > kThreads) return LB_EUNSUPPORTED;
+  if (G < 1 || G > kXThreads || G % 32 != 0) return LB_EUNSUPPORTED;
   PersistPlan *P = new PersistPlan();
   P->device = device;
   P->G = G;
   P->nunits = (int)unit_begin.size();
   P->nlayers = (int)layers.size();
-  int64_t ty = 0;
-  for (auto *Lr : layers) ty += Lr->ly.b;
-  int64_t tx = ty;
-  int spw_max = 1;
+  int64_t tx = 0;
+  for (auto *Lr : layers) tx += Lr->ly.b;
+  auto unsupported = [&]() { delete P; return LB_EUNSUPPORTED; };
   for (int u = 0; u < P->nunits; ++u) {
     PUnit U{};
     U.first = unit_begin[u];
     U.n = unit_size[u];
+    if (U.n > kMaxUnitLayers) return unsupported();
     const Layer &L0 = layers[U.first]->ly;
     U.a = (int)L0.a;
     U.b = (int)L0.b;
     U.c_out = kappa / std::sqrt((float)U.n);
     U.trace_x = tx;
     tx += U.a;
-    int col = 0, ct = 0;
+    int col = 0;
     int64_t yoff = 0;
     for (int i = 0; i < U.first; ++i) yoff += layers[i]->ly.b;
-    if (U.n > kMaxUnitLayers) { delete P; return LB_EUNSUPPORTED; }
     for (int m = 0; m < U.n; ++m) {
       const Layer &Ly = layers[U.first + m]->ly;
-      if (Ly.P > 2) { delete P; return LB_EUNSUPPORTED; }
       PLayer D{};
-      D.m1 = Ly.m1; D.m2 = Ly.m2; D.h = Ly.h; D.g = Ly.g; D.l = Ly.l;
-      D.a = (int)Ly.a; D.b = (int)Ly.b; D.s = (int)Ly.s; D.P = Ly.P;
-      D.Q = (int)Ly.Q; D.Qp = (int)Ly.Qp; D.NCT = (int)Ly.NCT; D.L = (int)Ly.L;
-      D.T16a = (int)Ly.T16a; D.T16b = (int)Ly.T16b;
-      D.col0 = col; D.ct0 = ct;
+      D.su2t = Ly.su2t; D.sv16 = Ly.sv16; D.ht = Ly.ht; D.gt = Ly.gt; D.l = Ly.l;
+      D.a = (int)Ly.a; D.b = (int)Ly.b; D.s = (int)Ly.s; D.P = Ly.P; D.L = (int)Ly.L;
+      D.Lp = (int)Ly.Lp; D.Wk = (int)Ly.Wk; D.a16 = (int)Ly.a16; D.b16 = (int)Ly.b16;
+      D.s8 = (int)Ly.s8;
+      D.col0 = col;
       D.trace_y = yoff;
       yoff += Ly.b;
       col += (int)Ly.L;
-      ct += (int)Ly.NCT;
       P->h_layers.push_back(D);
     }
     U.Lu = col;
-    U.nct = ct;
-    if (U.Lu > kLuMax || (U.nct + kWaves - 1) / kWaves > kKMax) { delete P; return LB_EUNSUPPORTED; }
-    // row tiles per workgroup must fit the per-phase buffers
-    const int ta = ((U.a + 15) / 16 + G - 1) / G, tb = ((U.b + 15) / 16 + G - 1) / G;
-    if (ta > kTMax || tb > kTMax) { delete P; return LB_EUNSUPPORTED; }
-    // wq capacity: sum over layers/paths of 4*Qp
-    int wq = 0;
-    for (int m = 0; m < U.n; ++m) wq += layers[U.first + m]->ly.P * 4 * (int)layers[U.first + m]->ly.Qp;
-    if (wq > kLuMax + 64 * kMaxUnitLayers) { delete P; return LB_EUNSUPPORTED; }
-    const int spw = (U.Lu + G - 1) / G;
-    if (spw > 16) { delete P; return LB_EUNSUPPORTED; }
-    if (spw > spw_max) spw_max = spw;
+    if (U.Lu > kLuMax) return unsupported();
     P->h_units.push_back(U);
   }
-  // units must chain
   for (int u = 1; u < P->nunits; ++u)
     if (P->h_units[u].a != P->h_units[u - 1].b) { delete P; return LB_EINVAL; }
-  P->spw_max = spw_max;
+  // per-phase capacity: tiles, staged bytes, tables
+  for (int ph = 0; ph <= P->nunits; ++ph) {
+    const int width = ph == 0 ? P->h_units[0].a : P->h_units[ph - 1].b;
+    const int nt = ((width + 15) / 16 + G - 1) / G;
+    if (nt > kTMax) return unsupported();
+    long stg = 0, tab2 = 0, tab1 = 0;
+    if (ph > 0) {
+      const PUnit &U = P->h_units[ph - 1];
+      for (int m = 0; m < U.n; ++m) {
+        const PLayer &D = P->h_layers[U.first + m];
+        stg += (long)D.P * ((long)D.Wk * 64 * nt + 32 * nt + 2 * D.s8);
+        tab2 += (long)D.P * D.Wk * 128;
+      }
+    }
+    if (ph < P->nunits) {
+      const PUnit &U = P->h_units[ph];
+      for (int m = 0; m < U.n; ++m) {
+        const PLayer &D = P->h_layers[U.first + m];
+        stg += (long)nt * D.Lp * 2 + (long)D.P * 32 * nt;
+        tab1 += (long)D.P * 64 * nt;
+      }
+    }
+    if (stg > kStgBytes || tab2 > kTab2Floats || tab1 > kTab1Floats) return unsupported();
+  }
   P->lds = lds_bytes();
-  if (P->lds > (size_t)prop.sharedMemPerBlock) { delete P; return LB_EUNSUPPORTED; }
+  if (P->lds > (size_t)prop.sharedMemPerBlock) return unsupported();
+  const size_t nflags = ((size_t)G + kLuMax / 8 + 1) * kFlagStride;
   bool ok = hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
             hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
-            hipMalloc(&P->xpart, sizeof(float) * (size_t)G * G * spw_max) == hipSuccess &&
+            hipMalloc(&P->xpart, sizeof(float) * (size_t)G * kLuMax) == hipSuccess &&
             hipMalloc(&P->xT, sizeof(float) * kLuMax) == hipSuccess &&
-            hipMalloc(&P->flags, sizeof(unsigned) * (2 * (size_t)G + 64)) == hipSuccess;
-  ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemset(P->flags, 0, sizeof(unsigned) * (2 * (size_t)G + 64)) == hipSuccess;
+            hipMalloc(&P->flags, sizeof(unsigned) * nflags) == hipSuccess;
+  ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits,
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers,
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemset(P->flags, 0, sizeof(unsigned) * nflags) == hipSuccess;
+  ok = ok && hipMemset(P->xpart, 0, sizeof(float) * (size_t)G * kLuMax) == hipSuccess;
   ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)P->lds) == hipSuccess;
   int occ = 0;
-  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_persist, kThreads, P->lds) == hipSuccess;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_persist, kThreads, P->lds) ==
+                 hipSuccess;
   if (!ok || occ < 1) {
     persist_free(P);
     return ok ? LB_EUNSUPPORTED : LB_EHIP;
@@ -549,12 +662,13 @@ void persist_free(PersistPlan *p) {
   delete p;
 }
 
-lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace,
-                      int64_t M, hipStream_t st, std::string *msg) {
+lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace, int64_t M,
+                      hipStream_t st, std::string *msg) {
   if (M != 1) return LB_EUNSUPPORTED;
+  const size_t nflags = ((size_t)p->G + kLuMax / 8 + 1) * kFlagStride;
   if (p->broken) {
     // a previous launch timed out: reset the flags before reuse
-    if (hipMemset(p->flags, 0, sizeof(unsigned) * (2 * (size_t)p->G + 64)) != hipSuccess) return LB_EHIP;
+    if (hipMemset(p->flags, 0, sizeof(unsigned) * nflags) != hipSuccess) return LB_EHIP;
     p->gen = 0;
     p->broken = false;
   }
@@ -569,9 +683,9 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.xpart = p->xpart;
   A.xT = p->xT;
   A.flag1 = p->flags;
-  A.flag2 = p->flags + p->G;
-  A.err = p->flags + 2 * p->G;
-  A.spw_max = p->spw_max;
+  A.flag2 = p->flags + (size_t)p->G * kFlagStride;
+  A.err = p->flags + ((size_t)p->G + kLuMax / 8) * kFlagStride;
+  A.timeline = p->timeline;
   hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -582,9 +696,15 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   return LB_OK;
 }
 
+void persist_set_timeline(PersistPlan *p, uint64_t *buf) { p->timeline = buf; }
+int persist_grid(const PersistPlan *p) { return p->G; }
+int persist_phases(const PersistPlan *p) { return p->nunits + 1; }
+
 lb_status persist_check(PersistPlan *p, std::string *msg) {
   unsigned e = 0;
-  if (hipMemcpy(&e, p->flags + 2 * p->G, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(&e, p->flags + ((size_t)p->G + kLuMax / 8) * kFlagStride, sizeof(unsigned),
+                hipMemcpyDeviceToHost) !=
+      hipSuccess)
     return LB_EHIP;
   if (e) {
     p->broken = true;

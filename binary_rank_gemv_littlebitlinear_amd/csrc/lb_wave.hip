@@ -42,7 +42,7 @@ constexpr int kS1Threads = 256;
 // part[(c*M + m)*L + col] = 2 * sum_{bit} z - sum z over the chunk.
 __global__ void __launch_bounds__(kS1Threads)
 k_wave_stage1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
-              const uint16_t *__restrict__ x, int64_t a, int64_t s, int64_t L, int P,
+              const uint16_t *__restrict__ x, int64_t a, int64_t a16, int64_t s, int64_t L, int P,
               int64_t R1, int M, int G, float *__restrict__ part) {
   extern __shared__ float smem[];
   const int c = blockIdx.x;
@@ -62,7 +62,7 @@ k_wave_stage1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
     const int il = rem - p * nrow;
     const int64_t i = r0 * 32 + il;
     float v = 0.f;
-    if (i < a) v = h2f(g[p * a + i]) * h2f(x[(int64_t)m * a + i]);
+    if (i < a) v = h2f(g[p * a16 + i]) * h2f(x[(int64_t)m * a + i]);
     z[(m * P + p) * zstride + il] = v;
   }
   __syncthreads();
@@ -92,14 +92,16 @@ k_wave_stage1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
 
 // w[m*L + col] = l[col] * sum_c part[(c*M + m)*L + col]
 __global__ void k_wave_reduce(const float *__restrict__ part, const uint16_t *__restrict__ l,
-                              int64_t L, int M, int nchunk, float *__restrict__ w) {
+                              int64_t s, int64_t s8, int64_t L, int M, int nchunk,
+                              float *__restrict__ w) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * L) return;
   const int m = (int)(idx / L);
   const int64_t col = idx - (int64_t)m * L;
   float t = 0.f;
   for (int c = 0; c < nchunk; ++c) t += part[((int64_t)c * M + m) * L + col];
-  w[idx] = h2f(l[col]) * t;
+  const int64_t p = col / s;
+  w[idx] = h2f(l[p * s8 + (col - p * s)]) * t;
 }
 
 constexpr int kS2Threads = 256;
@@ -107,8 +109,8 @@ constexpr int kS2Threads = 256;
 // One thread per output row j.  LDS holds w for one row of x at a time.
 __global__ void __launch_bounds__(kS2Threads)
 k_wave_stage2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
-              const float *__restrict__ w, int64_t b, int64_t s, int64_t L, int P, int64_t Wk,
-              int M, uint16_t *__restrict__ y) {
+              const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
+              int64_t Wk, int M, uint16_t *__restrict__ y) {
   extern __shared__ float smem[];
   float *wl = smem;           // [L]
   float *ws = smem + L;       // [P]
@@ -131,7 +133,7 @@ k_wave_stage2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
         const float *wp = wl + p * s;
         float acc = 0.f;
         for (int64_t q = 0; q < Wk; ++q) {
-          const uint32_t wd = su2[(p * Wk + q) * b + j];
+          const uint32_t wd = su2[(p * Wk + q) * b16 + j];
           const int64_t kb = q * 32;
           const int nb = (s - kb) < 32 ? (int)(s - kb) : 32;
           if (nb == 32) {
@@ -141,7 +143,7 @@ k_wave_stage2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
             for (int bit = 0; bit < nb; ++bit) acc += ((wd >> bit) & 1u) ? wp[kb + bit] : 0.f;
           }
         }
-        out += h2f(h[p * b + j]) * (2.f * acc - ws[p]);
+        out += h2f(h[p * b16 + j]) * (2.f * acc - ws[p]);
       }
       y[(int64_t)m * b + j] = f2h(out);
     }
@@ -176,12 +178,12 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
   const size_t lds = ((size_t)M * Ly.P * G * 32 + (size_t)M * Ly.P + 16) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_wave_stage1, dim3(nch), dim3(kS1Threads), lds, st, Ly.sv1, Ly.g, x, Ly.a,
-                     Ly.s, Ly.L, Ly.P, Ly.R1, (int)M, G, ws);
+                     Ly.a16, Ly.s, Ly.L, Ly.P, Ly.R1, (int)M, G, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = M * Ly.L;
   hipLaunchKernelGGL(k_wave_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ws, Ly.l,
-                     Ly.L, (int)M, nch, w_out);
+                     Ly.s, Ly.s8, Ly.L, (int)M, nch, w_out);
   return hipGetLastError();
 }
 
@@ -190,8 +192,8 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
   const size_t lds = ((size_t)Ly.L + 2 + 16) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_wave_stage2, dim3((unsigned)((Ly.b + kS2Threads - 1) / kS2Threads)),
-                     dim3(kS2Threads), lds, st, Ly.su2, Ly.h, w, Ly.b, Ly.s, Ly.L, Ly.P, Ly.Wk,
-                     (int)M, y);
+                     dim3(kS2Threads), lds, st, Ly.su2, Ly.h, w, Ly.b, Ly.b16, Ly.s, Ly.L, Ly.P,
+                     Ly.Wk, (int)M, y);
   return hipGetLastError();
 }
 

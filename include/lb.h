@@ -151,6 +151,13 @@ lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t *elems);
  * its synchronisation words before the next sweep).  LB_OK otherwise. */
 lb_status lb_stack_check(lb_stack *S);
 
+/* Diagnostics: record, in later persistent sweeps, four device timestamps
+ * (100 MHz counter) per phase and workgroup into the caller's device buffer
+ * buf (uint64, layout [workgroup][phase][4]: phase start, second product
+ * done, first product done, exchange done).  *needed receives the element
+ * count.  buf = NULL turns recording off.  The buffer must outlive its use. */
+lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed);
+
 /* Select the execution mode of lb_stack_forward: 0 = automatic, 1 = per
  * layer kernels only, 2 = persistent only (LB_EUNSUPPORTED if impossible). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);
