@@ -59,7 +59,7 @@ constexpr int kTab1Floats = 4096;
 constexpr long kSpin = 4000000;  // polls before a wait gives up
 constexpr int kFlagStride = 64;  // flags 256 bytes apart (separate lines and channels)
 
-struct PLayer {
+struct alignas(16) PLayer {
   const uint32_t *su2t;
   const uint16_t *sv16, *ht, *gt, *l;
   int a, b, s, P, L, Lp, Wk, a16, b16, s8;
@@ -67,13 +67,34 @@ struct PLayer {
   int64_t trace_y;  // element offset of this layer's output in the trace
 };
 
-struct PUnit {
+struct alignas(16) PUnit {
   int first, n;
   int a, b;
   int Lu;
   float c_out;      // kappa / sqrt(n): combine of this unit's outputs
   int64_t trace_x;  // element offset of this unit's input in the trace
 };
+
+// One block a workgroup copies into LDS for a phase: src + t0 * stride,
+// fixed + nt * per_tile bytes (t0, nt: the workgroup's first tile and tile
+// count).  A phase's list starts with a header record (per_tile = the
+// phase's row width, fixed = record count).  Lists are kMaxSeg records
+// apart, so the next phase's list is found without reading this one.
+enum : int { kSegHeader = 0, kSegUnits = 1, kSegLayers = 2, kSegS2 = 3, kSegH = 4, kSegL = 5,
+             kSegS1 = 6, kSegG = 7 };
+constexpr int kMaxSeg = 3 + 5 * kMaxUnitLayers;
+
+struct alignas(16) PSeg {
+  const void *src;
+  long long stride;
+  int per_tile;
+  int fixed;
+  int kind;  // kind | layer << 8
+  int pad;
+};
+
+static_assert(sizeof(PLayer) % 16 == 0 && sizeof(PUnit) % 16 == 0 && sizeof(PSeg) == 32,
+              "descriptors are copied to LDS in 16-byte units");
 
 struct PArgs {
   const PUnit *units;
@@ -89,6 +110,7 @@ struct PArgs {
   unsigned *flag2;  // [kLuMax / 8] flags, kFlagStride words apart
   unsigned *err;
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
+  const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
 };
 
 struct PersistPlan {
@@ -98,6 +120,7 @@ struct PersistPlan {
   size_t lds = 0;
   PUnit *d_units = nullptr;
   PLayer *d_layers = nullptr;
+  PSeg *d_segs = nullptr;
   std::vector<PUnit> h_units;
   std::vector<PLayer> h_layers;
   float *xpart = nullptr, *xT = nullptr;
@@ -164,6 +187,19 @@ __device__ bool wait_flags(unsigned *flags, int n, unsigned gen, unsigned *err, 
 }
 
 // ------------------------------------------------------ LDS arrangement
+// Everything a phase reads besides its tables lives in LDS: the staged
+// sign bits and scales, and a copy of the descriptors of the two units the
+// phase touches (unit A = ph-1 for the second product, unit B = ph for the
+// first), so the compute never waits on global memory.
+struct PhaseCtx {
+  PUnit ua, ub;                       // copied by LDS-DMA (adjacent units)
+  PLayer la[2 * kMaxUnitLayers];      // layers of A, then of B (copied by LDS-DMA)
+  int has_a;                          // the phase has a second product (ph > 0)
+  int t0, t1;                         // row tiles of the phase
+  int s2_off[kMaxUnitLayers], h_off[kMaxUnitLayers], l_off[kMaxUnitLayers];
+  int s1_off[kMaxUnitLayers], g_off[kMaxUnitLayers];
+};
+
 struct Lds {
   unsigned char *stg;  // kStgBytes staged bits and scales of the phase
   float *tab2;         // kTab2Floats second-product tables
@@ -172,67 +208,80 @@ struct Lds {
   float *T;            // kLuMax
   float *acc2;         // kMaxUnitLayers * 2 * 16 * kTMax
   float *xs;           // 16 * kTMax input rows (fp16 values as fp32)
-  float *red;          // 8 * kXThreads exchange scratch
+  float *red;          // kXThreads exchange scratch
   int *flags8;         // kWaves
+  PhaseCtx *ctx;
+  PSeg *segbuf;        // [2][kMaxSeg] copy lists of this and the next phase
 };
 
-// Offsets of the staged blocks of one phase (identical in every wave).
-struct Stage {
-  // second product of unit ph-1
-  int s2_off[kMaxUnitLayers];  // uint32 [nt][P][Wk][16]
-  int h_off[kMaxUnitLayers];   // fp16  [nt][P][16]
-  int l_off[kMaxUnitLayers];   // fp16  [P][s8]
-  // first product of unit ph
-  int s1_off[kMaxUnitLayers];  // uint16 [nt][Lp]
-  int g_off[kMaxUnitLayers];   // fp16  [nt][P][16]
-};
-
-// Lay out the blocks of phase ph for tiles [t0, t1) and copy them into
-// LDS with LDS-DMA loads (16 bytes per lane, 1 KB per wave instruction);
-// the instructions of all blocks go round-robin to waves 4-7.
-__device__ void stage_phase(const PArgs &A, int ph, int t0, int t1, unsigned char *stg, Stage &S) {
+// Stage phase ph: copy the blocks of its list (descriptors of units ph-1
+// and ph, sign bits, scales) into LDS with LDS-DMA loads (16 bytes per
+// lane, 1 KB per wave instruction) issued round-robin by waves 4-7, and
+// the next phase's list into the other list buffer.  The list itself was
+// staged one phase earlier, so nothing here reads global memory.  Wave 4
+// writes the block offsets into the phase context.  Waves 4-7 only.
+__device__ void stage_phase(const PArgs &A, int ph, Lds &L) {
+  const int G = gridDim.x;
+  const PSeg *lst = L.segbuf + (ph & 1) * kMaxSeg;
+  const int width = lst[0].per_tile, nseg = lst[0].fixed;
+  int t0, t1;
+  my_tiles((width + 15) / 16, G, blockIdx.x, t0, t1);
   const int nt = t1 - t0;
   int off = 0, kglob = 0;
   const int pw = wave_id() - 4;  // prefetch wave index 0..3
   const int lane = threadIdx.x & 63;
-  auto copy = [&](const void *src, int dst, int nbytes) {
+  PhaseCtx &C = *L.ctx;
+  auto copy = [&](const void *src, unsigned char *dst, int nbytes) {
     const int units = nbytes / 16;
     const int nch = (units + 63) / 64;
     for (int c = 0; c < nch; ++c, ++kglob) {
-      if (pw < 0 || (kglob & 3) != pw) continue;
+      if ((kglob & 3) != pw) continue;
       const int u = c * 64 + lane;
       if (u < units)
-        __builtin_amdgcn_global_load_lds((const char *)src + (size_t)u * 16, stg + dst + c * 1024, 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const char *)src + (size_t)u * 16, dst + c * 1024, 16, 0, 0);
     }
   };
-  if (ph > 0) {
-    const PUnit &U = A.units[ph - 1];
-    for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = A.layers[U.first + m];
-      S.s2_off[m] = off;
-      copy(Ly.su2t + (size_t)t0 * Ly.P * Ly.Wk * 16, off, nt * Ly.P * Ly.Wk * 64);
-      off += nt * Ly.P * Ly.Wk * 64;
-      S.h_off[m] = off;
-      copy(Ly.ht + (size_t)t0 * Ly.P * 16, off, nt * Ly.P * 32);
-      off += nt * Ly.P * 32;
-      S.l_off[m] = off;
-      copy(Ly.l, off, Ly.P * Ly.s8 * 2);
-      off += Ly.P * Ly.s8 * 2;
-    }
+  const bool lead = pw == 0 && lane == 0;
+  if (lead) {
+    C.has_a = ph > 0;
+    C.t0 = t0;
+    C.t1 = t1;
   }
-  if (ph < A.nunits) {
-    const PUnit &U = A.units[ph];
-    for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = A.layers[U.first + m];
-      S.s1_off[m] = off;
-      copy(Ly.sv16 + (size_t)t0 * Ly.Lp, off, nt * Ly.Lp * 2);
-      off += nt * Ly.Lp * 2;
-      S.g_off[m] = off;
-      copy(Ly.gt + (size_t)t0 * Ly.P * 16, off, nt * Ly.P * 32);
-      off += nt * Ly.P * 32;
+  for (int k = 1; k < nseg; ++k) {
+    const PSeg sg = lst[k];
+    const int bytes = sg.fixed + nt * sg.per_tile;
+    const char *src = (const char *)sg.src + (long long)t0 * sg.stride;
+    const int kind = sg.kind & 255, m = sg.kind >> 8;
+    unsigned char *dst;
+    if (kind == kSegUnits) {
+      dst = reinterpret_cast<unsigned char *>(ph > 0 ? &C.ua : &C.ub);
+    } else if (kind == kSegLayers) {
+      dst = reinterpret_cast<unsigned char *>(C.la);
+    } else {
+      dst = L.stg + off;
+      if (lead) {
+        if (kind == kSegS2) C.s2_off[m] = off;
+        else if (kind == kSegH) C.h_off[m] = off;
+        else if (kind == kSegL) C.l_off[m] = off;
+        else if (kind == kSegS1) C.s1_off[m] = off;
+        else if (kind == kSegG) C.g_off[m] = off;
+      }
+      off += bytes;
     }
+    copy(src, dst, bytes);
   }
+  if (ph < A.nunits)
+    copy(A.segs + (size_t)(ph + 1) * kMaxSeg,
+         reinterpret_cast<unsigned char *>(L.segbuf + ((ph + 1) & 1) * kMaxSeg), kMaxSeg * 32);
+}
+
+// a[i] for a runtime i without a dynamically indexed (scratch) array.
+template <int N>
+__device__ __forceinline__ int pick(const int (&a)[N], int i) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) v = k == i ? a[k] : v;
+  return v;
 }
 
 // Entries lo + 4*hi (lo = 0..3) of the table over (v0, v1, v2, v3), entry
@@ -249,46 +298,45 @@ __device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float
 }
 
 // ----------------------------------------------------------- products
-// Second product of unit U over the workgroup's rows (tiles [t0, t1)):
-// every layer's fp16 outputs (trace), their combine into xs, and the
-// output rows on the last phase.
-__device__ void second_product(const PArgs &A, const PUnit &U, int ph, int t0, int t1, Lds &L,
-                               const Stage &S) {
-  const int nt = t1 - t0, rows = 16 * nt;
-  int tbase[kMaxUnitLayers * 2];
+// Second product of unit A over the workgroup's rows: every layer's fp16
+// outputs (trace), their combine into xs, and the output rows on the last
+// phase.  All descriptors come from the LDS phase context.
+__device__ void second_product(const PArgs &A, int ph, Lds &L) {
+  const PhaseCtx &C = *L.ctx;
+  const PUnit &U = C.ua;
+  const int t0 = C.t0, nt = C.t1 - C.t0, rows = 16 * nt;
+  // table bases and task counts per (layer, path): small uniform loop over LDS
+  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
   int ntask = 0;
   {
     int toff = 0;
-    for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = A.layers[U.first + m];
-      for (int p = 0; p < 2; ++p) {
-        tbase[m * 2 + p] = toff;
-        if (p < Ly.P) {
-          toff += Ly.Wk * 8 * 16;
-          ntask += Ly.Wk * 8 * 4;
-        }
-      }
+#pragma unroll
+    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
+      const int m = mp >> 1, p = mp & 1;
+      const bool live = m < U.n && p < C.la[m].P;
+      tbase[mp] = toff;
+      tcnt[mp] = live ? C.la[m].Wk * 8 * 4 : 0;
+      toff += live ? C.la[m].Wk * 8 * 16 : 0;
+      ntask += tcnt[mp];
     }
   }
   // tables from w = l * t: task = (layer, path, group, hi)
   for (int task = threadIdx.x; task < ntask; task += kThreads) {
-    int rem = task, m = 0, p = 0;
-    while (true) {
-      const int per = A.layers[U.first + m].Wk * 8 * 4;
-      if (rem < per) break;
-      rem -= per;
-      if (++p == A.layers[U.first + m].P) { p = 0; ++m; }
-    }
-    const PLayer &Ly = A.layers[U.first + m];
+    int rem = task, mp = 0;
+#pragma unroll
+    for (int i = 0; i < 2 * kMaxUnitLayers; ++i)
+      if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
+    const int m = mp >> 1, p = mp & 1;
+    const PLayer &Ly = C.la[m];
     const int grp = rem >> 2, hi = rem & 3;
-    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + S.l_off[m]) + p * Ly.s8;
+    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + C.l_off[m]) + p * Ly.s8;
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = 4 * grp + j;
       v[j] = k < Ly.s ? h2f(lv[k]) * L.T[Ly.col0 + p * Ly.s + k] : 0.f;
     }
-    table_quad(L.tab2 + tbase[m * 2 + p] + grp * 16, v[0], v[1], v[2], v[3], hi);
+    table_quad(L.tab2 + pick(tbase, mp) + grp * 16, v[0], v[1], v[2], v[3], hi);
   }
   __syncthreads();
   // lookups: task = (layer, path, row); lpt lanes of a task split the words
@@ -301,12 +349,13 @@ __device__ void second_product(const PArgs &A, const PUnit &U, int ph, int t0, i
       const int tk = tk0 + (int)threadIdx.x / lpt;
       const int r = tk % rows, mp = tk / rows, m = mp >> 1, p = mp & 1;
       float acc = 0.f;
-      if (tk < ntk && p < A.layers[U.first + m].P) {
-        const PLayer &Ly = A.layers[U.first + m];
-        const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + S.s2_off[m]) +
+      if (tk < ntk && p < C.la[m].P) {
+        const PLayer &Ly = C.la[m];
+        const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + C.s2_off[m]) +
                              ((size_t)((r >> 4) * Ly.P + p) * Ly.Wk) * 16 + (r & 15);
-        const float *tb = L.tab2 + tbase[m * 2 + p];
-        for (int q = sub; q < Ly.Wk; q += lpt) {
+        const float *tb = L.tab2 + pick(tbase, mp);
+        const int Wk = Ly.Wk;
+        for (int q = sub; q < Wk; q += lpt) {
           const uint32_t wd = wb[q * 16];
           const float *tq = tb + q * 128;
 #pragma unroll
@@ -323,8 +372,8 @@ __device__ void second_product(const PArgs &A, const PUnit &U, int ph, int t0, i
     const int j = 16 * t0 + r;
     float ys = 0.f;
     for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = A.layers[U.first + m];
-      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + S.h_off[m]);
+      const PLayer &Ly = C.la[m];
+      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + C.h_off[m]);
       float yv = 0.f;
       for (int p = 0; p < Ly.P; ++p)
         yv += h2f(hv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.acc2[(m * 2 + p) * (16 * kTMax) + r];
@@ -338,55 +387,55 @@ __device__ void second_product(const PArgs &A, const PUnit &U, int ph, int t0, i
       if (ph == A.nunits)
         A.y[j] = xv;
       else if (A.trace)
-        A.trace[A.units[ph].trace_x + j] = xv;
+        A.trace[C.ub.trace_x + j] = xv;
     }
   }
   __syncthreads();
 }
 
-// First product of unit U over the workgroup's rows: part[col] for every
+// First product of unit B over the workgroup's rows: part[col] for every
 // latent column of every layer of the unit.
-__device__ void first_product(const PArgs &A, const PUnit &U, int t0, int t1, Lds &L,
-                              const Stage &S) {
-  const int nt = t1 - t0, rows = 16 * nt, quads = 4 * nt;
+__device__ void first_product(Lds &L) {
+  const PhaseCtx &C = *L.ctx;
+  const PUnit &U = C.ub;
+  const PLayer *LB = C.la + (C.has_a ? C.ua.n : 0);
+  const int nt = C.t1 - C.t0, quads = 4 * nt;
   if (nt == 0) {
     for (int c = threadIdx.x; c < U.Lu; c += kThreads) L.part[c] = 0.f;
     __syncthreads();
     return;
   }
-  int tbase[kMaxUnitLayers * 2];
+  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
   int ntask = 0;
   {
     int toff = 0;
-    for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = A.layers[U.first + m];
-      for (int p = 0; p < 2; ++p) {
-        tbase[m * 2 + p] = toff;
-        if (p < Ly.P) {
-          toff += quads * 16;
-          ntask += quads * 4;
-        }
-      }
+#pragma unroll
+    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
+      const int m = mp >> 1, p = mp & 1;
+      const bool live = m < U.n && p < LB[m].P;
+      tbase[mp] = toff;
+      tcnt[mp] = live ? quads * 4 : 0;
+      toff += live ? quads * 16 : 0;
+      ntask += tcnt[mp];
     }
   }
   // tables from z = g * x: task = (layer, path, quad, hi)
   for (int task = threadIdx.x; task < ntask; task += kThreads) {
-    const int per = quads * 4;
-    int mp_lin = task / per;
-    const int rem = task - mp_lin * per;
-    int m = 0;
-    while (mp_lin >= A.layers[U.first + m].P) { mp_lin -= A.layers[U.first + m].P; ++m; }
-    const int p = mp_lin;
-    const PLayer &Ly = A.layers[U.first + m];
+    int rem = task, mp = 0;
+#pragma unroll
+    for (int i = 0; i < 2 * kMaxUnitLayers; ++i)
+      if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
+    const int m = mp >> 1, p = mp & 1;
+    const PLayer &Ly = LB[m];
     const int qd = rem >> 2, hi = rem & 3;
-    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + S.g_off[m]);
+    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + C.g_off[m]);
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * qd + j;
       v[j] = h2f(gv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.xs[r];
     }
-    table_quad(L.tab1 + tbase[m * 2 + p] + qd * 16, v[0], v[1], v[2], v[3], hi);
+    table_quad(L.tab1 + pick(tbase, mp) + qd * 16, v[0], v[1], v[2], v[3], hi);
   }
   __syncthreads();
   int lpt = 1;
@@ -397,14 +446,15 @@ __device__ void first_product(const PArgs &A, const PUnit &U, int t0, int t1, Ld
     float acc = 0.f;
     if (c < U.Lu) {
       int m = 0;
-      while (m + 1 < U.n && A.layers[U.first + m + 1].col0 <= c) ++m;
-      const PLayer &Ly = A.layers[U.first + m];
+      while (m + 1 < U.n && LB[m + 1].col0 <= c) ++m;
+      const PLayer &Ly = LB[m];
       const int cl = c - Ly.col0;
       const int p = cl < Ly.s ? 0 : 1;
-      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + S.s1_off[m]) + cl;
-      const float *tb = L.tab1 + tbase[m * 2 + p];
+      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + C.s1_off[m]) + cl;
+      const float *tb = L.tab1 + pick(tbase, m * 2 + p);
+      const int Lp = Ly.Lp;
       for (int gi = sub; gi < nt; gi += lpt) {
-        const uint32_t wd = bits[gi * Ly.Lp];
+        const uint32_t wd = bits[gi * Lp];
         const float *tq = tb + gi * 64;
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
@@ -485,9 +535,6 @@ __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A) {
 }
 
 // --------------------------------------------------------------- kernel
-__device__ __forceinline__ int phase_width(const PArgs &A, int ph) {
-  return ph == 0 ? A.units[0].a : A.units[ph - 1].b;
-}
 
 __global__ void __launch_bounds__(kThreads)
 k_persist(PArgs A) {
@@ -495,6 +542,8 @@ k_persist(PArgs A) {
   Lds L;
   {
     unsigned char *p = smem;
+    L.ctx = reinterpret_cast<PhaseCtx *>(p); p += (sizeof(PhaseCtx) + 15) / 16 * 16;
+    L.segbuf = reinterpret_cast<PSeg *>(p); p += 2 * kMaxSeg * sizeof(PSeg);
     L.stg = p; p += kStgBytes;
     L.tab2 = reinterpret_cast<float *>(p); p += kTab2Floats * 4;
     L.tab1 = reinterpret_cast<float *>(p); p += kTab1Floats * 4;
@@ -502,52 +551,52 @@ k_persist(PArgs A) {
     L.T = reinterpret_cast<float *>(p); p += kLuMax * 4;
     L.acc2 = reinterpret_cast<float *>(p); p += kMaxUnitLayers * 2 * 16 * kTMax * 4;
     L.xs = reinterpret_cast<float *>(p); p += 16 * kTMax * 4;
-    L.red = reinterpret_cast<float *>(p); p += 8 * kXThreads * 4;
+    L.red = reinterpret_cast<float *>(p); p += kXThreads * 4;
     L.flags8 = reinterpret_cast<int *>(p);
   }
-  const int G = gridDim.x, w = blockIdx.x;
+  const int w = blockIdx.x;
   const int U = A.nunits;
   uint64_t *tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * 4 : nullptr;
-  Stage S;
-  int t0, t1;
-  my_tiles((phase_width(A, 0) + 15) / 16, G, w, t0, t1);
-  stage_phase(A, 0, t0, t1, L.stg, S);
+  // phase 0's copy list (kMaxSeg records of two 16-byte words), then its blocks
+  for (int i = threadIdx.x; i < kMaxSeg * 2; i += kThreads)
+    reinterpret_cast<uint4 *>(L.segbuf)[i] = reinterpret_cast<const uint4 *>(A.segs)[i];
+  __syncthreads();
+  if (wave_id() >= 4) stage_phase(A, 0, L);
   for (int ph = 0; ph <= U; ++ph) {
     if (wave_id() >= 4) __builtin_amdgcn_s_waitcnt(0);  // this phase's staged blocks landed
     __syncthreads();
     if (tl && threadIdx.x == 0) tl[ph * 4 + 0] = __builtin_amdgcn_s_memrealtime();
-    {
-      const bool bad = threadIdx.x == 0 && ld_u(A.err) != 0;
-      if (!block_all(!bad, L.flags8)) return;
-    }
+    const int t0 = L.ctx->t0, t1 = L.ctx->t1;
     if (ph == 0) {
+      const PUnit &U0 = L.ctx->ub;
       for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
         const int i = 16 * t0 + r;
-        const uint16_t v = i < A.units[0].a ? A.x0[i] : (uint16_t)0;
+        const uint16_t v = i < U0.a ? A.x0[i] : (uint16_t)0;
         L.xs[r] = h2f(v);
-        if (A.trace && i < A.units[0].a) A.trace[A.units[0].trace_x + i] = v;
+        if (A.trace && i < U0.a) A.trace[U0.trace_x + i] = v;
       }
       __syncthreads();
     } else {
-      second_product(A, A.units[ph - 1], ph, t0, t1, L, S);
+      second_product(A, ph, L);
       if (tl && threadIdx.x == 0) tl[ph * 4 + 1] = __builtin_amdgcn_s_memrealtime();
       if (ph == U) break;
     }
-    first_product(A, A.units[ph], t0, t1, L, S);
+    first_product(L);
+    const int Lu = L.ctx->ub.Lu;
     if (tl && threadIdx.x == 0) tl[ph * 4 + 2] = __builtin_amdgcn_s_memrealtime();
+    __syncthreads();  // everyone has read the phase context before it is restaged
     // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
-    my_tiles((phase_width(A, ph + 1) + 15) / 16, G, w, t0, t1);
-    stage_phase(A, ph + 1, t0, t1, L.stg, S);
-    if (!exchange(L, A.units[ph].Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
+    if (wave_id() >= 4) stage_phase(A, ph + 1, L);
+    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
     if (tl && threadIdx.x == 0) tl[ph * 4 + 3] = __builtin_amdgcn_s_memrealtime();
   }
 }
 
 // ------------------------------------------------------------------ host
 static size_t lds_bytes() {
-  return (size_t)kStgBytes + (size_t)(kTab2Floats + kTab1Floats + 2 * kLuMax +
-                                      kMaxUnitLayers * 2 * 16 * kTMax + 16 * kTMax +
-                                      8 * kXThreads + kWaves) * 4 + 64;
+  return (sizeof(PhaseCtx) + 15) / 16 * 16 + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
+         (size_t)(kTab2Floats + kTab1Floats + 2 * kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
+                  16 * kTMax + kXThreads + kWaves) * 4 + 64;
 }
 
 int64_t persist_max_rows() { return 1; }
@@ -600,7 +649,11 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     P->h_units.push_back(U);
   }
   for (int u = 1; u < P->nunits; ++u)
-    if (P->h_units[u].a != P->h_units[u - 1].b) { delete P; return LB_EINVAL; }
+    if (P->h_units[u].a != P->h_units[u - 1].b ||
+        P->h_units[u].first != P->h_units[u - 1].first + P->h_units[u - 1].n) {
+      delete P;
+      return LB_EINVAL;
+    }
   // per-phase capacity: tiles, staged bytes, tables
   for (int ph = 0; ph <= P->nunits; ++ph) {
     const int width = ph == 0 ? P->h_units[0].a : P->h_units[ph - 1].b;
@@ -637,6 +690,46 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers,
                        hipMemcpyHostToDevice) == hipSuccess;
+  // per-phase copy lists (device addresses of the descriptors are known now)
+  std::vector<PSeg> segs((size_t)(P->nunits + 1) * kMaxSeg);
+  for (int ph = 0; ph <= P->nunits && ok; ++ph) {
+    PSeg *lst = &segs[(size_t)ph * kMaxSeg];
+    int n = 1;
+    auto add = [&](const void *src, long long stride, int per_tile, int fixed, int kind, int m) {
+      lst[n++] = PSeg{src, stride, per_tile, fixed, kind | (m << 8), 0};
+    };
+    const int ua = ph > 0 ? ph - 1 : 0;
+    const int nun = (ph > 0) + (ph < P->nunits);
+    add(P->d_units + ua, 0, 0, (int)sizeof(PUnit) * nun, kSegUnits, 0);
+    int nly = 0;
+    if (ph > 0) nly += P->h_units[ph - 1].n;
+    if (ph < P->nunits) nly += P->h_units[ph].n;
+    add(P->d_layers + P->h_units[ua].first, 0, 0, (int)sizeof(PLayer) * nly, kSegLayers, 0);
+    if (ph > 0) {
+      const PUnit &U = P->h_units[ph - 1];
+      for (int m = 0; m < U.n; ++m) {
+        const PLayer &D = P->h_layers[U.first + m];
+        add(D.su2t, (long long)D.P * D.Wk * 64, D.P * D.Wk * 64, 0, kSegS2, m);
+        add(D.ht, 32LL * D.P, 32 * D.P, 0, kSegH, m);
+        add(D.l, 0, 0, 2 * D.P * D.s8, kSegL, m);
+      }
+    }
+    if (ph < P->nunits) {
+      const PUnit &U = P->h_units[ph];
+      for (int m = 0; m < U.n; ++m) {
+        const PLayer &D = P->h_layers[U.first + m];
+        add(D.sv16, 2LL * D.Lp, 2 * D.Lp, 0, kSegS1, m);
+        add(D.gt, 32LL * D.P, 32 * D.P, 0, kSegG, m);
+      }
+    }
+    const int width = ph == 0 ? P->h_units[0].a : P->h_units[ph - 1].b;
+    lst[0] = PSeg{nullptr, 0, width, n, kSegHeader, 0};
+    for (int k = 1; k < n; ++k)
+      if ((lst[k].per_tile | lst[k].fixed) % 16 != 0) ok = false;  // DMA moves 16-byte units
+  }
+  ok = ok && hipMalloc(&P->d_segs, sizeof(PSeg) * segs.size()) == hipSuccess;
+  ok = ok && hipMemcpy(P->d_segs, segs.data(), sizeof(PSeg) * segs.size(), hipMemcpyHostToDevice) ==
+                 hipSuccess;
   ok = ok && hipMemset(P->flags, 0, sizeof(unsigned) * nflags) == hipSuccess;
   ok = ok && hipMemset(P->xpart, 0, sizeof(float) * (size_t)G * kLuMax) == hipSuccess;
   ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -656,6 +749,7 @@ void persist_free(PersistPlan *p) {
   if (!p) return;
   if (p->d_units) (void)hipFree(p->d_units);
   if (p->d_layers) (void)hipFree(p->d_layers);
+  if (p->d_segs) (void)hipFree(p->d_segs);
   if (p->xpart) (void)hipFree(p->xpart);
   if (p->xT) (void)hipFree(p->xT);
   if (p->flags) (void)hipFree(p->flags);
@@ -686,6 +780,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.flag2 = p->flags + (size_t)p->G * kFlagStride;
   A.err = p->flags + ((size_t)p->G + kLuMax / 8) * kFlagStride;
   A.timeline = p->timeline;
+  A.segs = p->d_segs;
   hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
