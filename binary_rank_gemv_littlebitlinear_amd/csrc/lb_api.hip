@@ -3,6 +3,7 @@
 // effective-bit arithmetic of [LB2 column] Ch. 1 and the stack runner.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -38,7 +39,9 @@ struct DevCtx {
   DeviceInfo info;
   void *ws = nullptr;  // shared forward workspace of this device
   size_t ws_bytes = 0;
+  unsigned *cnt = nullptr;  // split-K tile counters of the MFMA path (kept zero)
 };
+constexpr size_t kDevCounters = 4096;
 std::mutex g_mu;
 std::map<int, DevCtx> g_dev;
 
@@ -53,6 +56,9 @@ lb_status get_dev(int device, DevCtx **out) {
     if (e != hipSuccess) return fail(LB_EHIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
     c.info.cu_count = prop.multiProcessorCount;
     c.info.coop = prop.cooperativeLaunch;
+    e = hipMalloc(&c.cnt, kDevCounters * sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(c.cnt, 0, kDevCounters * sizeof(unsigned));
+    if (e != hipSuccess) return fail(LB_ENOMEM, std::string("counter hipMalloc: ") + hipGetErrorString(e));
     it = g_dev.emplace(device, c).first;
   }
   *out = &it->second;
@@ -113,14 +119,14 @@ void transpose32(uint32_t m[32]) {
 static inline DevCtx *ctx_of(const lb_layer *L) { return static_cast<DevCtx *>(L->ctx); }
 
 // --------------------------------------------------------- workspace need
-static size_t layer_ws_need(const Layer &Ly, const DeviceInfo &dev) {
+static size_t layer_ws_need(const Layer &Ly, const MfmaPlan *mp, const DeviceInfo &dev) {
   size_t need = 0;
   for (int64_t M = 1; M < 64; ++M) {
     const int nch = wave_nchunk(Ly, M, dev);
     const size_t b = (wave_ws_floats(Ly, M, nch) + (size_t)M * Ly.L) * sizeof(float) + 512;
     if (b > need) need = b;
   }
-  const size_t mf = mfma_ws_bytes(Ly, 256);
+  const size_t mf = mfma_unit_ws_bytes(mp);
   if (mf > need) need = mf;
   return need;
 }
@@ -170,7 +176,15 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
       return fail(LB_EHIP, std::string("lb_create: hipMemset: ") + hipGetErrorString(e));
     }
   }
-  st = ensure_ws(dc, layer_ws_need(Ly, dc->info));
+  {
+    const Layer *one = &Ly;
+    L->mplan = mfma_plan_build(&one, 1);
+  }
+  if (!L->mplan || mfma_cnt_entries(L->mplan) > kDevCounters) {
+    lb_destroy(L);
+    return fail(LB_EUNSUPPORTED, "lb_create: shape not supported by the MFMA path");
+  }
+  st = ensure_ws(dc, layer_ws_need(Ly, L->mplan, dc->info));
   if (st != LB_OK) {
     lb_destroy(L);
     return st;
@@ -186,6 +200,7 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt};
   for (void *p : ps)
     if (p) (void)hipFree(p);
+  mfma_plan_free(L->mplan);
   delete L;
   return LB_OK;
 }
@@ -341,7 +356,8 @@ static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y,
     if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 2: ") + hipGetErrorString(e));
     return LB_OK;
   }
-  hipError_t e = launch_mfma_forward(Ly, x, y, M, dc->ws, dc->info, st);
+  uint16_t *ys[1] = {y};
+  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, dc->ws, dc->cnt, dc->info, st);
   if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma path: ") + hipGetErrorString(e));
   return LB_OK;
 }
@@ -438,6 +454,9 @@ struct lb_stack {
   void *xbuf[2] = {nullptr, nullptr};  // unit input ping-pong (cap_M x max a)
   int64_t max_width = 0;
   PersistPlan *persist = nullptr;
+  std::vector<MfmaPlan *> uplan;  // per unit, for M >= 64
+  void *mws = nullptr;            // unit-path workspace (largest unit)
+  unsigned *mcnt = nullptr;       // unit-path tile counters (kept zero)
 };
 
 static void stack_free_scratch(lb_stack *S) {
@@ -520,6 +539,28 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     delete S;
     return st;
   }
+  {
+    size_t wsb = 0, nc = 0;
+    for (int u = 0; u < n_units; ++u) {
+      std::vector<const Layer *> ls;
+      for (int k = 0; k < S->unit_size[u]; ++k) ls.push_back(&S->layers[S->unit_begin[u] + k]->ly);
+      MfmaPlan *mp = mfma_plan_build(ls.data(), (int)ls.size());
+      S->uplan.push_back(mp);
+      if (!mp) {
+        lb_stack_destroy(S);
+        return fail(LB_EUNSUPPORTED, "lb_stack_create: unit not supported by the MFMA path");
+      }
+      wsb = std::max(wsb, mfma_unit_ws_bytes(mp));
+      nc = std::max(nc, mfma_cnt_entries(mp));
+    }
+    hipError_t e = hipMalloc(&S->mws, wsb);
+    if (e == hipSuccess) e = hipMalloc(&S->mcnt, nc * sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(S->mcnt, 0, nc * sizeof(unsigned));
+    if (e != hipSuccess) {
+      lb_stack_destroy(S);
+      return fail(LB_ENOMEM, std::string("lb_stack_create: hipMalloc: ") + hipGetErrorString(e));
+    }
+  }
   st = persist_build(S->layers, S->unit_begin, S->unit_size, S->kappa, S->device, &S->persist);
   if (st != LB_OK && st != LB_EUNSUPPORTED) {
     stack_free_scratch(S);
@@ -558,6 +599,9 @@ extern "C" lb_status lb_stack_destroy(lb_stack *S) {
   DeviceGuard dg(S->device);
   stack_free_scratch(S);
   persist_free(S->persist);
+  for (MfmaPlan *mp : S->uplan) mfma_plan_free(mp);
+  if (S->mws) (void)hipFree(S->mws);
+  if (S->mcnt) (void)hipFree(S->mcnt);
   delete S;
   return LB_OK;
 }
@@ -609,6 +653,28 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
   }
   lb_status rs = stack_reserve(S, M);
   if (rs != LB_OK) return rs;
+  if (M >= 64 && S->mode != 1) {
+    // one stage-1 and one stage-2 launch per unit; stage 2 also combines
+    const uint16_t *cur = (const uint16_t *)x0;
+    if (trace)
+      LB_HIP(hipMemcpyAsync(tX[0], x0, (size_t)M * S->layers[0]->ly.a * 2, hipMemcpyDeviceToDevice, st));
+    for (int u = 0; u < U; ++u) {
+      const int b0 = S->unit_begin[u], nu = S->unit_size[u];
+      uint16_t *next;
+      if (u == U - 1)
+        next = (uint16_t *)y;
+      else if (trace)
+        next = tX[u + 1];
+      else
+        next = (uint16_t *)S->xbuf[u & 1];
+      hipError_t e = launch_mfma_unit(S->uplan[u], cur, M, trace ? &tY[b0] : nullptr, next,
+                                      S->kappa / std::sqrt((float)nu), false, S->mws, S->mcnt,
+                                      ctx_of(S->layers[b0])->info, st);
+      if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma unit: ") + hipGetErrorString(e));
+      cur = next;
+    }
+    return LB_OK;
+  }
   const uint16_t *cur = (const uint16_t *)x0;
   if (trace) {
     LB_HIP(hipMemcpyAsync(tX[0], x0, (size_t)M * S->layers[0]->ly.a * 2, hipMemcpyDeviceToDevice, st));

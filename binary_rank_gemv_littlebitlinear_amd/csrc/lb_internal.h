@@ -77,6 +77,8 @@ struct Layer {
   }
 };
 
+struct MfmaPlan;
+
 }  // namespace lbi
 
 // The C ABI's opaque layer handle.
@@ -84,6 +86,7 @@ struct lb_layer {
   lbi::Layer ly;
   void *ctx = nullptr;  // the device context (workspace owner)
   void *plan = nullptr; // single-layer persistent plan (M = 1), may be null
+  lbi::MfmaPlan *mplan = nullptr;  // the layer as a one-layer MFMA unit
 };
 
 namespace lbi {
@@ -99,10 +102,23 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
                               hipStream_t st);
 
-// MFMA path, any M (used for M >= 64).  ws must hold mfma_ws_bytes().
-size_t mfma_ws_bytes(const Layer &Ly, int64_t M);
-hipError_t launch_mfma_forward(const Layer &Ly, const uint16_t *x, uint16_t *y, int64_t M,
-                               void *ws, const DeviceInfo &dev, hipStream_t st);
+// MFMA path (used for M >= 64) over a unit: 1..kMaxUnitLayersM layers of
+// one shape that read the same input.  Rows are processed kMfmaRows at a
+// time.  ws must hold mfma_unit_ws_bytes() and cnt mfma_cnt_entries()
+// counters that are zero before the first launch (the kernels leave them
+// zero).  direct: y_layers[0] = the layer's output; otherwise xout =
+// fp16(c_out * sum_m fp16(y_m)) and each non-null y_layers[m] receives y_m.
+constexpr int kMaxUnitLayersM = 8;
+constexpr int kMaxUnitSegs = 2 * kMaxUnitLayersM;
+constexpr int kMfmaRows = 256;
+struct MfmaPlan;
+MfmaPlan *mfma_plan_build(const Layer *const *layers, int n);  // null if unsupported
+void mfma_plan_free(MfmaPlan *p);
+size_t mfma_unit_ws_bytes(const MfmaPlan *p);
+size_t mfma_cnt_entries(const MfmaPlan *p);
+hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
+                            uint16_t *const *y_layers, uint16_t *xout, float c_out, bool direct,
+                            void *ws, unsigned *cnt, const DeviceInfo &dev, hipStream_t st);
 
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,

@@ -76,6 +76,15 @@ def test_mfma_path_shapes(lbm, a, b, s, M):
     _check(lbm, a, b, s, True, M, a * 7 + s, "mfma")
 
 
+@pytest.mark.parametrize("a,b,s,res,M", [(257, 129, 63, False, 65), (1000, 3, 33, True, 64),
+                                         (3, 1000, 31, False, 100), (4096, 4096, 86, False, 128),
+                                         (33, 65, 1, True, 513)])
+def test_mfma_path_odd_shapes(lbm, a, b, s, res, M):
+    """Widths and ranks off every tile size, single and residual paths,
+    row counts across the 256-row chunking."""
+    _check(lbm, a, b, s, res, M, a + 3 * b + s, "mfma-odd")
+
+
 def test_rows_are_independent(lbm):
     """Row m of a batched call matches the M = 1 call on row m."""
     a, b, s = 512, 256, 40

@@ -100,11 +100,42 @@ def test_mlp_stack_two_blocks(lbm, M):
     check_stack(wl, paths, x0, y, tr, M)
 
 
-def test_full_block_stack_M128(lbm):
+@pytest.mark.parametrize("mode", [0, 1])
+def test_full_block_stack_M128(lbm, mode):
+    """Mode 0 runs one unit (q/k/v, o, gate/up, down) per launch pair with
+    the combine fused; mode 1 runs each layer alone, then a combine."""
     wl, S, paths = build_stack(lbm, "llama7b_full_stack_M128", blocks=1)
-    say("[case] full block stack M=128")
-    x0, y, tr = run_stack(lbm, wl, S, 128)
+    say(f"[case] full block stack M=128 mode={mode}")
+    x0, y, tr = run_stack(lbm, wl, S, 128, mode=mode)
     check_stack(wl, paths, x0, y, tr, 128)
+
+
+@pytest.mark.parametrize("M", [64, 70, 257])
+def test_unit_path_odd_widths(lbm, M):
+    wl, S, paths = _odd_stack(lbm)
+    say(f"[case] unit path odd widths M={M}")
+    x0, y, tr = run_stack(lbm, wl, S, M, mode=0)
+    check_stack(wl, paths, x0, y, tr, M)
+    _, y1, _ = run_stack(lbm, wl, S, M, mode=1)
+    assert_parity(y.astype(np.float64), y1.astype(np.float64), "unit vs per-layer")
+
+
+def test_unit_path_repeated_and_deterministic(lbm):
+    """Split-K partial sums are combined in a fixed order: repeated batched
+    runs are bitwise identical, and the tile counters are left at zero."""
+    torch = lbtest.torch_dev()
+    wl, S, paths = build_stack(lbm, "llama7b_full_stack_M128", blocks=1)
+    say("[case] unit path repeated M=128")
+    x0, y, tr = run_stack(lbm, wl, S, 128, mode=0)
+    xd = lbtest.to_dev(x0)
+    outs = []
+    for _ in range(10):
+        y2 = torch.empty((128, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+        S.forward(xd, y2, None)
+        outs.append(y2)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), y.view(np.uint16))
 
 
 def test_stack_without_trace_matches_trace_run(lbm):
