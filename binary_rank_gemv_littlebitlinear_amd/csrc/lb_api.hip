@@ -40,6 +40,7 @@ struct DevCtx {
   void *ws = nullptr;  // shared forward workspace of this device
   size_t ws_bytes = 0;
   unsigned *cnt = nullptr;  // split-K tile counters of the MFMA path (kept zero)
+  void *zero = nullptr;     // 256 zero bytes (copy source for padding)
 };
 constexpr size_t kDevCounters = 4096;
 std::mutex g_mu;
@@ -56,8 +57,9 @@ lb_status get_dev(int device, DevCtx **out) {
     if (e != hipSuccess) return fail(LB_EHIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
     c.info.cu_count = prop.multiProcessorCount;
     c.info.coop = prop.cooperativeLaunch;
-    e = hipMalloc(&c.cnt, kDevCounters * sizeof(unsigned));
-    if (e == hipSuccess) e = hipMemset(c.cnt, 0, kDevCounters * sizeof(unsigned));
+    e = hipMalloc(&c.cnt, kDevCounters * sizeof(unsigned) + 256);
+    if (e == hipSuccess) e = hipMemset(c.cnt, 0, kDevCounters * sizeof(unsigned) + 256);
+    c.zero = c.cnt + kDevCounters;
     if (e != hipSuccess) return fail(LB_ENOMEM, std::string("counter hipMalloc: ") + hipGetErrorString(e));
     it = g_dev.emplace(device, c).first;
   }
@@ -96,6 +98,20 @@ struct DeviceGuard {
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
+
+// Word in the matrix-core bit order (see lb_internal.h): bits inverted and
+// permuted so that (w << (4 g + j)) & 0x80008000 holds the sign flips of
+// elements 8 g + 2 j and 8 g + 2 j + 1.
+inline uint32_t mfma_bit_order(uint32_t w) {
+  uint32_t o = 0;
+  for (int g = 0; g < 4; ++g)
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t flip = ((w >> (8 * g + e)) & 1u) ^ 1u;
+      const int pos = (e & 1) ? 31 - (e >> 1) - 4 * g : 15 - (e >> 1) - 4 * g;
+      o |= flip << pos;
+    }
+  return o;
+}
 
 inline uint32_t tail_mask(int64_t s, int64_t q) {
   const int64_t n = s - 32 * q;
@@ -163,7 +179,9 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
       {(void **)&Ly.sv16, (size_t)Ly.T16a * Ly.Lp * 2},
       {(void **)&Ly.su2t, (size_t)Ly.T16b * Ly.P * Ly.Wk * 16 * 4},
       {(void **)&Ly.ht, (size_t)Ly.T16b * Ly.P * 16 * 2},
-      {(void **)&Ly.gt, (size_t)Ly.T16a * Ly.P * 16 * 2}};
+      {(void **)&Ly.gt, (size_t)Ly.T16a * Ly.P * 16 * 2},
+      {(void **)&Ly.sv1m, (size_t)Ly.R1 * Ly.L * 4},
+      {(void **)&Ly.su2m, (size_t)Ly.P * Ly.Wk * Ly.b16 * 4}};
   for (auto &al : allocs) {
     hipError_t e = hipMalloc(al.p, al.n);
     if (e != hipSuccess) {
@@ -197,7 +215,7 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   if (!L) return LB_OK;
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
-  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt};
+  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   mfma_plan_free(L->mplan);
@@ -239,6 +257,11 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
   }
   LB_HIP(hipMemcpy(Ly.su2 + (size_t)path * Wk * b16, u2.data(), u2.size() * 4, hipMemcpyHostToDevice));
   {
+    std::vector<uint32_t> u2m(u2.size());
+    for (size_t i = 0; i < u2.size(); ++i) u2m[i] = mfma_bit_order(u2[i]);
+    LB_HIP(hipMemcpy(Ly.su2m + (size_t)path * Wk * b16, u2m.data(), u2m.size() * 4, hipMemcpyHostToDevice));
+  }
+  {
     // tile-major: for tile tau, this path's Wk x 16 words are one 64*Wk-byte run
     std::vector<uint32_t> u2t((size_t)Ly.T16b * Wk * 16);
     for (int64_t tau = 0; tau < Ly.T16b; ++tau)
@@ -266,6 +289,11 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
       }
     }
     LB_HIP(hipMemcpy(Ly.sv1, v1.data(), v1.size() * 4, hipMemcpyHostToDevice));
+    {
+      std::vector<uint32_t> v1m(v1.size());
+      for (size_t i = 0; i < v1.size(); ++i) v1m[i] = mfma_bit_order(v1[i]);
+      LB_HIP(hipMemcpy(Ly.sv1m, v1m.data(), v1m.size() * 4, hipMemcpyHostToDevice));
+    }
     // sv16[gi*Lp + c]: the 16-row halves of the sv1 words
     for (int64_t gi = 0; gi < Ly.T16a; ++gi)
       for (int64_t c = 0; c < Lc; ++c)
@@ -357,7 +385,8 @@ static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y,
     return LB_OK;
   }
   uint16_t *ys[1] = {y};
-  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, dc->ws, dc->cnt, dc->info, st);
+  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, dc->ws, dc->cnt, dc->zero,
+                                 dc->info, st);
   if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma path: ") + hipGetErrorString(e));
   return LB_OK;
 }
@@ -669,7 +698,7 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
         next = (uint16_t *)S->xbuf[u & 1];
       hipError_t e = launch_mfma_unit(S->uplan[u], cur, M, trace ? &tY[b0] : nullptr, next,
                                       S->kappa / std::sqrt((float)nu), false, S->mws, S->mcnt,
-                                      ctx_of(S->layers[b0])->info, st);
+                                      ctx_of(S->layers[b0])->zero, ctx_of(S->layers[b0])->info, st);
       if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma unit: ") + hipGetErrorString(e));
       cur = next;
     }

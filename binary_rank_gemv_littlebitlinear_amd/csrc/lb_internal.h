@@ -31,6 +31,14 @@
 //   ht[(tau * P + p) * 16 + r] = h[p*b16 + 16 tau + r]   (fp16)
 //   gt[(tau * P + p) * 16 + r] = g[p*a16 + 16 tau + r]   (fp16)
 //
+// Copies for the matrix-core path, same indexing as sv1 / su2 but with each
+// word's bits inverted (1 = sign -1) and permuted: the sign of element
+// 8 g + e (g = 0..3, e = 0..7) sits at bit 15 - e/2 - 4 g for even e and
+// 31 - (e - 1)/2 - 4 g for odd e.  Shifting the word left by 4 g + j and
+// masking 0x80008000 then gives the fp16 sign flips of elements 8 g + 2 j
+// and 8 g + 2 j + 1, one 32-bit operand register of a lane's 8 values:
+//   sv1m[r * L + c], su2m[(p*Wk + q) * b16 + j]
+//
 // Padding bits and padding scales are zero, so they contribute nothing.
 #pragma once
 
@@ -67,6 +75,8 @@ struct Layer {
   uint32_t *su2t = nullptr; // T16b * P * Wk * 16
   uint16_t *ht = nullptr;   // T16b * P * 16
   uint16_t *gt = nullptr;   // T16a * P * 16
+  uint32_t *sv1m = nullptr; // R1 * L words (matrix-core bit order)
+  uint32_t *su2m = nullptr; // P * Wk * b16 words (matrix-core bit order)
   // workspace: stage-1 partials / latent vectors, sized at create time
   float *ws = nullptr;
   size_t ws_bytes = 0;
@@ -106,7 +116,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
 // one shape that read the same input.  Rows are processed kMfmaRows at a
 // time.  ws must hold mfma_unit_ws_bytes() and cnt mfma_cnt_entries()
 // counters that are zero before the first launch (the kernels leave them
-// zero).  direct: y_layers[0] = the layer's output; otherwise xout =
+// zero); zero points to >= 256 zero bytes of device memory.  direct: y_layers[0] = the layer's output; otherwise xout =
 // fp16(c_out * sum_m fp16(y_m)) and each non-null y_layers[m] receives y_m.
 constexpr int kMaxUnitLayersM = 8;
 constexpr int kMaxUnitSegs = 2 * kMaxUnitLayersM;
@@ -118,7 +128,8 @@ size_t mfma_unit_ws_bytes(const MfmaPlan *p);
 size_t mfma_cnt_entries(const MfmaPlan *p);
 hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             uint16_t *const *y_layers, uint16_t *xout, float c_out, bool direct,
-                            void *ws, unsigned *cnt, const DeviceInfo &dev, hipStream_t st);
+                            void *ws, unsigned *cnt, const void *zero, const DeviceInfo &dev,
+                            hipStream_t st);
 
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,

@@ -27,16 +27,21 @@
 // element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2), register
 // 4 * (i / 8) + i % 4.
 //
-// Both stages compute 64 x 64 output tiles with 4 waves per workgroup.
-// The waves split K (interleaved 32-row chunks); their partial tiles are
-// summed in a fixed order through LDS.  Stage 1 also splits K across
-// workgroups when the tile count alone cannot fill the chip; the last
-// workgroup of a tile to finish (an atomic counter per tile) sums the
-// partials in split order, so the result does not depend on timing.
+// Stage 1 computes 32 x 128 tiles (each of 4 waves owns 32 columns, so no
+// cross-wave sum); stage 2 computes 32 x 64 tiles with the 4 waves
+// interleaved over the (path, 32-column) chunks of K and their partials
+// summed in wave order through LDS.  Each workgroup copies its operands
+// into LDS with LDS-DMA in rounds (x or T rows, sign words and the
+// per-k scales g or l), the next round in flight while the current one
+// is multiplied.  Stage 1 also splits K across workgroups when the tiles
+// alone cannot fill the chip; the last workgroup of a tile to finish (an
+// atomic counter per tile) sums the partials in split order, so the
+// result does not depend on timing.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <vector>
 
 #include "lb_internal.h"
@@ -45,13 +50,31 @@ namespace lbi {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kRP = 64 + 4;    // LDS pitch (floats) of a 64 x 64 partial tile
 constexpr int kMaxSplit = 8;
+// stage 1: a workgroup computes 32 rows x 128 latent columns (32 per wave);
+// a round stages kRC1 32-row chunks of the input dimension in LDS
+constexpr int kRC1 = 14;
+constexpr int kS1X = kRC1 * 4 * 512;   // x rows: [c8][32 rows][8 fp16]
+constexpr int kS1W = 4 * kRC1 * 128;   // sign words: [wave][chunk][32 columns]
+constexpr int kS1G = 4 * 1024;         // column scales g: [wave][16 chunks][32 rows]
+constexpr int kS1Buf = kS1X + kS1W + kS1G;
+// stage 2: a workgroup computes 32 rows x 64 outputs; a round stages kRC2
+// (path, 32-column) chunks of one layer's latent rows and sign words
+constexpr int kRC2 = 28;
+constexpr int kS2T = kRC2 * 4 * 512;   // T rows: [c8][32 rows][8 fp16]
+constexpr int kS2W = kRC2 * 256;       // sign words: [chunk][64 outputs]
+constexpr int kS2L = 32 * 64;          // latent scales l: [chunk][32] (2 instructions of 16 chunks)
+constexpr int kS2Buf = kS2T + kS2W + kS2L;
+constexpr int kRP2 = 64 + 4;           // LDS pitch (floats) of a wave's 32 x 64 partial
+static_assert(4 * 32 * kRP2 * 4 <= kS2Buf, "the reduction buffer fits one round buffer");
+static_assert(kRC1 % 2 == 0 && kRC1 <= 16, "stage-1 round: two chunks of words, 16 of g per instruction");
+static_assert(kRC2 <= 32, "stage-2 round: l of 16 chunks per instruction, two instructions");
 
 struct S1Seg {
-  const uint32_t *bits;  // sv1 + p*s: word (row group r, column k) at bits[r * pitch + k]
+  const uint32_t *bits;  // sv1m + p*s: word (row group r, column k) at bits[r * pitch + k]
   const uint16_t *g;     // g + p*a16
   int pitch;             // latent columns L of the layer
   int s;                 // valid columns of the segment
@@ -65,13 +88,14 @@ struct S1Args {
   uint16_t *T;
   float *part;
   unsigned *cnt;
-  int64_t M;  // rows of this chunk
+  const void *zero;  // >= 16 zero bytes (DMA source for padding)
+  int64_t M;         // rows of this chunk
   int a, a16, Lt, ntile32, kcps, nsplit, nseg, xvec;
   S1Seg seg[kMaxUnitSegs];
 };
 
 struct S2Layer {
-  const uint32_t *su2;
+  const uint32_t *su2;  // su2m (matrix-core bit order)
   const uint16_t *l;
   const uint16_t *h;
   uint16_t *y;  // per-layer output (may be null)
@@ -82,17 +106,18 @@ static_assert(sizeof(S2Layer) == 64, "S2Layer layout");
 struct S2Args {
   const uint16_t *T;
   uint16_t *xout;  // combined output (stack) or null
+  const void *zero;
   int64_t M;
   int b, Lt, nl, direct;
   float c_out;
-  int pad_;
+  int nrounds;
   S2Layer ly[kMaxUnitLayersM];
 };
 
 struct MfmaPlan {
   int nl = 0;
   int64_t a = 0, b = 0;
-  int a16 = 0, Lt = 0, ntile32 = 0, nseg = 0;
+  int a16 = 0, Lt = 0, ntile32 = 0, nseg = 0, nrounds2 = 0;
   S1Seg seg[kMaxUnitSegs];
   S2Layer ly[kMaxUnitLayersM];
 };
@@ -106,17 +131,26 @@ __device__ __forceinline__ void st_rel(float *p, float v) {
 __device__ __forceinline__ float ld_rel(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ half8_t as_h8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+// LDS-DMA: lane i's 16 (4) source bytes land at dst + 16 i (dst + 4 i).
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
 
-// Flip the fp16 sign bit of element e of v where bit e of `bits` is 0
-// (sign -1); bit 1 (sign +1) keeps the value.
-__device__ __forceinline__ uint4 apply_signs(uint4 v, uint32_t bits) {
-  const uint32_t nb = ~bits;
-  v.x ^= ((nb << 15) & 0x8000u) | ((nb << 30) & 0x80000000u);
-  v.y ^= ((nb << 13) & 0x8000u) | ((nb << 28) & 0x80000000u);
-  v.z ^= ((nb << 11) & 0x8000u) | ((nb << 26) & 0x80000000u);
-  v.w ^= ((nb << 9) & 0x8000u) | ((nb << 24) & 0x80000000u);
+__device__ __forceinline__ half8_t as_h8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
+
+// Flip the fp16 signs of a lane's 8 operand values: wl is its sign word
+// in the matrix-core bit order, already shifted left by 4 g for the lane's
+// group g of 8 elements, so (wl << j) & 0x80008000 flips elements 2 j, 2 j + 1.
+__device__ __forceinline__ u32x4 flip_signs(u32x4 v, uint32_t wl) {
+  v.x ^= wl & 0x80008000u;
+  v.y ^= (wl << 1) & 0x80008000u;
+  v.z ^= (wl << 2) & 0x80008000u;
+  v.w ^= (wl << 3) & 0x80008000u;
   return v;
 }
 
@@ -129,345 +163,367 @@ __device__ __forceinline__ uint4 pack8(const float *v) {
   return o;
 }
 
-// 8 fp16 of row `tok` of x from column i0 (zero outside the matrix).
-__device__ __forceinline__ uint4 load_x8(const uint16_t *__restrict__ x, int64_t M, int a,
-                                         int xvec, int64_t tok, int i0) {
-  uint4 v = {0u, 0u, 0u, 0u};
-  if (tok >= M || i0 >= a) return v;
-  const uint16_t *p = x + tok * a + i0;
-  if (xvec && i0 + 8 <= a) return *reinterpret_cast<const uint4 *>(p);
-  uint32_t h[8];
+// 8 fp16 to row-major [rows x n] at (row, col..col+7), columns >= n dropped.
+__device__ __forceinline__ void store8(uint16_t *base, int n, int64_t row, int col, const float *v) {
+  uint16_t *dst = base + row * n + col;
+  if ((n & 7) == 0 && col + 8 <= n) {
+    *reinterpret_cast<uint4 *>(dst) = pack8(v);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = i0 + e < a ? p[e] : 0u;
-  v.x = h[0] | (h[1] << 16); v.y = h[2] | (h[3] << 16);
-  v.z = h[4] | (h[5] << 16); v.w = h[6] | (h[7] << 16);
-  return v;
-}
-
-// This wave's 2 x 2 tiles of 32 x 32 into red[wave] (64 rows, pitch kRP),
-// column tile ni scaled by sc[ni].
-__device__ __forceinline__ void spill_acc(float *red, const float16_t (&acc)[2][2], float sc0,
-                                          float sc1) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  float *rw = red + wave * 64 * kRP;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mi * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-        rw[row * kRP + ni * 32 + lr] = acc[mi][ni][r] * (ni ? sc1 : sc0);
-      }
-}
-
-// Sum of the 4 waves' tiles, in wave order, at (row, 8 columns from c0).
-__device__ __forceinline__ void sum_waves(const float *red, int row, int c0, float *v) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int o = row * kRP + c0 + e;
-    v[e] = ((red[o] + red[64 * kRP + o]) + red[2 * 64 * kRP + o]) + red[3 * 64 * kRP + o];
+    for (int e = 0; e < 8; ++e)
+      if (col + e < n) dst[e] = mf2h(v[e]);
   }
 }
 
 // ------------------------------------------------------------- stage 1
-// grid = (Lt / 64, ceil(M / 64), nsplit).  Block (cx, ty, z) computes
-// columns [64 cx, 64 cx + 64) of rows [64 ty, 64 ty + 64) over the 32-row
-// chunks [z * kcps, (z + 1) * kcps) of the input dimension.  Rows past M
-// come out as zeros, so every row of T the second stage reads is written.
+// grid = (Lt / 128, ceil(M / 32), nsplit).  Block (cx, ty, z) computes
+// columns [128 cx, 128 cx + 128) of rows [32 ty, 32 ty + 32) over the
+// 32-row chunks [z * kcps, (z + 1) * kcps) of the input dimension; wave w
+// owns columns 32 w .. 32 w + 31 of the block.  Rows past M and columns
+// past the last segment come out as zeros, so every element of T that
+// the second stage reads is written.
 __global__ void __launch_bounds__(kThreads)
 k_unit_s1(S1Args A) {
-  extern __shared__ __align__(16) float red[];  // 4 x 64 x kRP
+  extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
   __shared__ int s_last;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const int t = threadIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.y * 64;
+  const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+  const int t32 = blockIdx.x * 4 + w;
+  const int64_t tok0 = (int64_t)blockIdx.y * 32;
 
-  // per 32-column tile ni: the lane's column, its bits and scales
-  const uint32_t *bp[2];
-  const uint16_t *gp[2];
-  int pitch[2];
-  bool cval[2];
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int t32 = blockIdx.x * 2 + ni;
-    bp[ni] = nullptr; gp[ni] = nullptr; pitch[ni] = 0; cval[ni] = false;
-    if (t32 < A.ntile32) {
-      int e = 0;
-      for (int q = 1; q < A.nseg; ++q)
-        if (t32 * 32 >= A.seg[q].seg0) e = q;
-      const int k = t32 * 32 - A.seg[e].seg0 + lr;
-      cval[ni] = k < A.seg[e].s;
-      bp[ni] = A.seg[e].bits + k;
-      gp[ni] = A.seg[e].g;
-      pitch[ni] = A.seg[e].pitch;
-    }
+  // the wave's 32 columns lie in one segment
+  const bool active = t32 < A.ntile32;
+  bool cval = false, full_cols = false;
+  const uint32_t *bb = nullptr;
+  const uint16_t *gb = nullptr;
+  int pitch = 0;
+  if (active) {
+    int e = 0;
+    for (int q = 1; q < A.nseg; ++q)
+      if (t32 * 32 >= A.seg[q].seg0) e = q;
+    const int k = t32 * 32 - A.seg[e].seg0 + lr;
+    cval = k < A.seg[e].s;
+    full_cols = t32 * 32 - A.seg[e].seg0 + 32 <= A.seg[e].s;  // uniform
+    bb = A.seg[e].bits + k;
+    gb = A.seg[e].g;
+    pitch = A.seg[e].pitch;
   }
-
   const int nkc = (A.a + 31) >> 5;
   const int kc0 = blockIdx.z * A.kcps;
   const int kc1 = min(nkc, kc0 + A.kcps);
+  const int nr = (kc1 - kc0 + kRC1 - 1) / kRC1;
 
-  float16_t acc[2][2];
+  // round r: chunks [kc0 + r kRC1, +nch) of x rows (all waves) and of the
+  // wave's sign words, into buffer r & 1
+  auto issue = [&](int r) {
+    unsigned char *buf = smem + (r & 1) * kS1Buf;
+    const int kcr = kc0 + r * kRC1, nch = min(kRC1, kc1 - kcr);
+    if (A.xvec) {
+      for (int u = w; u < nch * 2; u += 4) {
+        const int c8 = 2 * u + lh;
+        const int64_t tok = tok0 + lr;
+        const int i = kcr * 32 + c8 * 8;
+        const void *src = (tok < A.M && i < A.a) ? (const void *)(A.x + tok * A.a + i) : A.zero;
+        dma16(src, buf + u * 1024);
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < nch * 4 * 32; idx += kThreads) {
+        const int c8 = idx >> 5, row = idx & 31;
+        const int64_t tok = tok0 + row;
+        const int i = kcr * 32 + c8 * 8;
+        uint32_t hv[8];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  // raw operands of one 32-row chunk: x[step][mi], g[step][ni], words[ni];
-  // the next chunk's are loaded while the current one is multiplied
-  uint4 cx[2][2], cg[2][2], nx[2][2], ng[2][2];
-  uint32_t cw[2], nw[2];
-  auto load = [&](int kc, uint4 (&xo)[2][2], uint4 (&go)[2][2], uint32_t (&wo)[2]) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) wo[ni] = cval[ni] ? bp[ni][(size_t)kc * pitch[ni]] : 0u;
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const int i0 = kc * 32 + step * 16 + lh * 8;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        xo[step][mi] = load_x8(A.x, A.M, A.a, A.xvec, tok0 + mi * 32 + lr, i0);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        go[step][ni] = (gp[ni] && i0 + 8 <= A.a16) ? *reinterpret_cast<const uint4 *>(gp[ni] + i0)
-                                                   : uint4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e) hv[e] = (tok < A.M && i + e < A.a) ? A.x[tok * A.a + i + e] : 0u;
+        uint4 o;
+        o.x = hv[0] | (hv[1] << 16); o.y = hv[2] | (hv[3] << 16);
+        o.z = hv[4] | (hv[5] << 16); o.w = hv[6] | (hv[7] << 16);
+        *reinterpret_cast<uint4 *>(buf + idx * 16) = o;
+      }
+    }
+    if (active) {
+      for (int v = 0; v < (nch + 1) / 2; ++v) {
+        const int kk = 2 * v + lh;
+        const void *src = (cval && kk < nch) ? (const void *)(bb + (size_t)(kcr + kk) * pitch) : A.zero;
+        dma4(src, buf + kS1X + (w * kRC1 + 2 * v) * 128);
+      }
+      // g of the chunks: lane = 4 chunk + piece, 8 rows per piece
+      const int kk = lane >> 2, i = (kcr + kk) * 32 + 8 * (lane & 3);
+      const void *src = (kk < nch && i + 8 <= A.a16) ? (const void *)(gb + i) : A.zero;
+      dma16(src, buf + kS1X + kS1W + w * 1024);
     }
   };
-  int kc = kc0 + wave;
-  if (kc < kc1) load(kc, cx, cg, cw);
-  for (; kc < kc1; kc += 4) {
-    if (kc + 4 < kc1) load(kc + 4, nx, ng, nw);
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        uint4 bv = apply_signs(cg[step][ni], (cw[ni] >> (8 * (2 * step + lh))) & 255u);
-        if (!cval[ni]) bv = uint4{0u, 0u, 0u, 0u};
-        const half8_t bh = as_h8(bv);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(cx[step][mi]), bh, acc[mi][ni], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int step = 0; step < 2; ++step)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        cx[step][i] = nx[step][i];
-        cg[step][i] = ng[step][i];
-      }
-    cw[0] = nw[0];
-    cw[1] = nw[1];
-  }
 
-  spill_acc(red, acc, 1.f, 1.f);
-  __syncthreads();
-
-  // thread t owns (row = P & 63, 8 columns from 8 * (P >> 6)) for P = t, t + 256
-  float v[2][8];
+  // two accumulators (even / odd chunks) keep two independent MFMA chains
+  float16_t acc0, acc1;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int P = t + 256 * hh;
-    sum_waves(red, P & 63, 8 * (P >> 6), v[hh]);
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  issue(0);
+  for (int r = 0; r < nr; ++r) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of round r landed
+    __syncthreads();                // ... and every other wave's
+    if (r + 1 < nr) issue(r + 1);   // overlaps the products below
+    if (!active) continue;
+    const unsigned char *buf = smem + (r & 1) * kS1Buf;
+    const int kcr = kc0 + r * kRC1, nch = min(kRC1, kc1 - kcr);
+    const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
+    const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + kS1X) + w * kRC1 * 32;
+    const u32x4 *gsd = reinterpret_cast<const u32x4 *>(buf + kS1X + kS1W + w * 1024);
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    // operands of one chunk: x rows (A), g (B values before the signs), words
+    struct Ops { u32x4 a[2], g[2]; uint32_t wd; };
+    auto fetch = [&](int kk, Ops &o) {
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        o.a[step] = xs[(kk * 4 + 2 * step + lh) * 32 + lr];
+        o.g[step] = gsd[kk * 4 + 2 * step + lh];  // g of rows 32 kk + 16 step + 8 lh ..
+      }
+      o.wd = wsd[kk * 32 + lr];
+    };
+    auto mma = [&](const Ops &o, float16_t &acc, auto masked) {
+      const uint32_t wl = o.wd << (4 * lh);  // group g = 2 step + lh
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        u32x4 bv = flip_signs(o.g[step], wl << (8 * step));
+        if (decltype(masked)::value && !cval) bv = z4;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(o.a[step]), as_h8(bv), acc, 0, 0, 0);
+      }
+    };
+    // the prefetches are unconditional (index clamped) so the wait before a
+    // chunk's products covers only that chunk's reads
+    auto sweep = [&](auto masked) {
+      Ops c0, c1;
+      fetch(0, c0);
+      fetch(min(1, nch - 1), c1);
+      for (int kk = 0; kk < nch; kk += 2) {
+        Ops n0, n1;
+        fetch(min(kk + 2, nch - 1), n0);
+        fetch(min(kk + 3, nch - 1), n1);
+        mma(c0, acc0, masked);
+        if (kk + 1 < nch) mma(c1, acc1, masked);
+        c0 = n0;
+        c1 = n1;
+      }
+    };
+    if (full_cols)
+      sweep(std::false_type());
+    else
+      sweep(std::true_type());
   }
+  __syncthreads();  // the round buffers are free
+
   const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = acc0[r] + acc1[r];
   if (A.nsplit > 1) {
-    // split z's partial: value (hh, e) of thread t at [((tile*nsplit + z)*16 + hh*8 + e)*256 + t]
+    // split z's partial: register r of lane l of wave w at [(tile*nsplit + z)*4096 + (16 w + r)*64 + l]
     float *pp = A.part + ((size_t)tile * A.nsplit + blockIdx.z) * 4096;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st_rel(&pp[(hh * 8 + e) * 256 + t], v[hh][e]);
+    for (int r = 0; r < 16; ++r) st_rel(&pp[(w * 16 + r) * 64 + lane], v[r]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t == 0) {
+    if (threadIdx.x == 0) {
       const unsigned old =
           __hip_atomic_fetch_add(&A.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = old == (unsigned)(A.nsplit - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    const float *pt = A.part + (size_t)tile * A.nsplit * 4096;
+    // the last block of the tile sums the splits in split order
+    const float *pt = A.part + (size_t)tile * A.nsplit * 4096 + (w * 16) * 64 + lane;
+    // every load unconditional (splits past nsplit re-read the last one) so
+    // all of them are in flight at once
+    float q[kMaxSplit][16];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float q[kMaxSplit][8];
+    for (int z = 0; z < kMaxSplit; ++z) {
+      const float *pz = pt + (size_t)min(z, A.nsplit - 1) * 4096;
 #pragma unroll
-      for (int z = 0; z < kMaxSplit; ++z)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          q[z][e] = z < A.nsplit ? ld_rel(&pt[((size_t)z * 16 + hh * 8 + e) * 256 + t]) : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float s = q[0][e];
-#pragma unroll
-        for (int z = 1; z < kMaxSplit; ++z)
-          if (z < A.nsplit) s += q[z][e];
-        v[hh][e] = s;
-      }
+      for (int r = 0; r < 16; ++r) q[z][r] = ld_rel(&pz[r * 64]);
     }
-    if (t == 0) __hip_atomic_store(&A.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const int Lt8 = A.Lt >> 3;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int P = t + 256 * hh;
-    const int row = P & 63, c8 = blockIdx.x * 8 + (P >> 6);
-    const int64_t tb = (tok0 >> 5) + (row >> 5);
-    *reinterpret_cast<uint4 *>(A.T + ((tb * Lt8 + c8) * 32 + (row & 31)) * 8) = pack8(v[hh]);
+    for (int r = 0; r < 16; ++r) {
+      float sum = q[0][r];
+#pragma unroll
+      for (int z = 1; z < kMaxSplit; ++z)
+        if (z < A.nsplit) sum += q[z][r];
+      v[r] = sum;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&A.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // fp16 tile [16 c8][32 rows][8] in LDS, then one contiguous 8 KB copy into T
+  uint16_t *tl = reinterpret_cast<uint16_t *>(smem);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * lh + (r & 3), col = w * 32 + lr;
+    tl[((col >> 3) * 32 + row) * 8 + (col & 7)] = mf2h(v[r]);
+  }
+  __syncthreads();
+  uint4 *dst = reinterpret_cast<uint4 *>(A.T + ((size_t)blockIdx.y * (A.Lt >> 3) + blockIdx.x * 16) * 256);
+  const uint4 *srcl = reinterpret_cast<const uint4 *>(smem);
+  dst[threadIdx.x] = srcl[threadIdx.x];
+  dst[threadIdx.x + kThreads] = srcl[threadIdx.x + kThreads];
 }
 
 // ------------------------------------------------------------- stage 2
-// grid = (ceil(b / 64), ceil(M / 64)).  Block (jx, ty) computes outputs
-// [64 jx, 64 jx + 64) of rows [64 ty, 64 ty + 64) for every layer of the
-// unit, then their combine.
+// grid = (ceil(b / 64), ceil(M / 32)).  Block (jx, ty) computes outputs
+// [64 jx, 64 jx + 64) of rows [32 ty, 32 ty + 32) for every layer of the
+// unit, then their combine.  The waves interleave over a layer's
+// (path, 32-column) chunks, each wave accumulating 32 x 64 per path; the
+// four partials are summed in wave order through LDS.
 __global__ void __launch_bounds__(kThreads)
 k_unit_s2(S2Args A) {
-  extern __shared__ __align__(16) float red[];  // 4 x 64 x kRP
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+  extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
+  const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int t = threadIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.y * 64;
+  const int tb = blockIdx.y;
+  const int64_t tok0 = (int64_t)tb * 32;
   const int j0 = blockIdx.x * 64;
   const int Lt8 = A.Lt >> 3;
-  const int64_t tb0 = tok0 >> 5;
-  // thread t owns (row = P >> 3, 8 columns from 8 * (P & 7)) for P = t, t + 256
-  float ys[2][8];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ys[hh][e] = 0.f;
 
+  // round r -> (layer m, first chunk ch0, chunk count nch); chunk ch of a
+  // layer is path ch / Wk, 32-column block ch % Wk
+  auto round_of = [&](int r, int &m, int &ch0, int &nch) {
+    m = 0;
+    int rr = r;
+    while (true) {
+      const int nc = A.ly[m].P * A.ly[m].Wk;
+      const int nrm = (nc + kRC2 - 1) / kRC2;
+      if (rr < nrm) {
+        ch0 = rr * kRC2;
+        nch = min(kRC2, nc - ch0);
+        return;
+      }
+      rr -= nrm;
+      ++m;
+    }
+  };
+  auto issue = [&](int r) {
+    int m, ch0, nch;
+    round_of(r, m, ch0, nch);
+    const S2Layer &Ly = A.ly[m];
+    unsigned char *buf = smem + (r & 1) * kS2Buf;
+    const uint16_t *tsrc = A.T + ((size_t)tb * Lt8 + (Ly.seg0[0] >> 3) + ch0 * 4) * 256;
+    for (int u = w; u < nch * 2; u += 4) dma16(tsrc + u * 512 + lane * 8, buf + u * 1024);
+    for (int v = w; v < (nch + 3) / 4; v += 4) {
+      const int chl = 4 * v + (lane >> 4);
+      const int j = j0 + 4 * (lane & 15);
+      const void *src = (chl < nch && j + 4 <= Ly.b16)
+                            ? (const void *)(Ly.su2 + (size_t)(ch0 + chl) * Ly.b16 + j)
+                            : A.zero;
+      dma16(src, buf + kS2T + v * 1024);
+    }
+    // l of the chunks: lane = 4 chunk + piece, 8 latent columns per piece
+    for (int v = w; v < (nch + 15) / 16; v += 4) {
+      const int chl = 16 * v + (lane >> 2);
+      const int ch = ch0 + chl;
+      const int p = ch >= Ly.Wk ? 1 : 0;
+      const int k = (ch - p * Ly.Wk) * 32 + 8 * (lane & 3);
+      const void *src = (chl < nch && k + 8 <= Ly.s8) ? (const void *)(Ly.l + (size_t)p * Ly.s8 + k) : A.zero;
+      dma16(src, buf + kS2T + kS2W + v * 1024);
+    }
+  };
+
+  float ys[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ys[e] = 0.f;
+  const int row_o = t >> 3, c_o = 8 * (t & 7);  // this thread's 8 outputs per layer
+  issue(0);
+  int r = 0;
   for (int m = 0; m < A.nl; ++m) {
     const S2Layer &Ly = A.ly[m];
-    // waves 0-1 take path 0 and 2-3 path 1 (or all four path 0), and
-    // interleave over the path's 32-column chunks
-    int p, q0, qs;
-    if (Ly.P == 2) {
-      p = wave >> 1; q0 = wave & 1; qs = 2;
-    } else {
-      p = 0; q0 = wave; qs = 4;
-    }
-    const uint32_t *wb[2];
-    bool jv[2];
+    const int nc = Ly.P * Ly.Wk, nrm = (nc + kRC2 - 1) / kRC2;
+    float hv[2][2];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int j = j0 + ni * 32 + lr;
-      jv[ni] = j < A.b;
-      wb[ni] = Ly.su2 + (size_t)p * Ly.Wk * Ly.b16 + j;
-    }
-    const uint16_t *lb = Ly.l + (size_t)p * Ly.s8;
-    const int c8b = Ly.seg0[p] >> 3;
-    const int Wk = Ly.Wk, b16 = Ly.b16, s8 = Ly.s8;
-
-    float16_t acc[2][2];
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-    uint4 ca[2][2], cl[2], na[2][2], nl[2];
-    uint32_t cw[2], nw[2];
-    auto load = [&](int q, uint4 (&ao)[2][2], uint4 (&lo)[2], uint32_t (&wo)[2]) {
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) wo[ni] = jv[ni] ? wb[ni][(size_t)q * b16] : 0u;
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-        const int k = q * 32 + step * 16 + lh * 8;
-        lo[step] = k + 8 <= s8 ? *reinterpret_cast<const uint4 *>(lb + k) : uint4{0u, 0u, 0u, 0u};
-        const int c8 = c8b + q * 4 + step * 2 + lh;
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          ao[step][mi] = *reinterpret_cast<const uint4 *>(A.T + (((tb0 + mi) * Lt8 + c8) * 32 + lr) * 8);
+      for (int ni = 0; ni < 2; ++ni) {
+        const int j = j0 + ni * 32 + lr;
+        hv[p][ni] = (p < Ly.P && j < A.b) ? mh2f(Ly.h[(size_t)p * Ly.b16 + j]) : 0.f;
       }
-    };
-    int q = q0;
-    if (q < Wk) load(q, ca, cl, cw);
-    for (; q < Wk; q += qs) {
-      if (q + qs < Wk) load(q + qs, na, nl, nw);
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const half8_t bh = as_h8(apply_signs(cl[step], (cw[ni] >> (8 * (2 * step + lh))) & 255u));
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(ca[step][mi]), bh, acc[mi][ni], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int step = 0; step < 2; ++step) {
-        cl[step] = nl[step];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) ca[step][mi] = na[step][mi];
-      }
-      cw[0] = nw[0];
-      cw[1] = nw[1];
-    }
-    float hv[2];
+    float16_t acc0[2], acc1[2];
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
-      hv[ni] = jv[ni] ? mh2f(Ly.h[(size_t)p * b16 + j0 + ni * 32 + lr]) : 0.f;
-    spill_acc(red, acc, hv[0], hv[1]);
-    __syncthreads();
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int P = t + 256 * hh;
-      const int row = P >> 3, c0 = 8 * (P & 7);
-      float v[8];
-      sum_waves(red, row, c0, v);
-      const int64_t tok = tok0 + row;
-      const int jj = j0 + c0;
-      uint16_t y16[8];
+      for (int e = 0; e < 16; ++e) acc0[ni][e] = acc1[ni][e] = 0.f;
+    for (int rm = 0; rm < nrm; ++rm, ++r) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (r + 1 < A.nrounds) issue(r + 1);
+      const unsigned char *buf = smem + (r & 1) * kS2Buf;
+      const int ch0 = rm * kRC2, nch = min(kRC2, nc - ch0);
+      const u32x4 *ts = reinterpret_cast<const u32x4 *>(buf);
+      const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + kS2T);
+      const u32x4 *lsd = reinterpret_cast<const u32x4 *>(buf + kS2T + kS2W);
+      struct Ops { u32x4 a[2], l[2]; uint32_t wd[2]; };
+      auto fetch = [&](int chl, Ops &o) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y16[e] = mf2h(v[e]);
-        ys[hh][e] += mh2f(y16[e]);
-      }
-      if (Ly.y && tok < A.M) {
-        uint16_t *dst = Ly.y + tok * A.b + jj;
-        if ((A.b & 7) == 0 && jj + 8 <= A.b) {
-          uint4 o;
-          o.x = y16[0] | ((uint32_t)y16[1] << 16); o.y = y16[2] | ((uint32_t)y16[3] << 16);
-          o.z = y16[4] | ((uint32_t)y16[5] << 16); o.w = y16[6] | ((uint32_t)y16[7] << 16);
-          *reinterpret_cast<uint4 *>(dst) = o;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (jj + e < A.b) dst[e] = y16[e];
+        for (int step = 0; step < 2; ++step) {
+          o.a[step] = ts[(chl * 4 + 2 * step + lh) * 32 + lr];
+          o.l[step] = lsd[chl * 4 + 2 * step + lh];  // l of columns 32 q + 16 step + 8 lh ..
         }
-      }
+        o.wd[0] = wsd[chl * 64 + lr];
+        o.wd[1] = wsd[chl * 64 + 32 + lr];
+      };
+      auto mma = [&](const Ops &o, float16_t (&acc)[2]) {
+        const uint32_t wl0 = o.wd[0] << (4 * lh), wl1 = o.wd[1] << (4 * lh);  // group g = 2 step + lh
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+          const half8_t av = as_h8(o.a[step]);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              av, as_h8(flip_signs(o.l[step], wl0 << (8 * step))), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              av, as_h8(flip_signs(o.l[step], wl1 << (8 * step))), acc[1], 0, 0, 0);
+        }
+      };
+      // chunks are path-major: [0, nch0) are path 0, [nch0, nch) path 1;
+      // wave w takes the chunks chl = w (mod 4), path by path
+      const int nch0 = max(0, min(nch, Ly.Wk - ch0));
+      auto run = [&](int lo, int hi, float16_t (&acc)[2]) {
+        int chl = lo + ((w - lo) % 4 + 4) % 4;
+        if (chl >= hi) return;
+        Ops c;
+        fetch(chl, c);
+        for (; chl < hi; chl += 4) {
+          Ops n;
+          fetch(min(chl + 4, hi - 1), n);  // unconditional: see stage 1
+          mma(c, acc);
+          c = n;
+        }
+      };
+      run(0, nch0, acc0);
+      run(nch0, nch, acc1);
     }
+    // layer epilogue: the layer's last round buffer becomes the reduction area
     __syncthreads();
-  }
-  if (A.direct || !A.xout) return;
+    float *red = reinterpret_cast<float *>(smem + ((r - 1) & 1) * kS2Buf);
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int P = t + 256 * hh;
-    const int row = P >> 3, c0 = 8 * (P & 7);
-    const int64_t tok = tok0 + row;
-    const int jj = j0 + c0;
-    if (tok >= A.M) continue;
-    float o[8];
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = A.c_out * ys[hh][e];
-    uint16_t *dst = A.xout + tok * A.b + jj;
-    if ((A.b & 7) == 0 && jj + 8 <= A.b) {
-      *reinterpret_cast<uint4 *>(dst) = pack8(o);
-    } else {
+      for (int e = 0; e < 16; ++e) {
+        const int row = 8 * (e >> 2) + 4 * lh + (e & 3), col = ni * 32 + lr;
+        red[(w * 32 + row) * kRP2 + col] = hv[0][ni] * acc0[ni][e] + hv[1][ni] * acc1[ni][e];
+      }
+    __syncthreads();
+    float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (jj + e < A.b) dst[e] = mf2h(o[e]);
+    for (int e = 0; e < 8; ++e) {
+      const int o = row_o * kRP2 + c_o + e;
+      v[e] = ((red[o] + red[32 * kRP2 + o]) + red[2 * 32 * kRP2 + o]) + red[3 * 32 * kRP2 + o];
+      v[e] = mh2f(mf2h(v[e]));  // the layer's fp16 output
+      ys[e] += v[e];
     }
+    if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + c_o, v);
   }
+  if (A.direct || !A.xout || tok0 + row_o >= A.M) return;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = A.c_out * ys[e];
+  store8(A.xout, A.b, tok0 + row_o, j0 + c_o, o);
 }
 
 // ------------------------------------------------------------------ host
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
-static constexpr size_t kRedBytes = (size_t)4 * 64 * kRP * sizeof(float);
+static constexpr size_t kS1Lds = (size_t)2 * kS1Buf;
+static constexpr size_t kS2Lds = (size_t)2 * kS2Buf;
 
 MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
   if (n < 1 || n > kMaxUnitLayersM) return nullptr;
@@ -476,7 +532,7 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
   P->a = layers[0]->a;
   P->b = layers[0]->b;
   P->a16 = (int)layers[0]->a16;
-  int col = 0, nseg = 0;
+  int col = 0, nseg = 0, nr2 = 0;
   for (int m = 0; m < n; ++m) {
     const Layer &Ly = *layers[m];
     if (Ly.a != P->a || Ly.b != P->b) {
@@ -484,13 +540,13 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
       return nullptr;
     }
     S2Layer &D = P->ly[m];
-    D.su2 = Ly.su2; D.l = Ly.l; D.h = Ly.h; D.y = nullptr;
+    D.su2 = Ly.su2m; D.l = Ly.l; D.h = Ly.h; D.y = nullptr;
     D.b16 = (int)Ly.b16; D.s8 = (int)Ly.s8; D.Wk = (int)Ly.Wk; D.P = Ly.P;
     D.seg0[0] = D.seg0[1] = 0;
     D.pad_[0] = D.pad_[1] = 0;
     for (int p = 0; p < Ly.P; ++p) {
       S1Seg &S = P->seg[nseg++];
-      S.bits = Ly.sv1 + (size_t)p * Ly.s;
+      S.bits = Ly.sv1m + (size_t)p * Ly.s;
       S.g = Ly.g + (size_t)p * Ly.a16;
       S.pitch = (int)Ly.L;
       S.s = (int)Ly.s;
@@ -499,21 +555,25 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
       D.seg0[p] = col;
       col += (int)round_up(Ly.s, 32);
     }
+    nr2 += (int)((Ly.P * Ly.Wk + kRC2 - 1) / kRC2);
   }
   P->nseg = nseg;
   P->ntile32 = col / 32;
-  P->Lt = (int)round_up(col, 64);
+  P->Lt = (int)round_up(col, 128);
+  P->nrounds2 = nr2;
   return P;
 }
 
 void mfma_plan_free(MfmaPlan *p) { delete p; }
 
+static int64_t s1_tiles(const MfmaPlan &P, int64_t Mc) { return (int64_t)(P.Lt / 128) * ((Mc + 31) / 32); }
+
 static int s1_nsplit(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *kcps) {
-  const int64_t tiles = (int64_t)(P.Lt / 64) * ((Mc + 63) / 64);
+  const int64_t tiles = s1_tiles(P, Mc);
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int nkc = (int)((P.a + 31) / 32);
   int ns = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, (cus + tiles - 1) / tiles));
-  ns = std::min(ns, std::max(1, nkc / 8));  // at least two chunks per wave
+  ns = std::min(ns, nkc);
   const int k = (nkc + ns - 1) / ns;
   *kcps = k;
   return (nkc + k - 1) / k;
@@ -521,28 +581,29 @@ static int s1_nsplit(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *
 
 size_t mfma_unit_ws_bytes(const MfmaPlan *p) {
   const size_t T = (size_t)round_up((int64_t)kMfmaRows * p->Lt * 2, 256);
-  const size_t part = (size_t)kMaxSplit * (p->Lt / 64) * (kMfmaRows / 64) * 4096 * sizeof(float);
+  const size_t part = (size_t)kMaxSplit * s1_tiles(*p, kMfmaRows) * 4096 * sizeof(float);
   return T + part;
 }
 
-size_t mfma_cnt_entries(const MfmaPlan *p) { return (size_t)(p->Lt / 64) * (kMfmaRows / 64); }
+size_t mfma_cnt_entries(const MfmaPlan *p) { return (size_t)s1_tiles(*p, kMfmaRows); }
 
 static hipError_t set_lds_attr(int device) {
   static std::atomic<uint64_t> done{0};
   const uint64_t bit = device >= 0 && device < 64 ? (1ull << device) : 0;
   if (bit && (done.load() & bit)) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void *)k_unit_s1,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRedBytes);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS1Lds);
   if (e == hipSuccess)
     e = hipFuncSetAttribute((const void *)k_unit_s2, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kRedBytes);
+                            (int)kS2Lds);
   if (e == hipSuccess && bit) done.fetch_or(bit);
   return e;
 }
 
 hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             uint16_t *const *y_layers, uint16_t *xout, float c_out, bool direct,
-                            void *ws, unsigned *cnt, const DeviceInfo &dev, hipStream_t st) {
+                            void *ws, unsigned *cnt, const void *zero, const DeviceInfo &dev,
+                            hipStream_t st) {
   hipError_t e = set_lds_attr(dev.device);
   if (e != hipSuccess) return e;
   uint16_t *T = reinterpret_cast<uint16_t *>(ws);
@@ -555,6 +616,7 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A1.T = T;
     A1.part = part;
     A1.cnt = cnt;
+    A1.zero = zero;
     A1.M = Mc;
     A1.a = (int)p->a;
     A1.a16 = p->a16;
@@ -564,27 +626,28 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A1.nseg = p->nseg;
     A1.xvec = (p->a % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
     for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = p->seg[i];
-    dim3 g1((unsigned)(p->Lt / 64), (unsigned)((Mc + 63) / 64), (unsigned)A1.nsplit);
-    hipLaunchKernelGGL(k_unit_s1, g1, dim3(kThreads), kRedBytes, st, A1);
+    dim3 g1((unsigned)(p->Lt / 128), (unsigned)((Mc + 31) / 32), (unsigned)A1.nsplit);
+    hipLaunchKernelGGL(k_unit_s1, g1, dim3(kThreads), kS1Lds, st, A1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     S2Args A2;
     A2.T = T;
     A2.xout = xout ? xout + mb * p->b : nullptr;
+    A2.zero = zero;
     A2.M = Mc;
     A2.b = (int)p->b;
     A2.Lt = p->Lt;
     A2.nl = p->nl;
     A2.direct = direct ? 1 : 0;
     A2.c_out = c_out;
-    A2.pad_ = 0;
+    A2.nrounds = p->nrounds2;
     for (int m = 0; m < kMaxUnitLayersM; ++m) {
       A2.ly[m] = p->ly[m];
       A2.ly[m].y = (m < p->nl && y_layers && y_layers[m]) ? y_layers[m] + mb * p->b : nullptr;
     }
-    dim3 g2((unsigned)((p->b + 63) / 64), (unsigned)((Mc + 63) / 64));
-    hipLaunchKernelGGL(k_unit_s2, g2, dim3(kThreads), kRedBytes, st, A2);
+    dim3 g2((unsigned)((p->b + 63) / 64), (unsigned)((Mc + 31) / 32));
+    hipLaunchKernelGGL(k_unit_s2, g2, dim3(kThreads), kS2Lds, st, A2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
