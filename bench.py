@@ -15,6 +15,7 @@ a bounded sample of the same workload as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -79,6 +80,42 @@ def time_steps(torch, stack, x, y, steps, warmup):
     return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
 
 
+KERNEL_SRC = {"persistent": "binary_rank_gemv_littlebitlinear_amd/csrc/lb_persist.hip",
+              "unit": "binary_rank_gemv_littlebitlinear_amd/csrc/lb_mfma.hip"}
+
+
+def kernel_hash(kind: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SRC[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str, blocks):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the same
+    counters on a copy of known size), or None when there is no summary for
+    this workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_hash(kind) or t.get("blocks") != blocks:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_probe(torch, mib: int):
+    """An elementwise kernel of known size (reads and writes MIB MiB each;
+    calibrates the HBM byte counters)."""
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: 3 x neg over {mib} MiB", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(wl: dict, M: int, budget_s: float) -> dict:
     """Time the float64 oracle on a bounded sample of the workload's layers."""
     import oracle
@@ -119,10 +156,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="llama7b_full_stack_M128",
                     help="extra workload measured in the same run ('' to skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the layer's multi-GPU split is described in DESIGN.md and not run.", file=sys.stderr)
+              "multi-GPU runs are not part of this benchmark.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -136,6 +175,7 @@ def main():
         print(f"[bench] building {name} ({len(wl['layers'])} matrices, M={M})", file=sys.stderr, flush=True)
         stack, t_build = build(lbm, wl)
         stack.set_mode(args.mode)
+        stack.reserve(M)
         x = torch.from_numpy(lb_synth.activations(M, wl["layers"][0]["a"], seed=wl["seed"])).cuda()
         y = torch.empty((M, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
         print(f"[bench] built in {t_build:.1f} s; timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -149,11 +189,15 @@ def main():
         torch.cuda.synchronize()
         return res
 
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
     r = measure(args.workload, args.blocks, not args.no_cpu_baseline)
     wl, M, ms = r["wl"], r["M"], r["ms"]
     gbs = r["bytes"] / (ms * 1e-3) / 1e9
     tflops = r["flops"] / (ms * 1e-3) / 1e12
     batch1 = M < 64
+    kind = "persistent" if (M <= 1 and args.mode != 1) else "unit"
+    traffic = measured_traffic(wl["name"], kind, wl["blocks"]) if kind == "persistent" else None
     out = {
         "metric": METRIC,
         "value": round(gbs if batch1 else tflops, 3),
@@ -173,8 +217,10 @@ def main():
                      "peak": HBM_PEAK_GBS if batch1 else MFMA_FP16_PEAK_TFLOPS,
                      "unit": "GB/s" if batch1 else "TFLOP/s",
                      "frac": round((gbs / HBM_PEAK_GBS) if batch1 else (tflops / MFMA_FP16_PEAK_TFLOPS), 4),
-                     "traffic": None,
-                     "kernel": "whole sweep (stream events around each step)"},
+                     "traffic": traffic,
+                     "kernel": ("k_persist: one launch per step, timed with events on its stream"
+                                if kind == "persistent" else
+                                "k_unit_s1 + k_unit_s2 per unit, timed together with events on their stream")},
     }
     if "cpu" in r:
         out["cpu_baseline"] = r["cpu"]

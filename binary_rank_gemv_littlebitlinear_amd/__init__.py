@@ -56,6 +56,7 @@ def load_library(path: str = LIB_PATH):
         "lb_stack_create": ([vp, i32, vp, i32, C.c_float, P(vp)], i32),
         "lb_stack_forward": ([vp, vp, vp, vp, i64, vp], i32),
         "lb_stack_trace_elems": ([vp, i64, P(i64)], i32),
+        "lb_stack_reserve": ([vp, i64], i32),
         "lb_stack_set_mode": ([vp, i32], i32),
         "lb_stack_check": ([vp], i32),
         "lb_stack_timeline": ([vp, vp, i64, P(i64)], i32),
@@ -75,8 +76,8 @@ def load_library(path: str = LIB_PATH):
 EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
-            "lb_stack_trace_elems", "lb_stack_set_mode", "lb_stack_check", "lb_stack_timeline", "lb_stack_destroy", "lb_status_str",
-            "lb_last_error", "lb_version")
+            "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
+            "lb_stack_timeline", "lb_stack_destroy", "lb_status_str", "lb_last_error", "lb_version")
 
 
 def _status_name(st: int) -> str:
@@ -204,6 +205,10 @@ def lb_stack_trace_elems(stack: int, M: int) -> int:
     return n.value
 
 
+def lb_stack_reserve(stack: int, M: int):
+    _check(load_library().lb_stack_reserve(stack, int(M)))
+
+
 def lb_stack_set_mode(stack: int, mode: int):
     _check(load_library().lb_stack_set_mode(stack, int(mode)))
 
@@ -270,6 +275,9 @@ class Stack:
 
     def set_mode(self, mode: int):
         lb_stack_set_mode(self.handle, mode)
+
+    def reserve(self, M: int):
+        lb_stack_reserve(self.handle, M)
 
     def check(self):
         lb_stack_check(self.handle)

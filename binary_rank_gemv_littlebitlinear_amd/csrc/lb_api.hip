@@ -651,6 +651,12 @@ extern "C" lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t 
   return LB_OK;
 }
 
+extern "C" lb_status lb_stack_reserve(lb_stack *S, int64_t M) {
+  if (!S || M < 0) return fail(LB_EINVAL, "lb_stack_reserve: bad argument");
+  DeviceGuard dg(S->device);
+  return stack_reserve(S, M);
+}
+
 extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                                       void *stream) {
   if (!S) return fail(LB_EINVAL, "lb_stack_forward: NULL stack");

@@ -35,9 +35,12 @@
  *   - Device pointers (x, y) are caller-owned, contiguous, row-major and
  *     16-byte aligned, and x must not overlap y.
  *   - Forward calls are asynchronous on the given hipStream_t (passed as
- *     void*, NULL = the null stream), make no allocation and no host
- *     synchronisation.  Calls that use one layer or stack must be ordered
- *     on one stream: they share the object's device workspace.
+ *     void*, NULL = the null stream) and make no host synchronisation.
+ *     lb_forward never allocates; lb_stack_forward allocates (and
+ *     synchronises the device) only when M exceeds the rows reserved with
+ *     lb_stack_reserve or by an earlier call.  Calls that use one layer or
+ *     stack must be ordered on one stream: they share the object's device
+ *     workspace.
  */
 #ifndef LB_H
 #define LB_H
@@ -83,9 +86,11 @@ lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t
 
 /* y[M x b] = layer(x[M x a]); x, y are device fp16.  M = 0 is a no-op.
  * M < 64 runs the wave-level binary GEMV path (sign-flip identity on
- * packed bits); M >= 64 runs the fp16 MFMA path, in which the latent
- * vector t is rounded once to fp16 before the second product.
- * Returns LB_ENOTREADY unless every path has signs and scales. */
+ * packed bits, fp32 throughout); M >= 64 runs the fp16 matrix-core path
+ * (two launches: the first product with split K, then the second), in
+ * which the latent vector t is rounded once to fp16 before the second
+ * product; the +-g and +-l operands are exact.  Returns LB_ENOTREADY
+ * unless every path has signs and scales. */
 lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
 
 /* Read the device signs of one path back into canonical words (padding
@@ -137,11 +142,23 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
 /* Run the whole stack on device fp16 x0 [M x a_0] into y [M x b_last].
  * trace, when not NULL, receives every layer's fp16 output followed by
  * every unit's fp16 input, each M rows, in stack order (size from
- * lb_stack_trace_elems).  M < 64 runs one persistent cooperative launch
- * for the whole sweep when the device can co-schedule it, else (and for
- * M >= 64) the per-layer kernels in order. */
+ * lb_stack_trace_elems).  Automatic mode:
+ *   M = 1       one launch for the whole sweep: one workgroup per compute
+ *               unit, the latent vector of each unit summed across
+ *               workgroups through device memory with bounded waits (a
+ *               wait that gives up sets a flag lb_stack_check reports);
+ *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
+ *               per unit;
+ *   M >= 64     two matrix-core launches per unit, the combine fused into
+ *               the second.
+ * x0, y and trace must be 16-byte aligned; y must not overlap x0. */
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
+
+/* Reserve the stack's scratch for up to M rows now (allocates and
+ * synchronises the device), so that later lb_stack_forward calls with at
+ * most M rows allocate nothing. */
+lb_status lb_stack_reserve(lb_stack *S, int64_t M);
 
 /* Number of fp16 elements lb_stack_forward writes to trace for M rows. */
 lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t *elems);
@@ -158,8 +175,10 @@ lb_status lb_stack_check(lb_stack *S);
  * count.  buf = NULL turns recording off.  The buffer must outlive its use. */
 lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed);
 
-/* Select the execution mode of lb_stack_forward: 0 = automatic, 1 = per
- * layer kernels only, 2 = persistent only (LB_EUNSUPPORTED if impossible). */
+/* Select the execution mode of lb_stack_forward: 0 = automatic (above),
+ * 1 = every layer alone (as lb_forward) followed by a combine kernel per
+ * unit, 2 = the one-launch sweep only (LB_EUNSUPPORTED unless M = 1 and
+ * the device can hold one workgroup per compute unit). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);
 
 lb_status lb_stack_destroy(lb_stack *S);
