@@ -90,7 +90,7 @@ struct alignas(16) PSeg {
   int per_tile;
   int fixed;
   int kind;  // kind | layer << 8
-  int pad;
+  int offp;  // LDS offset in the staging buffer: (offp & 0xffff) + nt * (offp >> 16)
 };
 
 static_assert(sizeof(PLayer) % 16 == 0 && sizeof(PUnit) % 16 == 0 && sizeof(PSeg) == 32,
@@ -216,62 +216,78 @@ struct Lds {
 
 // Stage phase ph: copy the blocks of its list (descriptors of units ph-1
 // and ph, sign bits, scales) into LDS with LDS-DMA loads (16 bytes per
-// lane, 1 KB per wave instruction) issued round-robin by waves 4-7, and
-// the next phase's list into the other list buffer.  The list itself was
-// staged one phase earlier, so nothing here reads global memory.  Wave 4
-// writes the block offsets into the phase context.  Waves 4-7 only.
+// lane, 1 KB per wave instruction), and the next phase's list into the
+// other list buffer.  Waves 4-7 only: wave 4 + i takes records 1 + i,
+// 5 + i, ...  It reads all of its records with one vector LDS load and
+// takes their fields with readlane, so the issue loop has no LDS reads
+// (they would queue behind the incoming copies), and the host-computed
+// block offsets need no running sum.
 __device__ void stage_phase(const PArgs &A, int ph, Lds &L) {
   const int G = gridDim.x;
   const PSeg *lst = L.segbuf + (ph & 1) * kMaxSeg;
+  const uint32_t *lw = reinterpret_cast<const uint32_t *>(lst);
+  const int pw = wave_id() - 4;  // 0..3
+  const int lane = threadIdx.x & 63;
   const int width = lst[0].per_tile, nseg = lst[0].fixed;
+  // record 1 + pw + 4 j, dword f, for j = 8 b + (lane >> 3), f = lane & 7
+  uint32_t rv0, rv1;
+  {
+    const int k0 = 1 + pw + 4 * (lane >> 3), k1 = k0 + 32;
+    rv0 = k0 < kMaxSeg ? lw[k0 * 8 + (lane & 7)] : 0u;
+    rv1 = k1 < kMaxSeg ? lw[k1 * 8 + (lane & 7)] : 0u;
+  }
   int t0, t1;
   my_tiles((width + 15) / 16, G, blockIdx.x, t0, t1);
   const int nt = t1 - t0;
-  int off = 0, kglob = 0;
-  const int pw = wave_id() - 4;  // prefetch wave index 0..3
-  const int lane = threadIdx.x & 63;
   PhaseCtx &C = *L.ctx;
-  auto copy = [&](const void *src, unsigned char *dst, int nbytes) {
-    const int units = nbytes / 16;
-    const int nch = (units + 63) / 64;
-    for (int c = 0; c < nch; ++c, ++kglob) {
-      if ((kglob & 3) != pw) continue;
-      const int u = c * 64 + lane;
-      if (u < units)
-        __builtin_amdgcn_global_load_lds((const char *)src + (size_t)u * 16, dst + c * 1024, 16, 0, 0);
-    }
-  };
-  const bool lead = pw == 0 && lane == 0;
-  if (lead) {
+  if (pw == 0 && lane == 0) {
     C.has_a = ph > 0;
     C.t0 = t0;
     C.t1 = t1;
   }
-  for (int k = 1; k < nseg; ++k) {
-    const PSeg sg = lst[k];
-    const int bytes = sg.fixed + nt * sg.per_tile;
-    const char *src = (const char *)sg.src + (long long)t0 * sg.stride;
-    const int kind = sg.kind & 255, m = sg.kind >> 8;
+  auto copy = [&](const char *src, unsigned char *dst, int nbytes) {
+    const int units = nbytes / 16;
+    const int nch = (units + 63) / 64;
+    for (int c = 0; c < nch; ++c) {
+      const int u = c * 64 + lane;
+      if (u < units) __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, dst + c * 1024, 16, 0, 0);
+    }
+  };
+  for (int j = 0; 1 + pw + 4 * j < nseg; ++j) {
+    const uint32_t v = j < 8 ? rv0 : rv1;
+    const int base = 8 * (j & 7);
+    // readlane returns int: every field goes through uint32_t before it is
+    // widened, so a low word with bit 31 set is not sign-extended
+    uint32_t f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (uint32_t)__builtin_amdgcn_readlane((int)v, base + i);
+    const uint64_t srcv = (uint64_t)f[0] | ((uint64_t)f[1] << 32);
+    const int64_t stride = (int64_t)((uint64_t)f[2] | ((uint64_t)f[3] << 32));
+    const int per_tile = (int)f[4], fixed = (int)f[5], kindm = (int)f[6];
+    const uint32_t offp = f[7];
+    const int bytes = fixed + nt * per_tile;
+    const char *src = reinterpret_cast<const char *>(srcv) + (int64_t)t0 * stride;
+    const int kind = kindm & 255, m = kindm >> 8;
     unsigned char *dst;
     if (kind == kSegUnits) {
       dst = reinterpret_cast<unsigned char *>(ph > 0 ? &C.ua : &C.ub);
     } else if (kind == kSegLayers) {
       dst = reinterpret_cast<unsigned char *>(C.la);
     } else {
+      const int off = (int)(offp & 0xffffu) + nt * (int)(offp >> 16);
       dst = L.stg + off;
-      if (lead) {
+      if (lane == 0) {
         if (kind == kSegS2) C.s2_off[m] = off;
         else if (kind == kSegH) C.h_off[m] = off;
         else if (kind == kSegL) C.l_off[m] = off;
         else if (kind == kSegS1) C.s1_off[m] = off;
         else if (kind == kSegG) C.g_off[m] = off;
       }
-      off += bytes;
     }
     copy(src, dst, bytes);
   }
-  if (ph < A.nunits)
-    copy(A.segs + (size_t)(ph + 1) * kMaxSeg,
+  if (ph < A.nunits && pw == 3)
+    copy(reinterpret_cast<const char *>(A.segs + (size_t)(ph + 1) * kMaxSeg),
          reinterpret_cast<unsigned char *>(L.segbuf + ((ph + 1) & 1) * kMaxSeg), kMaxSeg * 32);
 }
 
@@ -298,14 +314,26 @@ __device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float
 }
 
 // ----------------------------------------------------------- products
+// The phase context lives in LDS.  Every function below first loads the
+// context fields it needs for all layers at once (unconditional loads, so
+// they are in flight together) and only then branches on them; a chain
+// of dependent LDS reads costs ~0.1 us per link.
+
 // Second product of unit A over the workgroup's rows: every layer's fp16
 // outputs (trace), their combine into xs, and the output rows on the last
-// phase.  All descriptors come from the LDS phase context.
+// phase.
 __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   const PhaseCtx &C = *L.ctx;
   const PUnit &U = C.ua;
+  const int na = U.n, ub = U.b;
   const int t0 = C.t0, nt = C.t1 - C.t0, rows = 16 * nt;
-  // table bases and task counts per (layer, path): small uniform loop over LDS
+  int Pm[kMaxUnitLayers], Wkm[kMaxUnitLayers];
+#pragma unroll
+  for (int m = 0; m < kMaxUnitLayers; ++m) {
+    Pm[m] = C.la[m].P;
+    Wkm[m] = C.la[m].Wk;
+  }
+  // table bases and task counts per (layer, path)
   int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
   int ntask = 0;
   {
@@ -313,10 +341,10 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
 #pragma unroll
     for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
       const int m = mp >> 1, p = mp & 1;
-      const bool live = m < U.n && p < C.la[m].P;
+      const bool live = m < na && p < Pm[m];
       tbase[mp] = toff;
-      tcnt[mp] = live ? C.la[m].Wk * 8 * 4 : 0;
-      toff += live ? C.la[m].Wk * 8 * 16 : 0;
+      tcnt[mp] = live ? Wkm[m] * 8 * 4 : 0;
+      toff += live ? Wkm[m] * 8 * 16 : 0;
       ntask += tcnt[mp];
     }
   }
@@ -328,20 +356,23 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
     const int m = mp >> 1, p = mp & 1;
     const PLayer &Ly = C.la[m];
+    const int s = Ly.s, s8 = Ly.s8, lat = Ly.col0 + p * Ly.s, loff = C.l_off[m];
     const int grp = rem >> 2, hi = rem & 3;
-    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + C.l_off[m]) + p * Ly.s8;
+    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + loff) + p * s8;
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = 4 * grp + j;
-      v[j] = k < Ly.s ? h2f(lv[k]) * L.T[Ly.col0 + p * Ly.s + k] : 0.f;
+      const int kc = k < s ? k : 0;
+      const float lk = h2f(lv[kc]), tk = L.T[lat + kc];
+      v[j] = k < s ? lk * tk : 0.f;
     }
     table_quad(L.tab2 + pick(tbase, mp) + grp * 16, v[0], v[1], v[2], v[3], hi);
   }
   __syncthreads();
   // lookups: task = (layer, path, row); lpt lanes of a task split the words
   if (rows > 0) {
-    const int ntk = U.n * 2 * rows;
+    const int ntk = na * 2 * rows;
     int lpt = 1;
     while (lpt < 64 && ntk * lpt * 2 <= kThreads) lpt *= 2;
     const int sub = threadIdx.x & (lpt - 1);
@@ -349,45 +380,64 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const int tk = tk0 + (int)threadIdx.x / lpt;
       const int r = tk % rows, mp = tk / rows, m = mp >> 1, p = mp & 1;
       float acc = 0.f;
-      if (tk < ntk && p < C.la[m].P) {
-        const PLayer &Ly = C.la[m];
-        const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + C.s2_off[m]) +
-                             ((size_t)((r >> 4) * Ly.P + p) * Ly.Wk) * 16 + (r & 15);
+      const int mc = tk < ntk ? m : 0;
+      const int P = pick(Pm, mc), Wk = pick(Wkm, mc), s2o = C.s2_off[mc];
+      if (tk < ntk && p < P) {
+        const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
+                             ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
         const float *tb = L.tab2 + pick(tbase, mp);
-        const int Wk = Ly.Wk;
-        for (int q = sub; q < Wk; q += lpt) {
+        // two words in flight per step
+        for (int q = sub; q < Wk; q += 2 * lpt) {
+          const int q2 = q + lpt;
           const uint32_t wd = wb[q * 16];
+          const uint32_t wd2 = q2 < Wk ? wb[q2 * 16] : 0u;
           const float *tq = tb + q * 128;
 #pragma unroll
           for (int n = 0; n < 8; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
+          if (q2 < Wk) {
+            const float *tq2 = tb + q2 * 128;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc += tq2[n * 16 + ((wd2 >> (4 * n)) & 15u)];
+          }
         }
       }
       for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
       if (sub == 0 && tk < ntk) L.acc2[mp * (16 * kTMax) + r] = acc;
     }
   }
+  // per-layer offsets for the epilogue, loaded before the barrier
+  int hoff[kMaxUnitLayers];
+  int64_t trace_y[kMaxUnitLayers];
+#pragma unroll
+  for (int m = 0; m < kMaxUnitLayers; ++m) {
+    hoff[m] = C.h_off[m];
+    trace_y[m] = C.la[m].trace_y;
+  }
+  const float c_out = U.c_out;
+  const int64_t trace_x = C.ub.trace_x;
   __syncthreads();
   // epilogue: y per layer, combine, output
   for (int r = threadIdx.x; r < rows; r += kThreads) {
     const int j = 16 * t0 + r;
     float ys = 0.f;
-    for (int m = 0; m < U.n; ++m) {
-      const PLayer &Ly = C.la[m];
-      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + C.h_off[m]);
-      float yv = 0.f;
-      for (int p = 0; p < Ly.P; ++p)
-        yv += h2f(hv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.acc2[(m * 2 + p) * (16 * kTMax) + r];
+#pragma unroll
+    for (int m = 0; m < kMaxUnitLayers; ++m) {
+      if (m >= na) break;
+      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + hoff[m]);
+      const int P = Pm[m];
+      float yv = h2f(hv[((r >> 4) * P) * 16 + (r & 15)]) * L.acc2[(m * 2) * (16 * kTMax) + r];
+      if (P > 1) yv += h2f(hv[((r >> 4) * P + 1) * 16 + (r & 15)]) * L.acc2[(m * 2 + 1) * (16 * kTMax) + r];
       const uint16_t y16 = f2h(yv);
-      if (j < U.b && A.trace) A.trace[Ly.trace_y + j] = y16;
+      if (j < ub && A.trace) A.trace[trace_y[m] + j] = y16;
       ys += h2f(y16);
     }
-    const uint16_t xv = f2h(U.c_out * ys);
-    L.xs[r] = j < U.b ? h2f(xv) : 0.f;
-    if (j < U.b) {
+    const uint16_t xv = f2h(c_out * ys);
+    L.xs[r] = j < ub ? h2f(xv) : 0.f;
+    if (j < ub) {
       if (ph == A.nunits)
         A.y[j] = xv;
       else if (A.trace)
-        A.trace[C.ub.trace_x + j] = xv;
+        A.trace[trace_x + j] = xv;
     }
   }
   __syncthreads();
@@ -398,12 +448,19 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
 __device__ void first_product(Lds &L) {
   const PhaseCtx &C = *L.ctx;
   const PUnit &U = C.ub;
+  const int nb = U.n, Lu = U.Lu;
   const PLayer *LB = C.la + (C.has_a ? C.ua.n : 0);
   const int nt = C.t1 - C.t0, quads = 4 * nt;
   if (nt == 0) {
-    for (int c = threadIdx.x; c < U.Lu; c += kThreads) L.part[c] = 0.f;
+    for (int c = threadIdx.x; c < Lu; c += kThreads) L.part[c] = 0.f;
     __syncthreads();
     return;
+  }
+  int Pm[kMaxUnitLayers], col0m[kMaxUnitLayers];
+#pragma unroll
+  for (int m = 0; m < kMaxUnitLayers; ++m) {
+    Pm[m] = LB[m].P;
+    col0m[m] = LB[m].col0;
   }
   int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
   int ntask = 0;
@@ -412,7 +469,7 @@ __device__ void first_product(Lds &L) {
 #pragma unroll
     for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
       const int m = mp >> 1, p = mp & 1;
-      const bool live = m < U.n && p < LB[m].P;
+      const bool live = m < nb && p < Pm[m];
       tbase[mp] = toff;
       tcnt[mp] = live ? quads * 4 : 0;
       toff += live ? quads * 16 : 0;
@@ -426,33 +483,41 @@ __device__ void first_product(Lds &L) {
     for (int i = 0; i < 2 * kMaxUnitLayers; ++i)
       if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
     const int m = mp >> 1, p = mp & 1;
-    const PLayer &Ly = LB[m];
+    const int P = pick(Pm, m), goff = C.g_off[m];
     const int qd = rem >> 2, hi = rem & 3;
-    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + C.g_off[m]);
+    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + goff);
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * qd + j;
-      v[j] = h2f(gv[((r >> 4) * Ly.P + p) * 16 + (r & 15)]) * L.xs[r];
+      v[j] = h2f(gv[((r >> 4) * P + p) * 16 + (r & 15)]) * L.xs[r];
     }
     table_quad(L.tab1 + pick(tbase, mp) + qd * 16, v[0], v[1], v[2], v[3], hi);
   }
+  int s1o[kMaxUnitLayers], sm[kMaxUnitLayers], Lpm[kMaxUnitLayers];
+#pragma unroll
+  for (int m = 0; m < kMaxUnitLayers; ++m) {
+    s1o[m] = C.s1_off[m];
+    sm[m] = LB[m].s;
+    Lpm[m] = LB[m].Lp;
+  }
   __syncthreads();
   int lpt = 1;
-  while (lpt < 64 && lpt < nt && U.Lu * lpt * 2 <= kThreads) lpt *= 2;
+  while (lpt < 64 && lpt < nt && Lu * lpt * 2 <= kThreads) lpt *= 2;
   const int sub = threadIdx.x & (lpt - 1);
-  for (int c0 = 0; c0 < U.Lu; c0 += kThreads / lpt) {
+  for (int c0 = 0; c0 < Lu; c0 += kThreads / lpt) {
     const int c = c0 + (int)threadIdx.x / lpt;
     float acc = 0.f;
-    if (c < U.Lu) {
+    if (c < Lu) {
       int m = 0;
-      while (m + 1 < U.n && LB[m + 1].col0 <= c) ++m;
-      const PLayer &Ly = LB[m];
-      const int cl = c - Ly.col0;
-      const int p = cl < Ly.s ? 0 : 1;
-      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + C.s1_off[m]) + cl;
+#pragma unroll
+      for (int i = 1; i < kMaxUnitLayers; ++i)
+        if (i < nb && col0m[i] <= c) m = i;
+      const int cl = c - pick(col0m, m);
+      const int p = cl < pick(sm, m) ? 0 : 1;
+      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + pick(s1o, m)) + cl;
       const float *tb = L.tab1 + pick(tbase, m * 2 + p);
-      const int Lp = Ly.Lp;
+      const int Lp = pick(Lpm, m);
       for (int gi = sub; gi < nt; gi += lpt) {
         const uint32_t wd = bits[gi * Lp];
         const float *tq = tb + gi * 64;
@@ -461,7 +526,7 @@ __device__ void first_product(Lds &L) {
       }
     }
     for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
-    if (sub == 0 && c < U.Lu) L.part[c] = acc;
+    if (sub == 0 && c < Lu) L.part[c] = acc;
   }
   __syncthreads();
 }
@@ -695,8 +760,15 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   for (int ph = 0; ph <= P->nunits && ok; ++ph) {
     PSeg *lst = &segs[(size_t)ph * kMaxSeg];
     int n = 1;
+    int off_fixed = 0, off_tile = 0;  // running LDS offset = off_fixed + nt * off_tile
     auto add = [&](const void *src, long long stride, int per_tile, int fixed, int kind, int m) {
-      lst[n++] = PSeg{src, stride, per_tile, fixed, kind | (m << 8), 0};
+      int offp = 0;
+      if (kind >= kSegS2) {
+        offp = off_fixed | (off_tile << 16);
+        off_fixed += fixed;
+        off_tile += per_tile;
+      }
+      lst[n++] = PSeg{src, stride, per_tile, fixed, kind | (m << 8), offp};
     };
     const int ua = ph > 0 ? ph - 1 : 0;
     const int nun = (ph > 0) + (ph < P->nunits);
@@ -726,6 +798,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     lst[0] = PSeg{nullptr, 0, width, n, kSegHeader, 0};
     for (int k = 1; k < n; ++k)
       if ((lst[k].per_tile | lst[k].fixed) % 16 != 0) ok = false;  // DMA moves 16-byte units
+    if (off_fixed > 0xffff || off_tile > 0xffff) ok = false;  // offsets packed in 16 bits
   }
   ok = ok && hipMalloc(&P->d_segs, sizeof(PSeg) * segs.size()) == hipSuccess;
   ok = ok && hipMemcpy(P->d_segs, segs.data(), sizeof(PSeg) * segs.size(), hipMemcpyHostToDevice) ==
