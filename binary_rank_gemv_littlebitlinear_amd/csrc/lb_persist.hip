@@ -29,12 +29,12 @@
 // exchange, so HBM latency overlaps the device-wide synchronisation.
 //
 // Exchange.  Partial latent vectors (one per workgroup) are all-reduced
-// between phases: each workgroup stores its partials contiguously and
-// raises a flag; workgroup r sums the 8-column slice r over all
-// workgroups in a fixed order and raises a second flag; everyone reads the
-// reduced vector.  Exchanged words are written and read with relaxed
-// device-coherent (sc1) atomics, a store's completion (s_waitcnt) comes
-// before the flag that publishes it, and flags carry a generation number.
+// between phases: each workgroup stores its partials contiguously;
+// workgroup r sums the 8-column slice r over all workgroups in a fixed
+// order; everyone reads the reduced vector.  Every exchanged word is a
+// 64-bit value | generation pair written and read with relaxed
+// device-coherent (sc1) atomics, so a reader knows a word is current from
+// the word itself and no flag (or store-completion wait) is needed.
 // Every wait is bounded: on timeout a device error word is set, all
 // workgroups leave, and lb_stack_check returns LB_ETIMEOUT.
 #include <hip/hip_fp16.h>
@@ -57,7 +57,6 @@ constexpr int kStgBytes = 56 * 1024;
 constexpr int kTab2Floats = 10240;
 constexpr int kTab1Floats = 4096;
 constexpr long kSpin = 4000000;  // polls before a wait gives up
-constexpr int kFlagStride = 64;  // flags 256 bytes apart (separate lines and channels)
 
 struct alignas(16) PLayer {
   const uint32_t *su2t;
@@ -104,10 +103,8 @@ struct PArgs {
   uint16_t *y;
   uint16_t *trace;  // may be null
   unsigned gen_base;
-  float *xpart;     // [G][kLuMax] partials
-  float *xT;        // [kLuMax] reduced latent
-  unsigned *flag1;  // [G] flags, kFlagStride words apart
-  unsigned *flag2;  // [kLuMax / 8] flags, kFlagStride words apart
+  uint64_t *xpart;  // [G][kLuMax] tagged partials (value bits | generation << 32)
+  uint64_t *xT;     // [kLuMax] tagged reduced latent
   unsigned *err;
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
   const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
@@ -123,8 +120,8 @@ struct PersistPlan {
   PSeg *d_segs = nullptr;
   std::vector<PUnit> h_units;
   std::vector<PLayer> h_layers;
-  float *xpart = nullptr, *xT = nullptr;
-  unsigned *flags = nullptr;  // flag1 [G], flag2 [kLuMax/8], err [64]
+  uint64_t *xpart = nullptr, *xT = nullptr;
+  unsigned *err = nullptr;  // 64 words; word 0 is the error word
   unsigned gen = 0;
   bool broken = false;
   uint64_t *timeline = nullptr;
@@ -145,7 +142,16 @@ __device__ __forceinline__ float ld_f(float *p) {
 __device__ __forceinline__ void st_f(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool reached(unsigned v, unsigned gen) { return (int)(v - gen) >= 0; }
+// A tagged word: fp32 value bits in the low half, the generation (phase
+// number of the sweep, never 0) in the high half; one aligned 64-bit
+// atomic store, so a reader sees the old word or the new one.
+__device__ __forceinline__ void st_tag(uint64_t *p, float v, unsigned gen) {
+  __hip_atomic_store(p, (uint64_t)__float_as_uint(v) | ((uint64_t)gen << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // 16-row tiles [t0, t1) owned by workgroup w out of `tiles`.
@@ -164,26 +170,6 @@ __device__ __forceinline__ bool block_all(bool ok, int *flags8) {
   for (int i = 0; i < kWaves; ++i) r &= flags8[i];
   __syncthreads();
   return r != 0;
-}
-
-// Wait until flags[0..n) reached gen; threads < kXThreads poll.
-__device__ bool wait_flags(unsigned *flags, int n, unsigned gen, unsigned *err, int *flags8) {
-  long spins = 0;
-  while (true) {
-    bool ok = true;
-    if ((int)threadIdx.x < kXThreads)
-      for (int i = threadIdx.x; i < n; i += kXThreads)
-        ok = ok && reached(ld_u(&flags[(size_t)i * kFlagStride]), gen);
-    if (block_all(ok, flags8)) return true;
-    if ((++spins & 63) == 0) {
-      const bool bad = threadIdx.x == 0 && ld_u(err) != 0;
-      if (!block_all(!bad, flags8)) return false;
-      if (spins > kSpin) {
-        if (threadIdx.x == 0) atomicOr(err, 1u);
-        return false;
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------ LDS arrangement
@@ -532,71 +518,97 @@ __device__ void first_product(Lds &L) {
 }
 
 // -------------------------------------------------------- the exchange
-// part (LDS, Lu floats) of every workgroup -> T (LDS) = their sum.  Only
-// threads < kXThreads touch global memory; the others (the prefetch
-// waves) only join the barriers.  Every step issues all of its loads
-// before using any of them, so each step costs one memory round trip.
-constexpr int kXLoads = kLuMax / kXThreads;  // per-thread loads of one step
+// part (LDS, Lu floats) of every workgroup -> T (LDS) = their sum.
+// Reduce-scatter then all-gather through device memory with tagged words
+// and no separate flags: workgroup w stores its partials tagged with this
+// phase's generation; the owner of slice r (8 columns) spins on the 8 G
+// words of its slice until every one carries the generation, sums them in
+// a fixed order and stores the 8 sums tagged; everyone spins on the Lu
+// tagged sums.  Each level costs one store and one read (plus re-reads
+// while words are missing).  Only threads < kXThreads touch memory; every
+// spin is bounded and checks the error word every 64 rounds.
+constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
+
+// Wait (per thread) until the words at p(k), k < kXLoads with valid(k),
+// carry gen; their values go to vals.  False on give-up or error.
+template <class Ptr, class Valid>
+__device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, unsigned *err,
+                                            float (&vals)[kXLoads]) {
+  unsigned pend = 0;
+#pragma unroll
+  for (int k = 0; k < kXLoads; ++k) {
+    vals[k] = 0.f;
+    if (valid(k)) pend |= 1u << k;
+  }
+  long spins = 0;
+  while (pend) {
+    uint64_t wds[kXLoads];
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k) wds[k] = ((pend >> k) & 1u) ? ld_tag(p(k)) : 0ull;
+#pragma unroll
+    for (int k = 0; k < kXLoads; ++k)
+      if (((pend >> k) & 1u) && (unsigned)(wds[k] >> 32) == gen) {
+        vals[k] = __uint_as_float((unsigned)wds[k]);
+        pend &= ~(1u << k);
+      }
+    if (pend && (++spins & 63) == 0) {
+      if (ld_u(err) != 0) return false;
+      if (spins > kSpin) {
+        atomicOr(err, 1u);
+        return false;
+      }
+    }
+  }
+  return true;
+}
 
 __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A) {
   const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
   const bool xw = t < kXThreads;
   const int nsl = (Lu + 7) / 8;
+  bool ok = true;
   if (xw) {
 #pragma unroll
     for (int k = 0; k < kXLoads; ++k) {
       const int c = t + k * kXThreads;
-      if (c < nsl * 8) st_f(&A.xpart[(size_t)w * kLuMax + c], c < Lu ? L.part[c] : 0.f);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();
-  if (t == 0) st_u(&A.flag1[(size_t)w * kFlagStride], gen);
-  if (w < nsl) {
-    if (!wait_flags(A.flag1, G, gen, A.err, L.flags8)) return false;
-    for (int r = w; r < nsl; r += G) {
-      // lane t of load k reads element e = 256 k + t of the (producer, j)
-      // grid: 8 lanes cover one producer's 32 contiguous bytes.  Thread t
-      // sums column j = t % 8 over its producers in fixed order.
-      if (xw) {
-        float vals[kXLoads];
-#pragma unroll
-        for (int k = 0; k < kXLoads; ++k) {
-          const int e = t + k * kXThreads;
-          vals[k] = e < G * 8 ? ld_f(&A.xpart[(size_t)(e >> 3) * kLuMax + 8 * r + (e & 7)]) : 0.f;
-        }
-        float v = 0.f;
-#pragma unroll
-        for (int k = 0; k < kXLoads; ++k) v += vals[k];
-        L.red[t] = v;
-      }
-      __syncthreads();
-      for (int st = kXThreads / 2; st >= 8; st >>= 1) {
-        if (t < st) L.red[t] += L.red[t + st];
-        __syncthreads();
-      }
-      if (t < 8) st_f(&A.xT[8 * r + t], L.red[t]);
-      if (xw) __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t == 0) st_u(&A.flag2[(size_t)r * kFlagStride], gen);
+      if (c < nsl * 8) st_tag(&A.xpart[(size_t)w * kLuMax + c], c < Lu ? L.part[c] : 0.f, gen);
     }
   }
-  if (!wait_flags(A.flag2, nsl, gen, A.err, L.flags8)) return false;
+  for (int r = w; r < nsl; r += G) {
+    // word k of thread t: element e = 256 k + t of the (producer, column)
+    // grid, producer e / 8, column 8 r + e % 8.  Thread t sums column t % 8
+    // over its producers in k order; the tree below then sums the threads.
+    if (xw) {
+      float vals[kXLoads];
+      ok = ok && spin_tagged(
+          [&](int k) {
+            const int e = t + k * kXThreads;
+            return &A.xpart[(size_t)(e >> 3) * kLuMax + 8 * r + (e & 7)];
+          },
+          [&](int k) { return t + k * kXThreads < G * 8; }, gen, A.err, vals);
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < kXLoads; ++k) v += vals[k];
+      L.red[t] = v;
+    }
+    __syncthreads();
+    for (int st = kXThreads / 2; st >= 8; st >>= 1) {
+      if (t < st) L.red[t] += L.red[t + st];
+      __syncthreads();
+    }
+    if (t < 8) st_tag(&A.xT[8 * r + t], L.red[t], gen);
+  }
   if (xw) {
     float vals[kXLoads];
-#pragma unroll
-    for (int k = 0; k < kXLoads; ++k) {
-      const int c = t + k * kXThreads;
-      vals[k] = c < Lu ? ld_f(&A.xT[c]) : 0.f;
-    }
+    ok = ok && spin_tagged([&](int k) { return &A.xT[t + k * kXThreads]; },
+                           [&](int k) { return t + k * kXThreads < Lu; }, gen, A.err, vals);
 #pragma unroll
     for (int k = 0; k < kXLoads; ++k) {
       const int c = t + k * kXThreads;
       if (c < Lu) L.T[c] = vals[k];
     }
   }
-  __syncthreads();
-  return true;
+  return block_all(ok, L.flags8);
 }
 
 // --------------------------------------------------------------- kernel
@@ -745,12 +757,11 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   }
   P->lds = lds_bytes();
   if (P->lds > (size_t)prop.sharedMemPerBlock) return unsupported();
-  const size_t nflags = ((size_t)G + kLuMax / 8 + 1) * kFlagStride;
   bool ok = hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
             hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
-            hipMalloc(&P->xpart, sizeof(float) * (size_t)G * kLuMax) == hipSuccess &&
-            hipMalloc(&P->xT, sizeof(float) * kLuMax) == hipSuccess &&
-            hipMalloc(&P->flags, sizeof(unsigned) * nflags) == hipSuccess;
+            hipMalloc(&P->xpart, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess &&
+            hipMalloc(&P->xT, sizeof(uint64_t) * kLuMax) == hipSuccess &&
+            hipMalloc(&P->err, sizeof(unsigned) * 64) == hipSuccess;
   ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits,
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers,
@@ -803,8 +814,9 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   ok = ok && hipMalloc(&P->d_segs, sizeof(PSeg) * segs.size()) == hipSuccess;
   ok = ok && hipMemcpy(P->d_segs, segs.data(), sizeof(PSeg) * segs.size(), hipMemcpyHostToDevice) ==
                  hipSuccess;
-  ok = ok && hipMemset(P->flags, 0, sizeof(unsigned) * nflags) == hipSuccess;
-  ok = ok && hipMemset(P->xpart, 0, sizeof(float) * (size_t)G * kLuMax) == hipSuccess;
+  ok = ok && hipMemset(P->err, 0, sizeof(unsigned) * 64) == hipSuccess;
+  ok = ok && hipMemset(P->xpart, 0, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess;
+  ok = ok && hipMemset(P->xT, 0, sizeof(uint64_t) * kLuMax) == hipSuccess;
   ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)P->lds) == hipSuccess;
   int occ = 0;
@@ -825,17 +837,19 @@ void persist_free(PersistPlan *p) {
   if (p->d_segs) (void)hipFree(p->d_segs);
   if (p->xpart) (void)hipFree(p->xpart);
   if (p->xT) (void)hipFree(p->xT);
-  if (p->flags) (void)hipFree(p->flags);
+  if (p->err) (void)hipFree(p->err);
   delete p;
 }
 
 lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace, int64_t M,
                       hipStream_t st, std::string *msg) {
   if (M != 1) return LB_EUNSUPPORTED;
-  const size_t nflags = ((size_t)p->G + kLuMax / 8 + 1) * kFlagStride;
   if (p->broken) {
-    // a previous launch timed out: reset the flags before reuse
-    if (hipMemset(p->flags, 0, sizeof(unsigned) * nflags) != hipSuccess) return LB_EHIP;
+    // a previous launch gave up a wait: clear the error word and every tag
+    if (hipMemset(p->err, 0, sizeof(unsigned) * 64) != hipSuccess ||
+        hipMemset(p->xpart, 0, sizeof(uint64_t) * (size_t)p->G * kLuMax) != hipSuccess ||
+        hipMemset(p->xT, 0, sizeof(uint64_t) * kLuMax) != hipSuccess)
+      return LB_EHIP;
     p->gen = 0;
     p->broken = false;
   }
@@ -849,9 +863,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.gen_base = p->gen;
   A.xpart = p->xpart;
   A.xT = p->xT;
-  A.flag1 = p->flags;
-  A.flag2 = p->flags + (size_t)p->G * kFlagStride;
-  A.err = p->flags + ((size_t)p->G + kLuMax / 8) * kFlagStride;
+  A.err = p->err;
   A.timeline = p->timeline;
   A.segs = p->d_segs;
   hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
@@ -870,7 +882,7 @@ int persist_phases(const PersistPlan *p) { return p->nunits + 1; }
 
 lb_status persist_check(PersistPlan *p, std::string *msg) {
   unsigned e = 0;
-  if (hipMemcpy(&e, p->flags + ((size_t)p->G + kLuMax / 8) * kFlagStride, sizeof(unsigned),
+  if (hipMemcpy(&e, p->err, sizeof(unsigned),
                 hipMemcpyDeviceToHost) !=
       hipSuccess)
     return LB_EHIP;
