@@ -319,7 +319,8 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
     Pm[m] = C.la[m].P;
     Wkm[m] = C.la[m].Wk;
   }
-  // table bases and task counts per (layer, path)
+  // table bases and group counts per (layer, path); a group is 4 latent
+  // columns and its table has 16 entries
   int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
   int ntask = 0;
   {
@@ -329,12 +330,12 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const int m = mp >> 1, p = mp & 1;
       const bool live = m < na && p < Pm[m];
       tbase[mp] = toff;
-      tcnt[mp] = live ? Wkm[m] * 8 * 4 : 0;
+      tcnt[mp] = live ? Wkm[m] * 8 : 0;
       toff += live ? Wkm[m] * 8 * 16 : 0;
       ntask += tcnt[mp];
     }
   }
-  // tables from w = l * t: task = (layer, path, group, hi)
+  // tables from w = l * t: one thread builds the whole table of a group
   for (int task = threadIdx.x; task < ntask; task += kThreads) {
     int rem = task, mp = 0;
 #pragma unroll
@@ -343,7 +344,7 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
     const int m = mp >> 1, p = mp & 1;
     const PLayer &Ly = C.la[m];
     const int s = Ly.s, s8 = Ly.s8, lat = Ly.col0 + p * Ly.s, loff = C.l_off[m];
-    const int grp = rem >> 2, hi = rem & 3;
+    const int grp = rem;
     const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + loff) + p * s8;
     float v[4];
 #pragma unroll
@@ -353,7 +354,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const float lk = h2f(lv[kc]), tk = L.T[lat + kc];
       v[j] = k < s ? lk * tk : 0.f;
     }
-    table_quad(L.tab2 + pick(tbase, mp) + grp * 16, v[0], v[1], v[2], v[3], hi);
+    float *tab = L.tab2 + pick(tbase, mp) + grp * 16;
+#pragma unroll
+    for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
   }
   __syncthreads();
   // lookups: task = (layer, path, row); lpt lanes of a task split the words
@@ -372,18 +375,22 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
                              ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
         const float *tb = L.tab2 + pick(tbase, mp);
-        // two words in flight per step
-        for (int q = sub; q < Wk; q += 2 * lpt) {
-          const int q2 = q + lpt;
-          const uint32_t wd = wb[q * 16];
-          const uint32_t wd2 = q2 < Wk ? wb[q2 * 16] : 0u;
-          const float *tq = tb + q * 128;
+        // four words in flight per step
+        for (int q = sub; q < Wk; q += 4 * lpt) {
+          uint32_t wd[4];
 #pragma unroll
-          for (int n = 0; n < 8; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
-          if (q2 < Wk) {
-            const float *tq2 = tb + q2 * 128;
+          for (int i = 0; i < 4; ++i) {
+            const int qi = q + i * lpt;
+            wd[i] = qi < Wk ? wb[qi * 16] : 0u;
+          }
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc += tq2[n * 16 + ((wd2 >> (4 * n)) & 15u)];
+          for (int i = 0; i < 4; ++i) {
+            const int qi = q + i * lpt;
+            if (qi < Wk) {
+              const float *tq = tb + qi * 128;
+#pragma unroll
+              for (int n = 0; n < 8; ++n) acc += tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
+            }
           }
         }
       }
@@ -457,12 +464,12 @@ __device__ void first_product(Lds &L) {
       const int m = mp >> 1, p = mp & 1;
       const bool live = m < nb && p < Pm[m];
       tbase[mp] = toff;
-      tcnt[mp] = live ? quads * 4 : 0;
+      tcnt[mp] = live ? quads : 0;
       toff += live ? quads * 16 : 0;
       ntask += tcnt[mp];
     }
   }
-  // tables from z = g * x: task = (layer, path, quad, hi)
+  // tables from z = g * x: one thread builds the whole table of a quad of rows
   for (int task = threadIdx.x; task < ntask; task += kThreads) {
     int rem = task, mp = 0;
 #pragma unroll
@@ -470,7 +477,7 @@ __device__ void first_product(Lds &L) {
       if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
     const int m = mp >> 1, p = mp & 1;
     const int P = pick(Pm, m), goff = C.g_off[m];
-    const int qd = rem >> 2, hi = rem & 3;
+    const int qd = rem;
     const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + goff);
     float v[4];
 #pragma unroll
@@ -478,7 +485,9 @@ __device__ void first_product(Lds &L) {
       const int r = 4 * qd + j;
       v[j] = h2f(gv[((r >> 4) * P + p) * 16 + (r & 15)]) * L.xs[r];
     }
-    table_quad(L.tab1 + pick(tbase, mp) + qd * 16, v[0], v[1], v[2], v[3], hi);
+    float *tab = L.tab1 + pick(tbase, mp) + qd * 16;
+#pragma unroll
+    for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
   }
   int s1o[kMaxUnitLayers], sm[kMaxUnitLayers], Lpm[kMaxUnitLayers];
 #pragma unroll
@@ -504,11 +513,20 @@ __device__ void first_product(Lds &L) {
       const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + pick(s1o, m)) + cl;
       const float *tb = L.tab1 + pick(tbase, m * 2 + p);
       const int Lp = pick(Lpm, m);
-      for (int gi = sub; gi < nt; gi += lpt) {
-        const uint32_t wd = bits[gi * Lp];
-        const float *tq = tb + gi * 64;
+      uint32_t wds[kTMax];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc += tq[n * 16 + ((wd >> (4 * n)) & 15u)];
+      for (int i = 0; i < kTMax; ++i) {
+        const int gi = sub + i * lpt;
+        wds[i] = gi < nt ? bits[gi * Lp] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kTMax; ++i) {
+        const int gi = sub + i * lpt;
+        if (gi < nt) {
+          const float *tq = tb + gi * 64;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc += tq[n * 16 + ((wds[i] >> (4 * n)) & 15u)];
+        }
       }
     }
     for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
