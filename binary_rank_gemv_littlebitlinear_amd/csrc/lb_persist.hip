@@ -191,7 +191,6 @@ struct Lds {
   float *tab2;         // kTab2Floats second-product tables
   float *tab1;         // kTab1Floats first-product tables
   float *part;         // kLuMax
-  float *T;            // kLuMax
   float *acc2;         // kMaxUnitLayers * 2 * 16 * kTMax
   float *xs;           // 16 * kTMax input rows (fp16 values as fp32)
   float *red;          // kXThreads exchange scratch
@@ -319,10 +318,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
     Pm[m] = C.la[m].P;
     Wkm[m] = C.la[m].Wk;
   }
-  // table bases and group counts per (layer, path); a group is 4 latent
-  // columns and its table has 16 entries
-  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
-  int ntask = 0;
+  // table bases per (layer, path): a group is 4 latent columns and its
+  // table has 16 entries; the tables were built by the previous exchange
+  int tbase[2 * kMaxUnitLayers];
   {
     int toff = 0;
 #pragma unroll
@@ -330,35 +328,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const int m = mp >> 1, p = mp & 1;
       const bool live = m < na && p < Pm[m];
       tbase[mp] = toff;
-      tcnt[mp] = live ? Wkm[m] * 8 : 0;
       toff += live ? Wkm[m] * 8 * 16 : 0;
-      ntask += tcnt[mp];
     }
   }
-  // tables from w = l * t: one thread builds the whole table of a group
-  for (int task = threadIdx.x; task < ntask; task += kThreads) {
-    int rem = task, mp = 0;
-#pragma unroll
-    for (int i = 0; i < 2 * kMaxUnitLayers; ++i)
-      if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
-    const int m = mp >> 1, p = mp & 1;
-    const PLayer &Ly = C.la[m];
-    const int s = Ly.s, s8 = Ly.s8, lat = Ly.col0 + p * Ly.s, loff = C.l_off[m];
-    const int grp = rem;
-    const uint16_t *lv = reinterpret_cast<const uint16_t *>(L.stg + loff) + p * s8;
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 4 * grp + j;
-      const int kc = k < s ? k : 0;
-      const float lk = h2f(lv[kc]), tk = L.T[lat + kc];
-      v[j] = k < s ? lk * tk : 0.f;
-    }
-    float *tab = L.tab2 + pick(tbase, mp) + grp * 16;
-#pragma unroll
-    for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
-  }
-  __syncthreads();
   // lookups: task = (layer, path, row); lpt lanes of a task split the words
   if (rows > 0) {
     const int ntk = na * 2 * rows;
@@ -580,7 +552,67 @@ __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, un
   return true;
 }
 
-__device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A) {
+// The second product's tables of the next phase (unit B of this phase):
+// group g (4 latent columns of one layer and path) is built by exchange
+// thread g % 256 from the reduced latent words and l.  TabPlan holds a
+// thread's groups, read from the phase context before it is restaged.
+constexpr int kGroupsPerThread = (kTab2Floats / 16 + kXThreads - 1) / kXThreads;
+struct TabPlan {
+  int n;                                 // groups of this thread
+  int tcol[kGroupsPerThread];            // latent column of the group's first word
+  int nval[kGroupsPerThread];            // valid columns (< s) of the group, 1..4
+  int dst[kGroupsPerThread];             // table offset in tab2 (floats)
+  const uint16_t *lp[kGroupsPerThread];  // l of the group (global)
+};
+
+__device__ TabPlan plan_tables(const Lds &L) {
+  const PhaseCtx &C = *L.ctx;
+  const int na = C.has_a ? C.ua.n : 0, nb = C.ub.n;
+  const PLayer *LB = C.la + na;
+  int Pm[kMaxUnitLayers], Wkm[kMaxUnitLayers];
+#pragma unroll
+  for (int m = 0; m < kMaxUnitLayers; ++m) {
+    Pm[m] = LB[m].P;
+    Wkm[m] = LB[m].Wk;
+  }
+  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers], ng = 0;
+  {
+    int toff = 0;
+#pragma unroll
+    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
+      const int m = mp >> 1, p = mp & 1;
+      const bool live = m < nb && p < Pm[m];
+      tbase[mp] = toff;
+      tcnt[mp] = live ? Wkm[m] * 8 : 0;
+      toff += live ? Wkm[m] * 8 * 16 : 0;
+      ng += tcnt[mp];
+    }
+  }
+  TabPlan T;
+  T.n = 0;
+#pragma unroll
+  for (int i = 0; i < kGroupsPerThread; ++i) {
+    T.tcol[i] = 0; T.nval[i] = 0; T.dst[i] = 0; T.lp[i] = nullptr;
+    const int g = (int)threadIdx.x + i * kXThreads;
+    if ((int)threadIdx.x < kXThreads && g < ng) {
+      int rem = g, mp = 0;
+#pragma unroll
+      for (int k = 0; k < 2 * kMaxUnitLayers; ++k)
+        if (mp == k && rem >= tcnt[k]) { rem -= tcnt[k]; ++mp; }
+      const int m = mp >> 1, p = mp & 1;
+      const PLayer &Ly = LB[m];
+      const int s = Ly.s;
+      T.tcol[i] = Ly.col0 + p * s + 4 * rem;
+      T.nval[i] = min(4, s - 4 * rem);
+      T.dst[i] = pick(tbase, mp) + rem * 16;
+      T.lp[i] = Ly.l + (size_t)p * Ly.s8 + 4 * rem;
+      T.n = i + 1;
+    }
+  }
+  return T;
+}
+
+__device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp) {
   const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
   const bool xw = t < kXThreads;
   const int nsl = (Lu + 7) / 8;
@@ -616,14 +648,22 @@ __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A) {
     }
     if (t < 8) st_tag(&A.xT[8 * r + t], L.red[t], gen);
   }
+  // all-gather, straight into the next phase's tables: w = l * t per group
   if (xw) {
-    float vals[kXLoads];
-    ok = ok && spin_tagged([&](int k) { return &A.xT[t + k * kXThreads]; },
-                           [&](int k) { return t + k * kXThreads < Lu; }, gen, A.err, vals);
 #pragma unroll
-    for (int k = 0; k < kXLoads; ++k) {
-      const int c = t + k * kXThreads;
-      if (c < Lu) L.T[c] = vals[k];
+    for (int i = 0; i < kGroupsPerThread; ++i) {
+      if (i >= tp.n) break;
+      const uint2 lraw = *reinterpret_cast<const uint2 *>(tp.lp[i]);  // 4 fp16 l
+      float tv[kXLoads];
+      ok = ok && spin_tagged([&](int k) { return &A.xT[tp.tcol[i] + (k & 3)]; },
+                             [&](int k) { return k < tp.nval[i]; }, gen, A.err, tv);
+      const float w0 = tp.nval[i] > 0 ? h2f((uint16_t)(lraw.x & 0xffffu)) * tv[0] : 0.f;
+      const float w1 = tp.nval[i] > 1 ? h2f((uint16_t)(lraw.x >> 16)) * tv[1] : 0.f;
+      const float w2 = tp.nval[i] > 2 ? h2f((uint16_t)(lraw.y & 0xffffu)) * tv[2] : 0.f;
+      const float w3 = tp.nval[i] > 3 ? h2f((uint16_t)(lraw.y >> 16)) * tv[3] : 0.f;
+      float *tab = L.tab2 + tp.dst[i];
+#pragma unroll
+      for (int hi = 0; hi < 4; ++hi) table_quad(tab, w0, w1, w2, w3, hi);
     }
   }
   return block_all(ok, L.flags8);
@@ -643,7 +683,6 @@ k_persist(PArgs A) {
     L.tab2 = reinterpret_cast<float *>(p); p += kTab2Floats * 4;
     L.tab1 = reinterpret_cast<float *>(p); p += kTab1Floats * 4;
     L.part = reinterpret_cast<float *>(p); p += kLuMax * 4;
-    L.T = reinterpret_cast<float *>(p); p += kLuMax * 4;
     L.acc2 = reinterpret_cast<float *>(p); p += kMaxUnitLayers * 2 * 16 * kTMax * 4;
     L.xs = reinterpret_cast<float *>(p); p += 16 * kTMax * 4;
     L.red = reinterpret_cast<float *>(p); p += kXThreads * 4;
@@ -662,6 +701,9 @@ k_persist(PArgs A) {
     __syncthreads();
     if (tl && threadIdx.x == 0) tl[ph * 4 + 0] = __builtin_amdgcn_s_memrealtime();
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
+    // this thread's share of the next phase's tables (built in the
+    // exchange), planned now so the reads overlap the products
+    const TabPlan tp = plan_tables(L);
     if (ph == 0) {
       const PUnit &U0 = L.ctx->ub;
       for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
@@ -682,7 +724,7 @@ k_persist(PArgs A) {
     __syncthreads();  // everyone has read the phase context before it is restaged
     // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
     if (wave_id() >= 4) stage_phase(A, ph + 1, L);
-    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A)) return;
+    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A, tp)) return;
     if (tl && threadIdx.x == 0) tl[ph * 4 + 3] = __builtin_amdgcn_s_memrealtime();
   }
 }
@@ -690,7 +732,7 @@ k_persist(PArgs A) {
 // ------------------------------------------------------------------ host
 static size_t lds_bytes() {
   return (sizeof(PhaseCtx) + 15) / 16 * 16 + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
-         (size_t)(kTab2Floats + kTab1Floats + 2 * kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
+         (size_t)(kTab2Floats + kTab1Floats + kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
                   16 * kTMax + kXThreads + kWaves) * 4 + 64;
 }
 
