@@ -131,6 +131,13 @@ __device__ __forceinline__ void st_rel(float *p, float v) {
 __device__ __forceinline__ float ld_rel(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte stores / loads with the cache policy of relaxed agent-scope
+// atomics (sc1: coherent across the device's L2s), through a buffer
+// resource over [base, base + bytes)
+constexpr int kCoherent = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // LDS-DMA: lane i's 16 (4) source bytes land at dst + 16 i (dst + 4 i).
@@ -315,10 +322,18 @@ k_unit_s1(S1Args A) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) v[r] = acc0[r] + acc1[r];
   if (A.nsplit > 1) {
-    // split z's partial: register r of lane l of wave w at [(tile*nsplit + z)*4096 + (16 w + r)*64 + l]
-    float *pp = A.part + ((size_t)tile * A.nsplit + blockIdx.z) * 4096;
+    // split z's partial: registers 4q..4q+3 of lane l of wave w as one
+    // 16-byte word at [(tile*nsplit + z)*1024 + (4 w + q)*64 + l] (float4 units)
+    const __amdgpu_buffer_rsrc_t rs =
+        coherent_rsrc(A.part + (size_t)tile * A.nsplit * 4096, (uint32_t)A.nsplit * 16384u);
+    const int o0 = blockIdx.z * 16384 + ((w * 4) * 64 + lane) * 16;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st_rel(&pp[(w * 16 + r) * 64 + lane], v[r]);
+    for (int q = 0; q < 4; ++q) {
+      u32x4 o;
+      o.x = __float_as_uint(v[4 * q]); o.y = __float_as_uint(v[4 * q + 1]);
+      o.z = __float_as_uint(v[4 * q + 2]); o.w = __float_as_uint(v[4 * q + 3]);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, o0 + q * 1024, 0, kCoherent);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -328,25 +343,27 @@ k_unit_s1(S1Args A) {
     }
     __syncthreads();
     if (!s_last) return;
-    // the last block of the tile sums the splits in split order
-    const float *pt = A.part + (size_t)tile * A.nsplit * 4096 + (w * 16) * 64 + lane;
-    // every load unconditional (splits past nsplit re-read the last one) so
-    // all of them are in flight at once
-    float q[kMaxSplit][16];
+    // the last block of the tile sums the splits in split order; every load
+    // is unconditional (splits past nsplit re-read the last one) so all of
+    // them are in flight at once
+    u32x4 q[kMaxSplit][4];
+    const int l0 = ((w * 4) * 64 + lane) * 16;
 #pragma unroll
-    for (int z = 0; z < kMaxSplit; ++z) {
-      const float *pz = pt + (size_t)min(z, A.nsplit - 1) * 4096;
+    for (int z = 0; z < kMaxSplit; ++z)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) q[z][r] = ld_rel(&pz[r * 64]);
-    }
+      for (int j = 0; j < 4; ++j)
+        q[z][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, min(z, A.nsplit - 1) * 16384 + l0 + j * 1024, 0,
+                                                        kCoherent);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float sum = q[0][r];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int z = 1; z < kMaxSplit; ++z)
-        if (z < A.nsplit) sum += q[z][r];
-      v[r] = sum;
-    }
+      for (int e = 0; e < 4; ++e) {
+        float sum = __uint_as_float(q[0][j][e]);
+#pragma unroll
+        for (int z = 1; z < kMaxSplit; ++z)
+          if (z < A.nsplit) sum += __uint_as_float(q[z][j][e]);
+        v[4 * j + e] = sum;
+      }
     if (threadIdx.x == 0) __hip_atomic_store(&A.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // fp16 tile [16 c8][32 rows][8] in LDS, then one contiguous 8 KB copy into T
