@@ -52,26 +52,29 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 256;   // 4 waves (second stage)
+constexpr int kThreads1 = 512;  // 8 waves (first stage)
 constexpr int kMaxSplit = 8;
-// stage 1: a workgroup computes 32 rows x 128 latent columns (32 per wave);
-// a round stages kRC1 32-row chunks of the input dimension in LDS
-constexpr int kRC1 = 14;
-constexpr int kS1X = kRC1 * 4 * 512;   // x rows: [c8][32 rows][8 fp16]
-constexpr int kS1W = 4 * kRC1 * 128;   // sign words: [wave][chunk][32 columns]
-constexpr int kS1G = 4 * 1024;         // column scales g: [wave][16 chunks][32 rows]
-constexpr int kS1Buf = kS1X + kS1W + kS1G;
-// stage 2: a workgroup computes 32 rows x 64 outputs; a round stages kRC2
-// (path, 32-column) chunks of one layer's latent rows and sign words
-constexpr int kRC2 = 28;
-constexpr int kS2T = kRC2 * 4 * 512;   // T rows: [c8][32 rows][8 fp16]
-constexpr int kS2W = kRC2 * 256;       // sign words: [chunk][64 outputs]
-constexpr int kS2L = 32 * 64;          // latent scales l: [chunk][32] (2 instructions of 16 chunks)
-constexpr int kS2Buf = kS2T + kS2W + kS2L;
+// stage 1: a workgroup computes 32 rows x 128 latent columns (32 per wave)
+// over a range of 32-row chunks of the input dimension.  A round stages up
+// to C chunks at once (C even, at most kS1MaxC): x rows, and per wave its
+// columns' sign words and the chunks' scales g.
+constexpr int kS1MaxC = 56;
+constexpr int kS1RoundC = 14;  // chunks per round when a split takes several (two buffers)
+__host__ __device__ constexpr int s1_c16(int C) { return (C + 15) & ~15; }
+__host__ __device__ constexpr int s1_words_off(int C) { return C * 2048; }
+__host__ __device__ constexpr int s1_g_off(int C) { return C * 2048 + 4 * C * 128; }
+__host__ __device__ constexpr int s1_lds_bytes(int C) { return s1_g_off(C) + 4 * s1_c16(C) * 64; }
+static_assert(s1_lds_bytes(kS1MaxC) <= 160 * 1024, "a stage-1 round fits the LDS");
+static_assert(2 * s1_lds_bytes(kS1RoundC) <= 80 * 1024, "two buffered rounds leave room for two blocks per CU");
+// stage 2: a workgroup computes 32 rows x 64 nb outputs; a round stages
+// up to kRC2 (path, 32-column) chunks of one layer's latent rows and sign
+// words (two round buffers)
+constexpr int kRC2 = 28;  // a multiple of 4
+constexpr int kS2MinC = 18;            // the wave partials fit one round buffer from here
+constexpr int kS2Lds = 160 * 1024;
 constexpr int kRP2 = 64 + 4;           // LDS pitch (floats) of a wave's 32 x 64 partial
-static_assert(4 * 32 * kRP2 * 4 <= kS2Buf, "the reduction buffer fits one round buffer");
-static_assert(kRC1 % 2 == 0 && kRC1 <= 16, "stage-1 round: two chunks of words, 16 of g per instruction");
-static_assert(kRC2 <= 32, "stage-2 round: l of 16 chunks per instruction, two instructions");
+static_assert(4 * 32 * kRP2 * 4 <= kS2MinC * 2048, "the reduction buffer fits one round buffer");
 
 struct S1Seg {
   const uint32_t *bits;  // sv1m + p*s: word (row group r, column k) at bits[r * pitch + k]
@@ -80,8 +83,9 @@ struct S1Seg {
   int s;                 // valid columns of the segment
   int seg0;              // first column of the segment in T (multiple of 32)
   int pad_;
+  const uint16_t *l;     // l + p*s8: the latent scale folded into T
 };
-static_assert(sizeof(S1Seg) == 32, "S1Seg layout");
+static_assert(sizeof(S1Seg) == 40, "S1Seg layout");
 
 struct S1Args {
   const uint16_t *x;
@@ -90,7 +94,7 @@ struct S1Args {
   unsigned *cnt;
   const void *zero;  // >= 16 zero bytes (DMA source for padding)
   int64_t M;         // rows of this chunk
-  int a, a16, Lt, ntile32, kcps, nsplit, nseg, xvec;
+  int a, a16, Lt, ntile32, kcps, cround, nsplit, nseg, xvec;
   S1Seg seg[kMaxUnitSegs];
 };
 
@@ -111,13 +115,15 @@ struct S2Args {
   int b, Lt, nl, direct;
   float c_out;
   int nrounds;
+  int nb;  // 64-output column pairs per block (1, 2 or 4)
+  int c2;  // chunks per round
   S2Layer ly[kMaxUnitLayersM];
 };
 
 struct MfmaPlan {
   int nl = 0;
   int64_t a = 0, b = 0;
-  int a16 = 0, Lt = 0, ntile32 = 0, nseg = 0, nrounds2 = 0;
+  int a16 = 0, Lt = 0, ntile32 = 0, nseg = 0;
   S1Seg seg[kMaxUnitSegs];
   S2Layer ly[kMaxUnitLayersM];
 };
@@ -161,6 +167,17 @@ __device__ __forceinline__ u32x4 flip_signs(u32x4 v, uint32_t wl) {
   return v;
 }
 
+// The lane's 8 operand values +-1 (fp16) from its sign word, same bit
+// convention as flip_signs: bit set = -1.
+__device__ __forceinline__ u32x4 sign_ones(uint32_t wl) {
+  u32x4 v;
+  v.x = (wl & 0x80008000u) | 0x3C003C00u;
+  v.y = ((wl << 1) & 0x80008000u) | 0x3C003C00u;
+  v.z = ((wl << 2) & 0x80008000u) | 0x3C003C00u;
+  v.w = ((wl << 3) & 0x80008000u) | 0x3C003C00u;
+  return v;
+}
+
 __device__ __forceinline__ uint4 pack8(const float *v) {
   uint4 o;
   o.x = mf2h(v[0]) | ((uint32_t)mf2h(v[1]) << 16);
@@ -185,21 +202,38 @@ __device__ __forceinline__ void store8(uint16_t *base, int n, int64_t row, int c
 // ------------------------------------------------------------- stage 1
 // grid = (Lt / 128, ceil(M / 32), nsplit).  Block (cx, ty, z) computes
 // columns [128 cx, 128 cx + 128) of rows [32 ty, 32 ty + 32) over the
-// 32-row chunks [z * kcps, (z + 1) * kcps) of the input dimension; wave w
-// owns columns 32 w .. 32 w + 31 of the block.  Rows past M and columns
+// 32-row chunks [z * kcps, (z + 1) * kcps) of the input dimension.  Waves
+// w and w + 4 own columns 32 w .. 32 w + 31 of the block, the even and the
+// odd chunks respectively; their sums are added in that order, then each
+// finishes half of the tile's values.  Rows past M and columns
 // past the last segment come out as zeros, so every element of T that
 // the second stage reads is written.
-__global__ void __launch_bounds__(kThreads)
+//
+// All of a round's operands are requested at once; a round is the block's
+// whole chunk range when it fits (up to kS1MaxC chunks), so the copies run
+// at the full depth the memory system allows.  Longer ranges go in rounds
+// of kS1RoundC chunks through two buffers, the next round's copies
+// overlapping this round's products.  LDS layout of a round of C chunks:
+//   x      [chunk][row 32][4 pieces of 8 fp16], piece c8 of row r stored in
+//          slot c8 ^ swz(r): one copy instruction reads 16 rows x 64 bytes,
+//          and the operand reads (32 rows, one piece) hit distinct banks
+//   words  [wave][chunk C][32 columns]
+//   g      [wave][chunk c16(C)][4 pieces of 8 fp16]
+__device__ __forceinline__ int s1_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__global__ void __launch_bounds__(kThreads1)
 k_unit_s1(S1Args A) {
-  extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
+  extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_last;
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
-  const int t32 = blockIdx.x * 4 + w;
+  const int tw = w & 3, par = w >> 2;  // column tile, chunk parity
+  const int t32 = blockIdx.x * 4 + tw;
   const int64_t tok0 = (int64_t)blockIdx.y * 32;
 
-  // the wave's 32 columns lie in one segment
+  // the tile's 32 columns lie in one segment
   const bool active = t32 < A.ntile32;
   bool cval = false, full_cols = false;
+  float lcol = 0.f;  // l of the lane's column (0 past the segment)
   const uint32_t *bb = nullptr;
   const uint16_t *gb = nullptr;
   int pitch = 0;
@@ -213,30 +247,37 @@ k_unit_s1(S1Args A) {
     bb = A.seg[e].bits + k;
     gb = A.seg[e].g;
     pitch = A.seg[e].pitch;
+    if (cval) lcol = mh2f(A.seg[e].l[k]);
   }
   const int nkc = (A.a + 31) >> 5;
   const int kc0 = blockIdx.z * A.kcps;
   const int kc1 = min(nkc, kc0 + A.kcps);
-  const int nr = (kc1 - kc0 + kRC1 - 1) / kRC1;
+  const int C = A.cround;
+  const int nr = (kc1 - kc0 + C - 1) / C;
+  const int wofs = s1_words_off(C), gofs = s1_g_off(C), c16 = s1_c16(C);
 
-  // round r: chunks [kc0 + r kRC1, +nch) of x rows (all waves) and of the
-  // wave's sign words, into buffer r & 1
+  // round r: chunks [kc0 + r C, +nch) of x rows (all waves), and of the
+  // tile's sign words and g (waves 0-3, one tile each)
   auto issue = [&](int r) {
-    unsigned char *buf = smem + (r & 1) * kS1Buf;
-    const int kcr = kc0 + r * kRC1, nch = min(kRC1, kc1 - kcr);
+    unsigned char *buf = smem + (r & 1) * s1_lds_bytes(C);
+    const int kcr = kc0 + r * C, nch = min(C, kc1 - kcr);
     if (A.xvec) {
-      for (int u = w; u < nch * 2; u += 4) {
-        const int c8 = 2 * u + lh;
-        const int64_t tok = tok0 + lr;
-        const int i = kcr * 32 + c8 * 8;
+      // instruction u: chunk u / 2, rows 16 (u & 1) + lane / 4
+      const int rw = lane >> 2;
+      for (int u = w; u < nch * 2; u += kThreads1 / 64) {
+        const int row = 16 * (u & 1) + rw;
+        const int c8 = (lane & 3) ^ s1_swz(row);
+        const int64_t tok = tok0 + row;
+        const int i = (kcr + (u >> 1)) * 32 + c8 * 8;
         const void *src = (tok < A.M && i < A.a) ? (const void *)(A.x + tok * A.a + i) : A.zero;
         dma16(src, buf + u * 1024);
       }
     } else {
-      for (int idx = threadIdx.x; idx < nch * 4 * 32; idx += kThreads) {
-        const int c8 = idx >> 5, row = idx & 31;
+      for (int idx = threadIdx.x; idx < nch * 128; idx += kThreads1) {
+        const int kk = idx >> 7, row = (idx >> 2) & 31;
+        const int c8 = (idx & 3) ^ s1_swz(row);
         const int64_t tok = tok0 + row;
-        const int i = kcr * 32 + c8 * 8;
+        const int i = (kcr + kk) * 32 + c8 * 8;
         uint32_t hv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = (tok < A.M && i + e < A.a) ? A.x[tok * A.a + i + e] : 0u;
@@ -246,66 +287,83 @@ k_unit_s1(S1Args A) {
         *reinterpret_cast<uint4 *>(buf + idx * 16) = o;
       }
     }
-    if (active) {
+    if (active && par == 0) {
+      // words: lanes 0-31 chunk 2 v, lanes 32-63 chunk 2 v + 1 (C is even)
       for (int v = 0; v < (nch + 1) / 2; ++v) {
         const int kk = 2 * v + lh;
         const void *src = (cval && kk < nch) ? (const void *)(bb + (size_t)(kcr + kk) * pitch) : A.zero;
-        dma4(src, buf + kS1X + (w * kRC1 + 2 * v) * 128);
+        dma4(src, buf + wofs + (tw * C + 2 * v) * 128);
       }
-      // g of the chunks: lane = 4 chunk + piece, 8 rows per piece
-      const int kk = lane >> 2, i = (kcr + kk) * 32 + 8 * (lane & 3);
-      const void *src = (kk < nch && i + 8 <= A.a16) ? (const void *)(gb + i) : A.zero;
-      dma16(src, buf + kS1X + kS1W + w * 1024);
+      // g: lane = 4 chunk + piece, 16 chunks per instruction
+      for (int v = 0; v < (nch + 15) / 16; ++v) {
+        const int kk = 16 * v + (lane >> 2), i = (kcr + kk) * 32 + 8 * (lane & 3);
+        const void *src = (kk < nch && i + 8 <= A.a16) ? (const void *)(gb + i) : A.zero;
+        dma16(src, buf + gofs + (tw * c16 + 16 * v) * 64);
+      }
     }
   };
 
-  // two accumulators (even / odd chunks) keep two independent MFMA chains
+  // chunks of the wave's parity alternate between two accumulators, so two
+  // independent MFMA chains interleave
   float16_t acc0, acc1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  const int xo0 = lr * 4 + (lh ^ s1_swz(lr)), xo1 = lr * 4 + ((2 + lh) ^ s1_swz(lr));
+  const int bstride = s1_lds_bytes(C);  // rounds alternate between two buffers when there are several
   issue(0);
   for (int r = 0; r < nr; ++r) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of round r landed
     __syncthreads();                // ... and every other wave's
     if (r + 1 < nr) issue(r + 1);   // overlaps the products below
     if (!active) continue;
-    const unsigned char *buf = smem + (r & 1) * kS1Buf;
-    const int kcr = kc0 + r * kRC1, nch = min(kRC1, kc1 - kcr);
+    const unsigned char *buf = smem + (r & 1) * bstride;
     const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
-    const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + kS1X) + w * kRC1 * 32;
-    const u32x4 *gsd = reinterpret_cast<const u32x4 *>(buf + kS1X + kS1W + w * 1024);
+    const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + wofs) + tw * C * 32;
+    const u32x4 *gsd = reinterpret_cast<const u32x4 *>(buf + gofs) + tw * c16 * 4;
+    const int nch = min(C, kc1 - kc0 - r * C);
+    if (par >= nch) continue;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
     // operands of one chunk: x rows (A), g (B values before the signs), words
     struct Ops { u32x4 a[2], g[2]; uint32_t wd; };
     auto fetch = [&](int kk, Ops &o) {
+      o.a[0] = xs[kk * 128 + xo0];
+      o.a[1] = xs[kk * 128 + xo1];
 #pragma unroll
-      for (int step = 0; step < 2; ++step) {
-        o.a[step] = xs[(kk * 4 + 2 * step + lh) * 32 + lr];
-        o.g[step] = gsd[kk * 4 + 2 * step + lh];  // g of rows 32 kk + 16 step + 8 lh ..
-      }
+      for (int step = 0; step < 2; ++step) o.g[step] = gsd[kk * 4 + 2 * step + lh];  // rows 32 kk + 16 step + 8 lh ..
       o.wd = wsd[kk * 32 + lr];
     };
-    auto mma = [&](const Ops &o, float16_t &acc, auto masked) {
+    auto bvals = [&](const Ops &o, u32x4 (&bv)[2], auto masked) {
       const uint32_t wl = o.wd << (4 * lh);  // group g = 2 step + lh
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
-        u32x4 bv = flip_signs(o.g[step], wl << (8 * step));
-        if (decltype(masked)::value && !cval) bv = z4;
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(o.a[step]), as_h8(bv), acc, 0, 0, 0);
+        bv[step] = flip_signs(o.g[step], wl << (8 * step));
+        if (decltype(masked)::value && !cval) bv[step] = z4;
       }
     };
     // the prefetches are unconditional (index clamped) so the wait before a
     // chunk's products covers only that chunk's reads
     auto sweep = [&](auto masked) {
       Ops c0, c1;
-      fetch(0, c0);
-      fetch(min(1, nch - 1), c1);
-      for (int kk = 0; kk < nch; kk += 2) {
+      fetch(par, c0);
+      fetch(min(par + 2, nch - 1), c1);
+      for (int kk = par; kk < nch; kk += 4) {
         Ops n0, n1;
-        fetch(min(kk + 2, nch - 1), n0);
-        fetch(min(kk + 3, nch - 1), n1);
-        mma(c0, acc0, masked);
-        if (kk + 1 < nch) mma(c1, acc1, masked);
+        fetch(min(kk + 4, nch - 1), n0);
+        fetch(min(kk + 6, nch - 1), n1);
+        u32x4 b0[2], b1[2];
+        bvals(c0, b0, masked);
+        if (kk + 2 < nch) {
+          bvals(c1, b1, masked);
+#pragma unroll
+          for (int step = 0; step < 2; ++step) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(c0.a[step]), as_h8(b0[step]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(c1.a[step]), as_h8(b1[step]), acc1, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int step = 0; step < 2; ++step)
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(c0.a[step]), as_h8(b0[step]), acc0, 0, 0, 0);
+        }
         c0 = n0;
         c1 = n1;
       }
@@ -316,23 +374,44 @@ k_unit_s1(S1Args A) {
       sweep(std::true_type());
   }
   __syncthreads();  // the round buffers are free
+  // the pair (w, w + 4) splits the tile's 16 registers: wave w finishes
+  // 0-7, wave w + 4 finishes 8-15, each adding parity 0's sum to parity 1's
+  const int r0 = 8 * par;
+  float v[8];
+  {
+    float *red = reinterpret_cast<float *>(smem);
+    float lo[8], hi[8];  // sums of registers 0-7 and 8-15 (constant indices: no scratch)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      lo[r] = acc0[r] + acc1[r];
+      hi[r] = acc0[8 + r] + acc1[8 + r];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)  // the partner's half
+      red[((par * 4 + tw) * 8 + r) * 64 + lane] = par == 0 ? hi[r] : lo[r];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float other = red[(((1 - par) * 4 + tw) * 8 + r) * 64 + lane];
+      v[r] = par == 0 ? lo[r] + other : other + hi[r];
+    }
+    __syncthreads();  // red is free again
+  }
 
   const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-  float v[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) v[r] = acc0[r] + acc1[r];
   if (A.nsplit > 1) {
-    // split z's partial: registers 4q..4q+3 of lane l of wave w as one
-    // 16-byte word at [(tile*nsplit + z)*1024 + (4 w + q)*64 + l] (float4 units)
+    // split z's partial: registers 4q..4q+3 of lane l of tile tw as one
+    // 16-byte word at [(tile*nsplit + z)*1024 + (4 tw + q)*64 + l] (float4
+    // units); wave (tw, par) holds q = 2 par, 2 par + 1
     const __amdgpu_buffer_rsrc_t rs =
         coherent_rsrc(A.part + (size_t)tile * A.nsplit * 4096, (uint32_t)A.nsplit * 16384u);
-    const int o0 = blockIdx.z * 16384 + ((w * 4) * 64 + lane) * 16;
+    const int l0 = ((tw * 4 + 2 * par) * 64 + lane) * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       u32x4 o;
       o.x = __float_as_uint(v[4 * q]); o.y = __float_as_uint(v[4 * q + 1]);
       o.z = __float_as_uint(v[4 * q + 2]); o.w = __float_as_uint(v[4 * q + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(o, rs, o0 + q * 1024, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, blockIdx.z * 16384 + l0 + q * 1024, 0, kCoherent);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -346,16 +425,15 @@ k_unit_s1(S1Args A) {
     // the last block of the tile sums the splits in split order; every load
     // is unconditional (splits past nsplit re-read the last one) so all of
     // them are in flight at once
-    u32x4 q[kMaxSplit][4];
-    const int l0 = ((w * 4) * 64 + lane) * 16;
+    u32x4 q[kMaxSplit][2];
 #pragma unroll
     for (int z = 0; z < kMaxSplit; ++z)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         q[z][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, min(z, A.nsplit - 1) * 16384 + l0 + j * 1024, 0,
                                                         kCoherent);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float sum = __uint_as_float(q[0][j][e]);
@@ -369,32 +447,44 @@ k_unit_s1(S1Args A) {
   // fp16 tile [16 c8][32 rows][8] in LDS, then one contiguous 8 KB copy into T
   uint16_t *tl = reinterpret_cast<uint16_t *>(smem);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * lh + (r & 3), col = w * 32 + lr;
-    tl[((col >> 3) * 32 + row) * 8 + (col & 7)] = mf2h(v[r]);
+  for (int r = 0; r < 8; ++r) {
+    const int rr = r0 + r;
+    const int row = 8 * (rr >> 2) + 4 * lh + (rr & 3), col = tw * 32 + lr;
+    tl[((col >> 3) * 32 + row) * 8 + (col & 7)] = mf2h(v[r] * lcol);
   }
   __syncthreads();
   uint4 *dst = reinterpret_cast<uint4 *>(A.T + ((size_t)blockIdx.y * (A.Lt >> 3) + blockIdx.x * 16) * 256);
   const uint4 *srcl = reinterpret_cast<const uint4 *>(smem);
   dst[threadIdx.x] = srcl[threadIdx.x];
-  dst[threadIdx.x + kThreads] = srcl[threadIdx.x + kThreads];
 }
 
 // ------------------------------------------------------------- stage 2
-// grid = (ceil(b / 64), ceil(M / 32)).  Block (jx, ty) computes outputs
-// [64 jx, 64 jx + 64) of rows [32 ty, 32 ty + 32) for every layer of the
-// unit, then their combine.  The waves interleave over a layer's
-// (path, 32-column) chunks, each wave accumulating 32 x 64 per path; the
-// four partials are summed in wave order through LDS.
+// grid = (ceil(b / (64 nb)), ceil(M / 32)).  Block (jx, ty) computes
+// outputs [64 nb jx, 64 nb (jx + 1)) of rows [32 ty, 32 ty + 32) for every
+// layer of the unit, then their combine.  T already carries l (the first
+// stage folds it in), so the B operand is the +-1 signs of S_U alone.
+// Wave w works on column pair cp = w % nb (64 outputs, two 32-column
+// tiles) and takes the layer's (path, 32-column) chunks of phase
+// w / nb (mod 4 / nb), accumulating 32 x 64 per path; the 4 / nb phase
+// partials of a pair are summed in phase order through LDS.
+// LDS round buffer of C chunks (C a multiple of 4): T rows
+// [chunk][c8 4][32 rows][8 fp16], then the sign words [pair][chunk][64 outputs].
+__host__ __device__ constexpr int s2_buf_bytes(int C, int nb) { return C * 2048 + nb * C * 256; }
+
+template <int NB>
 __global__ void __launch_bounds__(kThreads)
 k_unit_s2(S2Args A) {
   extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int t = threadIdx.x;
+  constexpr int nb = NB, nph = 4 / NB;
+  const int C = A.c2;
+  const int cp = w % nb, phase = w / nb;
   const int tb = blockIdx.y;
   const int64_t tok0 = (int64_t)tb * 32;
-  const int j0 = blockIdx.x * 64;
+  const int j0 = blockIdx.x * 64 * nb;
   const int Lt8 = A.Lt >> 3;
+  const int bufb = s2_buf_bytes(C, nb), wofs = C * 2048;
 
   // round r -> (layer m, first chunk ch0, chunk count nch); chunk ch of a
   // layer is path ch / Wk, 32-column block ch % Wk
@@ -403,10 +493,10 @@ k_unit_s2(S2Args A) {
     int rr = r;
     while (true) {
       const int nc = A.ly[m].P * A.ly[m].Wk;
-      const int nrm = (nc + kRC2 - 1) / kRC2;
+      const int nrm = (nc + C - 1) / C;
       if (rr < nrm) {
-        ch0 = rr * kRC2;
-        nch = min(kRC2, nc - ch0);
+        ch0 = rr * C;
+        nch = min(C, nc - ch0);
         return;
       }
       rr -= nrm;
@@ -417,44 +507,50 @@ k_unit_s2(S2Args A) {
     int m, ch0, nch;
     round_of(r, m, ch0, nch);
     const S2Layer &Ly = A.ly[m];
-    unsigned char *buf = smem + (r & 1) * kS2Buf;
+    unsigned char *buf = smem + (r & 1) * bufb;
     const uint16_t *tsrc = A.T + ((size_t)tb * Lt8 + (Ly.seg0[0] >> 3) + ch0 * 4) * 256;
-    for (int u = w; u < nch * 2; u += 4) dma16(tsrc + u * 512 + lane * 8, buf + u * 1024);
-    for (int v = w; v < (nch + 3) / 4; v += 4) {
+    // the blocks of a row tile all read the same T rows: each starts at its
+    // own place in the list so they do not queue on the same lines
+    const int nu = nch * 2, u0 = (blockIdx.x * 4) % nu;
+    for (int i = w; i < nu; i += 4) {
+      const int u = u0 + i < nu ? u0 + i : u0 + i - nu;
+      dma16(tsrc + u * 512 + lane * 8, buf + u * 1024);
+    }
+    // words: instruction (pair q, v) covers chunks 4 v .. 4 v + 3 of pair q
+    const int nv = (nch + 3) / 4;
+    for (int iv = w; iv < nb * nv; iv += 4) {
+      const int q = iv / nv, v = iv - q * nv;
       const int chl = 4 * v + (lane >> 4);
-      const int j = j0 + 4 * (lane & 15);
+      const int j = j0 + q * 64 + 4 * (lane & 15);
       const void *src = (chl < nch && j + 4 <= Ly.b16)
                             ? (const void *)(Ly.su2 + (size_t)(ch0 + chl) * Ly.b16 + j)
                             : A.zero;
-      dma16(src, buf + kS2T + v * 1024);
-    }
-    // l of the chunks: lane = 4 chunk + piece, 8 latent columns per piece
-    for (int v = w; v < (nch + 15) / 16; v += 4) {
-      const int chl = 16 * v + (lane >> 2);
-      const int ch = ch0 + chl;
-      const int p = ch >= Ly.Wk ? 1 : 0;
-      const int k = (ch - p * Ly.Wk) * 32 + 8 * (lane & 3);
-      const void *src = (chl < nch && k + 8 <= Ly.s8) ? (const void *)(Ly.l + (size_t)p * Ly.s8 + k) : A.zero;
-      dma16(src, buf + kS2T + kS2W + v * 1024);
+      dma16(src, buf + wofs + (q * C + 4 * v) * 256);
     }
   };
 
-  float ys[8];
+  // outputs of thread t: row t / 8, columns q * 64 + 8 (t % 8) .. + 7 of each pair q
+  float ys[NB][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ys[e] = 0.f;
-  const int row_o = t >> 3, c_o = 8 * (t & 7);  // this thread's 8 outputs per layer
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ys[q][e] = 0.f;
+  const int row_o = t >> 3, c_o = 8 * (t & 7);
   issue(0);
   int r = 0;
   for (int m = 0; m < A.nl; ++m) {
     const S2Layer &Ly = A.ly[m];
-    const int nc = Ly.P * Ly.Wk, nrm = (nc + kRC2 - 1) / kRC2;
+    const int nc = Ly.P * Ly.Wk, nrm = (nc + C - 1) / C;
+    // h of the wave's columns; the loads are unconditional (clamped index)
+    // so no wait for them lands before the round's copies are needed
     float hv[2][2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const int j = j0 + ni * 32 + lr;
-        hv[p][ni] = (p < Ly.P && j < A.b) ? mh2f(Ly.h[(size_t)p * Ly.b16 + j]) : 0.f;
+        const int j = j0 + cp * 64 + ni * 32 + lr;
+        const uint16_t hraw = Ly.h[(size_t)min(p, Ly.P - 1) * Ly.b16 + min(j, Ly.b16 - 1)];
+        hv[p][ni] = (p < Ly.P && j < A.b) ? mh2f(hraw) : 0.f;
       }
     float16_t acc0[2], acc1[2];
 #pragma unroll
@@ -465,18 +561,14 @@ k_unit_s2(S2Args A) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (r + 1 < A.nrounds) issue(r + 1);
-      const unsigned char *buf = smem + (r & 1) * kS2Buf;
-      const int ch0 = rm * kRC2, nch = min(kRC2, nc - ch0);
+      const unsigned char *buf = smem + (r & 1) * bufb;
+      const int ch0 = rm * C, nch = min(C, nc - ch0);
       const u32x4 *ts = reinterpret_cast<const u32x4 *>(buf);
-      const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + kS2T);
-      const u32x4 *lsd = reinterpret_cast<const u32x4 *>(buf + kS2T + kS2W);
-      struct Ops { u32x4 a[2], l[2]; uint32_t wd[2]; };
+      const uint32_t *wsd = reinterpret_cast<const uint32_t *>(buf + wofs) + cp * C * 64;
+      struct Ops { u32x4 a[2]; uint32_t wd[2]; };
       auto fetch = [&](int chl, Ops &o) {
 #pragma unroll
-        for (int step = 0; step < 2; ++step) {
-          o.a[step] = ts[(chl * 4 + 2 * step + lh) * 32 + lr];
-          o.l[step] = lsd[chl * 4 + 2 * step + lh];  // l of columns 32 q + 16 step + 8 lh ..
-        }
+        for (int step = 0; step < 2; ++step) o.a[step] = ts[(chl * 4 + 2 * step + lh) * 32 + lr];
         o.wd[0] = wsd[chl * 64 + lr];
         o.wd[1] = wsd[chl * 64 + 32 + lr];
       };
@@ -485,23 +577,21 @@ k_unit_s2(S2Args A) {
 #pragma unroll
         for (int step = 0; step < 2; ++step) {
           const half8_t av = as_h8(o.a[step]);
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              av, as_h8(flip_signs(o.l[step], wl0 << (8 * step))), acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              av, as_h8(flip_signs(o.l[step], wl1 << (8 * step))), acc[1], 0, 0, 0);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, as_h8(sign_ones(wl0 << (8 * step))), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, as_h8(sign_ones(wl1 << (8 * step))), acc[1], 0, 0, 0);
         }
       };
       // chunks are path-major: [0, nch0) are path 0, [nch0, nch) path 1;
-      // wave w takes the chunks chl = w (mod 4), path by path
+      // the wave takes the chunks chl = phase (mod nph), path by path
       const int nch0 = max(0, min(nch, Ly.Wk - ch0));
       auto run = [&](int lo, int hi, float16_t (&acc)[2]) {
-        int chl = lo + ((w - lo) % 4 + 4) % 4;
+        int chl = lo + ((phase - lo) % nph + nph) % nph;
         if (chl >= hi) return;
         Ops c;
         fetch(chl, c);
-        for (; chl < hi; chl += 4) {
+        for (; chl < hi; chl += nph) {
           Ops n;
-          fetch(min(chl + 4, hi - 1), n);  // unconditional: see stage 1
+          fetch(min(chl + nph, hi - 1), n);  // unconditional: see stage 1
           mma(c, acc);
           c = n;
         }
@@ -511,7 +601,7 @@ k_unit_s2(S2Args A) {
     }
     // layer epilogue: the layer's last round buffer becomes the reduction area
     __syncthreads();
-    float *red = reinterpret_cast<float *>(smem + ((r - 1) & 1) * kS2Buf);
+    float *red = reinterpret_cast<float *>(smem + ((r - 1) & 1) * bufb);
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -520,27 +610,35 @@ k_unit_s2(S2Args A) {
         red[(w * 32 + row) * kRP2 + col] = hv[0][ni] * acc0[ni][e] + hv[1][ni] * acc1[ni][e];
       }
     __syncthreads();
-    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int o = row_o * kRP2 + c_o + e;
-      v[e] = ((red[o] + red[32 * kRP2 + o]) + red[2 * 32 * kRP2 + o]) + red[3 * 32 * kRP2 + o];
-      v[e] = mh2f(mf2h(v[e]));  // the layer's fp16 output
-      ys[e] += v[e];
+    for (int q = 0; q < NB; ++q) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // phases of pair q are waves q, q + nb, ...: summed in phase order
+        const int o = (q * 32 + row_o) * kRP2 + c_o + e;
+        float sum = red[o];
+#pragma unroll
+        for (int ph = 1; ph < nph; ++ph) sum += red[o + ph * nb * 32 * kRP2];
+        v[e] = mh2f(mf2h(sum));  // the layer's fp16 output
+        ys[q][e] += v[e];
+      }
+      if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + q * 64 + c_o, v);
     }
-    if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + c_o, v);
   }
   if (A.direct || !A.xout || tok0 + row_o >= A.M) return;
-  float o[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = A.c_out * ys[e];
-  store8(A.xout, A.b, tok0 + row_o, j0 + c_o, o);
+  for (int q = 0; q < NB; ++q) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = A.c_out * ys[q][e];
+    store8(A.xout, A.b, tok0 + row_o, j0 + q * 64 + c_o, o);
+  }
 }
 
 // ------------------------------------------------------------------ host
 static inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
-static constexpr size_t kS1Lds = (size_t)2 * kS1Buf;
-static constexpr size_t kS2Lds = (size_t)2 * kS2Buf;
+static constexpr size_t kS1Lds = (size_t)s1_lds_bytes(kS1MaxC);
 
 MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
   if (n < 1 || n > kMaxUnitLayersM) return nullptr;
@@ -549,7 +647,7 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
   P->a = layers[0]->a;
   P->b = layers[0]->b;
   P->a16 = (int)layers[0]->a16;
-  int col = 0, nseg = 0, nr2 = 0;
+  int col = 0, nseg = 0;
   for (int m = 0; m < n; ++m) {
     const Layer &Ly = *layers[m];
     if (Ly.a != P->a || Ly.b != P->b) {
@@ -569,15 +667,14 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
       S.s = (int)Ly.s;
       S.seg0 = col;
       S.pad_ = 0;
+      S.l = Ly.l + (size_t)p * Ly.s8;
       D.seg0[p] = col;
       col += (int)round_up(Ly.s, 32);
     }
-    nr2 += (int)((Ly.P * Ly.Wk + kRC2 - 1) / kRC2);
   }
   P->nseg = nseg;
   P->ntile32 = col / 32;
   P->Lt = (int)round_up(col, 128);
-  P->nrounds2 = nr2;
   return P;
 }
 
@@ -585,15 +682,41 @@ void mfma_plan_free(MfmaPlan *p) { delete p; }
 
 static int64_t s1_tiles(const MfmaPlan &P, int64_t Mc) { return (int64_t)(P.Lt / 128) * ((Mc + 31) / 32); }
 
-static int s1_nsplit(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *kcps) {
+// Splits of the input dimension: at most one block per CU (at most
+// kMaxSplit splits), kcps chunks per split.  A split of at most kS1MaxC chunks is
+// one round (cround = kcps rounded up to even); a longer one runs in
+// double-buffered rounds of kS1RoundC chunks.
+static int s1_nsplit(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *kcps, int *cround) {
   const int64_t tiles = s1_tiles(P, Mc);
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int nkc = (int)((P.a + 31) / 32);
-  int ns = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, (cus + tiles - 1) / tiles));
+  // one 8-wave block per CU: as many splits as fill the CUs in one wave of blocks
+  int ns = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, cus / tiles));
   ns = std::min(ns, nkc);
   const int k = (nkc + ns - 1) / ns;
   *kcps = k;
+  *cround = k <= kS1MaxC ? (k + 1) & ~1 : kS1RoundC;
   return (nkc + k - 1) / k;
+}
+
+// Stage-2 block width: the widest (nb column pairs) that still gives about
+// 0.6 blocks per CU, so wide outputs do not re-read T from many blocks;
+// c2 = chunks per round, as many as two buffers allow.
+static void s2_shape(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *nb, int *c2) {
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  const int64_t rt = (Mc + 31) / 32;
+  int n = 4;
+  while (n > 1 && (P.b + 64 * n - 1) / (64 * n) * rt < cus * 6 / 10) n /= 2;
+  *nb = n;
+  // a multiple of 4: one word instruction covers 4 chunks of a pair, and
+  // must not spill into the next pair's words
+  *c2 = std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, n)) & ~3;
+  static_assert(kS2Lds / 2 / s2_buf_bytes(1, 4) >= kS2MinC, "rounds hold the wave partials");
+}
+
+static size_t s1_lds_launch(int kcps, int cround) {
+  const size_t one = (size_t)s1_lds_bytes(cround);
+  return std::max<size_t>(kcps > cround ? 2 * one : one, 16384);  // >= the epilogue's wave sums
 }
 
 size_t mfma_unit_ws_bytes(const MfmaPlan *p) {
@@ -610,9 +733,9 @@ static hipError_t set_lds_attr(int device) {
   if (bit && (done.load() & bit)) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void *)k_unit_s1,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS1Lds);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void *)k_unit_s2, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kS2Lds);
+  const void *s2k[3] = {(const void *)k_unit_s2<1>, (const void *)k_unit_s2<2>, (const void *)k_unit_s2<4>};
+  for (int i = 0; i < 3 && e == hipSuccess; ++i)
+    e = hipFuncSetAttribute(s2k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS2Lds);
   if (e == hipSuccess && bit) done.fetch_or(bit);
   return e;
 }
@@ -639,12 +762,13 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A1.a16 = p->a16;
     A1.Lt = p->Lt;
     A1.ntile32 = p->ntile32;
-    A1.nsplit = s1_nsplit(*p, Mc, dev, &A1.kcps);
+    A1.nsplit = s1_nsplit(*p, Mc, dev, &A1.kcps, &A1.cround);
     A1.nseg = p->nseg;
     A1.xvec = (p->a % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
     for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = p->seg[i];
     dim3 g1((unsigned)(p->Lt / 128), (unsigned)((Mc + 31) / 32), (unsigned)A1.nsplit);
-    hipLaunchKernelGGL(k_unit_s1, g1, dim3(kThreads), kS1Lds, st, A1);
+    const size_t lds1 = s1_lds_launch(A1.kcps, A1.cround);
+    hipLaunchKernelGGL(k_unit_s1, g1, dim3(kThreads1), lds1, st, A1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -658,13 +782,21 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A2.nl = p->nl;
     A2.direct = direct ? 1 : 0;
     A2.c_out = c_out;
-    A2.nrounds = p->nrounds2;
+    s2_shape(*p, Mc, dev, &A2.nb, &A2.c2);
+    A2.nrounds = 0;
+    for (int m = 0; m < p->nl; ++m) A2.nrounds += (p->ly[m].P * p->ly[m].Wk + A2.c2 - 1) / A2.c2;
     for (int m = 0; m < kMaxUnitLayersM; ++m) {
       A2.ly[m] = p->ly[m];
       A2.ly[m].y = (m < p->nl && y_layers && y_layers[m]) ? y_layers[m] + mb * p->b : nullptr;
     }
-    dim3 g2((unsigned)((p->b + 63) / 64), (unsigned)((Mc + 31) / 32));
-    hipLaunchKernelGGL(k_unit_s2, g2, dim3(kThreads), kS2Lds, st, A2);
+    dim3 g2((unsigned)((p->b + 64 * A2.nb - 1) / (64 * A2.nb)), (unsigned)((Mc + 31) / 32));
+    const size_t lds2 = (size_t)2 * s2_buf_bytes(A2.c2, A2.nb);
+    if (A2.nb == 4)
+      hipLaunchKernelGGL(k_unit_s2<4>, g2, dim3(kThreads), lds2, st, A2);
+    else if (A2.nb == 2)
+      hipLaunchKernelGGL(k_unit_s2<2>, g2, dim3(kThreads), lds2, st, A2);
+    else
+      hipLaunchKernelGGL(k_unit_s2<1>, g2, dim3(kThreads), lds2, st, A2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
