@@ -66,12 +66,24 @@ struct alignas(16) PLayer {
   int64_t trace_y;  // element offset of this layer's output in the trace
 };
 
+// One group of the second product's tables: 4 latent columns of one
+// layer and path, built by one exchange thread from the reduced latent
+// words tcol .. tcol + nval - 1 and their l (lp).
+struct alignas(16) PGroup {
+  const uint16_t *lp;
+  int tcol;
+  int nd;  // nval (0..4) | table offset in floats << 4
+};
+
 struct alignas(16) PUnit {
   int first, n;
   int a, b;
   int Lu;
   float c_out;      // kappa / sqrt(n): combine of this unit's outputs
   int64_t trace_x;  // element offset of this unit's input in the trace
+  const PGroup *grp;  // the unit's table groups, in table order
+  int ngrp;
+  int pad_;
 };
 
 // One block a workgroup copies into LDS for a phase: src + t0 * stride,
@@ -92,7 +104,8 @@ struct alignas(16) PSeg {
   int offp;  // LDS offset in the staging buffer: (offp & 0xffff) + nt * (offp >> 16)
 };
 
-static_assert(sizeof(PLayer) % 16 == 0 && sizeof(PUnit) % 16 == 0 && sizeof(PSeg) == 32,
+static_assert(sizeof(PLayer) % 16 == 0 && sizeof(PUnit) % 16 == 0 && sizeof(PSeg) == 32 &&
+                  sizeof(PGroup) == 16,
               "descriptors are copied to LDS in 16-byte units");
 
 struct PArgs {
@@ -118,6 +131,7 @@ struct PersistPlan {
   PUnit *d_units = nullptr;
   PLayer *d_layers = nullptr;
   PSeg *d_segs = nullptr;
+  PGroup *d_groups = nullptr;
   std::vector<PUnit> h_units;
   std::vector<PLayer> h_layers;
   uint64_t *xpart = nullptr, *xT = nullptr;
@@ -554,60 +568,34 @@ __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, un
 
 // The second product's tables of the next phase (unit B of this phase):
 // group g (4 latent columns of one layer and path) is built by exchange
-// thread g % 256 from the reduced latent words and l.  TabPlan holds a
-// thread's groups, read from the phase context before it is restaged.
+// thread g % 256 from the reduced latent words and l.  The groups are
+// listed on the host; a thread loads its own at the start of the phase, so
+// the loads are long done when the exchange needs them.
 constexpr int kGroupsPerThread = (kTab2Floats / 16 + kXThreads - 1) / kXThreads;
 struct TabPlan {
   int n;                                 // groups of this thread
   int tcol[kGroupsPerThread];            // latent column of the group's first word
-  int nval[kGroupsPerThread];            // valid columns (< s) of the group, 1..4
+  int nval[kGroupsPerThread];            // valid columns (< s) of the group, 0..4
   int dst[kGroupsPerThread];             // table offset in tab2 (floats)
   const uint16_t *lp[kGroupsPerThread];  // l of the group (global)
 };
 
-__device__ TabPlan plan_tables(const Lds &L) {
-  const PhaseCtx &C = *L.ctx;
-  const int na = C.has_a ? C.ua.n : 0, nb = C.ub.n;
-  const PLayer *LB = C.la + na;
-  int Pm[kMaxUnitLayers], Wkm[kMaxUnitLayers];
-#pragma unroll
-  for (int m = 0; m < kMaxUnitLayers; ++m) {
-    Pm[m] = LB[m].P;
-    Wkm[m] = LB[m].Wk;
-  }
-  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers], ng = 0;
-  {
-    int toff = 0;
-#pragma unroll
-    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
-      const int m = mp >> 1, p = mp & 1;
-      const bool live = m < nb && p < Pm[m];
-      tbase[mp] = toff;
-      tcnt[mp] = live ? Wkm[m] * 8 : 0;
-      toff += live ? Wkm[m] * 8 * 16 : 0;
-      ng += tcnt[mp];
-    }
-  }
+__device__ TabPlan load_tables(const Lds &L, bool live) {
+  const PUnit &UB = L.ctx->ub;
+  const PGroup *gp = UB.grp;
+  const int ng = live ? UB.ngrp : 0;
   TabPlan T;
   T.n = 0;
 #pragma unroll
   for (int i = 0; i < kGroupsPerThread; ++i) {
-    T.tcol[i] = 0; T.nval[i] = 0; T.dst[i] = 0; T.lp[i] = nullptr;
     const int g = (int)threadIdx.x + i * kXThreads;
-    if ((int)threadIdx.x < kXThreads && g < ng) {
-      int rem = g, mp = 0;
-#pragma unroll
-      for (int k = 0; k < 2 * kMaxUnitLayers; ++k)
-        if (mp == k && rem >= tcnt[k]) { rem -= tcnt[k]; ++mp; }
-      const int m = mp >> 1, p = mp & 1;
-      const PLayer &Ly = LB[m];
-      const int s = Ly.s;
-      T.tcol[i] = Ly.col0 + p * s + 4 * rem;
-      T.nval[i] = min(4, s - 4 * rem);
-      T.dst[i] = pick(tbase, mp) + rem * 16;
-      T.lp[i] = Ly.l + (size_t)p * Ly.s8 + 4 * rem;
-      T.n = i + 1;
-    }
+    const bool v = (int)threadIdx.x < kXThreads && g < ng;
+    const uint4 raw = v ? *reinterpret_cast<const uint4 *>(gp + g) : make_uint4(0u, 0u, 0u, 0u);
+    T.lp[i] = reinterpret_cast<const uint16_t *>((uint64_t)raw.x | ((uint64_t)raw.y << 32));
+    T.tcol[i] = (int)raw.z;
+    T.nval[i] = (int)(raw.w & 15u);
+    T.dst[i] = (int)(raw.w >> 4);
+    if (v) T.n = i + 1;
   }
   return T;
 }
@@ -703,7 +691,7 @@ k_persist(PArgs A) {
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
     // this thread's share of the next phase's tables (built in the
     // exchange), planned now so the reads overlap the products
-    const TabPlan tp = plan_tables(L);
+    const TabPlan tp = load_tables(L, ph < U);
     if (ph == 0) {
       const PUnit &U0 = L.ctx->ub;
       for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
@@ -785,6 +773,32 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     if (U.Lu > kLuMax) return unsupported();
     P->h_units.push_back(U);
   }
+  // table groups of every unit, in the order the tables are laid out
+  // (layer-major, path, 4-column group)
+  std::vector<PGroup> groups;
+  std::vector<size_t> gfirst;
+  for (int u = 0; u < P->nunits; ++u) {
+    PUnit &U = P->h_units[u];
+    gfirst.push_back(groups.size());
+    int toff = 0;
+    for (int m = 0; m < U.n; ++m) {
+      const PLayer &D = P->h_layers[U.first + m];
+      for (int p = 0; p < D.P; ++p) {
+        for (int rem = 0; rem < D.Wk * 8; ++rem) {
+          const int nval = std::max(0, std::min(4, D.s - 4 * rem));
+          PGroup g{};
+          // a group past s reads nothing; its l pointer is the (valid) base
+          g.lp = nval > 0 ? D.l + (size_t)p * D.s8 + 4 * rem : D.l;
+          g.tcol = D.col0 + p * D.s + 4 * rem;
+          g.nd = nval | ((toff + rem * 16) << 4);
+          groups.push_back(g);
+        }
+        toff += D.Wk * 8 * 16;
+      }
+    }
+    U.ngrp = (int)(groups.size() - gfirst.back());
+    if (toff > kTab2Floats) return unsupported();
+  }
   for (int u = 1; u < P->nunits; ++u)
     if (P->h_units[u].a != P->h_units[u - 1].b ||
         P->h_units[u].first != P->h_units[u - 1].first + P->h_units[u - 1].n) {
@@ -817,7 +831,11 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   }
   P->lds = lds_bytes();
   if (P->lds > (size_t)prop.sharedMemPerBlock) return unsupported();
-  bool ok = hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
+  bool ok = hipMalloc(&P->d_groups, sizeof(PGroup) * std::max<size_t>(1, groups.size())) == hipSuccess &&
+            hipMemcpy(P->d_groups, groups.data(), sizeof(PGroup) * groups.size(),
+                      hipMemcpyHostToDevice) == hipSuccess;
+  for (int u = 0; u < P->nunits && ok; ++u) P->h_units[u].grp = P->d_groups + gfirst[u];
+  ok = ok && hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
             hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
             hipMalloc(&P->xpart, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess &&
             hipMalloc(&P->xT, sizeof(uint64_t) * kLuMax) == hipSuccess &&
@@ -895,6 +913,7 @@ void persist_free(PersistPlan *p) {
   if (p->d_units) (void)hipFree(p->d_units);
   if (p->d_layers) (void)hipFree(p->d_layers);
   if (p->d_segs) (void)hipFree(p->d_segs);
+  if (p->d_groups) (void)hipFree(p->d_groups);
   if (p->xpart) (void)hipFree(p->xpart);
   if (p->xT) (void)hipFree(p->xT);
   if (p->err) (void)hipFree(p->err);
