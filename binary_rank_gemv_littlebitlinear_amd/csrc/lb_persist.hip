@@ -63,6 +63,7 @@ struct alignas(16) PLayer {
   const uint16_t *sv16, *ht, *gt, *l;
   int a, b, s, P, L, Lp, Wk, a16, b16, s8;
   int col0;         // first latent column within the unit
+  int tb2;          // offset (floats) of the layer's path-0 second-product tables; path p at + p Wk 128
   int64_t trace_y;  // element offset of this layer's output in the trace
 };
 
@@ -290,15 +291,6 @@ __device__ void stage_phase(const PArgs &A, int ph, Lds &L) {
          reinterpret_cast<unsigned char *>(L.segbuf + ((ph + 1) & 1) * kMaxSeg), kMaxSeg * 32);
 }
 
-// a[i] for a runtime i without a dynamically indexed (scratch) array.
-template <int N>
-__device__ __forceinline__ int pick(const int (&a)[N], int i) {
-  int v = 0;
-#pragma unroll
-  for (int k = 0; k < N; ++k) v = k == i ? a[k] : v;
-  return v;
-}
-
 // Entries lo + 4*hi (lo = 0..3) of the table over (v0, v1, v2, v3), entry
 // e = sum_j (bit j of e ? v_j : -v_j), summed as ((+-v0 +- v1) + (+-v2 +- v3)).
 __device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float v2, float v3,
@@ -326,41 +318,35 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   const PUnit &U = C.ua;
   const int na = U.n, ub = U.b;
   const int t0 = C.t0, nt = C.t1 - C.t0, rows = 16 * nt;
-  int Pm[kMaxUnitLayers], Wkm[kMaxUnitLayers];
+  int Pm[kMaxUnitLayers];
 #pragma unroll
-  for (int m = 0; m < kMaxUnitLayers; ++m) {
-    Pm[m] = C.la[m].P;
-    Wkm[m] = C.la[m].Wk;
-  }
-  // table bases per (layer, path): a group is 4 latent columns and its
-  // table has 16 entries; the tables were built by the previous exchange
-  int tbase[2 * kMaxUnitLayers];
-  {
-    int toff = 0;
-#pragma unroll
-    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
-      const int m = mp >> 1, p = mp & 1;
-      const bool live = m < na && p < Pm[m];
-      tbase[mp] = toff;
-      toff += live ? Wkm[m] * 8 * 16 : 0;
-    }
-  }
-  // lookups: task = (layer, path, row); lpt lanes of a task split the words
+  for (int m = 0; m < kMaxUnitLayers; ++m) Pm[m] = C.la[m].P;
+  // lookups: task = (layer, path, row) over every layer and both path
+  // slots; lpt lanes of a task split its words.  The task's pair index is
+  // (task / 16) / nt, by a 64-bit multiply with a per-phase constant.  The
+  // layer's fields come from indexed LDS reads; its tables (a group is 4
+  // latent columns with a 16-entry table) were built by the previous exchange.
   if (rows > 0) {
     const int ntk = na * 2 * rows;
-    int lpt = 1;
-    while (lpt < 64 && ntk * lpt * 2 <= kThreads) lpt *= 2;
+    int lpt = 1, lg = 0;
+    while (lpt < 64 && ntk * lpt * 2 <= kThreads) {
+      lpt *= 2;
+      ++lg;
+    }
+    // ceil(2^32 / nt) needs 33 bits for nt = 1: the product is taken in 64 bits
+    const uint64_t magic = (0x100000000ull + (unsigned)nt - 1) / (unsigned)nt;
     const int sub = threadIdx.x & (lpt - 1);
-    for (int tk0 = 0; tk0 < ntk; tk0 += kThreads / lpt) {
-      const int tk = tk0 + (int)threadIdx.x / lpt;
-      const int r = tk % rows, mp = tk / rows, m = mp >> 1, p = mp & 1;
+    for (int tk0 = 0; tk0 < ntk; tk0 += kThreads >> lg) {
+      const int tk = tk0 + ((int)threadIdx.x >> lg);
+      const int mp = (int)(((uint64_t)((unsigned)tk >> 4) * magic) >> 32), r = tk - mp * rows;
+      const int m = tk < ntk ? mp >> 1 : 0, p = mp & 1;
+      const PLayer &Ly = C.la[m];
+      const int P = Ly.P, Wk = Ly.Wk, s2o = C.s2_off[m];
+      const float *tb = L.tab2 + Ly.tb2 + p * Wk * 128;
       float acc = 0.f;
-      const int mc = tk < ntk ? m : 0;
-      const int P = pick(Pm, mc), Wk = pick(Wkm, mc), s2o = C.s2_off[mc];
       if (tk < ntk && p < P) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
                              ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
-        const float *tb = L.tab2 + pick(tbase, mp);
         // four words in flight per step
         for (int q = sub; q < Wk; q += 4 * lpt) {
           uint32_t wd[4];
@@ -435,70 +421,51 @@ __device__ void first_product(Lds &L) {
     __syncthreads();
     return;
   }
-  int Pm[kMaxUnitLayers], col0m[kMaxUnitLayers];
-#pragma unroll
-  for (int m = 0; m < kMaxUnitLayers; ++m) {
-    Pm[m] = LB[m].P;
-    col0m[m] = LB[m].col0;
-  }
-  int tbase[2 * kMaxUnitLayers], tcnt[2 * kMaxUnitLayers];
-  int ntask = 0;
+  // every layer of a unit has the same path count Pu; pair j = m Pu + p
+  // (layer m, path p) has its tables at tab1 + j * quads * 16
+  const int Pu = LB[0].P;
+  // tables from z = g * x: thread t builds the table of quad t % 32 of pair t / 32
   {
-    int toff = 0;
+    const int j = (int)threadIdx.x >> 5, qd = (int)threadIdx.x & 31;
+    const int m = Pu == 2 ? j >> 1 : j, p = j - m * Pu;
+    if (m < nb && qd < quads) {
+      const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + C.g_off[m]);
+      float v[4];
 #pragma unroll
-    for (int mp = 0; mp < 2 * kMaxUnitLayers; ++mp) {
-      const int m = mp >> 1, p = mp & 1;
-      const bool live = m < nb && p < Pm[m];
-      tbase[mp] = toff;
-      tcnt[mp] = live ? quads : 0;
-      toff += live ? quads * 16 : 0;
-      ntask += tcnt[mp];
+      for (int k = 0; k < 4; ++k) {
+        const int r = 4 * qd + k;
+        v[k] = h2f(gv[((r >> 4) * Pu + p) * 16 + (r & 15)]) * L.xs[r];
+      }
+      float *tab = L.tab1 + (j * quads + qd) * 16;
+#pragma unroll
+      for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
     }
   }
-  // tables from z = g * x: one thread builds the whole table of a quad of rows
-  for (int task = threadIdx.x; task < ntask; task += kThreads) {
-    int rem = task, mp = 0;
+  int col0m[kMaxUnitLayers];
 #pragma unroll
-    for (int i = 0; i < 2 * kMaxUnitLayers; ++i)
-      if (mp == i && rem >= tcnt[i]) { rem -= tcnt[i]; ++mp; }
-    const int m = mp >> 1, p = mp & 1;
-    const int P = pick(Pm, m), goff = C.g_off[m];
-    const int qd = rem;
-    const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + goff);
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * qd + j;
-      v[j] = h2f(gv[((r >> 4) * P + p) * 16 + (r & 15)]) * L.xs[r];
-    }
-    float *tab = L.tab1 + pick(tbase, mp) + qd * 16;
-#pragma unroll
-    for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
-  }
-  int s1o[kMaxUnitLayers], sm[kMaxUnitLayers], Lpm[kMaxUnitLayers];
-#pragma unroll
-  for (int m = 0; m < kMaxUnitLayers; ++m) {
-    s1o[m] = C.s1_off[m];
-    sm[m] = LB[m].s;
-    Lpm[m] = LB[m].Lp;
-  }
+  for (int m = 0; m < kMaxUnitLayers; ++m) col0m[m] = LB[m].col0;
   __syncthreads();
-  int lpt = 1;
-  while (lpt < 64 && lpt < nt && Lu * lpt * 2 <= kThreads) lpt *= 2;
+  // lookups: column c of the unit; lpt lanes split its nt words
+  int lpt = 1, lg = 0;
+  while (lpt < 64 && lpt < nt && Lu * lpt * 2 <= kThreads) {
+    lpt *= 2;
+    ++lg;
+  }
   const int sub = threadIdx.x & (lpt - 1);
-  for (int c0 = 0; c0 < Lu; c0 += kThreads / lpt) {
-    const int c = c0 + (int)threadIdx.x / lpt;
+  for (int c0 = 0; c0 < Lu; c0 += kThreads >> lg) {
+    const int c = c0 + ((int)threadIdx.x >> lg);
     float acc = 0.f;
     if (c < Lu) {
       int m = 0;
 #pragma unroll
       for (int i = 1; i < kMaxUnitLayers; ++i)
         if (i < nb && col0m[i] <= c) m = i;
-      const int cl = c - pick(col0m, m);
-      const int p = cl < pick(sm, m) ? 0 : 1;
-      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + pick(s1o, m)) + cl;
-      const float *tb = L.tab1 + pick(tbase, m * 2 + p);
-      const int Lp = pick(Lpm, m);
+      // the layer's fields by an indexed LDS read (no select chains)
+      const PLayer &Ly = LB[m];
+      const int cl = c - Ly.col0, s = Ly.s, Lp = Ly.Lp, s1o = C.s1_off[m];
+      const int p = cl < s ? 0 : 1;
+      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + s1o) + cl;
+      const float *tb = L.tab1 + (m * Pu + p) * quads * 16;
       uint32_t wds[kTMax];
 #pragma unroll
       for (int i = 0; i < kTMax; ++i) {
@@ -771,6 +738,8 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     }
     U.Lu = col;
     if (U.Lu > kLuMax) return unsupported();
+    for (int m = 1; m < U.n; ++m)  // the products assume one path count per unit
+      if (layers[U.first + m]->ly.P != L0.P) return unsupported();
     P->h_units.push_back(U);
   }
   // table groups of every unit, in the order the tables are laid out
@@ -782,7 +751,8 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     gfirst.push_back(groups.size());
     int toff = 0;
     for (int m = 0; m < U.n; ++m) {
-      const PLayer &D = P->h_layers[U.first + m];
+      PLayer &D = P->h_layers[U.first + m];
+      D.tb2 = toff;
       for (int p = 0; p < D.P; ++p) {
         for (int rem = 0; rem < D.Wk * 8; ++rem) {
           const int nval = std::max(0, std::min(4, D.s - 4 * rem));
