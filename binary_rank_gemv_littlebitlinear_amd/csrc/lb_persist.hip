@@ -57,6 +57,7 @@ constexpr int kStgBytes = 56 * 1024;
 constexpr int kTab2Floats = 10240;
 constexpr int kTab1Floats = 4096;
 constexpr long kSpin = 4000000;  // polls before a wait gives up
+constexpr int kXCopies = 8;      // copies of the reduced vector; workgroup w polls copy w % 8
 
 struct alignas(16) PLayer {
   const uint32_t *su2t;
@@ -118,7 +119,7 @@ struct PArgs {
   uint16_t *trace;  // may be null
   unsigned gen_base;
   uint64_t *xpart;  // [G][kLuMax] tagged partials (value bits | generation << 32)
-  uint64_t *xT;     // [kLuMax] tagged reduced latent
+  uint64_t *xT;     // [kXCopies][kLuMax] tagged reduced latent (copies of one vector)
   unsigned *err;
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
   const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
@@ -601,16 +602,19 @@ __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A, const Tab
       if (t < st) L.red[t] += L.red[t + st];
       __syncthreads();
     }
-    if (t < 8) st_tag(&A.xT[8 * r + t], L.red[t], gen);
+    // every copy gets the 8 sums (one 64-byte line per copy), so each line
+    // is polled by G / kXCopies workgroups rather than all of them
+    if (t < 8 * kXCopies) st_tag(&A.xT[(size_t)(t >> 3) * kLuMax + 8 * r + (t & 7)], L.red[t & 7], gen);
   }
   // all-gather, straight into the next phase's tables: w = l * t per group
+  uint64_t *xTw = A.xT + (size_t)(w % kXCopies) * kLuMax;
   if (xw) {
 #pragma unroll
     for (int i = 0; i < kGroupsPerThread; ++i) {
       if (i >= tp.n) break;
       const uint2 lraw = *reinterpret_cast<const uint2 *>(tp.lp[i]);  // 4 fp16 l
       float tv[kXLoads];
-      ok = ok && spin_tagged([&](int k) { return &A.xT[tp.tcol[i] + (k & 3)]; },
+      ok = ok && spin_tagged([&](int k) { return &xTw[tp.tcol[i] + (k & 3)]; },
                              [&](int k) { return k < tp.nval[i]; }, gen, A.err, tv);
       const float w0 = tp.nval[i] > 0 ? h2f((uint16_t)(lraw.x & 0xffffu)) * tv[0] : 0.f;
       const float w1 = tp.nval[i] > 1 ? h2f((uint16_t)(lraw.x >> 16)) * tv[1] : 0.f;
@@ -808,7 +812,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   ok = ok && hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
             hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
             hipMalloc(&P->xpart, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess &&
-            hipMalloc(&P->xT, sizeof(uint64_t) * kLuMax) == hipSuccess &&
+            hipMalloc(&P->xT, sizeof(uint64_t) * kXCopies * kLuMax) == hipSuccess &&
             hipMalloc(&P->err, sizeof(unsigned) * 64) == hipSuccess;
   ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits,
                        hipMemcpyHostToDevice) == hipSuccess;
@@ -864,7 +868,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
                  hipSuccess;
   ok = ok && hipMemset(P->err, 0, sizeof(unsigned) * 64) == hipSuccess;
   ok = ok && hipMemset(P->xpart, 0, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess;
-  ok = ok && hipMemset(P->xT, 0, sizeof(uint64_t) * kLuMax) == hipSuccess;
+  ok = ok && hipMemset(P->xT, 0, sizeof(uint64_t) * kXCopies * kLuMax) == hipSuccess;
   ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)P->lds) == hipSuccess;
   int occ = 0;
@@ -897,7 +901,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
     // a previous launch gave up a wait: clear the error word and every tag
     if (hipMemset(p->err, 0, sizeof(unsigned) * 64) != hipSuccess ||
         hipMemset(p->xpart, 0, sizeof(uint64_t) * (size_t)p->G * kLuMax) != hipSuccess ||
-        hipMemset(p->xT, 0, sizeof(uint64_t) * kLuMax) != hipSuccess)
+        hipMemset(p->xT, 0, sizeof(uint64_t) * kXCopies * kLuMax) != hipSuccess)
       return LB_EHIP;
     p->gen = 0;
     p->broken = false;
