@@ -75,6 +75,8 @@ constexpr int kS2MinC = 18;            // the wave partials fit one round buffer
 constexpr int kS2Lds = 160 * 1024;
 constexpr int kRP2 = 64 + 4;           // LDS pitch (floats) of a wave's 32 x 64 partial
 static_assert(4 * 32 * kRP2 * 4 <= kS2MinC * 2048, "the reduction buffer fits one round buffer");
+// with 8 waves (nb = 2 or 4) the partials need 8 * 32 rows: they fit the
+// round buffer of the chunk counts s2_shape picks for those widths
 
 struct S1Seg {
   const uint32_t *bits;  // sv1m + p*s: word (row group r, column k) at bits[r * pitch + k]
@@ -463,21 +465,22 @@ k_unit_s1(S1Args A) {
 // outputs [64 nb jx, 64 nb (jx + 1)) of rows [32 ty, 32 ty + 32) for every
 // layer of the unit, then their combine.  T already carries l (the first
 // stage folds it in), so the B operand is the +-1 signs of S_U alone.
-// Wave w works on column pair cp = w % nb (64 outputs, two 32-column
-// tiles) and takes the layer's (path, 32-column) chunks of phase
-// w / nb (mod 4 / nb), accumulating 32 x 64 per path; the 4 / nb phase
-// partials of a pair are summed in phase order through LDS.
+// NW waves (4 or 8): wave w works on column pair cp = w % nb (64 outputs,
+// two 32-column tiles) and takes the layer's (path, 32-column) chunks of
+// phase w / nb (mod NW / nb), accumulating 32 x 64 per path; the phase
+// partials of a pair are summed in phase order through LDS.  With 8 waves
+// two share each SIMD, so one's sign expansion overlaps the other's MFMAs.
 // LDS round buffer of C chunks (C a multiple of 4): T rows
 // [chunk][c8 4][32 rows][8 fp16], then the sign words [pair][chunk][64 outputs].
 __host__ __device__ constexpr int s2_buf_bytes(int C, int nb) { return C * 2048 + nb * C * 256; }
 
-template <int NB>
-__global__ void __launch_bounds__(kThreads)
+template <int NB, int NW>
+__global__ void __launch_bounds__(NW * 64)
 k_unit_s2(S2Args A) {
   extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int t = threadIdx.x;
-  constexpr int nb = NB, nph = 4 / NB;
+  constexpr int nb = NB, nph = NW / NB;
   const int C = A.c2;
   const int cp = w % nb, phase = w / nb;
   const int tb = blockIdx.y;
@@ -512,13 +515,13 @@ k_unit_s2(S2Args A) {
     // the blocks of a row tile all read the same T rows: each starts at its
     // own place in the list so they do not queue on the same lines
     const int nu = nch * 2, u0 = (blockIdx.x * 4) % nu;
-    for (int i = w; i < nu; i += 4) {
+    for (int i = w; i < nu; i += NW) {
       const int u = u0 + i < nu ? u0 + i : u0 + i - nu;
       dma16(tsrc + u * 512 + lane * 8, buf + u * 1024);
     }
     // words: instruction (pair q, v) covers chunks 4 v .. 4 v + 3 of pair q
     const int nv = (nch + 3) / 4;
-    for (int iv = w; iv < nb * nv; iv += 4) {
+    for (int iv = w; iv < nb * nv; iv += NW) {
       const int q = iv / nv, v = iv - q * nv;
       const int chl = 4 * v + (lane >> 4);
       const int j = j0 + q * 64 + 4 * (lane & 15);
@@ -612,6 +615,7 @@ k_unit_s2(S2Args A) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
+      if (t >= 256) break;  // threads 0-255 own the outputs
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -626,7 +630,7 @@ k_unit_s2(S2Args A) {
       if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + q * 64 + c_o, v);
     }
   }
-  if (A.direct || !A.xout || tok0 + row_o >= A.M) return;
+  if (t >= 256 || A.direct || !A.xout || tok0 + row_o >= A.M) return;
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     float o[8];
@@ -712,6 +716,9 @@ static void s2_shape(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *
   // must not spill into the next pair's words
   *c2 = std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, n)) & ~3;
   static_assert(kS2Lds / 2 / s2_buf_bytes(1, 4) >= kS2MinC, "rounds hold the wave partials");
+  static_assert(8 * 32 * kRP2 * 4 <= s2_buf_bytes((kS2Lds / 2 / s2_buf_bytes(1, 4)) & ~3, 4) &&
+                    8 * 32 * kRP2 * 4 <= s2_buf_bytes(std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, 2)) & ~3, 2),
+                "8-wave partials fit the round buffer");
 }
 
 static size_t s1_lds_launch(int kcps, int cround) {
@@ -733,7 +740,8 @@ static hipError_t set_lds_attr(int device) {
   if (bit && (done.load() & bit)) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void *)k_unit_s1,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS1Lds);
-  const void *s2k[3] = {(const void *)k_unit_s2<1>, (const void *)k_unit_s2<2>, (const void *)k_unit_s2<4>};
+  const void *s2k[3] = {(const void *)k_unit_s2<1, 4>, (const void *)k_unit_s2<2, 8>,
+                        (const void *)k_unit_s2<4, 8>};
   for (int i = 0; i < 3 && e == hipSuccess; ++i)
     e = hipFuncSetAttribute(s2k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS2Lds);
   if (e == hipSuccess && bit) done.fetch_or(bit);
@@ -792,11 +800,11 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     dim3 g2((unsigned)((p->b + 64 * A2.nb - 1) / (64 * A2.nb)), (unsigned)((Mc + 31) / 32));
     const size_t lds2 = (size_t)2 * s2_buf_bytes(A2.c2, A2.nb);
     if (A2.nb == 4)
-      hipLaunchKernelGGL(k_unit_s2<4>, g2, dim3(kThreads), lds2, st, A2);
+      hipLaunchKernelGGL((k_unit_s2<4, 8>), g2, dim3(512), lds2, st, A2);
     else if (A2.nb == 2)
-      hipLaunchKernelGGL(k_unit_s2<2>, g2, dim3(kThreads), lds2, st, A2);
+      hipLaunchKernelGGL((k_unit_s2<2, 8>), g2, dim3(512), lds2, st, A2);
     else
-      hipLaunchKernelGGL(k_unit_s2<1>, g2, dim3(kThreads), lds2, st, A2);
+      hipLaunchKernelGGL((k_unit_s2<1, 4>), g2, dim3(kThreads), lds2, st, A2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
