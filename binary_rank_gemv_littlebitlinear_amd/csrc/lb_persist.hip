@@ -348,22 +348,21 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       if (tk < ntk && p < P) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
                              ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
-        // four words in flight per step
+        // four words per step; every read is unconditional (index clamped,
+        // result masked), so the step's reads are all in flight at once
+        // instead of waiting word by word behind branches
         for (int q = sub; q < Wk; q += 4 * lpt) {
           uint32_t wd[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int qi = q + i * lpt;
-            wd[i] = qi < Wk ? wb[qi * 16] : 0u;
-          }
+          for (int i = 0; i < 4; ++i) wd[i] = wb[min(q + i * lpt, Wk - 1) * 16];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int qi = q + i * lpt;
-            if (qi < Wk) {
-              const float *tq = tb + qi * 128;
+            const float *tq = tb + min(qi, Wk - 1) * 128;
+            float e = 0.f;
 #pragma unroll
-              for (int n = 0; n < 8; ++n) acc += tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
-            }
+            for (int n = 0; n < 8; ++n) e += tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
+            acc += qi < Wk ? e : 0.f;
           }
         }
       }
@@ -467,19 +466,19 @@ __device__ void first_product(Lds &L) {
       const int p = cl < s ? 0 : 1;
       const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + s1o) + cl;
       const float *tb = L.tab1 + (m * Pu + p) * quads * 16;
-      uint32_t wds[kTMax];
+      // the lane's words gi = sub, sub + lpt, ... < nt, four per step; every
+      // read is unconditional (index clamped, result masked)
+      for (int g0 = sub; g0 < nt; g0 += 4 * lpt) {
+        uint32_t wds[4];
 #pragma unroll
-      for (int i = 0; i < kTMax; ++i) {
-        const int gi = sub + i * lpt;
-        wds[i] = gi < nt ? bits[gi * Lp] : 0u;
-      }
+        for (int i = 0; i < 4; ++i) wds[i] = bits[min(g0 + i * lpt, nt - 1) * Lp];
 #pragma unroll
-      for (int i = 0; i < kTMax; ++i) {
-        const int gi = sub + i * lpt;
-        if (gi < nt) {
-          const float *tq = tb + gi * 64;
-#pragma unroll
-          for (int n = 0; n < 4; ++n) acc += tq[n * 16 + ((wds[i] >> (4 * n)) & 15u)];
+        for (int i = 0; i < 4; ++i) {
+          const int gi = g0 + i * lpt;
+          const float *tq = tb + min(gi, nt - 1) * 64;
+          const float e = (tq[wds[i] & 15u] + tq[16 + ((wds[i] >> 4) & 15u)]) +
+                          (tq[32 + ((wds[i] >> 8) & 15u)] + tq[48 + ((wds[i] >> 12) & 15u)]);
+          acc += gi < nt ? e : 0.f;
         }
       }
     }
