@@ -123,6 +123,7 @@ struct PArgs {
   unsigned *err;
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
   const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
+  const PGroup *grp0;  // the first table group (a valid address for idle loads)
 };
 
 struct PersistPlan {
@@ -547,17 +548,25 @@ struct TabPlan {
   const uint16_t *lp[kGroupsPerThread];  // l of the group (global)
 };
 
-__device__ TabPlan load_tables(const Lds &L, bool live) {
+__device__ TabPlan load_tables(const PArgs &A, const Lds &L, bool live) {
   const PUnit &UB = L.ctx->ub;
-  const PGroup *gp = UB.grp;
+  // every load is unconditional (index clamped into a valid list), so the
+  // three are in flight together and nothing waits for them before the
+  // exchange uses them
+  const PGroup *gp = live ? UB.grp : A.grp0;
   const int ng = live ? UB.ngrp : 0;
+  const int gmax = (live ? ng : 1) - 1;
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) u4v *global_u4;
+  const global_u4 gg = (global_u4)(uintptr_t)gp;  // a device-memory list: global, not flat, loads
   TabPlan T;
   T.n = 0;
 #pragma unroll
   for (int i = 0; i < kGroupsPerThread; ++i) {
     const int g = (int)threadIdx.x + i * kXThreads;
     const bool v = (int)threadIdx.x < kXThreads && g < ng;
-    const uint4 raw = v ? *reinterpret_cast<const uint4 *>(gp + g) : make_uint4(0u, 0u, 0u, 0u);
+    const u4v rv = gg[min(g, gmax)];
+    const uint4 raw = v ? make_uint4(rv.x, rv.y, rv.z, rv.w) : make_uint4(0u, 0u, 0u, 0u);
     T.lp[i] = reinterpret_cast<const uint16_t *>((uint64_t)raw.x | ((uint64_t)raw.y << 32));
     T.tcol[i] = (int)raw.z;
     T.nval[i] = (int)(raw.w & 15u);
@@ -661,7 +670,7 @@ k_persist(PArgs A) {
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
     // this thread's share of the next phase's tables (built in the
     // exchange), planned now so the reads overlap the products
-    const TabPlan tp = load_tables(L, ph < U);
+    const TabPlan tp = load_tables(A, L, ph < U);
     if (ph == 0) {
       const PUnit &U0 = L.ctx->ub;
       for (int r = threadIdx.x; r < 16 * (t1 - t0); r += kThreads) {
@@ -918,6 +927,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.err = p->err;
   A.timeline = p->timeline;
   A.segs = p->d_segs;
+  A.grp0 = p->d_groups;
   hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
