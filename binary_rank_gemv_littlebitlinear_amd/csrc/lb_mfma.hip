@@ -5,17 +5,18 @@
 // is a group of layers that read the same input (one layer for a plain
 // forward; q/k/v or gate/up in a stack).  Per unit:
 //
-//   stage 1: T[M x Lt] = x[M x a] . B1[a x Lt],  B1[i][col(m,p,k)] = S_V,mp[i,k] * g_mp[i]
+//   stage 1: T[M x Lt] = fp16( (x[M x a] . B1[a x Lt]) * l ),
+//            B1[i][col(m,p,k)] = S_V,mp[i,k] * g_mp[i], l = l_mp[k] of the column
 //   stage 2: y_m[M x b] = fp16( sum_p h_mp * ( T_mp[M x s] . B2_mp[s x b] ) ),
-//            B2_mp[k][j] = S_U,mp[j,k] * l_mp[k]
+//            B2_mp[k][j] = S_U,mp[j,k]  (+-1)
 //            and, in a stack, x_next = fp16(c_out * sum_m y_m) in the same
 //            epilogue.
 //
-// +-g and +-l are exact in fp16 (a sign flip of the stored scale), so the
-// only rounding of an operand is T -> fp16, once.  Accumulation is fp32.
-// The sign bits are expanded in registers right before the MFMA that uses
-// them: a lane's 8 operand values are 8 stored scales with the fp16 sign
-// bit flipped where the sign is -1.
+// +-g and +-1 are exact in fp16 (a sign flip of the stored scale, or of
+// 1.0), so the only rounding of an operand is l * t -> fp16, once.
+// Accumulation is fp32.  The sign bits are expanded in registers right
+// before the MFMA that uses them: a lane's 8 operand values are 8 stored
+// scales (or 1.0) with the fp16 sign bit set where the sign is -1.
 //
 // Latent columns: every (layer m, path p) owns a segment of T of s
 // columns rounded up to 32; padding columns are exactly zero.  T is kept
@@ -27,16 +28,16 @@
 // element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2), register
 // 4 * (i / 8) + i % 4.
 //
-// Stage 1 computes 32 x 128 tiles (each of 4 waves owns 32 columns, so no
-// cross-wave sum); stage 2 computes 32 x 64 tiles with the 4 waves
-// interleaved over the (path, 32-column) chunks of K and their partials
-// summed in wave order through LDS.  Each workgroup copies its operands
-// into LDS with LDS-DMA in rounds (x or T rows, sign words and the
-// per-k scales g or l), the next round in flight while the current one
-// is multiplied.  Stage 1 also splits K across workgroups when the tiles
-// alone cannot fill the chip; the last workgroup of a tile to finish (an
-// atomic counter per tile) sums the partials in split order, so the
-// result does not depend on timing.
+// Stage 1 computes 32 x 128 tiles with 8 waves (two per 32 columns, on
+// the even and the odd input chunks) and requests a split's whole operand
+// range at once when it fits in LDS.  Stage 2 computes 32 x 64 nb tiles
+// (nb = 1, 2 or 4), the waves interleaved over the (path, 32-column) chunks
+// of K and their partials summed in a fixed order through LDS.  Each
+// workgroup copies its operands into LDS with LDS-DMA (x or T rows, sign
+// words, and g in stage 1).  Stage 1 also splits K across workgroups (one
+// per CU); the last workgroup of a tile to finish (an atomic counter per
+// tile) sums the partials in split order, so the result does not depend
+// on timing.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>

@@ -31,7 +31,8 @@
 // Exchange.  Partial latent vectors (one per workgroup) are all-reduced
 // between phases: each workgroup stores its partials contiguously;
 // workgroup r sums the 8-column slice r over all workgroups in a fixed
-// order; everyone reads the reduced vector.  Every exchanged word is a
+// order and writes it into each of kXCopies copies of the reduced vector;
+// workgroup w reads copy w % kXCopies.  Every exchanged word is a
 // 64-bit value | generation pair written and read with relaxed
 // device-coherent (sc1) atomics, so a reader knows a word is current from
 // the word itself and no flag (or store-completion wait) is needed.
@@ -495,8 +496,9 @@ __device__ void first_product(Lds &L) {
 // and no separate flags: workgroup w stores its partials tagged with this
 // phase's generation; the owner of slice r (8 columns) spins on the 8 G
 // words of its slice until every one carries the generation, sums them in
-// a fixed order and stores the 8 sums tagged; everyone spins on the Lu
-// tagged sums.  Each level costs one store and one read (plus re-reads
+// a fixed order and stores the 8 sums tagged into every copy; a
+// workgroup spins on the Lu tagged sums of its copy.  Each level costs one
+// store and one read (plus re-reads
 // while words are missing).  Only threads < kXThreads touch memory; every
 // spin is bounded and checks the error word every 64 rounds.
 constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
