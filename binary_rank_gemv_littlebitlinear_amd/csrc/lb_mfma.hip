@@ -71,7 +71,7 @@ static_assert(2 * s1_lds_bytes(kS1RoundC) <= 80 * 1024, "two buffered rounds lea
 // stage 2: a workgroup computes 32 rows x 64 nb outputs; a round stages
 // up to kRC2 (path, 32-column) chunks of one layer's latent rows and sign
 // words (two round buffers)
-constexpr int kRC2 = 28;  // a multiple of 4
+constexpr int kRC2 = 32;  // a multiple of 4
 constexpr int kS2MinC = 18;            // the wave partials fit one round buffer from here
 constexpr int kS2Lds = 160 * 1024;
 constexpr int kRP2 = 64 + 4;           // LDS pitch (floats) of a wave's 32 x 64 partial
@@ -718,7 +718,8 @@ static void s2_shape(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *
   *c2 = std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, n)) & ~3;
   static_assert(kS2Lds / 2 / s2_buf_bytes(1, 4) >= kS2MinC, "rounds hold the wave partials");
   static_assert(8 * 32 * kRP2 * 4 <= s2_buf_bytes((kS2Lds / 2 / s2_buf_bytes(1, 4)) & ~3, 4) &&
-                    8 * 32 * kRP2 * 4 <= s2_buf_bytes(std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, 2)) & ~3, 2),
+                    8 * 32 * kRP2 * 4 <= s2_buf_bytes(std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, 2)) & ~3, 2) &&
+                    8 * 32 * kRP2 * 4 <= s2_buf_bytes(std::min(kRC2, kS2Lds / 2 / s2_buf_bytes(1, 1)) & ~3, 1),
                 "8-wave partials fit the round buffer");
 }
 
@@ -741,7 +742,7 @@ static hipError_t set_lds_attr(int device) {
   if (bit && (done.load() & bit)) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void *)k_unit_s1,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS1Lds);
-  const void *s2k[3] = {(const void *)k_unit_s2<1, 4>, (const void *)k_unit_s2<2, 8>,
+  const void *s2k[3] = {(const void *)k_unit_s2<1, 8>, (const void *)k_unit_s2<2, 8>,
                         (const void *)k_unit_s2<4, 8>};
   for (int i = 0; i < 3 && e == hipSuccess; ++i)
     e = hipFuncSetAttribute(s2k[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kS2Lds);
@@ -805,7 +806,7 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     else if (A2.nb == 2)
       hipLaunchKernelGGL((k_unit_s2<2, 8>), g2, dim3(512), lds2, st, A2);
     else
-      hipLaunchKernelGGL((k_unit_s2<1, 4>), g2, dim3(kThreads), lds2, st, A2);
+      hipLaunchKernelGGL((k_unit_s2<1, 8>), g2, dim3(512), lds2, st, A2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
