@@ -53,7 +53,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;   // 4 waves (second stage)
 constexpr int kThreads1 = 512;  // 8 waves (first stage)
 constexpr int kMaxSplit = 8;
 // stage 1: a workgroup computes 32 rows x 128 latent columns (32 per wave)
