@@ -44,6 +44,7 @@ import numpy as np
 __all__ = [
     "unpack_signs", "pack_signs", "num_bits", "eff_bits", "rank_for_bpw",
     "forward", "forward_path", "dense_weight", "combine", "stack_units",
+    "sign_words", "rank1_magnitude", "init_from_factors", "svd_factors", "dual_svid",
 ]
 
 
@@ -155,6 +156,80 @@ def dense_weight(paths) -> np.ndarray:
         Wp = (_f64(p["h"])[:, None] * S_U) @ (_f64(p["l"])[:, None] * (S_V * _f64(p["g"])[:, None]).T)
         W = Wp if W is None else W + Wp
     return W
+
+
+# --------------------------------------------------------------------------
+# Initialisation from real factors ([LB news] Sec. 2, Dual-SVID)
+#
+# The page gives one line: the factor signs come from a truncated SVD and
+# the magnitudes are turned into scales by a rank-1 approximation.
+# Readings (each also listed in the design notes):
+# * the singular values are split evenly between the factors,
+#   U' = U sqrt(Sigma), V' = V sqrt(Sigma), so that W ~= U' V'^T;
+# * sign(0) = +1 (bit 1), for -0.0 as well;
+# * the rank-1 approximation of a magnitude matrix is its top singular pair
+#   (Eckart-Young), split evenly: |U'| ~= r c^T with r = u sqrt(sigma),
+#   c = v sqrt(sigma), both nonnegative;
+# * |U'| gives the row scale h and a latent factor l_u, |V'| gives the
+#   column scale g and l_v, and l = l_u * l_v, so that
+#   U' V'^T ~= diag(h) S_U diag(l) S_V^T diag(g);
+# * the residual path takes the same steps on W minus the main path's
+#   dense weight (with its fp16 scales).
+# --------------------------------------------------------------------------
+def sign_words(F) -> np.ndarray:
+    """Canonical words of the signs of a real factor (rows x s); 0 and -0 count as +1."""
+    F = np.asarray(F, dtype=np.float64)
+    return pack_signs(np.where(F >= 0.0, 1, -1))
+
+
+def rank1_magnitude(F):
+    """Top singular pair of |F| (rows x s) as r (rows) and c (s), |F| ~= outer(r, c).
+
+    The pair is the best rank-1 approximation in the Frobenius norm
+    (np.linalg.svd is the textbook routine); a nonnegative matrix has a
+    nonnegative top pair, whose sign the SVD leaves open and which is fixed
+    here so that r and c are >= 0.  The singular value is split evenly.
+    """
+    A = np.abs(np.asarray(F, dtype=np.float64))
+    U, S, Vt = np.linalg.svd(A, full_matrices=False)
+    u, v, sig = U[:, 0], Vt[0], float(S[0])
+    if u.sum() < 0:
+        u, v = -u, -v
+    return u * np.sqrt(sig), v * np.sqrt(sig)
+
+
+def init_from_factors(U, V, round_fp16: bool = True) -> dict:
+    """One path from real factors U (b x s) and V (a x s), W ~= U V^T.
+
+    Signs of the factors, h and l_u from the rank-1 fit of |U|, g and l_v
+    from that of |V|, l = l_u * l_v.  The scales are rounded to fp16 (RNE)
+    unless ``round_fp16`` is False (then they stay float64).
+    """
+    U = np.asarray(U, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    h, lu = rank1_magnitude(U)
+    g, lv = rank1_magnitude(V)
+    l = lu * lv
+    cast = (lambda v: v.astype(np.float16)) if round_fp16 else (lambda v: v)
+    return {"s": U.shape[1], "su": sign_words(U), "sv": sign_words(V),
+            "h": cast(h), "g": cast(g), "l": cast(l)}
+
+
+def svd_factors(W, s: int):
+    """Rank-s truncated SVD of W (b x a) as U' = U sqrt(Sigma) (b x s) and V' (a x s)."""
+    W = np.asarray(W, dtype=np.float64)
+    U, S, Vt = np.linalg.svd(W, full_matrices=False)
+    r = np.sqrt(S[:s])
+    return U[:, :s] * r[None, :], Vt[:s].T * r[None, :]
+
+
+def dual_svid(W, s: int, residual: bool) -> list:
+    """Dual-SVID initialisation of a layer from a real W (b x a), rank s per path."""
+    W = np.asarray(W, dtype=np.float64)
+    paths = [init_from_factors(*svd_factors(W, s))]
+    if residual:
+        paths.append(init_from_factors(*svd_factors(W - dense_weight(paths), s)))
+    return paths
 
 
 # --------------------------------------------------------------------------
