@@ -47,6 +47,8 @@ def load_library(path: str = LIB_PATH):
         "lb_set_scales": ([vp, i32, vp, vp, vp], i32),
         "lb_forward": ([vp, vp, vp, i64, vp], i32),
         "lb_unpack_signs": ([vp, i32, vp, vp], i32),
+        "lb_get_scales": ([vp, i32, vp, vp, vp], i32),
+        "lb_init_from_factors": ([vp, i32, vp, vp, vp], i32),
         "lb_layer_shape": ([vp, P(i64), P(i64), P(i64), P(i32)], i32),
         "lb_destroy": ([vp], i32),
         "lb_forward_stage1": ([vp, vp, vp, i64, vp], i32),
@@ -74,6 +76,7 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
+            "lb_get_scales", "lb_init_from_factors",
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
             "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
@@ -161,6 +164,34 @@ def lb_unpack_signs(layer: int, path: int):
     sv = np.zeros((a, wk), np.uint32)
     _check(load_library().lb_unpack_signs(layer, path, su.ctypes.data, sv.ctypes.data))
     return su, sv
+
+
+def lb_get_scales(layer: int, path: int):
+    """(h, g, l) of one path as fp16 arrays."""
+    a, b, s, _ = lb_layer_shape(layer)
+    h = np.zeros(b, np.uint16)
+    g = np.zeros(a, np.uint16)
+    l = np.zeros(s, np.uint16)
+    _check(load_library().lb_get_scales(layer, path, h.ctypes.data, g.ctypes.data, l.ctypes.data))
+    return h.view(np.float16), g.view(np.float16), l.view(np.float16)
+
+
+def lb_init_from_factors(layer: int, path: int, U, V, stream=None):
+    """Signs and scales of one path from device fp32 factors U (b x s), V (a x s)."""
+    a, b, s, _ = lb_layer_shape(layer)
+    for name, t, rows in (("U", U, b), ("V", V, a)):
+        if isinstance(t, int):
+            continue
+        if (t.dtype != _torch_float32() or not t.is_contiguous() or t.device.type != "cuda"
+                or tuple(t.shape) != (rows, s)):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of shape "
+                             f"({rows}, {s})")
+    _check(load_library().lb_init_from_factors(layer, path, _ptr(U), _ptr(V), _stream(stream)))
+
+
+def _torch_float32():
+    import torch
+    return torch.float32
 
 
 def lb_layer_shape(layer: int):

@@ -233,11 +233,9 @@ extern "C" lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, i
   return LB_OK;
 }
 
-extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, const uint32_t *sv) {
-  if (!L || !su || !sv) return fail(LB_EINVAL, "lb_pack_signs: NULL argument");
-  Layer &Ly = L->ly;
-  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_pack_signs: path out of range");
-  DeviceGuard dg(Ly.device);
+// Re-lay host canonical words of one path out for the device (the caller
+// has checked the arguments and made the layer's device current).
+static lb_status pack_signs_impl(Layer &Ly, int path, const uint32_t *su, const uint32_t *sv) {
   const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L;
   // S_U: su2[(p*Wk + q)*b16 + j] = su[j*Wk + q] (padding masked, rows >= b zero)
   const int64_t b16 = Ly.b16;
@@ -304,6 +302,14 @@ extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, co
   return LB_OK;
 }
 
+extern "C" lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, const uint32_t *sv) {
+  if (!L || !su || !sv) return fail(LB_EINVAL, "lb_pack_signs: NULL argument");
+  Layer &Ly = L->ly;
+  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_pack_signs: path out of range");
+  DeviceGuard dg(Ly.device);
+  return pack_signs_impl(Ly, path, su, sv);
+}
+
 extern "C" lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, uint32_t *sv) {
   if (!L || !su || !sv) return fail(LB_EINVAL, "lb_unpack_signs: NULL argument");
   const Layer &Ly = L->ly;
@@ -330,12 +336,8 @@ extern "C" lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, 
   return LB_OK;
 }
 
-extern "C" lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t *g,
-                                   const uint16_t *l) {
-  if (!L || !h || !g || !l) return fail(LB_EINVAL, "lb_set_scales: NULL argument");
-  Layer &Ly = L->ly;
-  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_set_scales: path out of range");
-  DeviceGuard dg(Ly.device);
+static lb_status set_scales_impl(Layer &Ly, int path, const uint16_t *h, const uint16_t *g,
+                                 const uint16_t *l) {
   LB_HIP(hipMemcpy(Ly.h + (size_t)path * Ly.b16, h, Ly.b * 2, hipMemcpyHostToDevice));
   LB_HIP(hipMemcpy(Ly.g + (size_t)path * Ly.a16, g, Ly.a * 2, hipMemcpyHostToDevice));
   LB_HIP(hipMemcpy(Ly.l + (size_t)path * Ly.s8, l, Ly.s * 2, hipMemcpyHostToDevice));
@@ -351,6 +353,75 @@ extern "C" lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, con
   }
   Ly.scales_set[path] = true;
   return LB_OK;
+}
+
+extern "C" lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t *g,
+                                   const uint16_t *l) {
+  if (!L || !h || !g || !l) return fail(LB_EINVAL, "lb_set_scales: NULL argument");
+  Layer &Ly = L->ly;
+  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_set_scales: path out of range");
+  DeviceGuard dg(Ly.device);
+  return set_scales_impl(Ly, path, h, g, l);
+}
+
+extern "C" lb_status lb_get_scales(const lb_layer *L, int path, uint16_t *h, uint16_t *g,
+                                   uint16_t *l) {
+  if (!L || !h || !g || !l) return fail(LB_EINVAL, "lb_get_scales: NULL argument");
+  const Layer &Ly = L->ly;
+  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_get_scales: path out of range");
+  if (!Ly.scales_set[path]) return fail(LB_ENOTREADY, "lb_get_scales: scales of this path not set");
+  DeviceGuard dg(Ly.device);
+  LB_HIP(hipMemcpy(h, Ly.h + (size_t)path * Ly.b16, Ly.b * 2, hipMemcpyDeviceToHost));
+  LB_HIP(hipMemcpy(g, Ly.g + (size_t)path * Ly.a16, Ly.a * 2, hipMemcpyDeviceToHost));
+  LB_HIP(hipMemcpy(l, Ly.l + (size_t)path * Ly.s8, Ly.s * 2, hipMemcpyDeviceToHost));
+  return LB_OK;
+}
+
+extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const float *V,
+                                          void *stream) {
+  if (!L || !U || !V) return fail(LB_EINVAL, "lb_init_from_factors: NULL argument");
+  Layer &Ly = L->ly;
+  if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_init_from_factors: path out of range");
+  if (((uintptr_t)U | (uintptr_t)V) & 3u)
+    return fail(LB_EINVAL, "lb_init_from_factors: U and V must be 4-byte aligned");
+  DeviceGuard dg(Ly.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk;
+  std::vector<uint32_t> su, sv;
+  std::vector<uint16_t> h, g, l;
+  try {
+    su.resize((size_t)b * Wk);
+    sv.resize((size_t)a * Wk);
+    h.resize((size_t)b);
+    g.resize((size_t)a);
+    l.resize((size_t)s);
+  } catch (...) {
+    return fail(LB_ENOMEM, "lb_init_from_factors: host allocation");
+  }
+  void *ws = nullptr;
+  hipError_t e = hipMalloc(&ws, init_ws_bytes(a, b, s));
+  if (e != hipSuccess)
+    return fail(LB_ENOMEM, std::string("lb_init_from_factors: hipMalloc: ") + hipGetErrorString(e));
+  InitResult r;
+  e = init_from_factors_dev(U, V, a, b, s, ws, st, &r);
+  if (e == hipSuccess) e = hipMemcpyAsync(su.data(), r.su, su.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(sv.data(), r.sv, sv.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), r.h, h.size() * 2, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(g.data(), r.g, g.size() * 2, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(l.data(), r.l, l.size() * 2, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  const hipError_t ef = hipFree(ws);
+  if (e != hipSuccess)
+    return fail(LB_EHIP, std::string("lb_init_from_factors: ") + hipGetErrorString(e));
+  if (ef != hipSuccess)
+    return fail(LB_EHIP, std::string("lb_init_from_factors: hipFree: ") + hipGetErrorString(ef));
+  if (!r.converged)
+    return fail(LB_EUNSUPPORTED,
+                "lb_init_from_factors: power iteration did not settle (the top singular value "
+                "of |U| or |V| is not separated from the next one); the layer is unchanged");
+  lb_status sst = pack_signs_impl(Ly, path, su.data(), sv.data());
+  if (sst != LB_OK) return sst;
+  return set_scales_impl(Ly, path, h.data(), g.data(), l.data());
 }
 
 // ------------------------------------------------------------- forward

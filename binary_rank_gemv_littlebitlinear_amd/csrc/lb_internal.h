@@ -131,6 +131,22 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             void *ws, unsigned *cnt, const void *zero, const DeviceInfo &dev,
                             hipStream_t st);
 
+// Initialisation of one path from real device factors U (b x s) and
+// V (a x s), fp32 row-major.  ws holds init_ws_bytes(a, b, s) bytes; the
+// results are device pointers into ws: canonical sign words su (b x Wk),
+// sv (a x Wk), fp16 bits h (b), g (a), l (s), and sigma[0..1] (top singular
+// values of |U| and |V|).  Synchronises st while iterating.
+struct InitResult {
+  uint32_t *su = nullptr, *sv = nullptr;
+  uint16_t *h = nullptr, *g = nullptr, *l = nullptr;
+  double *sigma = nullptr;
+  int iters_u = 0, iters_v = 0;
+  bool converged = false;
+};
+size_t init_ws_bytes(int64_t a, int64_t b, int64_t s);
+hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
+                                 void *ws, hipStream_t st, InitResult *res);
+
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,
                           int64_t elems, hipStream_t st);

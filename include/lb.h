@@ -97,6 +97,36 @@ lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void 
  * bits zero).  Bit-exact inverse of lb_pack_signs; synchronous. */
 lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, uint32_t *sv);
 
+/* Read the fp16 scales of one path back (h: b values, g: a, l: s), the
+ * bit patterns lb_set_scales or lb_init_from_factors stored; synchronous.
+ * LB_ENOTREADY when that path's scales were never set. */
+lb_status lb_get_scales(const lb_layer *L, int path, uint16_t *h, uint16_t *g, uint16_t *l);
+
+/* Set the signs and scales of one path from real factors W ~= U V^T
+ * (Dual-SVID, [LB news] Sec. 2): U is b x s and V is a x s, fp32,
+ * row-major (row stride s), device memory on the layer's device, 4-byte
+ * aligned, read on `stream` after the work already queued there and left
+ * unchanged.  Readings of the one-line description, stated here:
+ *   S_U = sign(U), S_V = sign(V), with sign(0) = sign(-0) = +1;
+ *   |U| ~= h l_u^T and |V| ~= g l_v^T by the top singular pair of each
+ *   (the best rank-1 fit in the Frobenius norm; both vectors >= 0), the
+ *   singular value split evenly between the two vectors;
+ *   l = l_u * l_v (elementwise), so that diag(h) S_U diag(l) S_V^T diag(g)
+ *   approximates U V^T;
+ *   h, g and l are rounded once to fp16 (nearest even).
+ * The pair is found on the device by power iteration in fp64 with
+ * fixed-order sums (deterministic), until successive unit iterates differ
+ * by at most 1e-13 in every entry, within 2048 steps.  The truncated SVD
+ * that gives U and V from W, and the residual W - W_1 for path 1, are the
+ * caller's (e.g. a library SVD on the device).  Allocates device
+ * temporaries of about 8 (s max(a, b) / 64 + a + b + 4 s) bytes plus the
+ * sign words and scales, and synchronises `stream` several times; returns
+ * when the layer holds the new path.  LB_EUNSUPPORTED,
+ * with the layer unchanged, when the iteration has not settled (a top
+ * singular value of |U| or |V| not separated from the next). */
+lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const float *V,
+                               void *stream);
+
 /* Shape queries. */
 lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, int64_t *s, int *residual);
 

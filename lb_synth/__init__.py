@@ -85,6 +85,47 @@ def garbage_padding(words: np.ndarray, s: int, seed: int) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------------------
+# Real-valued stand-ins for initialisation from real weights (the pages start
+# from pretrained weights, which are not available here).
+# ---------------------------------------------------------------------------
+FACTOR_KEY = 0xFAC7
+WEIGHT_KEY = 0x3E16
+
+
+def factors(a: int, b: int, s: int, seed: int, stream: int = 0):
+    """Real factors U (b x s) and V (a x s), float32, shaped like rank-s SVD factors.
+
+    Columns of a truncated SVD's U sqrt(Sigma) are orthogonal with decaying
+    norms; here U = diag(r_U) G_U diag(d) and V = diag(r_V) G_V diag(d) with
+    G ~ N(0, 1), d_k = (k + 1) ** -0.25 (a decaying spectrum), and row gains
+    r ~ lognormal(0, 0.5) (uneven channel magnitudes).  Random Gaussian
+    columns are near-orthogonal for many rows.  Draw order: r_U, G_U, r_V,
+    G_V.
+    """
+    rng = _rng(seed, FACTOR_KEY, stream)
+    d = (np.arange(int(s), dtype=np.float64) + 1.0) ** -0.25
+    rU = rng.lognormal(0.0, 0.5, int(b))
+    U = (rU[:, None] * rng.standard_normal((int(b), int(s)))) * d[None, :]
+    rV = rng.lognormal(0.0, 0.5, int(a))
+    V = (rV[:, None] * rng.standard_normal((int(a), int(s)))) * d[None, :]
+    return U.astype(np.float32), V.astype(np.float32)
+
+
+def weight_matrix(a: int, b: int, seed: int) -> np.ndarray:
+    """A dense stand-in weight W (b x a), float64: row gains x N(0, 1/a) x column gains.
+
+    W = diag(r) G diag(c) / sqrt(a) with r, c ~ lognormal(0, 0.5) and G ~
+    N(0, 1): uneven row and column magnitudes, as in trained linear layers.
+    Draw order: r, G, c.
+    """
+    rng = _rng(seed, WEIGHT_KEY)
+    r = rng.lognormal(0.0, 0.5, int(b))
+    G = rng.standard_normal((int(b), int(a)))
+    c = rng.lognormal(0.0, 0.5, int(a))
+    return (r[:, None] * G * c[None, :]) / np.sqrt(float(a))
+
+
 def kappa(paths: int) -> float:
     """Gain that keeps stacked activations O(1) under this recipe.
 
