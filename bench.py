@@ -144,6 +144,27 @@ def cpu_baseline(wl: dict, M: int, budget_s: float) -> dict:
                       f"float64 numpy incl. bit unpack, {t_used:.1f} s"}
 
 
+def measure_init(torch, lbm, reps: int = 3) -> dict:
+    """Initialisation of one Llama2-70B gate projection (8192 -> 28672, rank
+    302) from real fp32 factors already on the device: wall time of the
+    synchronous lb_init_from_factors call (sign packing, the two rank-1
+    fits, scales and the device re-layout of the result)."""
+    a, b, s = 8192, 28672, 302
+    U, V = lb_synth.factors(a, b, s, seed=3)
+    Ud, Vd = torch.from_numpy(U).cuda(), torch.from_numpy(V).cuda()
+    L = lbm.Layer(a, b, s, True)
+    lbm.lb_init_from_factors(L.handle, 0, Ud, Vd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        lbm.lb_init_from_factors(L.handle, i % 2, Ud, Vd)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    L.close()
+    return {"layer": "llama70b gate 8192->28672", "s": s, "ms_per_call": round(ms, 3),
+            "factor_bytes": (a + b) * s * 4}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +177,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary", default="llama7b_full_stack_M128",
                     help="extra workload measured in the same run ('' to skip)")
+    ap.add_argument("--no-init", action="store_true",
+                    help="skip timing the initialisation from real factors")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -233,6 +256,9 @@ def main():
                             "mfma_frac": round(s2["flops"] / (ms2 * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
                             "GB/s": round(s2["bytes"] / (ms2 * 1e-3) / 1e9, 2),
                             "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1)}
+    if not args.no_init:
+        print("[bench] timing initialisation from real factors", file=sys.stderr, flush=True)
+        out["init"] = measure_init(torch, lbm)
     print(json.dumps(out), flush=True)
 
 

@@ -102,7 +102,9 @@ struct DeviceGuard {
 // Word in the matrix-core bit order (see lb_internal.h): bits inverted and
 // permuted so that (w << (4 g + j)) & 0x80008000 holds the sign flips of
 // elements 8 g + 2 j and 8 g + 2 j + 1.
-inline uint32_t mfma_bit_order(uint32_t w) {
+// The permutation is bytewise: byte g of w fills its own bit positions, so
+// a table per byte position gives the word in four lookups.
+inline uint32_t mfma_bit_order_slow(uint32_t w) {
   uint32_t o = 0;
   for (int g = 0; g < 4; ++g)
     for (int e = 0; e < 8; ++e) {
@@ -111,6 +113,22 @@ inline uint32_t mfma_bit_order(uint32_t w) {
       o |= flip << pos;
     }
   return o;
+}
+
+struct MfmaOrderTable {
+  uint32_t t[4][256];
+  MfmaOrderTable() {
+    for (int g = 0; g < 4; ++g)
+      for (uint32_t v = 0; v < 256; ++v)
+        // the other bytes set to all ones contribute no flips
+        t[g][v] = mfma_bit_order_slow((0xffffffffu & ~(0xffu << (8 * g))) | (v << (8 * g)));
+  }
+};
+const MfmaOrderTable g_mfma_order;
+
+inline uint32_t mfma_bit_order(uint32_t w) {
+  return g_mfma_order.t[0][w & 0xff] | g_mfma_order.t[1][(w >> 8) & 0xff] |
+         g_mfma_order.t[2][(w >> 16) & 0xff] | g_mfma_order.t[3][w >> 24];
 }
 
 inline uint32_t tail_mask(int64_t s, int64_t q) {
@@ -260,13 +278,17 @@ static lb_status pack_signs_impl(Layer &Ly, int path, const uint32_t *su, const 
     LB_HIP(hipMemcpy(Ly.su2m + (size_t)path * Wk * b16, u2m.data(), u2m.size() * 4, hipMemcpyHostToDevice));
   }
   {
-    // tile-major: for tile tau, this path's Wk x 16 words are one 64*Wk-byte run
-    std::vector<uint32_t> u2t((size_t)Ly.T16b * Wk * 16);
+    // tile-major: for tile tau, this path's Wk x 16 words are one 64*Wk-byte
+    // run.  The paths interleave per tile, so the whole buffer is rewritten
+    // in one contiguous copy (after reading back the other path's runs).
+    const size_t n = (size_t)Ly.T16b * Ly.P * Wk * 16;
+    std::vector<uint32_t> u2t(n, 0u);
+    if (Ly.P > 1) LB_HIP(hipMemcpy(u2t.data(), Ly.su2t, n * 4, hipMemcpyDeviceToHost));
     for (int64_t tau = 0; tau < Ly.T16b; ++tau)
       for (int64_t q = 0; q < Wk; ++q)
-        for (int r = 0; r < 16; ++r) u2t[((size_t)tau * Wk + q) * 16 + r] = u2[(size_t)q * b16 + 16 * tau + r];
-    LB_HIP(hipMemcpy2D(Ly.su2t + (size_t)path * Wk * 16, (size_t)Ly.P * Wk * 16 * 4, u2t.data(),
-                       (size_t)Wk * 16 * 4, (size_t)Wk * 16 * 4, (size_t)Ly.T16b, hipMemcpyHostToDevice));
+        for (int r = 0; r < 16; ++r)
+          u2t[(((size_t)tau * Ly.P + path) * Wk + q) * 16 + r] = u2[(size_t)q * b16 + 16 * tau + r];
+    LB_HIP(hipMemcpy(Ly.su2t, u2t.data(), n * 4, hipMemcpyHostToDevice));
   }
   // S_V: 32 x 32 bit transposes.  Block (row group r, word q) -> columns
   // p*s + 32q + kk of row group r.
@@ -342,14 +364,20 @@ static lb_status set_scales_impl(Layer &Ly, int path, const uint16_t *h, const u
   LB_HIP(hipMemcpy(Ly.g + (size_t)path * Ly.a16, g, Ly.a * 2, hipMemcpyHostToDevice));
   LB_HIP(hipMemcpy(Ly.l + (size_t)path * Ly.s8, l, Ly.s * 2, hipMemcpyHostToDevice));
   {
-    // tile-major copies of h and g: 16 values per (tile, path), zero padded
-    std::vector<uint16_t> hb((size_t)Ly.T16b * 16, 0), gb((size_t)Ly.T16a * 16, 0);
-    std::memcpy(hb.data(), h, Ly.b * 2);
-    std::memcpy(gb.data(), g, Ly.a * 2);
-    LB_HIP(hipMemcpy2D(Ly.ht + (size_t)path * 16, (size_t)Ly.P * 16 * 2, hb.data(), 32, 32,
-                       (size_t)Ly.T16b, hipMemcpyHostToDevice));
-    LB_HIP(hipMemcpy2D(Ly.gt + (size_t)path * 16, (size_t)Ly.P * 16 * 2, gb.data(), 32, 32,
-                       (size_t)Ly.T16a, hipMemcpyHostToDevice));
+    // tile-major copies of h and g: 16 values per (tile, path), zero padded;
+    // the paths interleave per tile, so each buffer is rewritten whole
+    const size_t nh = (size_t)Ly.T16b * Ly.P * 16, ng = (size_t)Ly.T16a * Ly.P * 16;
+    std::vector<uint16_t> hb(nh, 0), gb(ng, 0);
+    if (Ly.P > 1) {
+      LB_HIP(hipMemcpy(hb.data(), Ly.ht, nh * 2, hipMemcpyDeviceToHost));
+      LB_HIP(hipMemcpy(gb.data(), Ly.gt, ng * 2, hipMemcpyDeviceToHost));
+    }
+    for (int64_t j = 0; j < Ly.b16; ++j)
+      hb[((size_t)(j >> 4) * Ly.P + path) * 16 + (j & 15)] = j < Ly.b ? h[j] : (uint16_t)0;
+    for (int64_t i = 0; i < Ly.a16; ++i)
+      gb[((size_t)(i >> 4) * Ly.P + path) * 16 + (i & 15)] = i < Ly.a ? g[i] : (uint16_t)0;
+    LB_HIP(hipMemcpy(Ly.ht, hb.data(), nh * 2, hipMemcpyHostToDevice));
+    LB_HIP(hipMemcpy(Ly.gt, gb.data(), ng * 2, hipMemcpyHostToDevice));
   }
   Ly.scales_set[path] = true;
   return LB_OK;

@@ -12,13 +12,17 @@
 //   power iteration on A = |F| (n x s, fp32 in, fp64 arithmetic), started
 //   from the all-ones direction, whose overlap with the nonnegative top
 //   right singular vector of a nonnegative matrix is positive:
-//     k_pow_block   64 rows per workgroup: x_r = sum_k A[r,k] v_k (a wave
-//                   per row, lanes along k, fixed-order shuffle tree), then
-//                   the block's share of A^T x (a thread per column, rows in
-//                   order) into part[block][k].  The second read of the
-//                   block's rows hits the cache, so HBM sees A once.
-//     k_pow_reduce  w_k = sum over blocks of part[.][k], four fixed ranges
-//                   combined in a fixed order.
+//     k_pow_fused   (s <= 1024) about 512 workgroups of consecutive rows; a
+//                   wave per row, lanes along k: x_r = sum_k A[r,k] v_k by a
+//                   fixed-order shuffle tree, and with the same loaded values
+//                   each lane adds A[r,k] x_r into its register share of A^T x;
+//                   the block's share goes to part[block][k].  A is read once.
+//     k_pow_block   (any s) 64 rows per workgroup, the same x_r, then the
+//                   block's share of A^T x by a thread per column over the
+//                   block's rows (a second, cache-served read).  Also gives
+//                   x = A v for the final step.
+//     k_pow_reduce  w_k = sum over blocks of part[.][k], 64 fixed ranges per
+//                   column combined by a fixed pairwise tree.
 //     k_pow_normalize  one workgroup: v = w / ||w||, and max |v_new - v_old|
 //                   for the host's convergence test.
 //   Every sum has a fixed order, so a call is deterministic.  After the
@@ -114,19 +118,76 @@ __global__ void __launch_bounds__(256) k_pow_block(const float *__restrict__ F, 
   }
 }
 
+// Register-resident variant for s <= 64 KM: a lane keeps its KM columns of
+// v and of the block's A^T x share in registers, so every element of A is
+// loaded once: x_r = wave sum of |A[r, k]| v_k, then acc_k += |A[r, k]| x_r
+// with the same loaded values.  The four waves' shares are added in wave
+// order through LDS.
+template <int KM>
+__global__ void __launch_bounds__(256) k_pow_fused(const float *__restrict__ F, int64_t n, int s,
+                                                   int rpb, const double *__restrict__ v,
+                                                   double *__restrict__ part) {
+  __shared__ double sh[3][KM * 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb;
+  const int rows = (int)((n - r0) < rpb ? (n - r0) : rpb);
+  double vr[KM], acc[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const int k = lane + 64 * j;
+    vr[j] = k < s ? v[k] : 0.0;
+    acc[j] = 0.0;
+  }
+  for (int rr = wave; rr < rows; rr += 4) {
+    const float *row = F + (size_t)(r0 + rr) * s;
+    double av[KM];
+    double dot = 0.0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int k = lane + 64 * j;
+      av[j] = k < s ? fabs((double)row[k < s ? k : 0]) : 0.0;
+      dot += av[j] * vr[j];
+    }
+    const double x = wave_sum(dot);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) acc[j] += av[j] * x;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) sh[wave - 1][lane + 64 * j] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int k = lane + 64 * j;
+      const double sum = ((acc[j] + sh[0][lane + 64 * j]) + sh[1][lane + 64 * j]) + sh[2][lane + 64 * j];
+      if (k < s) part[(size_t)blockIdx.x * s + k] = sum;
+    }
+  }
+}
+
+// w_k = sum over blocks of part[.][k]: 4 columns per workgroup, 64 fixed
+// block ranges per column, combined by a fixed pairwise tree.
+constexpr int kRedCols = 4;
 __global__ void __launch_bounds__(256) k_pow_reduce(const double *__restrict__ part, int64_t nblk,
                                                     int64_t s, double *__restrict__ w) {
-  __shared__ double red[4][64];
-  const int t = threadIdx.x, c = t & 63, grp = t >> 6;
-  const int64_t k = (int64_t)blockIdx.x * 64 + c;
-  const int64_t q = (nblk + 3) / 4;
+  constexpr int G = 256 / kRedCols;
+  __shared__ double red[G][kRedCols];
+  const int t = threadIdx.x, c = t % kRedCols, grp = t / kRedCols;
+  const int64_t k = (int64_t)blockIdx.x * kRedCols + c;
+  const int64_t q = (nblk + G - 1) / G;
   const int64_t b0 = grp * q, b1 = (b0 + q) < nblk ? (b0 + q) : nblk;
   double acc = 0.0;
   if (k < s)
     for (int64_t bi = b0; bi < b1; ++bi) acc += part[(size_t)bi * s + k];
   red[grp][c] = acc;
   __syncthreads();
-  if (grp == 0 && k < s) w[k] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+  for (int o = G / 2; o >= 1; o >>= 1) {
+    if (grp < o) red[grp][c] += red[grp + o][c];
+    __syncthreads();
+  }
+  if (grp == 0 && k < s) w[k] = red[0][c];
 }
 
 // Fixed-order sum over a 1024-thread workgroup (tree over LDS).
@@ -206,6 +267,46 @@ inline unsigned grid_of(int64_t n, int per) { return (unsigned)((n + per - 1) / 
 // Rank-1 fit of |F| (n x s): v (s) the unit right vector, x = |F| v (n),
 // *sigma = ||x||.  Returns the first HIP error; *converged is false when the
 // iterate still moved by more than tol after max_iters steps.
+// Rows per workgroup of the register-resident step: about two workgroups
+// per compute unit over the matrix, at least 8 rows.
+constexpr int kFusedMaxKM = 16;
+constexpr int kFusedBlocks = 512;
+inline int fused_rpb(int64_t n) {
+  const int64_t r = (n + kFusedBlocks - 1) / kFusedBlocks;
+  return (int)(r < 8 ? 8 : r);
+}
+inline int64_t fused_nblk(int64_t n) { return (n + fused_rpb(n) - 1) / fused_rpb(n); }
+
+template <int KM>
+void launch_fused_km(const float *F, int64_t n, int s, const double *v, double *part,
+                     hipStream_t st) {
+  const int rpb = fused_rpb(n);
+  hipLaunchKernelGGL(k_pow_fused<KM>, dim3((unsigned)fused_nblk(n)), dim3(256), 0, st, F, n, s,
+                     rpb, v, part);
+}
+
+// One step's A^T (A v) partials; returns the number of partial rows.
+int64_t launch_pow_step(const float *F, int64_t n, int64_t s, const double *v, double *part,
+                        hipStream_t st) {
+  const int64_t km = (s + 63) / 64;
+  if (km > kFusedMaxKM) {
+    const int64_t nblk = (n + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(k_pow_block, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v, part,
+                       (double *)nullptr);
+    return nblk;
+  }
+  switch (km) {
+#define LB_KM(K) \
+  case K:        \
+    launch_fused_km<K>(F, n, (int)s, v, part, st); \
+    break;
+    LB_KM(1) LB_KM(2) LB_KM(3) LB_KM(4) LB_KM(5) LB_KM(6) LB_KM(7) LB_KM(8)
+    LB_KM(9) LB_KM(10) LB_KM(11) LB_KM(12) LB_KM(13) LB_KM(14) LB_KM(15) LB_KM(16)
+#undef LB_KM
+  }
+  return fused_nblk(n);
+}
+
 hipError_t fit_rank1(const float *F, int64_t n, int64_t s, double *v, double *x, double *w,
                      double *part, double *diff, double *sigma, int max_iters, double tol,
                      hipStream_t st, bool *converged, int *iters) {
@@ -218,9 +319,9 @@ hipError_t fit_rank1(const float *F, int64_t n, int64_t s, double *v, double *x,
   if (e != hipSuccess) return e;
   while (*iters < max_iters) {
     for (int i = 0; i < kCheckEvery; ++i) {
-      hipLaunchKernelGGL(k_pow_block, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v, part,
-                         (double *)nullptr);
-      hipLaunchKernelGGL(k_pow_reduce, dim3(grid_of(s, 64)), dim3(256), 0, st, part, nblk, s, w);
+      const int64_t np = launch_pow_step(F, n, s, v, part, st);
+      hipLaunchKernelGGL(k_pow_reduce, dim3(grid_of(s, kRedCols)), dim3(256), 0, st, part, np, s,
+                         w);
       hipLaunchKernelGGL(k_pow_normalize, dim3(1), dim3(1024), 0, st, w, s, v, diff);
     }
     *iters += kCheckEvery;
@@ -242,9 +343,15 @@ hipError_t fit_rank1(const float *F, int64_t n, int64_t s, double *v, double *x,
 
 }  // namespace
 
+// Partial rows of either step kind, for the larger factor.
+inline int64_t part_rows(int64_t nmax) {
+  const int64_t a = (nmax + kRowsPerBlock - 1) / kRowsPerBlock, b = fused_nblk(nmax);
+  return a > b ? a : b;
+}
+
 size_t init_ws_bytes(int64_t a, int64_t b, int64_t s) {
   const int64_t nmax = a > b ? a : b;
-  const int64_t nblk = (nmax + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t nblk = part_rows(nmax);
   const int64_t Wk = (s + 31) / 32;
   size_t d = (size_t)(4 * s + a + b + nblk * s + 4);  // doubles
   size_t bytes = d * 8;
@@ -256,7 +363,7 @@ size_t init_ws_bytes(int64_t a, int64_t b, int64_t s) {
 hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
                                  void *ws, hipStream_t st, InitResult *res) {
   const int64_t nmax = a > b ? a : b;
-  const int64_t nblk = (nmax + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t nblk = part_rows(nmax);
   const int64_t Wk = (s + 31) / 32;
   double *d = static_cast<double *>(ws);
   double *vU = d, *vV = vU + s, *w = vV + s, *xU = w + s, *xV = xU + b, *part = xV + a;

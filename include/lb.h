@@ -69,7 +69,7 @@ typedef enum {
 /* Create a layer with input width a, output width b, rank s, and one
  * path (residual = 0) or two (residual = 1), on the current HIP device.
  * [LB2 column] Ch. 1 names a, b, s and residual; [LB news] Sec. 2 the
- * structure.  a, b, s >= 1 and a, b, s <= 2^24.  Allocates the device
+ * structure.  a, b, s >= 1, a, b <= 2^24 and s <= 4096.  Allocates the device
  * storage for signs, scales and workspace.  *out is set on success only. */
 lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb_layer **out);
 

@@ -70,7 +70,8 @@ def _plant_zeros(U, V):
 
 @pytest.mark.parametrize("a,b,s", [
     (64, 48, 16), (100, 37, 5), (257, 129, 63), (33, 65, 1), (1, 1, 1), (3, 1000, 31),
-    (1000, 3, 33), (96, 200, 65), (4096, 4096, 86), (8192, 28672, 302), (28672, 8192, 302)])
+    (1000, 3, 33), (96, 200, 65), (100, 70, 1024), (300, 200, 1100), (2000, 64, 4096),
+    (4096, 4096, 86), (8192, 28672, 302), (28672, 8192, 302)])
 def test_init_matches_oracle(lbm, a, b, s):
     """Signs bit-exact (0 and -0 count as +1), scales within one fp16 step, forward at the bar."""
     say(f"[case] init a={a} b={b} s={s}")
