@@ -45,6 +45,7 @@ __all__ = [
     "unpack_signs", "pack_signs", "num_bits", "eff_bits", "rank_for_bpw",
     "forward", "forward_path", "dense_weight", "combine", "stack_units",
     "sign_words", "rank1_magnitude", "init_from_factors", "svd_factors", "dual_svid",
+    "sign_pm1", "procrustes_rotation", "itq_loss", "joint_itq_rotation", "joint_itq",
 ]
 
 
@@ -223,13 +224,83 @@ def svd_factors(W, s: int):
     return U[:, :s] * r[None, :], Vt[:s].T * r[None, :]
 
 
-def dual_svid(W, s: int, residual: bool) -> list:
-    """Dual-SVID initialisation of a layer from a real W (b x a), rank s per path."""
+def dual_svid(W, s: int, residual: bool, itq_iters: int = 0) -> list:
+    """Dual-SVID initialisation of a layer from a real W (b x a), rank s per path.
+
+    With ``itq_iters`` > 0 each path's factors are first rotated by the
+    Joint-ITQ rotation of that many steps (started from the identity), as
+    LittleBit-2 does before binarising ([LB2 column] Ch. 2).
+    """
     W = np.asarray(W, dtype=np.float64)
-    paths = [init_from_factors(*svd_factors(W, s))]
+
+    def one_path(Wm):
+        U, V = svd_factors(Wm, s)
+        if itq_iters > 0:
+            U, V, _ = joint_itq(U, V, itq_iters)
+        return init_from_factors(U, V)
+
+    paths = [one_path(W)]
     if residual:
-        paths.append(init_from_factors(*svd_factors(W - dense_weight(paths), s)))
+        paths.append(one_path(W - dense_weight(paths)))
     return paths
+
+
+# --------------------------------------------------------------------------
+# Joint-ITQ rotation ([LB2 column] Ch. 2)
+#
+# The page states: an orthogonal R (R^T R = I) inserted between the factors
+# leaves their product unchanged, (U R)(R^T V^T) = U V^T; LittleBit-2 stacks
+# the factors as X = [U; V] (its code concatenates U and the transpose of
+# its s x a V along rows, which is our a x s V), finds R by an iterative
+# rotation (50 steps by default), rotates both factors with it before
+# binarising, and the rotation costs nothing at inference.
+# Readings (each also listed in the design notes):
+# * "iterative rotation" is iterative quantization (ITQ): minimise the
+#   quantisation loss ||B - X R||_F^2 over B in {+-1}^((b+a) x s) and
+#   orthogonal R by alternating B = sign(X R) and the R that is optimal for
+#   that B, the orthogonal Procrustes solution R = P Q^T for
+#   X^T B = P S Q^T;
+# * one step = one B update followed by one R update, starting from
+#   R0 = I (the page names no start; a caller may pass its own);
+# * sign(0) = +1, as for the factor signs;
+# * U <- U R and V <- V R in our a x s layout (the page's V <- R^T V).
+# --------------------------------------------------------------------------
+def sign_pm1(A) -> np.ndarray:
+    """+1 where A >= 0 (0 and -0 included), -1 elsewhere, float64."""
+    return np.where(np.asarray(A, dtype=np.float64) >= 0.0, 1.0, -1.0)
+
+
+def procrustes_rotation(M) -> np.ndarray:
+    """The orthogonal R that maximises trace(R^T M): R = P Q^T for M = P S Q^T.
+
+    This is the orthogonal Procrustes solution (a textbook result via the
+    SVD, np.linalg.svd); it also minimises ||B - X R||_F for M = X^T B.
+    """
+    P, _, Qt = np.linalg.svd(np.asarray(M, dtype=np.float64))
+    return P @ Qt
+
+
+def itq_loss(X, R) -> float:
+    """Quantisation loss ||sign(X R) - X R||_F^2."""
+    Y = np.asarray(X, dtype=np.float64) @ np.asarray(R, dtype=np.float64)
+    return float(np.sum((sign_pm1(Y) - Y) ** 2))
+
+
+def joint_itq_rotation(U, V, iters: int = 50, R0=None) -> np.ndarray:
+    """Joint-ITQ rotation (s x s) of the stacked factors X = [U; V]."""
+    X = np.vstack([np.asarray(U, dtype=np.float64), np.asarray(V, dtype=np.float64)])
+    s = X.shape[1]
+    R = np.eye(s) if R0 is None else np.asarray(R0, dtype=np.float64).copy()
+    for _ in range(int(iters)):
+        B = sign_pm1(X @ R)                  # quantise with the current rotation
+        R = procrustes_rotation(X.T @ B)     # best rotation for these codes
+    return R
+
+
+def joint_itq(U, V, iters: int = 50, R0=None):
+    """(U R, V R, R) with R the Joint-ITQ rotation; (U R)(V R)^T = U V^T."""
+    R = joint_itq_rotation(U, V, iters, R0)
+    return (np.asarray(U, dtype=np.float64) @ R, np.asarray(V, dtype=np.float64) @ R, R)
 
 
 # --------------------------------------------------------------------------
