@@ -148,7 +148,8 @@ def measure_init(torch, lbm, reps: int = 3) -> dict:
     """Initialisation of one Llama2-70B gate projection (8192 -> 28672, rank
     302) from real fp32 factors already on the device: wall time of the
     synchronous lb_init_from_factors call (sign packing, the two rank-1
-    fits, scales and the device re-layout of the result)."""
+    fits, scales and the device re-layout of the result), of lb_joint_itq
+    with 50 steps, and of lb_init_from_factors from the rotated factors."""
     a, b, s = 8192, 28672, 302
     U, V = lb_synth.factors(a, b, s, seed=3)
     Ud, Vd = torch.from_numpy(U).cuda(), torch.from_numpy(V).cuda()
@@ -160,9 +161,26 @@ def measure_init(torch, lbm, reps: int = 3) -> dict:
         lbm.lb_init_from_factors(L.handle, i % 2, Ud, Vd)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / reps
+    # Joint-ITQ (50 steps, the pages' default) and the path from the rotated factors
+    R = lbm.lb_joint_itq(Ud, Vd, 50)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        R = lbm.lb_joint_itq(Ud, Vd, 50)
+    torch.cuda.synchronize()
+    itq_ms = (time.perf_counter() - t0) * 1e3 / reps
+    t0 = time.perf_counter()
+    for i in range(reps):
+        lbm.lb_init_from_factors(L.handle, i % 2, Ud, Vd, R)
+    torch.cuda.synchronize()
+    rot_ms = (time.perf_counter() - t0) * 1e3 / reps
     L.close()
+    n = a + b
+    itq_flops = 50 * 4 * n * s * s  # X R and X^T B per step (Newton-Schulz products not counted)
     return {"layer": "llama70b gate 8192->28672", "s": s, "ms_per_call": round(ms, 3),
-            "factor_bytes": (a + b) * s * 4}
+            "factor_bytes": (a + b) * s * 4, "joint_itq_50_ms": round(itq_ms, 3),
+            "joint_itq_gemm_tflops": round(itq_flops / (itq_ms * 1e-3) / 1e12, 3),
+            "init_rotated_ms": round(rot_ms, 3)}
 
 
 def main():

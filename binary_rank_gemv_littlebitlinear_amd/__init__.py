@@ -48,7 +48,8 @@ def load_library(path: str = LIB_PATH):
         "lb_forward": ([vp, vp, vp, i64, vp], i32),
         "lb_unpack_signs": ([vp, i32, vp, vp], i32),
         "lb_get_scales": ([vp, i32, vp, vp, vp], i32),
-        "lb_init_from_factors": ([vp, i32, vp, vp, vp], i32),
+        "lb_init_from_factors": ([vp, i32, vp, vp, vp, vp], i32),
+        "lb_joint_itq": ([vp, vp, i64, i64, i64, i32, vp, vp, vp], i32),
         "lb_layer_shape": ([vp, P(i64), P(i64), P(i64), P(i32)], i32),
         "lb_destroy": ([vp], i32),
         "lb_forward_stage1": ([vp, vp, vp, i64, vp], i32),
@@ -76,7 +77,7 @@ def load_library(path: str = LIB_PATH):
 
 
 EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
-            "lb_get_scales", "lb_init_from_factors",
+            "lb_get_scales", "lb_init_from_factors", "lb_joint_itq",
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
             "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
@@ -176,22 +177,38 @@ def lb_get_scales(layer: int, path: int):
     return h.view(np.float16), g.view(np.float16), l.view(np.float16)
 
 
-def lb_init_from_factors(layer: int, path: int, U, V, stream=None):
-    """Signs and scales of one path from device fp32 factors U (b x s), V (a x s)."""
-    a, b, s, _ = lb_layer_shape(layer)
-    for name, t, rows in (("U", U, b), ("V", V, a)):
-        if isinstance(t, int):
-            continue
-        if (t.dtype != _torch_float32() or not t.is_contiguous() or t.device.type != "cuda"
-                or tuple(t.shape) != (rows, s)):
-            raise ValueError(f"{name} must be a contiguous float32 device tensor of shape "
-                             f"({rows}, {s})")
-    _check(load_library().lb_init_from_factors(layer, path, _ptr(U), _ptr(V), _stream(stream)))
+def _check_dev(name, t, shape, dtype):
+    if isinstance(t, int) or t is None:
+        return
+    if (t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda"
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {shape}")
 
 
-def _torch_float32():
+def lb_init_from_factors(layer: int, path: int, U, V, R=None, stream=None):
+    """Signs and scales of one path from device fp32 factors U (b x s), V (a x s),
+    rotated first by the device fp64 rotation R (s x s) when given."""
     import torch
-    return torch.float32
+    a, b, s, _ = lb_layer_shape(layer)
+    _check_dev("U", U, (b, s), torch.float32)
+    _check_dev("V", V, (a, s), torch.float32)
+    _check_dev("R", R, (s, s), torch.float64)
+    _check(load_library().lb_init_from_factors(layer, path, _ptr(U), _ptr(V), _ptr(R),
+                                               _stream(stream)))
+
+
+def lb_joint_itq(U, V, iters: int = 50, R0=None, stream=None):
+    """Joint-ITQ rotation (device fp64 s x s tensor) of device fp32 factors U (b x s), V (a x s)."""
+    import torch
+    b, s = U.shape
+    a = V.shape[0]
+    _check_dev("U", U, (b, s), torch.float32)
+    _check_dev("V", V, (a, s), torch.float32)
+    _check_dev("R0", R0, (s, s), torch.float64)
+    R = torch.empty((s, s), dtype=torch.float64, device=U.device)
+    _check(load_library().lb_joint_itq(_ptr(U), _ptr(V), a, b, s, int(iters), _ptr(R0), _ptr(R),
+                                       _stream(stream)))
+    return R
 
 
 def lb_layer_shape(layer: int):

@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: ``python -m binary_rank_gemv_littlebitlinear_amd.build``.
 
 Compiles every ``csrc/*.hip`` for gfx950 with hipcc into ``liblb.so`` next
-to this file.  Packed-fp32 VALU instructions are disabled for device code.
+to this file and links rocBLAS (plain fp64 GEMMs of the Joint-ITQ rotation).
+Packed-fp32 VALU instructions are disabled for device code.
 """
 from __future__ import annotations
 
@@ -41,7 +42,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _drain(procs)
     _drain(procs)
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)

@@ -406,12 +406,13 @@ extern "C" lb_status lb_get_scales(const lb_layer *L, int path, uint16_t *h, uin
 }
 
 extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const float *V,
-                                          void *stream) {
+                                          const double *R, void *stream) {
   if (!L || !U || !V) return fail(LB_EINVAL, "lb_init_from_factors: NULL argument");
   Layer &Ly = L->ly;
   if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_init_from_factors: path out of range");
   if (((uintptr_t)U | (uintptr_t)V) & 3u)
     return fail(LB_EINVAL, "lb_init_from_factors: U and V must be 4-byte aligned");
+  if ((uintptr_t)R & 7u) return fail(LB_EINVAL, "lb_init_from_factors: R must be 8-byte aligned");
   DeviceGuard dg(Ly.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk;
@@ -426,12 +427,28 @@ extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U,
   } catch (...) {
     return fail(LB_ENOMEM, "lb_init_from_factors: host allocation");
   }
+  // with a rotation: the fp64 factors [U R; V R] first
+  double *rot = nullptr;
+  if (R) {
+    hipError_t e = hipMalloc(&rot, (size_t)(a + b) * s * sizeof(double));
+    if (e != hipSuccess)
+      return fail(LB_ENOMEM, std::string("lb_init_from_factors: hipMalloc: ") + hipGetErrorString(e));
+    std::string msg;
+    const int rc = rotate_factors_dev(U, V, a, b, s, R, rot, st, &msg);
+    if (rc != 0) {
+      (void)hipFree(rot);
+      return fail((lb_status)rc, "lb_init_from_factors: " + msg);
+    }
+  }
   void *ws = nullptr;
   hipError_t e = hipMalloc(&ws, init_ws_bytes(a, b, s));
-  if (e != hipSuccess)
+  if (e != hipSuccess) {
+    if (rot) (void)hipFree(rot);
     return fail(LB_ENOMEM, std::string("lb_init_from_factors: hipMalloc: ") + hipGetErrorString(e));
+  }
   InitResult r;
-  e = init_from_factors_dev(U, V, a, b, s, ws, st, &r);
+  e = rot ? init_from_factors_dev(rot, rot + (size_t)b * s, a, b, s, ws, st, &r)
+          : init_from_factors_dev(U, V, a, b, s, ws, st, &r);
   if (e == hipSuccess) e = hipMemcpyAsync(su.data(), r.su, su.size() * 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipMemcpyAsync(sv.data(), r.sv, sv.size() * 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipMemcpyAsync(h.data(), r.h, h.size() * 2, hipMemcpyDeviceToHost, st);
@@ -439,6 +456,7 @@ extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U,
   if (e == hipSuccess) e = hipMemcpyAsync(l.data(), r.l, l.size() * 2, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   const hipError_t ef = hipFree(ws);
+  if (rot) (void)hipFree(rot);
   if (e != hipSuccess)
     return fail(LB_EHIP, std::string("lb_init_from_factors: ") + hipGetErrorString(e));
   if (ef != hipSuccess)
@@ -450,6 +468,21 @@ extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U,
   lb_status sst = pack_signs_impl(Ly, path, su.data(), sv.data());
   if (sst != LB_OK) return sst;
   return set_scales_impl(Ly, path, h.data(), g.data(), l.data());
+}
+
+extern "C" lb_status lb_joint_itq(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
+                                  int iters, const double *R0, double *R, void *stream) {
+  if (!U || !V || !R) return fail(LB_EINVAL, "lb_joint_itq: NULL argument");
+  if (a < 1 || b < 1 || s < 1 || a > (1 << 24) || b > (1 << 24) || s > 4096 || iters < 0)
+    return fail(LB_EINVAL, "lb_joint_itq: need 1 <= a, b <= 2^24, 1 <= s <= 4096, iters >= 0");
+  if ((a + b) * s > ((int64_t)1 << 31) - 1)
+    return fail(LB_EINVAL, "lb_joint_itq: (a + b) * s must fit in 31 bits");
+  if ((((uintptr_t)U | (uintptr_t)V) & 3u) || (((uintptr_t)R | (uintptr_t)R0) & 7u))
+    return fail(LB_EINVAL, "lb_joint_itq: misaligned pointer");
+  std::string msg;
+  const int rc = joint_itq_dev(U, V, a, b, s, iters, R0, R, static_cast<hipStream_t>(stream), &msg);
+  if (rc != 0) return fail((lb_status)rc, "lb_joint_itq: " + msg);
+  return LB_OK;
 }
 
 // ------------------------------------------------------------- forward

@@ -73,24 +73,26 @@ __device__ inline uint16_t f16_bits_rne(double d) {
   return sign | (uint16_t)bits;
 }
 
-__global__ void __launch_bounds__(256) k_sign_words(const float *__restrict__ F, int64_t rows,
+template <typename T>
+__global__ void __launch_bounds__(256) k_sign_words(const T *__restrict__ F, int64_t rows,
                                                     int64_t s, int64_t Wk,
                                                     uint32_t *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
-  const float *row = F + (size_t)r * s;
+  const T *row = F + (size_t)r * s;
   uint32_t *o = out + (size_t)r * Wk;
   for (int64_t c0 = 0; c0 < s; c0 += 64) {
     const int64_t k = c0 + lane;
-    const bool bit = k < s && row[k < s ? k : 0] >= 0.0f;
+    const bool bit = k < s && row[k < s ? k : 0] >= (T)0;
     const uint64_t m = __ballot(bit);
     const int64_t q = (c0 >> 5) + lane;
     if (lane < 2 && q < Wk) o[q] = (uint32_t)(m >> (32 * lane));
   }
 }
 
-__global__ void __launch_bounds__(256) k_pow_block(const float *__restrict__ F, int64_t n,
+template <typename T>
+__global__ void __launch_bounds__(256) k_pow_block(const T *__restrict__ F, int64_t n,
                                                    int64_t s, const double *__restrict__ v,
                                                    double *__restrict__ part,
                                                    double *__restrict__ xout) {
@@ -99,7 +101,7 @@ __global__ void __launch_bounds__(256) k_pow_block(const float *__restrict__ F, 
   const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
   const int rows = (int)((n - r0) < kRowsPerBlock ? (n - r0) : kRowsPerBlock);
   for (int rr = wave; rr < rows; rr += 4) {
-    const float *row = F + (size_t)(r0 + rr) * s;
+    const T *row = F + (size_t)(r0 + rr) * s;
     double acc = 0.0;
     for (int64_t k = lane; k < s; k += 64) acc += fabs((double)row[k]) * v[k];
     acc = wave_sum(acc);
@@ -110,7 +112,7 @@ __global__ void __launch_bounds__(256) k_pow_block(const float *__restrict__ F, 
   }
   if (!part) return;
   __syncthreads();
-  const float *blk = F + (size_t)r0 * s;
+  const T *blk = F + (size_t)r0 * s;
   for (int64_t k = t; k < s; k += 256) {
     double acc = 0.0;
     for (int rr = 0; rr < rows; ++rr) acc += fabs((double)blk[(size_t)rr * s + k]) * xs[rr];
@@ -123,8 +125,8 @@ __global__ void __launch_bounds__(256) k_pow_block(const float *__restrict__ F, 
 // loaded once: x_r = wave sum of |A[r, k]| v_k, then acc_k += |A[r, k]| x_r
 // with the same loaded values.  The four waves' shares are added in wave
 // order through LDS.
-template <int KM>
-__global__ void __launch_bounds__(256) k_pow_fused(const float *__restrict__ F, int64_t n, int s,
+template <typename T, int KM>
+__global__ void __launch_bounds__(256) k_pow_fused(const T *__restrict__ F, int64_t n, int s,
                                                    int rpb, const double *__restrict__ v,
                                                    double *__restrict__ part) {
   __shared__ double sh[3][KM * 64];
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__(256) k_pow_fused(const float *__restrict__ F, 
     acc[j] = 0.0;
   }
   for (int rr = wave; rr < rows; rr += 4) {
-    const float *row = F + (size_t)(r0 + rr) * s;
+    const T *row = F + (size_t)(r0 + rr) * s;
     double av[KM];
     double dot = 0.0;
 #pragma unroll
@@ -277,28 +279,29 @@ inline int fused_rpb(int64_t n) {
 }
 inline int64_t fused_nblk(int64_t n) { return (n + fused_rpb(n) - 1) / fused_rpb(n); }
 
-template <int KM>
-void launch_fused_km(const float *F, int64_t n, int s, const double *v, double *part,
+template <typename T, int KM>
+void launch_fused_km(const T *F, int64_t n, int s, const double *v, double *part,
                      hipStream_t st) {
   const int rpb = fused_rpb(n);
-  hipLaunchKernelGGL(k_pow_fused<KM>, dim3((unsigned)fused_nblk(n)), dim3(256), 0, st, F, n, s,
+  hipLaunchKernelGGL((k_pow_fused<T, KM>), dim3((unsigned)fused_nblk(n)), dim3(256), 0, st, F, n, s,
                      rpb, v, part);
 }
 
 // One step's A^T (A v) partials; returns the number of partial rows.
-int64_t launch_pow_step(const float *F, int64_t n, int64_t s, const double *v, double *part,
+template <typename T>
+int64_t launch_pow_step(const T *F, int64_t n, int64_t s, const double *v, double *part,
                         hipStream_t st) {
   const int64_t km = (s + 63) / 64;
   if (km > kFusedMaxKM) {
     const int64_t nblk = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(k_pow_block, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v, part,
+    hipLaunchKernelGGL(k_pow_block<T>, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v, part,
                        (double *)nullptr);
     return nblk;
   }
   switch (km) {
 #define LB_KM(K) \
   case K:        \
-    launch_fused_km<K>(F, n, (int)s, v, part, st); \
+    launch_fused_km<T, K>(F, n, (int)s, v, part, st); \
     break;
     LB_KM(1) LB_KM(2) LB_KM(3) LB_KM(4) LB_KM(5) LB_KM(6) LB_KM(7) LB_KM(8)
     LB_KM(9) LB_KM(10) LB_KM(11) LB_KM(12) LB_KM(13) LB_KM(14) LB_KM(15) LB_KM(16)
@@ -307,7 +310,8 @@ int64_t launch_pow_step(const float *F, int64_t n, int64_t s, const double *v, d
   return fused_nblk(n);
 }
 
-hipError_t fit_rank1(const float *F, int64_t n, int64_t s, double *v, double *x, double *w,
+template <typename T>
+hipError_t fit_rank1(const T *F, int64_t n, int64_t s, double *v, double *x, double *w,
                      double *part, double *diff, double *sigma, int max_iters, double tol,
                      hipStream_t st, bool *converged, int *iters) {
   const int64_t nblk = (n + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -335,7 +339,7 @@ hipError_t fit_rank1(const float *F, int64_t n, int64_t s, double *v, double *x,
       break;
     }
   }
-  hipLaunchKernelGGL(k_pow_block, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v,
+  hipLaunchKernelGGL(k_pow_block<T>, dim3((unsigned)nblk), dim3(256), 0, st, F, n, s, v,
                      (double *)nullptr, x);
   hipLaunchKernelGGL(k_vec_norm, dim3(1), dim3(1024), 0, st, x, n, sigma);
   return hipGetLastError();
@@ -360,8 +364,9 @@ size_t init_ws_bytes(int64_t a, int64_t b, int64_t s) {
   return bytes;
 }
 
-hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
-                                 void *ws, hipStream_t st, InitResult *res) {
+template <typename T>
+hipError_t init_dev_impl(const T *U, const T *V, int64_t a, int64_t b, int64_t s, void *ws,
+                         hipStream_t st, InitResult *res) {
   const int64_t nmax = a > b ? a : b;
   const int64_t nblk = part_rows(nmax);
   const int64_t Wk = (s + 31) / 32;
@@ -379,8 +384,8 @@ hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int6
   res->l = l;
   res->sigma = scal;
 
-  hipLaunchKernelGGL(k_sign_words, dim3(grid_of(b, 4)), dim3(256), 0, st, U, b, s, Wk, su);
-  hipLaunchKernelGGL(k_sign_words, dim3(grid_of(a, 4)), dim3(256), 0, st, V, a, s, Wk, sv);
+  hipLaunchKernelGGL(k_sign_words<T>, dim3(grid_of(b, 4)), dim3(256), 0, st, U, b, s, Wk, su);
+  hipLaunchKernelGGL(k_sign_words<T>, dim3(grid_of(a, 4)), dim3(256), 0, st, V, a, s, Wk, sv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_iters = 2048;
@@ -397,6 +402,16 @@ hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int6
   hipLaunchKernelGGL(k_init_scales, dim3(grid_of(m, 256)), dim3(256), 0, st, xU, b, vU, xV, a, vV,
                      s, scal, h, g, l);
   return hipGetLastError();
+}
+
+hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
+                                 void *ws, hipStream_t st, InitResult *res) {
+  return init_dev_impl<float>(U, V, a, b, s, ws, st, res);
+}
+
+hipError_t init_from_factors_dev(const double *U, const double *V, int64_t a, int64_t b, int64_t s,
+                                 void *ws, hipStream_t st, InitResult *res) {
+  return init_dev_impl<double>(U, V, a, b, s, ws, st, res);
 }
 
 }  // namespace lbi

@@ -45,6 +45,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
 #include <vector>
 
 #include "../../include/lb.h"
@@ -146,6 +147,21 @@ struct InitResult {
 size_t init_ws_bytes(int64_t a, int64_t b, int64_t s);
 hipError_t init_from_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
                                  void *ws, hipStream_t st, InitResult *res);
+// The same from fp64 factors (the rotated factors of Joint-ITQ).
+hipError_t init_from_factors_dev(const double *U, const double *V, int64_t a, int64_t b, int64_t s,
+                                 void *ws, hipStream_t st, InitResult *res);
+
+// Joint-ITQ on the device.  Each returns 0 on success, otherwise an
+// lb_status value with the reason in *msg.
+//   joint_itq_dev: R (s x s, fp64 row-major, device) = the rotation after
+//     `iters` steps on X = [U; V] (U b x s, V a x s, fp32 device), started
+//     from R0 (device, fp64) or the identity when R0 is null.  Allocates its
+//     temporaries; synchronises st.
+//   rotate_factors_dev: out ((b + a) x s, fp64 device) = [U; V] R.
+int joint_itq_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s, int iters,
+                  const double *R0, double *R, hipStream_t st, std::string *msg);
+int rotate_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
+                       const double *R, double *out, hipStream_t st, std::string *msg);
 
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,

@@ -123,9 +123,35 @@ lb_status lb_get_scales(const lb_layer *L, int path, uint16_t *h, uint16_t *g, u
  * sign words and scales, and synchronises `stream` several times; returns
  * when the layer holds the new path.  LB_EUNSUPPORTED,
  * with the layer unchanged, when the iteration has not settled (a top
- * singular value of |U| or |V| not separated from the next). */
+ * singular value of |U| or |V| not separated from the next).
+ * R, when not NULL, is an s x s fp64 row-major rotation on the device (8-byte
+ * aligned, e.g. from lb_joint_itq): the path is then set from the fp64
+ * factors U R and V R instead (about 16 (a + b) s more bytes of device
+ * temporaries). */
 lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const float *V,
-                               void *stream);
+                               const double *R, void *stream);
+
+/* Joint-ITQ rotation ([LB2 column] Ch. 2): an orthogonal R between the
+ * factors leaves U V^T unchanged, so LittleBit-2 rotates U <- U R and
+ * V <- V R before binarising (pass R to lb_init_from_factors); R is found
+ * by iterating on the stacked factors X = [U; V].  Readings, stated here:
+ *   the iteration is iterative quantisation: one step sets B = sign(X R)
+ *   (sign(0) = +1), then R = the orthogonal polar factor of X^T B (the
+ *   orthogonal Procrustes solution, which minimises ||B - X R||_F), so the
+ *   loss never increases; the pages' default is 50 steps;
+ *   the start is R0 (device, s x s, fp64 row-major) or the identity when
+ *   R0 is NULL.
+ * U (b x s) and V (a x s) are fp32 row-major device arrays, read only; R
+ * receives the s x s fp64 row-major rotation (device; may be R0).  All
+ * arithmetic is fp64: the products are rocBLAS dgemm calls (atomics off,
+ * reproducible), the polar factor a Newton-Schulz iteration run until
+ * max |Z^T Z - I| <= 1e-12.  iters = 0 copies the start.  Needs
+ * 1 <= a, b <= 2^24, 1 <= s <= 4096 and (a + b) s < 2^31.  Allocates
+ * about 16 (a + b) s bytes of device temporaries, synchronises `stream`
+ * and returns when R is written.  LB_EUNSUPPORTED when X^T B is singular
+ * or nearly so (the polar factor does not settle within 200 steps). */
+lb_status lb_joint_itq(const float *U, const float *V, int64_t a, int64_t b, int64_t s, int iters,
+                       const double *R0, double *R, void *stream);
 
 /* Shape queries. */
 lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, int64_t *s, int *residual);

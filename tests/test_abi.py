@@ -81,7 +81,11 @@ def test_host_argument_errors():
     assert lib.lb_create(4, 4, 5000, 0, ctypes.byref(out)) == lbm.LB_EINVAL
     assert lib.lb_create(4, 4, 4, 0, None) == lbm.LB_EINVAL
     assert lib.lb_forward(None, None, None, 1, None) == lbm.LB_EINVAL
-    assert lib.lb_init_from_factors(None, 0, None, None, None) == lbm.LB_EINVAL
+    assert lib.lb_init_from_factors(None, 0, None, None, None, None) == lbm.LB_EINVAL
+    assert lib.lb_joint_itq(None, None, 4, 4, 4, 50, None, None, None) == lbm.LB_EINVAL
+    assert lib.lb_joint_itq(8, 8, 4, 4, 5000, 50, None, 8, None) == lbm.LB_EINVAL
+    assert lib.lb_joint_itq(8, 8, 4, 4, 4, -1, None, 8, None) == lbm.LB_EINVAL
+    assert lib.lb_joint_itq(8, 8, 4, 4, 4, 1, None, 12, None) == lbm.LB_EINVAL
     assert lib.lb_get_scales(None, 0, None, None, None) == lbm.LB_EINVAL
     assert lib.lb_stack_create(None, 0, None, 0, 1.0, ctypes.byref(out)) == lbm.LB_EINVAL
     assert b"NULL" in lib.lb_last_error() or len(lib.lb_last_error()) > 0

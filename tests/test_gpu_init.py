@@ -196,8 +196,10 @@ def test_init_argument_errors(lbm):
     L = lbm.Layer(8, 8, 4, False)
     torch = lbtest.torch_dev()
     U = torch.zeros((8, 4), dtype=torch.float32, device="cuda")
-    assert lib.lb_init_from_factors(L.handle, 1, U.data_ptr(), U.data_ptr(), None) == lbm.LB_EINVAL
-    assert lib.lb_init_from_factors(L.handle, 0, U.data_ptr() + 2, U.data_ptr(), None) == lbm.LB_EINVAL
+    p = U.data_ptr()
+    assert lib.lb_init_from_factors(L.handle, 1, p, p, None, None) == lbm.LB_EINVAL
+    assert lib.lb_init_from_factors(L.handle, 0, p + 2, p, None, None) == lbm.LB_EINVAL
+    assert lib.lb_init_from_factors(L.handle, 0, p, p, p + 4, None) == lbm.LB_EINVAL
     h = np.zeros(8, np.uint16)
     assert lib.lb_get_scales(L.handle, 0, h.ctypes.data, h.ctypes.data, h.ctypes.data) == \
         lbm.LB_ENOTREADY
