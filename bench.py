@@ -144,7 +144,21 @@ def cpu_baseline(wl: dict, M: int, budget_s: float) -> dict:
                       f"float64 numpy incl. bit unpack, {t_used:.1f} s"}
 
 
-def measure_init(torch, lbm, reps: int = 3) -> dict:
+def init_cpu_baseline(U, V) -> dict:
+    """The oracle's initialisation (one call) and Joint-ITQ (5 steps, scaled
+    to 50: every step costs the same) on the same factors, on the host."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.init_from_factors(U, V)
+    init_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.joint_itq_rotation(U, V, 5)
+    itq5_s = time.perf_counter() - t0
+    return {"init_ms": round(init_s * 1e3, 1), "joint_itq_50_ms": round(itq5_s * 10 * 1e3, 1),
+            "kind": "oracle", "sample": "one init call; Joint-ITQ timed over 5 steps x 10"}
+
+
+def measure_init(torch, lbm, reps: int = 3, with_cpu: bool = False) -> dict:
     """Initialisation of one Llama2-70B gate projection (8192 -> 28672, rank
     302) from real fp32 factors already on the device: wall time of the
     synchronous lb_init_from_factors call (sign packing, the two rank-1
@@ -177,10 +191,13 @@ def measure_init(torch, lbm, reps: int = 3) -> dict:
     L.close()
     n = a + b
     itq_flops = 50 * 4 * n * s * s  # X R and X^T B per step (Newton-Schulz products not counted)
-    return {"layer": "llama70b gate 8192->28672", "s": s, "ms_per_call": round(ms, 3),
-            "factor_bytes": (a + b) * s * 4, "joint_itq_50_ms": round(itq_ms, 3),
-            "joint_itq_gemm_tflops": round(itq_flops / (itq_ms * 1e-3) / 1e12, 3),
-            "init_rotated_ms": round(rot_ms, 3)}
+    out = {"layer": "llama70b gate 8192->28672", "s": s, "ms_per_call": round(ms, 3),
+           "factor_bytes": (a + b) * s * 4, "joint_itq_50_ms": round(itq_ms, 3),
+           "joint_itq_gemm_tflops": round(itq_flops / (itq_ms * 1e-3) / 1e12, 3),
+           "init_rotated_ms": round(rot_ms, 3)}
+    if with_cpu:
+        out["cpu_baseline"] = init_cpu_baseline(U, V)
+    return out
 
 
 def main():
@@ -276,7 +293,7 @@ def main():
                             "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1)}
     if not args.no_init:
         print("[bench] timing initialisation from real factors", file=sys.stderr, flush=True)
-        out["init"] = measure_init(torch, lbm)
+        out["init"] = measure_init(torch, lbm, with_cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 
