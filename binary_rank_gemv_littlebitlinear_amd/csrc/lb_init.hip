@@ -12,7 +12,7 @@
 //   power iteration on A = |F| (n x s, fp32 in, fp64 arithmetic), started
 //   from the all-ones direction, whose overlap with the nonnegative top
 //   right singular vector of a nonnegative matrix is positive:
-//     k_pow_fused   (s <= 1024) about 512 workgroups of consecutive rows; a
+//     k_pow_fused   (s <= 1024) about 1024 workgroups of consecutive rows; a
 //                   wave per row, lanes along k: x_r = sum_k A[r,k] v_k by a
 //                   fixed-order shuffle tree, and with the same loaded values
 //                   each lane adds A[r,k] x_r into its register share of A^T x;
@@ -21,7 +21,7 @@
 //                   block's share of A^T x by a thread per column over the
 //                   block's rows (a second, cache-served read).  Also gives
 //                   x = A v for the final step.
-//     k_pow_reduce  w_k = sum over blocks of part[.][k], 64 fixed ranges per
+//     k_pow_reduce  w_k = sum over blocks of part[.][k], 128 fixed ranges per
 //                   column combined by a fixed pairwise tree.
 //     k_pow_normalize  one workgroup: v = w / ||w||, and max |v_new - v_old|
 //                   for the host's convergence test.
@@ -169,9 +169,9 @@ __global__ void __launch_bounds__(256) k_pow_fused(const T *__restrict__ F, int6
   }
 }
 
-// w_k = sum over blocks of part[.][k]: 4 columns per workgroup, 64 fixed
+// w_k = sum over blocks of part[.][k]: 2 columns per workgroup, 128 fixed
 // block ranges per column, combined by a fixed pairwise tree.
-constexpr int kRedCols = 4;
+constexpr int kRedCols = 2;
 __global__ void __launch_bounds__(256) k_pow_reduce(const double *__restrict__ part, int64_t nblk,
                                                     int64_t s, double *__restrict__ w) {
   constexpr int G = 256 / kRedCols;
@@ -269,10 +269,11 @@ inline unsigned grid_of(int64_t n, int per) { return (unsigned)((n + per - 1) / 
 // Rank-1 fit of |F| (n x s): v (s) the unit right vector, x = |F| v (n),
 // *sigma = ||x||.  Returns the first HIP error; *converged is false when the
 // iterate still moved by more than tol after max_iters steps.
-// Rows per workgroup of the register-resident step: about two workgroups
-// per compute unit over the matrix, at least 8 rows.
+// Rows per workgroup of the register-resident step: about four workgroups
+// per compute unit over the matrix (enough waves to cover the load
+// latency; more make the partial sums cost more), at least 8 rows.
 constexpr int kFusedMaxKM = 16;
-constexpr int kFusedBlocks = 512;
+constexpr int kFusedBlocks = 1024;
 inline int fused_rpb(int64_t n) {
   const int64_t r = (n + kFusedBlocks - 1) / kFusedBlocks;
   return (int)(r < 8 ? 8 : r);
