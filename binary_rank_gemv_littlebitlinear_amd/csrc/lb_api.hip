@@ -413,6 +413,8 @@ extern "C" lb_status lb_init_from_factors(lb_layer *L, int path, const float *U,
   if (((uintptr_t)U | (uintptr_t)V) & 3u)
     return fail(LB_EINVAL, "lb_init_from_factors: U and V must be 4-byte aligned");
   if ((uintptr_t)R & 7u) return fail(LB_EINVAL, "lb_init_from_factors: R must be 8-byte aligned");
+  if (R && (Ly.a + Ly.b) * Ly.s > ((int64_t)1 << 31) - 1)
+    return fail(LB_EINVAL, "lb_init_from_factors: with R, (a + b) * s must fit in 31 bits");
   DeviceGuard dg(Ly.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk;

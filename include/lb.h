@@ -126,8 +126,8 @@ lb_status lb_get_scales(const lb_layer *L, int path, uint16_t *h, uint16_t *g, u
  * singular value of |U| or |V| not separated from the next).
  * R, when not NULL, is an s x s fp64 row-major rotation on the device (8-byte
  * aligned, e.g. from lb_joint_itq): the path is then set from the fp64
- * factors U R and V R instead (about 16 (a + b) s more bytes of device
- * temporaries). */
+ * factors U R and V R instead (one rocBLAS dgemm; about 16 (a + b) s more
+ * bytes of device temporaries; (a + b) s < 2^31). */
 lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const float *V,
                                const double *R, void *stream);
 
@@ -148,7 +148,10 @@ lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const floa
  * max |Z^T Z - I| <= 1e-12.  iters = 0 copies the start.  Needs
  * 1 <= a, b <= 2^24, 1 <= s <= 4096 and (a + b) s < 2^31.  Allocates
  * about 16 (a + b) s bytes of device temporaries, synchronises `stream`
- * and returns when R is written.  LB_EUNSUPPORTED when X^T B is singular
+ * and returns when R is written.  The library creates one rocBLAS handle
+ * per device on first use and keeps it until the process ends; calls that
+ * use it (this one and lb_init_from_factors with R) are serialised by a
+ * library-wide lock.  LB_EUNSUPPORTED when X^T B is singular
  * or nearly so (the polar factor does not settle within 200 steps). */
 lb_status lb_joint_itq(const float *U, const float *V, int64_t a, int64_t b, int64_t s, int iters,
                        const double *R0, double *R, void *stream);
