@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH):
         "lb_stack_reserve": ([vp, i64], i32),
         "lb_stack_set_mode": ([vp, i32], i32),
         "lb_stack_check": ([vp], i32),
+        "lb_stack_test_wait_failure": ([vp, i32], i32),
         "lb_stack_timeline": ([vp, vp, i64, P(i64)], i32),
         "lb_stack_destroy": ([vp], i32),
         "lb_status_str": ([i32], C.c_char_p),
@@ -81,6 +82,7 @@ EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unp
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
             "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
+            "lb_stack_test_wait_failure",
             "lb_stack_timeline", "lb_stack_destroy", "lb_status_str", "lb_last_error", "lb_version")
 
 
@@ -259,6 +261,10 @@ def lb_stack_reserve(stack: int, M: int):
 
 def lb_stack_set_mode(stack: int, mode: int):
     _check(load_library().lb_stack_set_mode(stack, int(mode)))
+
+
+def lb_stack_test_wait_failure(stack: int, enable: bool):
+    _check(load_library().lb_stack_test_wait_failure(stack, int(bool(enable))))
 
 
 def lb_stack_check(stack: int):

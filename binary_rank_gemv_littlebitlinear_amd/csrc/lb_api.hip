@@ -745,6 +745,14 @@ extern "C" lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity,
   return LB_OK;
 }
 
+extern "C" lb_status lb_stack_test_wait_failure(lb_stack *S, int enable) {
+  if (!S) return fail(LB_EINVAL, "lb_stack_test_wait_failure: NULL stack");
+  if (!S->persist)
+    return fail(LB_EUNSUPPORTED, "lb_stack_test_wait_failure: the stack has no persistent sweep");
+  persist_set_fail_test(S->persist, enable != 0);
+  return LB_OK;
+}
+
 extern "C" lb_status lb_stack_check(lb_stack *S) {
   if (!S) return fail(LB_EINVAL, "lb_stack_check: NULL stack");
   DeviceGuard dg(S->device);

@@ -23,6 +23,9 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
                       hipStream_t st, std::string *msg);
 // Diagnostics: per-phase device timestamps of every workgroup.
 void persist_set_timeline(PersistPlan *p, uint64_t *buf);
+// Failure test: later sweeps wait for a generation nobody writes, with a
+// short bound, so every wait gives up and sets the error word.
+void persist_set_fail_test(PersistPlan *p, bool on);
 int persist_grid(const PersistPlan *p);
 int persist_phases(const PersistPlan *p);
 // Synchronise and report a device-side wait timeout of an earlier launch.

@@ -57,7 +57,8 @@ constexpr int kLuMax = 2048;    // latent columns per unit
 constexpr int kStgBytes = 56 * 1024;
 constexpr int kTab2Floats = 10240;
 constexpr int kTab1Floats = 4096;
-constexpr long kSpin = 4000000;  // polls before a wait gives up
+constexpr long kSpin = 4000000;      // polls before a wait gives up
+constexpr long kSpinFailTest = 2048;  // the same in the host-requested failure test
 constexpr int kXCopies = 8;      // copies of the reduced vector; workgroup w polls copy w % 8
 
 struct alignas(16) PLayer {
@@ -125,6 +126,9 @@ struct PArgs {
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
   const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
   const PGroup *grp0;  // the first table group (a valid address for idle loads)
+  unsigned wait_skew;  // added to the generation a wait expects: 0, nonzero only in
+                       // the host-requested failure test (no wait can succeed;
+                       // each gives up after kSpinFailTest polls)
 };
 
 struct PersistPlan {
@@ -141,6 +145,7 @@ struct PersistPlan {
   uint64_t *xpart = nullptr, *xT = nullptr;
   unsigned *err = nullptr;  // 64 words; word 0 is the error word
   unsigned gen = 0;
+  bool fail_test = false;  // next sweeps: unsatisfiable waits with a short bound
   bool broken = false;
   uint64_t *timeline = nullptr;
 };
@@ -507,7 +512,7 @@ constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
 // carry gen; their values go to vals.  False on give-up or error.
 template <class Ptr, class Valid>
 __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, unsigned *err,
-                                            float (&vals)[kXLoads]) {
+                                            bool fail_test, float (&vals)[kXLoads]) {
   unsigned pend = 0;
 #pragma unroll
   for (int k = 0; k < kXLoads; ++k) {
@@ -527,7 +532,7 @@ __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, un
       }
     if (pend && (++spins & 63) == 0) {
       if (ld_u(err) != 0) return false;
-      if (spins > kSpin) {
+      if (spins > kSpin || (fail_test && spins > kSpinFailTest)) {
         atomicOr(err, 1u);
         return false;
       }
@@ -601,7 +606,8 @@ __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A, const Tab
             const int e = t + k * kXThreads;
             return &A.xpart[(size_t)(e >> 3) * kLuMax + 8 * r + (e & 7)];
           },
-          [&](int k) { return t + k * kXThreads < G * 8; }, gen, A.err, vals);
+          [&](int k) { return t + k * kXThreads < G * 8; }, gen + A.wait_skew, A.err, A.wait_skew != 0,
+          vals);
       float v = 0.f;
 #pragma unroll
       for (int k = 0; k < kXLoads; ++k) v += vals[k];
@@ -625,7 +631,8 @@ __device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A, const Tab
       const uint2 lraw = *reinterpret_cast<const uint2 *>(tp.lp[i]);  // 4 fp16 l
       float tv[kXLoads];
       ok = ok && spin_tagged([&](int k) { return &xTw[tp.tcol[i] + (k & 3)]; },
-                             [&](int k) { return k < tp.nval[i]; }, gen, A.err, tv);
+                             [&](int k) { return k < tp.nval[i]; }, gen + A.wait_skew, A.err,
+                             A.wait_skew != 0, tv);
       const float w0 = tp.nval[i] > 0 ? h2f((uint16_t)(lraw.x & 0xffffu)) * tv[0] : 0.f;
       const float w1 = tp.nval[i] > 1 ? h2f((uint16_t)(lraw.x >> 16)) * tv[1] : 0.f;
       const float w2 = tp.nval[i] > 2 ? h2f((uint16_t)(lraw.y & 0xffffu)) * tv[2] : 0.f;
@@ -693,7 +700,12 @@ k_persist(PArgs A) {
     __syncthreads();  // everyone has read the phase context before it is restaged
     // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
     if (wave_id() >= 4) stage_phase(A, ph + 1, L);
-    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A, tp)) return;
+    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A, tp)) {
+      // a wait gave up: let the next phase's copies into LDS land before
+      // the workgroup (and its LDS) ends
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
     if (tl && threadIdx.x == 0) tl[ph * 4 + 3] = __builtin_amdgcn_s_memrealtime();
   }
 }
@@ -930,6 +942,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.timeline = p->timeline;
   A.segs = p->d_segs;
   A.grp0 = p->d_groups;
+  A.wait_skew = p->fail_test ? 0x40000000u : 0u;
   hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -941,6 +954,7 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
 }
 
 void persist_set_timeline(PersistPlan *p, uint64_t *buf) { p->timeline = buf; }
+void persist_set_fail_test(PersistPlan *p, bool on) { p->fail_test = on; }
 int persist_grid(const PersistPlan *p) { return p->G; }
 int persist_phases(const PersistPlan *p) { return p->nunits + 1; }
 

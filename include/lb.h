@@ -234,6 +234,14 @@ lb_status lb_stack_check(lb_stack *S);
  * count.  buf = NULL turns recording off.  The buffer must outlive its use. */
 lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed);
 
+/* Diagnostics: test the failure path of the one-launch sweep.  With enable
+ * != 0, later persistent sweeps of this stack wait for words nobody writes,
+ * with a bound of 2048 polls, so every device-side wait gives up: the
+ * kernel ends normally, its output is undefined, and lb_stack_check then
+ * returns LB_ETIMEOUT.  enable = 0 restores normal sweeps.
+ * LB_EUNSUPPORTED when the stack has no persistent sweep. */
+lb_status lb_stack_test_wait_failure(lb_stack *S, int enable);
+
 /* Select the execution mode of lb_stack_forward: 0 = automatic (above),
  * 1 = every layer alone (as lb_forward) followed by a combine kernel per
  * unit, 2 = the one-launch sweep only (LB_EUNSUPPORTED unless M = 1 and

@@ -202,3 +202,29 @@ def test_persistent_repeated_and_deterministic(lbm):
     S.check()
     for o in outs:
         assert np.array_equal(o.cpu().numpy().view(np.uint16), y.view(np.uint16))
+
+
+def test_persistent_wait_failure_is_reported_and_recovers(lbm):
+    """Failure path of the one-launch sweep, forced from the host: every
+    device-side wait waits for words nobody writes (short bound), so the
+    kernel ends normally, lb_stack_check reports LB_ETIMEOUT, and the next
+    sweep resets the synchronisation words and is correct again."""
+    torch = lbtest.torch_dev()
+    say("[case] persistent sweep with unsatisfiable waits")
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    xd = lbtest.to_dev(x0)
+    y2 = torch.empty((1, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+    lbm.lb_stack_test_wait_failure(S.handle, True)
+    S.forward(xd, y2, None)
+    torch.cuda.synchronize()
+    with pytest.raises(lbm.LBError) as ei:
+        S.check()
+    assert ei.value.status == lbm.LB_ETIMEOUT
+    lbm.lb_stack_test_wait_failure(S.handle, False)
+    for _ in range(3):
+        S.forward(xd, y2, None)
+    torch.cuda.synchronize()
+    S.check()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
