@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama70b_mlp_stack", choices=sorted(lb_synth.WORKLOADS))
     ap.add_argument("--blocks", type=int, default=None)
+    ap.add_argument("--rows", type=int, default=None,
+                    help="override the workload's token count M (small-batch measurements)")
     ap.add_argument("--mode", type=int, default=0, help="0 auto, 1 per-layer kernels, 2 persistent")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,6 +231,8 @@ def main():
 
     def measure(name, blocks, with_cpu):
         wl = lb_synth.workload(name, blocks)
+        if args.rows is not None and name == args.workload:
+            wl["M"] = int(args.rows)
         M = wl["M"]
         print(f"[bench] building {name} ({len(wl['layers'])} matrices, M={M})", file=sys.stderr, flush=True)
         stack, t_build = build(lbm, wl)

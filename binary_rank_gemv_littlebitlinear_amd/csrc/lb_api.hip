@@ -799,6 +799,8 @@ extern "C" lb_status lb_stack_reserve(lb_stack *S, int64_t M) {
   return stack_reserve(S, M);
 }
 
+constexpr int64_t kPersistLoopRows = 4;
+
 extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                                       void *stream) {
   if (!S) return fail(LB_EINVAL, "lb_stack_forward: NULL stack");
@@ -826,6 +828,19 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     lb_status ps = persist_run(S->persist, (const uint16_t *)x0, (uint16_t *)y, (uint16_t *)trace, M,
                                st, &msg);
     if (ps != LB_OK) return fail(ps, msg);
+    return LB_OK;
+  }
+  // a few rows without a trace: one batch-1 sweep per row beats the
+  // per-layer kernels up to about four rows (rows are independent, so each
+  // row's result is exactly its batch-1 result)
+  if (S->persist && S->mode == 0 && !trace && M <= kPersistLoopRows) {
+    const int64_t a0 = S->layers[0]->ly.a, bl = S->layers.back()->ly.b;
+    for (int64_t m = 0; m < M; ++m) {
+      std::string msg;
+      lb_status ps = persist_run(S->persist, (const uint16_t *)x0 + m * a0, (uint16_t *)y + m * bl,
+                                 nullptr, 1, st, &msg);
+      if (ps != LB_OK) return fail(ps, msg);
+    }
     return LB_OK;
   }
   lb_status rs = stack_reserve(S, M);

@@ -207,7 +207,9 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               workgroups through device memory with bounded waits (a
  *               wait that gives up sets a flag lb_stack_check reports);
  *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
- *               per unit;
+ *               per unit; except that for M <= 4 without a trace the
+ *               one-launch sweep runs once per row (faster at these M; each
+ *               row's output is exactly its M = 1 output);
  *   M >= 64     two matrix-core launches per unit, the combine fused into
  *               the second.
  * x0, y and trace must be 16-byte aligned; y must not overlap x0. */

@@ -228,3 +228,32 @@ def test_persistent_wait_failure_is_reported_and_recovers(lbm):
     torch.cuda.synchronize()
     S.check()
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_small_batch_without_trace_runs_rows_as_batch1(lbm, M):
+    """For M <= 4 without a trace the automatic mode runs the batch-1 sweep
+    once per row: every row equals its own M = 1 result bit for bit (the
+    M = 1 sweep is checked against the oracle above), and the batch agrees
+    at the parity bar with the per-layer kernels that the same M uses when a
+    trace is asked for."""
+    torch = lbtest.torch_dev()
+    say(f"[case] small batch without trace M={M}")
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    x0, yt, tr = run_stack(lbm, wl, S, M)
+    check_stack(wl, paths, x0, yt, tr, M, sample=[0, 2, 5])
+    b_last = wl["layers"][-1]["b"]
+    xd = lbtest.to_dev(x0)
+    y = torch.empty((M, b_last), dtype=torch.float16, device="cuda")
+    S.forward(xd, y, None)
+    rows = []
+    for m in range(M):
+        ym = torch.empty((1, b_last), dtype=torch.float16, device="cuda")
+        S.forward(xd[m:m + 1].contiguous(), ym, None)
+        rows.append(ym)
+    torch.cuda.synchronize()
+    S.check()
+    got = y.cpu().numpy()
+    for m in range(M):
+        assert np.array_equal(got[m:m + 1].view(np.uint16), rows[m].cpu().numpy().view(np.uint16))
+    assert_parity(got, yt.astype(np.float64), f"per-row sweeps vs per-layer kernels M={M}")
