@@ -96,7 +96,6 @@ struct MfmaPlan;
 struct lb_layer {
   lbi::Layer ly;
   void *ctx = nullptr;  // the device context (workspace owner)
-  void *plan = nullptr; // single-layer persistent plan (M = 1), may be null
   lbi::MfmaPlan *mplan = nullptr;  // the layer as a one-layer MFMA unit
 };
 
