@@ -35,7 +35,9 @@
 // workgroup w reads copy w % kXCopies.  Every exchanged word is a
 // 64-bit value | generation pair written and read with relaxed
 // device-coherent (sc1) atomics, so a reader knows a word is current from
-// the word itself and no flag (or store-completion wait) is needed.
+// the word itself and no flag (or store-completion wait) is needed.  A
+// launch takes its generation base from the tags the previous launch left,
+// so a launch captured into a graph and replayed stays correct.
 // Every wait is bounded: on timeout a device error word is set, all
 // workgroups leave, and lb_stack_check returns LB_ETIMEOUT.
 #include <hip/hip_fp16.h>
@@ -119,7 +121,6 @@ struct PArgs {
   const uint16_t *x0;
   uint16_t *y;
   uint16_t *trace;  // may be null
-  unsigned gen_base;
   uint64_t *xpart;  // [G][kLuMax] tagged partials (value bits | generation << 32)
   uint64_t *xT;     // [kXCopies][kLuMax] tagged reduced latent (copies of one vector)
   unsigned *err;
@@ -144,7 +145,6 @@ struct PersistPlan {
   std::vector<PLayer> h_layers;
   uint64_t *xpart = nullptr, *xT = nullptr;
   unsigned *err = nullptr;  // 64 words; word 0 is the error word
-  unsigned gen = 0;
   bool fail_test = false;  // next sweeps: unsatisfiable waits with a short bound
   bool broken = false;
   uint64_t *timeline = nullptr;
@@ -165,9 +165,10 @@ __device__ __forceinline__ float ld_f(float *p) {
 __device__ __forceinline__ void st_f(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// A tagged word: fp32 value bits in the low half, the generation (phase
-// number of the sweep, never 0) in the high half; one aligned 64-bit
-// atomic store, so a reader sees the old word or the new one.
+// A tagged word: fp32 value bits in the low half, the generation in the
+// high half (a running phase count carried from launch to launch in the
+// tags themselves, plus the phase plus 1); one aligned 64-bit atomic
+// store, so a reader sees the old word or the new one.
 __device__ __forceinline__ void st_tag(uint64_t *p, float v, unsigned gen) {
   __hip_atomic_store(p, (uint64_t)__float_as_uint(v) | ((uint64_t)gen << 32), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -666,6 +667,12 @@ k_persist(PArgs A) {
   }
   const int w = blockIdx.x;
   const int U = A.nunits;
+  // the generation base: the tag of this workgroup's first partial word,
+  // which the previous launch's last exchange wrote as its base + U (every
+  // exchange writes it; zero after a reset), so launches, captured graph
+  // replays included, continue one running count
+  const unsigned gen_base = __builtin_amdgcn_readfirstlane(
+      (unsigned)(ld_tag(&A.xpart[(size_t)w * kLuMax]) >> 32));
   uint64_t *tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * 4 : nullptr;
   // phase 0's copy list (kMaxSeg records of two 16-byte words), then its blocks
   for (int i = threadIdx.x; i < kMaxSeg * 2; i += kThreads)
@@ -700,7 +707,7 @@ k_persist(PArgs A) {
     __syncthreads();  // everyone has read the phase context before it is restaged
     // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
     if (wave_id() >= 4) stage_phase(A, ph + 1, L);
-    if (!exchange(L, Lu, A.gen_base + (unsigned)ph + 1u, A, tp)) {
+    if (!exchange(L, Lu, gen_base + (unsigned)ph + 1u, A, tp)) {
       // a wait gave up: let the next phase's copies into LDS land before
       // the workgroup (and its LDS) ends
       __builtin_amdgcn_s_waitcnt(0);
@@ -925,7 +932,6 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
         hipMemset(p->xpart, 0, sizeof(uint64_t) * (size_t)p->G * kLuMax) != hipSuccess ||
         hipMemset(p->xT, 0, sizeof(uint64_t) * kXCopies * kLuMax) != hipSuccess)
       return LB_EHIP;
-    p->gen = 0;
     p->broken = false;
   }
   PArgs A{};
@@ -935,7 +941,6 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.x0 = x0;
   A.y = y;
   A.trace = trace;
-  A.gen_base = p->gen;
   A.xpart = p->xpart;
   A.xT = p->xT;
   A.err = p->err;
@@ -949,7 +954,6 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
     if (msg) *msg = std::string("persistent launch: ") + hipGetErrorString(e);
     return LB_EHIP;
   }
-  p->gen += (unsigned)p->nunits;
   return LB_OK;
 }
 

@@ -41,6 +41,11 @@
  *     lb_stack_reserve or by an earlier call.  Calls that use one layer or
  *     stack must be ordered on one stream: they share the object's device
  *     workspace.
+ *   - Without a trace, lb_forward and lb_stack_forward (M within the rows
+ *     already reserved) only launch kernels, so they can be captured into a
+ *     HIP graph and replayed; the one-launch sweep carries its exchange
+ *     generation from launch to launch on the device, so every replay is a
+ *     fresh launch.
  */
 #ifndef LB_H
 #define LB_H
