@@ -584,18 +584,25 @@ __device__ TabPlan load_tables(const PArgs &A, const Lds &L, bool live) {
   return T;
 }
 
-__device__ bool exchange(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp) {
-  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
-  const bool xw = t < kXThreads;
+// First half of the exchange: this workgroup's partials, tagged.
+__device__ void exchange_publish(const Lds &L, int Lu, unsigned gen, const PArgs &A) {
+  const int w = blockIdx.x, t = threadIdx.x;
   const int nsl = (Lu + 7) / 8;
-  bool ok = true;
-  if (xw) {
+  if (t < kXThreads) {
 #pragma unroll
     for (int k = 0; k < kXLoads; ++k) {
       const int c = t + k * kXThreads;
       if (c < nsl * 8) st_tag(&A.xpart[(size_t)w * kLuMax + c], c < Lu ? L.part[c] : 0.f, gen);
     }
   }
+}
+
+// Second half: the owned slices' sums, then the all-gather into the tables.
+__device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp) {
+  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+  const bool xw = t < kXThreads;
+  const int nsl = (Lu + 7) / 8;
+  bool ok = true;
   for (int r = w; r < nsl; r += G) {
     // word k of thread t: element e = 256 k + t of the (producer, column)
     // grid, producer e / 8, column 8 r + e % 8.  Thread t sums column t % 8
@@ -705,9 +712,13 @@ k_persist(PArgs A) {
     const int Lu = L.ctx->ub.Lu;
     if (tl && threadIdx.x == 0) tl[ph * 4 + 2] = __builtin_amdgcn_s_memrealtime();
     __syncthreads();  // everyone has read the phase context before it is restaged
-    // next phase's blocks: copied by waves 4-7 while waves 0-3 exchange
+    const unsigned gen = gen_base + (unsigned)ph + 1u;
+    exchange_publish(L, Lu, gen, A);
+    // the partials, on the critical path, are issued before the next
+    // phase's block copies (waves 4-7), which then overlap the waits
+    __syncthreads();
     if (wave_id() >= 4) stage_phase(A, ph + 1, L);
-    if (!exchange(L, Lu, gen_base + (unsigned)ph + 1u, A, tp)) {
+    if (!exchange_collect(L, Lu, gen, A, tp)) {
       // a wait gave up: let the next phase's copies into LDS land before
       // the workgroup (and its LDS) ends
       __builtin_amdgcn_s_waitcnt(0);
