@@ -598,6 +598,7 @@ __device__ void exchange_publish(const Lds &L, int Lu, unsigned gen, const PArgs
 }
 
 // Second half: the owned slices' sums, then the all-gather into the tables.
+static_assert(kXThreads == 4 * 64 && kXCopies <= 8, "the slice sum adds four waves; t < 64 stores");
 __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp) {
   const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
   const bool xw = t < kXThreads;
@@ -606,7 +607,9 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   for (int r = w; r < nsl; r += G) {
     // word k of thread t: element e = 256 k + t of the (producer, column)
     // grid, producer e / 8, column 8 r + e % 8.  Thread t sums column t % 8
-    // over its producers in k order; the tree below then sums the threads.
+    // over its producers in k order, shuffles (xor 32, 16, 8) sum the eight
+    // lanes of a wave that share the column, and the four waves' sums are
+    // added in wave order: a fixed order, with one barrier.
     if (xw) {
       float vals[kXLoads];
       ok = ok && spin_tagged(
@@ -619,16 +622,18 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
       float v = 0.f;
 #pragma unroll
       for (int k = 0; k < kXLoads; ++k) v += vals[k];
-      L.red[t] = v;
+      v += __shfl_xor(v, 32, 64);
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 8, 64);
+      if ((t & 63) < 8) L.red[(t >> 6) * 8 + (t & 7)] = v;
     }
     __syncthreads();
-    for (int st = kXThreads / 2; st >= 8; st >>= 1) {
-      if (t < st) L.red[t] += L.red[t + st];
-      __syncthreads();
+    if (t < 8 * kXCopies) {
+      const int c = t & 7;
+      const float sum = (L.red[c] + L.red[8 + c]) + (L.red[16 + c] + L.red[24 + c]);
+      st_tag(&A.xT[(size_t)(t >> 3) * kLuMax + 8 * r + c], sum, gen);
     }
-    // every copy gets the 8 sums (one 64-byte line per copy), so each line
-    // is polled by G / kXCopies workgroups rather than all of them
-    if (t < 8 * kXCopies) st_tag(&A.xT[(size_t)(t >> 3) * kLuMax + 8 * r + (t & 7)], L.red[t & 7], gen);
+    if (r + G < nsl) __syncthreads();
   }
   // all-gather, straight into the next phase's tables: w = l * t per group
   uint64_t *xTw = A.xT + (size_t)(w % kXCopies) * kLuMax;
