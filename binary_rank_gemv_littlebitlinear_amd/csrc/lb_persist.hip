@@ -185,17 +185,6 @@ __device__ __forceinline__ void my_tiles(int tiles, int G, int w, int &t0, int &
 }
 
 // Block-wide AND through LDS only (waits on LDS, never on global memory).
-__device__ __forceinline__ bool block_all(bool ok, int *flags8) {
-  const int wok = __all(ok);
-  if ((threadIdx.x & 63) == 0) flags8[wave_id()] = wok;
-  __syncthreads();
-  int r = 1;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) r &= flags8[i];
-  __syncthreads();
-  return r != 0;
-}
-
 // ------------------------------------------------------ LDS arrangement
 // Everything a phase reads besides its tables lives in LDS: the staged
 // sign bits and scales, and a copy of the descriptors of the two units the
@@ -655,7 +644,17 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
       for (int hi = 0; hi < 4; ++hi) table_quad(tab, w0, w1, w2, w3, hi);
     }
   }
-  return block_all(ok, L.flags8);
+  // one barrier ends the exchange and starts the next phase: waves 4-7 wait
+  // for their copies first, and the per-wave flags are next written a
+  // phase later, after the products' barriers
+  if (wave_id() >= 4) __builtin_amdgcn_s_waitcnt(0);
+  const int wok = __all(ok);
+  if ((t & 63) == 0) L.flags8[wave_id()] = wok;
+  __syncthreads();
+  int all = 1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) all &= L.flags8[i];
+  return all != 0;
 }
 
 // --------------------------------------------------------------- kernel
@@ -690,12 +689,17 @@ k_persist(PArgs A) {
   for (int i = threadIdx.x; i < kMaxSeg * 2; i += kThreads)
     reinterpret_cast<uint4 *>(L.segbuf)[i] = reinterpret_cast<const uint4 *>(A.segs)[i];
   __syncthreads();
-  if (wave_id() >= 4) stage_phase(A, 0, L);
+  if (wave_id() >= 4) {
+    stage_phase(A, 0, L);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
   for (int ph = 0; ph <= U; ++ph) {
-    if (wave_id() >= 4) __builtin_amdgcn_s_waitcnt(0);  // this phase's staged blocks landed
-    __syncthreads();
     if (tl && threadIdx.x == 0) tl[ph * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+    // every context field the phase uses is read before first_product's
+    // last barrier, after which waves 4-7 restage the context
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
+    const int Lu = L.ctx->ub.Lu;
     // this thread's share of the next phase's tables (built in the
     // exchange), planned now so the reads overlap the products
     const TabPlan tp = load_tables(A, L, ph < U);
@@ -714,9 +718,7 @@ k_persist(PArgs A) {
       if (ph == U) break;
     }
     first_product(L);
-    const int Lu = L.ctx->ub.Lu;
     if (tl && threadIdx.x == 0) tl[ph * 4 + 2] = __builtin_amdgcn_s_memrealtime();
-    __syncthreads();  // everyone has read the phase context before it is restaged
     const unsigned gen = gen_base + (unsigned)ph + 1u;
     exchange_publish(L, Lu, gen, A);
     // the partials, on the critical path, are issued before the next
