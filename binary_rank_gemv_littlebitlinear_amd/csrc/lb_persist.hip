@@ -89,7 +89,9 @@ struct alignas(16) PUnit {
   int64_t trace_x;  // element offset of this unit's input in the trace
   const PGroup *grp;  // the unit's table groups, in table order
   int ngrp;
-  int pad_;
+  // first product: adjacent columns per thread for workgroups with nt0 row
+  // tiles (bits 0-7) and with nt0 + 1 (bits 8-15); nt0 in bits 16-31
+  int cpt;
 };
 
 // One block a workgroup copies into LDS for a phase: src + t0 * stride,
@@ -198,6 +200,33 @@ struct PhaseCtx {
   int s2_off[kMaxUnitLayers], h_off[kMaxUnitLayers], l_off[kMaxUnitLayers];
   int s1_off[kMaxUnitLayers], g_off[kMaxUnitLayers];
 };
+
+// The LDS regions after the context start at multiples of 64 bytes, so a
+// 16-entry table's address has its entry index in bits 2..5 (or-ed in).
+constexpr size_t kCtxBytes = (sizeof(PhaseCtx) + 63) / 64 * 64;
+static_assert((2 * kMaxSeg * sizeof(PSeg)) % 64 == 0 && kStgBytes % 64 == 0 && (kTab2Floats * 4) % 64 == 0,
+              "table regions 64-byte aligned");
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+__device__ __forceinline__ float lds_f32(uint32_t a) {
+  return *(const __attribute__((address_space(3))) float *)(uintptr_t)a;
+}
+__device__ __forceinline__ uint32_t lds_u32(uint32_t a) {
+  return *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)a;
+}
+__device__ __forceinline__ uint2 lds_u64(uint32_t a) {
+  typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+  const u2v v = *(const __attribute__((address_space(3))) u2v *)(uintptr_t)a;
+  return make_uint2(v.x, v.y);
+}
+// Byte offset of entry (w >> sh) & 15 of a 16-float table.
+template <int sh>
+__device__ __forceinline__ uint32_t nib_off(uint32_t w) {
+  if constexpr (sh >= 2) return (w >> (sh - 2)) & 0x3cu;
+  else return (w << (2 - sh)) & 0x3cu;
+}
 
 struct Lds {
   unsigned char *stg;  // kStgBytes staged bits and scales of the phase
@@ -405,6 +434,84 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   __syncthreads();
 }
 
+// The first product's lookups: a thread takes CPT adjacent columns of one
+// layer (CPT divides every layer's column count, so a group never spans
+// two layers), and lpt lanes split the group's nt 16-row words; one LDS
+// read gives a tile's bits of all CPT columns.  Per column and tile the four
+// entries are summed as ((q0 + q1) + (q2 + q3)) and added in tile order.
+template <int CPT>
+__device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLayer *LB, int nb,
+                                           int Lu, int nt, int Pu,
+                                           const int (&col0m)[kMaxUnitLayers]) {
+  const int ngr = Lu / CPT;
+  int lpt = 1, lg = 0;
+  while (lpt < 64 && lpt < nt && ngr * lpt * 2 <= kThreads) {
+    lpt *= 2;
+    ++lg;
+  }
+  const int sub = threadIdx.x & (lpt - 1);
+  const uint32_t taba = lds_addr(L.tab1), stga = lds_addr(L.stg);
+  constexpr uint32_t kTileBytes = 256u;  // tables of one pair and tile: 4 x 16 floats
+  for (int q0 = 0; q0 < ngr; q0 += kThreads >> lg) {
+    const int q = q0 + ((int)threadIdx.x >> lg);
+    float acc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
+    if (q < ngr) {
+      const int c = q * CPT;
+      int m = 0;
+#pragma unroll
+      for (int i = 1; i < kMaxUnitLayers; ++i)
+        if (i < nb && col0m[i] <= c) m = i;
+      const PLayer &Ly = LB[m];
+      const int cl = c - Ly.col0, s = Ly.s, Lp = Ly.Lp, s1o = C.s1_off[m];
+      const uint32_t wa = stga + (uint32_t)(s1o + 2 * cl), wstride = 2u * (uint32_t)Lp;
+      uint32_t tq[CPT];  // the column's tile-0 tables (its path's)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        tq[j] = taba + kTileBytes * (uint32_t)((m * Pu + (cl + j < s ? 0 : 1)) * nt);
+      for (int g0 = sub; g0 < nt; g0 += 2 * lpt) {
+        uint32_t wd[2][(CPT + 1) / 2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t a = wa + (uint32_t)min(g0 + i * lpt, nt - 1) * wstride;
+          if constexpr (CPT == 4) {
+            const uint2 v = lds_u64(a);
+            wd[i][0] = v.x;
+            wd[i][1] = v.y;
+          } else if constexpr (CPT == 2) {
+            wd[i][0] = lds_u32(a);
+          } else {
+            wd[i][0] = *(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)a;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int gi = g0 + i * lpt;
+          const uint32_t toff = kTileBytes * (uint32_t)min(gi, nt - 1);
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) {
+            const uint32_t w = wd[i][j >> 1], tb = tq[j] + toff;
+            float e;
+            if ((j & 1) == 0)
+              e = (lds_f32(tb | nib_off<0>(w)) + lds_f32((tb | nib_off<4>(w)) + 64)) +
+                  (lds_f32((tb | nib_off<8>(w)) + 128) + lds_f32((tb | nib_off<12>(w)) + 192));
+            else
+              e = (lds_f32(tb | nib_off<16>(w)) + lds_f32((tb | nib_off<20>(w)) + 64)) +
+                  (lds_f32((tb | nib_off<24>(w)) + 128) + lds_f32((tb | nib_off<28>(w)) + 192));
+            acc[j] += gi < nt ? e : 0.f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      for (int o = 1; o < lpt; o <<= 1) acc[j] += __shfl_xor(acc[j], o, 64);
+      if (sub == 0 && q < ngr) L.part[q * CPT + j] = acc[j];
+    }
+  }
+}
+
 // First product of unit B over the workgroup's rows: part[col] for every
 // latent column of every layer of the unit.
 __device__ void first_product(Lds &L) {
@@ -441,47 +548,11 @@ __device__ void first_product(Lds &L) {
   int col0m[kMaxUnitLayers];
 #pragma unroll
   for (int m = 0; m < kMaxUnitLayers; ++m) col0m[m] = LB[m].col0;
+  const int cpt = nt == (U.cpt >> 16) ? (U.cpt & 255) : ((U.cpt >> 8) & 255);
   __syncthreads();
-  // lookups: column c of the unit; lpt lanes split its nt words
-  int lpt = 1, lg = 0;
-  while (lpt < 64 && lpt < nt && Lu * lpt * 2 <= kThreads) {
-    lpt *= 2;
-    ++lg;
-  }
-  const int sub = threadIdx.x & (lpt - 1);
-  for (int c0 = 0; c0 < Lu; c0 += kThreads >> lg) {
-    const int c = c0 + ((int)threadIdx.x >> lg);
-    float acc = 0.f;
-    if (c < Lu) {
-      int m = 0;
-#pragma unroll
-      for (int i = 1; i < kMaxUnitLayers; ++i)
-        if (i < nb && col0m[i] <= c) m = i;
-      // the layer's fields by an indexed LDS read (no select chains)
-      const PLayer &Ly = LB[m];
-      const int cl = c - Ly.col0, s = Ly.s, Lp = Ly.Lp, s1o = C.s1_off[m];
-      const int p = cl < s ? 0 : 1;
-      const uint16_t *bits = reinterpret_cast<const uint16_t *>(L.stg + s1o) + cl;
-      const float *tb = L.tab1 + (m * Pu + p) * quads * 16;
-      // the lane's words gi = sub, sub + lpt, ... < nt, four per step; every
-      // read is unconditional (index clamped, result masked)
-      for (int g0 = sub; g0 < nt; g0 += 4 * lpt) {
-        uint32_t wds[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wds[i] = bits[min(g0 + i * lpt, nt - 1) * Lp];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gi = g0 + i * lpt;
-          const float *tq = tb + min(gi, nt - 1) * 64;
-          const float e = (tq[wds[i] & 15u] + tq[16 + ((wds[i] >> 4) & 15u)]) +
-                          (tq[32 + ((wds[i] >> 8) & 15u)] + tq[48 + ((wds[i] >> 12) & 15u)]);
-          acc += gi < nt ? e : 0.f;
-        }
-      }
-    }
-    for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
-    if (sub == 0 && c < Lu) L.part[c] = acc;
-  }
+  if (cpt == 4) s1_lookups<4>(L, C, LB, nb, Lu, nt, Pu, col0m);
+  else if (cpt == 2) s1_lookups<2>(L, C, LB, nb, Lu, nt, Pu, col0m);
+  else s1_lookups<1>(L, C, LB, nb, Lu, nt, Pu, col0m);
   __syncthreads();
 }
 
@@ -498,24 +569,25 @@ __device__ void first_product(Lds &L) {
 // spin is bounded and checks the error word every 64 rounds.
 constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
 
-// Wait (per thread) until the words at p(k), k < kXLoads with valid(k),
+// Wait (per thread) until the words at p(k), k < N with valid(k),
 // carry gen; their values go to vals.  False on give-up or error.
-template <class Ptr, class Valid>
+template <class Ptr, class Valid, int N>
 __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, unsigned *err,
-                                            bool fail_test, float (&vals)[kXLoads]) {
+                                            bool fail_test, float (&vals)[N]) {
+  static_assert(N <= 32, "one pending bit per word");
   unsigned pend = 0;
 #pragma unroll
-  for (int k = 0; k < kXLoads; ++k) {
+  for (int k = 0; k < N; ++k) {
     vals[k] = 0.f;
     if (valid(k)) pend |= 1u << k;
   }
   long spins = 0;
   while (pend) {
-    uint64_t wds[kXLoads];
+    uint64_t wds[N];
 #pragma unroll
-    for (int k = 0; k < kXLoads; ++k) wds[k] = ((pend >> k) & 1u) ? ld_tag(p(k)) : 0ull;
+    for (int k = 0; k < N; ++k) wds[k] = ((pend >> k) & 1u) ? ld_tag(p(k)) : 0ull;
 #pragma unroll
-    for (int k = 0; k < kXLoads; ++k)
+    for (int k = 0; k < N; ++k)
       if (((pend >> k) & 1u) && (unsigned)(wds[k] >> 32) == gen) {
         vals[k] = __uint_as_float((unsigned)wds[k]);
         pend &= ~(1u << k);
@@ -627,18 +699,23 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   // all-gather, straight into the next phase's tables: w = l * t per group
   uint64_t *xTw = A.xT + (size_t)(w % kXCopies) * kLuMax;
   if (xw) {
+    uint2 lraw[kGroupsPerThread];  // 4 fp16 l per group
+#pragma unroll
+    for (int i = 0; i < kGroupsPerThread; ++i)
+      lraw[i] = i < tp.n ? *reinterpret_cast<const uint2 *>(tp.lp[i]) : make_uint2(0u, 0u);
+    // every group's words in one wait, so a thread with several groups
+    // polls them together rather than one round trip after another
+    float tv[4 * kGroupsPerThread];
+    ok = ok && spin_tagged([&](int k) { return &xTw[tp.tcol[k >> 2] + (k & 3)]; },
+                           [&](int k) { return (k >> 2) < tp.n && (k & 3) < tp.nval[k >> 2]; },
+                           gen + A.wait_skew, A.err, A.wait_skew != 0, tv);
 #pragma unroll
     for (int i = 0; i < kGroupsPerThread; ++i) {
       if (i >= tp.n) break;
-      const uint2 lraw = *reinterpret_cast<const uint2 *>(tp.lp[i]);  // 4 fp16 l
-      float tv[kXLoads];
-      ok = ok && spin_tagged([&](int k) { return &xTw[tp.tcol[i] + (k & 3)]; },
-                             [&](int k) { return k < tp.nval[i]; }, gen + A.wait_skew, A.err,
-                             A.wait_skew != 0, tv);
-      const float w0 = tp.nval[i] > 0 ? h2f((uint16_t)(lraw.x & 0xffffu)) * tv[0] : 0.f;
-      const float w1 = tp.nval[i] > 1 ? h2f((uint16_t)(lraw.x >> 16)) * tv[1] : 0.f;
-      const float w2 = tp.nval[i] > 2 ? h2f((uint16_t)(lraw.y & 0xffffu)) * tv[2] : 0.f;
-      const float w3 = tp.nval[i] > 3 ? h2f((uint16_t)(lraw.y >> 16)) * tv[3] : 0.f;
+      const float w0 = tp.nval[i] > 0 ? h2f((uint16_t)(lraw[i].x & 0xffffu)) * tv[4 * i] : 0.f;
+      const float w1 = tp.nval[i] > 1 ? h2f((uint16_t)(lraw[i].x >> 16)) * tv[4 * i + 1] : 0.f;
+      const float w2 = tp.nval[i] > 2 ? h2f((uint16_t)(lraw[i].y & 0xffffu)) * tv[4 * i + 2] : 0.f;
+      const float w3 = tp.nval[i] > 3 ? h2f((uint16_t)(lraw[i].y >> 16)) * tv[4 * i + 3] : 0.f;
       float *tab = L.tab2 + tp.dst[i];
 #pragma unroll
       for (int hi = 0; hi < 4; ++hi) table_quad(tab, w0, w1, w2, w3, hi);
@@ -665,7 +742,7 @@ k_persist(PArgs A) {
   Lds L;
   {
     unsigned char *p = smem;
-    L.ctx = reinterpret_cast<PhaseCtx *>(p); p += (sizeof(PhaseCtx) + 15) / 16 * 16;
+    L.ctx = reinterpret_cast<PhaseCtx *>(p); p += kCtxBytes;
     L.segbuf = reinterpret_cast<PSeg *>(p); p += 2 * kMaxSeg * sizeof(PSeg);
     L.stg = p; p += kStgBytes;
     L.tab2 = reinterpret_cast<float *>(p); p += kTab2Floats * 4;
@@ -737,12 +814,44 @@ k_persist(PArgs A) {
 
 // ------------------------------------------------------------------ host
 static size_t lds_bytes() {
-  return (sizeof(PhaseCtx) + 15) / 16 * 16 + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
+  return kCtxBytes + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
          (size_t)(kTab2Floats + kTab1Floats + kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
                   16 * kTMax + kXThreads + kWaves) * 4 + 64;
 }
 
 int64_t persist_max_rows() { return 1; }
+
+// Column-group width for the first product's lookups of a unit with Lu
+// columns on nt row tiles: among 1, 2, 4 (up to maxc, which divides every
+// layer's column count), the one whose busiest SIMD issues the fewest
+// instructions.  Lanes are ngr lpt (lpt by the kernel's rule); passes of
+// kThreads lanes; wave w runs on SIMD w % 4; a lane's pass costs about 40
+// instructions plus 16 per column and word slot (two slots per step).
+static int s1_width(int maxc, int Lu, int nt) {
+  int best = 1;
+  long best_cost = -1;
+  for (int c = 1; c <= maxc; c *= 2) {
+    const int ngr = Lu / c;
+    int lpt = 1;
+    while (lpt < 64 && lpt < nt && ngr * lpt * 2 <= kThreads) lpt *= 2;
+    const int wpl = (nt + lpt - 1) / lpt, slots = (wpl + 1) / 2 * 2;
+    const long per = 40 + 16L * c * slots;
+    const int N = ngr * lpt;
+    int worst = 0;
+    for (int s = 0; s < 4; ++s) {
+      int passes = 0;
+      for (int w = s; w < kWaves; w += 4)
+        if (N > w * 64) passes += (N - w * 64 + kThreads - 1) / kThreads;
+      worst = std::max(worst, passes);
+    }
+    const long cost = worst * per;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
 
 lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector<int> &unit_begin,
                         const std::vector<int> &unit_size, float kappa, int device,
@@ -789,6 +898,13 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     }
     U.Lu = col;
     if (U.Lu > kLuMax) return unsupported();
+    // column groups must divide every layer's column count P s (the
+    // layers' first columns are then multiples of them too)
+    int maxc = 4;
+    for (int m = 0; m < U.n; ++m)
+      while ((int)layers[U.first + m]->ly.L % maxc != 0) maxc /= 2;
+    const int tiles = (U.a + 15) / 16, nt0 = tiles / G;
+    U.cpt = s1_width(maxc, U.Lu, nt0) | (s1_width(maxc, U.Lu, nt0 + 1) << 8) | (nt0 << 16);
     for (int m = 1; m < U.n; ++m)  // the products assume one path count per unit
       if (layers[U.first + m]->ly.P != L0.P) return unsupported();
     P->h_units.push_back(U);
