@@ -331,6 +331,22 @@ __device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float
   *reinterpret_cast<float4 *>(tab + 4 * hi) = e;
 }
 
+// ceil(2^32 / n) for 1 <= n <= kTMax (the division for larger n).
+__device__ __forceinline__ uint64_t ceil_recip32(int n) {
+  static_assert(kTMax == 8, "constants for n <= 8");
+  switch (n) {
+    case 1: return 0x100000000ull;
+    case 2: return 0x80000000ull;
+    case 3: return 0x55555556ull;
+    case 4: return 0x40000000ull;
+    case 5: return 0x33333334ull;
+    case 6: return 0x2aaaaaabull;
+    case 7: return 0x24924925ull;
+    case 8: return 0x20000000ull;
+    default: return (0x100000000ull + (unsigned)n - 1) / (unsigned)n;
+  }
+}
+
 // ----------------------------------------------------------- products
 // The phase context lives in LDS.  Every function below first loads the
 // context fields it needs for all layers at once (unconditional loads, so
@@ -360,8 +376,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       lpt *= 2;
       ++lg;
     }
-    // ceil(2^32 / nt) needs 33 bits for nt = 1: the product is taken in 64 bits
-    const uint64_t magic = (0x100000000ull + (unsigned)nt - 1) / (unsigned)nt;
+    // ceil(2^32 / nt) (33 bits for nt = 1: the product is taken in 64 bits),
+    // from a constant for nt <= kTMax rather than a 64-bit division
+    const uint64_t magic = ceil_recip32(nt);
     const int sub = threadIdx.x & (lpt - 1);
     for (int tk0 = 0; tk0 < ntk; tk0 += kThreads >> lg) {
       const int tk = tk0 + ((int)threadIdx.x >> lg);
