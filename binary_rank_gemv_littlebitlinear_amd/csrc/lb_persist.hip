@@ -181,9 +181,11 @@ __device__ __forceinline__ uint64_t ld_tag(uint64_t *p) {
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // 16-row tiles [t0, t1) owned by workgroup w out of `tiles`.
+// tiles <= kTMax G (checked when the plan is built), so tiles (w + 1) fits
+// in 32 bits and the division is a 32-bit one.
 __device__ __forceinline__ void my_tiles(int tiles, int G, int w, int &t0, int &t1) {
-  t0 = (int)(((long)tiles * w) / G);
-  t1 = (int)(((long)tiles * (w + 1)) / G);
+  t0 = (int)((unsigned)(tiles * w) / (unsigned)G);
+  t1 = (int)((unsigned)(tiles * (w + 1)) / (unsigned)G);
 }
 
 // Block-wide AND through LDS only (waits on LDS, never on global memory).
