@@ -165,8 +165,12 @@ def _odd_stack(lbm, seed=5):
     return wl, lbm.Stack(layers, units, lb_synth.kappa(2)), paths
 
 
+# The first product's column width (1, 2 or 4 per thread) is chosen per unit:
+# the 70B MLP stack takes 2 (gate/up) and 1 (down), the 7B full block 4 (the
+# attention units) and 2 (its MLP), tiny_256 1.
 @pytest.mark.parametrize("name,blocks", [("llama7b_mlp_stack", 3), ("llama70b_mlp_stack", 2),
-                                         ("llama7b_attn_proj_4096", 1), ("tiny_256", 1)])
+                                         ("llama7b_attn_proj_4096", 1), ("tiny_256", 1),
+                                         ("llama7b_full_stack_M128", 2)])
 def test_persistent_sweep_parity(lbm, name, blocks):
     wl, S, paths = build_stack(lbm, name, blocks=blocks)
     say(f"[case] persistent sweep {name} blocks={blocks}")
