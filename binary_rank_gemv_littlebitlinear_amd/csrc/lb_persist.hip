@@ -20,13 +20,19 @@
 // signed sums, and each 4-bit nibble of a sign word selects one entry.  A
 // wave reads at most 16 distinct entries of one table per lookup, which
 // the LDS serves without bank conflicts.  The first product's tables are
-// built from z = g * x over the workgroup's own rows; the second
-// product's tables from w = l * t.
+// built from z = g * x over the workgroup's own rows (a thread looks up 1,
+// 2 or 4 adjacent latent columns per bit read, the width chosen per unit
+// on the host); the second product's tables from w = l * t.
+//
+// Issue.  Both products are bound by instruction issue on the busiest
+// SIMD, not by data: scalar setup on the critical wave (a 64-bit division,
+// say) shows up directly in the phase time.
 //
 // Memory.  The sign bits and scales a workgroup needs in a phase form a
 // few contiguous blocks (layouts in lb_internal.h).  Waves 4-7 copy them
 // into LDS with LDS-DMA loads while waves 0-3 run the previous phase's
-// exchange, so HBM latency overlaps the device-wide synchronisation.
+// exchange (the partials are issued first, the copies right after), so
+// HBM latency overlaps the device-wide synchronisation.
 //
 // Exchange.  Partial latent vectors (one per workgroup) are all-reduced
 // between phases: each workgroup stores its partials contiguously;
