@@ -826,7 +826,12 @@ k_persist(PArgs A) {
     // the partials, on the critical path, are issued before the next
     // phase's block copies (waves 4-7), which then overlap the waits
     __syncthreads();
-    if (wave_id() >= 4) stage_phase(A, ph + 1, L);
+    if (wave_id() >= 4) {
+      // the copy issue gets the SIMDs first while waves 0-3 only poll
+      __builtin_amdgcn_s_setprio(2);
+      stage_phase(A, ph + 1, L);
+      __builtin_amdgcn_s_setprio(0);
+    }
     if (!exchange_collect(L, Lu, gen, A, tp)) {
       // a wait gave up: let the next phase's copies into LDS land before
       // the workgroup (and its LDS) ends
