@@ -119,7 +119,7 @@ k_wave_s1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
     __syncthreads();
     // a thread per column: its words are loaded once, before the rows
     for (int64_t col = t; col < L; col += kS1Threads) {
-      const int p = (int)(col / s);
+      const int p = (int)((uint32_t)col / (uint32_t)s);  // col < L = P s <= 8192
       uint32_t wd[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) wd[r] = (r0 + r < r1) ? sv1[(r0 + r) * L + col] : 0u;
@@ -146,7 +146,8 @@ __global__ void __launch_bounds__(256) k_wave_reduce(const float *__restrict__ p
   const int t = threadIdx.x, cl = t & 15, grp = t >> 4;
   const int64_t idx = (int64_t)blockIdx.x * 16 + cl;
   const bool live = idx < (int64_t)M * L;
-  const int m = live ? (int)(idx / L) : 0;
+  // M < 64 and L = P s <= 8192 here, so idx, col and s fit 32-bit divisions
+  const int m = live ? (int)((uint32_t)idx / (uint32_t)L) : 0;
   const int64_t col = live ? idx - (int64_t)m * L : 0;
   const int q = (nchunk + 15) / 16;
   const int c0 = grp * q, c1 = (c0 + q) < nchunk ? (c0 + q) : nchunk;
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(256) k_wave_reduce(const float *__restrict__ p
     __syncthreads();
   }
   if (grp == 0 && live) {
-    const int64_t p = col / s;
+    const int64_t p = (uint32_t)col / (uint32_t)s;
     w[idx] = h2f(l[p * s8 + (col - p * s)]) * red[0][cl];
   }
 }
