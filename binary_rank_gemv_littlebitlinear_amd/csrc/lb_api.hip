@@ -616,6 +616,7 @@ struct lb_stack {
   std::vector<void *> ybuf;  // per layer output scratch (cap_M x b)
   void *xbuf[2] = {nullptr, nullptr};  // unit input ping-pong (cap_M x max a)
   int64_t max_width = 0;
+  int64_t loop_rows = 4;  // automatic mode: rows run as batch-1 sweeps (see lb_stack_forward)
   PersistPlan *persist = nullptr;
   std::vector<MfmaPlan *> uplan;  // per unit, for M >= 64
   void *mws = nullptr;            // unit-path workspace (largest unit)
@@ -725,6 +726,15 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     }
   }
   st = persist_build(S->layers, S->unit_begin, S->unit_size, S->kappa, S->device, &S->persist);
+  {
+    // a batch-1 sweep costs about the same for any matrix size (it is
+    // bound by its grid-wide exchanges), the per-layer kernels grow with
+    // it: measured crossovers are about 4 rows for 4096 x 11008 matrices
+    // and 7 for 8192 x 28672 ones, so the limit follows the mean size
+    double elems = 0;
+    for (const lb_layer *L : S->layers) elems += (double)L->ly.a * (double)L->ly.b;
+    S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 7 : 4;
+  }
   if (st != LB_OK && st != LB_EUNSUPPORTED) {
     stack_free_scratch(S);
     delete S;
@@ -799,8 +809,6 @@ extern "C" lb_status lb_stack_reserve(lb_stack *S, int64_t M) {
   return stack_reserve(S, M);
 }
 
-constexpr int64_t kPersistLoopRows = 4;
-
 extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                                       void *stream) {
   if (!S) return fail(LB_EINVAL, "lb_stack_forward: NULL stack");
@@ -831,9 +839,9 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     return LB_OK;
   }
   // a few rows without a trace: one batch-1 sweep per row beats the
-  // per-layer kernels up to about four rows (rows are independent, so each
-  // row's result is exactly its batch-1 result)
-  if (S->persist && S->mode == 0 && !trace && M <= kPersistLoopRows) {
+  // per-layer kernels up to S->loop_rows rows (rows are independent, so
+  // each row's result is exactly its batch-1 result)
+  if (S->persist && S->mode == 0 && !trace && M <= S->loop_rows) {
     const int64_t a0 = S->layers[0]->ly.a, bl = S->layers.back()->ly.b;
     for (int64_t m = 0; m < M; ++m) {
       std::string msg;

@@ -212,7 +212,8 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               workgroups through device memory with bounded waits (a
  *               wait that gives up sets a flag lb_stack_check reports);
  *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
- *               per unit; except that for M <= 4 without a trace the
+ *               per unit; except that for M <= 4 (M <= 7 when the stack's
+ *               mean matrix has at least 2^27 weights) without a trace the
  *               one-launch sweep runs once per row (faster at these M; each
  *               row's output is exactly its M = 1 output);
  *   M >= 64     two matrix-core launches per unit, the combine fused into

@@ -234,16 +234,18 @@ def test_persistent_wait_failure_is_reported_and_recovers(lbm):
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
-def test_small_batch_without_trace_runs_rows_as_batch1(lbm, M):
-    """For M <= 4 without a trace the automatic mode runs the batch-1 sweep
-    once per row: every row equals its own M = 1 result bit for bit (the
-    M = 1 sweep is checked against the oracle above), and the batch agrees
-    at the parity bar with the per-layer kernels that the same M uses when a
-    trace is asked for."""
+@pytest.mark.parametrize("name,M", [("llama7b_mlp_stack", 2), ("llama7b_mlp_stack", 3),
+                                    ("llama7b_mlp_stack", 4), ("llama70b_mlp_stack", 6),
+                                    ("llama70b_mlp_stack", 7)])
+def test_small_batch_without_trace_runs_rows_as_batch1(lbm, name, M):
+    """For M <= 4 (M <= 7 for stacks of 8192 x 28672 matrices) without a
+    trace the automatic mode runs the batch-1 sweep once per row: every row
+    equals its own M = 1 result bit for bit (the M = 1 sweep is checked
+    against the oracle above), and the batch agrees at the parity bar with
+    the per-layer kernels that the same M uses when a trace is asked for."""
     torch = lbtest.torch_dev()
-    say(f"[case] small batch without trace M={M}")
-    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    say(f"[case] small batch without trace {name} M={M}")
+    wl, S, paths = build_stack(lbm, name, blocks=2)
     x0, yt, tr = run_stack(lbm, wl, S, M)
     check_stack(wl, paths, x0, yt, tr, M, sample=[0, 2, 5])
     b_last = wl["layers"][-1]["b"]
