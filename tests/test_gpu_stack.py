@@ -149,20 +149,21 @@ def test_stack_without_trace_matches_trace_run(lbm):
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
 
 
-def _odd_stack(lbm, seed=5):
-    """A small stack with widths that are not multiples of 16."""
-    shapes = [(100, 37, 5), (100, 37, 5), (37, 70, 33), (70, 100, 17), (70, 100, 17)]
-    units = [2, 1, 2]
+def _odd_stack(lbm, seed=5, residual=True, shapes=None, units=None):
+    """A small stack with widths that are not multiples of 16 (by default)."""
+    if shapes is None:
+        shapes = [(100, 37, 5), (100, 37, 5), (37, 70, 33), (70, 100, 17), (70, 100, 17)]
+        units = [2, 1, 2]
     layers, paths = [], []
     for i, (a, b, s) in enumerate(shapes):
-        p = lb_synth.layer_inputs(a, b, s, True, seed=seed, layer=i)
+        p = lb_synth.layer_inputs(a, b, s, residual, seed=seed, layer=i)
         for q in p:
             q["a"], q["b"], q["s"] = a, b, s
         layers.append(lbm.Layer.from_paths(p))
         paths.append(p)
     wl = {"name": "odd", "seed": seed, "M": 1, "units": units,
-          "layers": [{"a": a, "b": b, "s": s, "residual": True} for (a, b, s) in shapes]}
-    return wl, lbm.Stack(layers, units, lb_synth.kappa(2)), paths
+          "layers": [{"a": a, "b": b, "s": s, "residual": residual} for (a, b, s) in shapes]}
+    return wl, lbm.Stack(layers, units, lb_synth.kappa(2 if residual else 1)), paths
 
 
 # The first product's column width (1, 2 or 4 per thread) is chosen per unit:
@@ -185,6 +186,19 @@ def test_persistent_sweep_parity(lbm, name, blocks):
 def test_persistent_odd_widths(lbm):
     wl, S, paths = _odd_stack(lbm)
     say("[case] persistent odd widths")
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    check_stack(wl, paths, x0, y, tr, 1)
+
+
+def test_persistent_single_path_wide_unit(lbm):
+    """One path per layer: a unit of four 3000 -> 1000 layers with s = 500
+    (2000 latent columns on one row tile per workgroup, so the first product
+    takes four columns per thread), then an odd 1000 -> 3000 layer (s = 37,
+    one column per thread)."""
+    shapes = [(3000, 1000, 500)] * 4 + [(1000, 3000, 37)]
+    wl, S, paths = _odd_stack(lbm, seed=11, residual=False, shapes=shapes, units=[4, 1])
+    say("[case] persistent single path, wide unit")
     x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
     S.check()
     check_stack(wl, paths, x0, y, tr, 1)
