@@ -120,6 +120,19 @@ def test_unit_path_odd_widths(lbm, M):
     assert_parity(y.astype(np.float64), y1.astype(np.float64), "unit vs per-layer")
 
 
+@pytest.mark.parametrize("M", [64, 130])
+def test_unit_path_single_path_wide_unit(lbm, M):
+    """The matrix-core unit kernels on one-path layers: a four-layer unit
+    (2000 latent columns) and an odd single layer."""
+    shapes = [(3000, 1000, 500)] * 4 + [(1000, 3000, 37)]
+    wl, S, paths = _odd_stack(lbm, seed=11, residual=False, shapes=shapes, units=[4, 1])
+    say(f"[case] unit path single path, wide unit M={M}")
+    x0, y, tr = run_stack(lbm, wl, S, M, mode=0)
+    check_stack(wl, paths, x0, y, tr, M, sample=[0, 3, 4])
+    _, y1, _ = run_stack(lbm, wl, S, M, mode=1)
+    assert_parity(y.astype(np.float64), y1.astype(np.float64), "unit vs per-layer")
+
+
 def test_unit_path_repeated_and_deterministic(lbm):
     """Split-K partial sums are combined in a fixed order: repeated batched
     runs are bitwise identical, and the tile counters are left at zero."""
