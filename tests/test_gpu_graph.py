@@ -6,7 +6,8 @@ Every replay runs after ordinary eager work has written a new input into
 the captured buffer, and must equal the eager result for that input bit for
 bit.  This covers the wave path, the matrix-core path, the one-launch sweep
 (whose exchange generation lives in device memory, so replays of one
-captured launch stay distinct), and stacks at M = 8 and M = 128.
+captured launch stay distinct), the sweep run once per row (M = 3: three
+captured launches in a row), and stacks at M = 8 and M = 128.
 """
 import numpy as np
 import pytest
@@ -62,7 +63,8 @@ def test_layer_forward_in_a_graph(lbm, M):
     _replays_match_eager(torch, lambda: L.forward(x, y), x, y, _inputs(torch, M, a))
 
 
-@pytest.mark.parametrize("name,blocks,M", [("llama7b_mlp_stack", 2, 1), ("llama7b_mlp_stack", 2, 8),
+@pytest.mark.parametrize("name,blocks,M", [("llama7b_mlp_stack", 2, 1), ("llama7b_mlp_stack", 2, 3),
+                                           ("llama7b_mlp_stack", 2, 8),
                                            ("llama7b_full_stack_M128", 1, 128)])
 def test_stack_forward_in_a_graph(lbm, name, blocks, M):
     torch = lbtest.torch_dev()
