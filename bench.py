@@ -116,32 +116,73 @@ def copy_probe(torch, mib: int):
     print(f"[bench] copy probe: 3 x neg over {mib} MiB", file=sys.stderr, flush=True)
 
 
+def _blas_setup():
+    """Every host core this process may use, with the BLAS thread count set to
+    match; returns (cores, BLAS description, limiter context or None)."""
+    cores = len(os.sched_getaffinity(0))
+    name, ctx = "unknown", None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            name = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info)
+        ctx = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        pass
+    return cores, name, ctx
+
+
 def cpu_baseline(wl: dict, M: int, budget_s: float) -> dict:
     """Time the float64 oracle on a bounded sample of the workload's layers."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    cores, blas, ctx = _blas_setup()
     x = lb_synth.activations(M, wl["layers"][0]["a"], seed=wl["seed"])
     done_bytes, done_layers, t_used = 0, 0, 0.0
     one = {"layers": None}
-    for sp in wl["layers"]:
-        paths = lb_synth.workload_layer_inputs(sp)
-        xin = x if x.shape[1] == sp["a"] else lb_synth.activations(M, sp["a"], seed=sp["block"])
-        t0 = time.perf_counter()
-        oracle.forward(xin, paths)
-        t_used += time.perf_counter() - t0
-        one["layers"] = [sp]
-        done_bytes += algorithmic_bytes(one, M)
-        done_layers += 1
-        if t_used >= budget_s:
-            break
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    try:
+        for sp in wl["layers"]:
+            paths = lb_synth.workload_layer_inputs(sp)
+            xin = x if x.shape[1] == sp["a"] else lb_synth.activations(M, sp["a"], seed=sp["block"])
+            t0 = time.perf_counter()
+            oracle.forward(xin, paths)
+            t_used += time.perf_counter() - t0
+            one["layers"] = [sp]
+            done_bytes += algorithmic_bytes(one, M)
+            done_layers += 1
+            if t_used >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "blas": blas,
             "sample": f"first {done_layers} of {len(wl['layers'])} matrices, M={M}, "
-                      f"float64 numpy incl. bit unpack, {t_used:.1f} s"}
+                      f"float64 numpy incl. bit unpack, {t_used:.1f} s, BLAS threads = cores"}
+
+
+def validate(torch, stack, x, y, M, mode):
+    """The timed output must be a valid sweep: no device-side wait gave up
+    (lb_stack_check), and a traced run of the same input (every layer's
+    output stored on the way) gives the same y, bit for bit where both runs
+    take the same kernels (M = 1 sweep, M >= 64 unit kernels, or mode 1),
+    else within the parity bar of the two runs.  Raises on failure."""
+    stack.check()
+    y_timed = y.clone()
+    trace = torch.empty(stack.trace_elems(M), dtype=torch.float16, device="cuda")
+    y2 = torch.empty_like(y)
+    stack.forward(x, y2, trace)
+    torch.cuda.synchronize()
+    stack.check()
+    same_kernels = M == 1 or M >= 64 or mode == 1
+    if same_kernels:
+        if not torch.equal(y_timed.view(torch.int16), y2.view(torch.int16)):
+            raise SystemExit("bench: the timed output differs from a traced run of the same input")
+        return "timed y == traced run, bit for bit; lb_stack_check ok"
+    a, b = y_timed.double(), y2.double()
+    rel = float((a - b).norm() / b.norm().clamp_min(1e-300))
+    if not (torch.isfinite(a).all() and rel <= 1e-3):
+        raise SystemExit(f"bench: the timed output differs from a traced run (rel L2 {rel:.2e})")
+    return f"timed y vs traced run (other kernels): rel L2 {rel:.1e}; lb_stack_check ok"
 
 
 def init_cpu_baseline(U, V) -> dict:
@@ -242,8 +283,11 @@ def main():
         y = torch.empty((M, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
         print(f"[bench] built in {t_build:.1f} s; timing {args.steps} steps", file=sys.stderr, flush=True)
         ms, wall_ms = time_steps(torch, stack, x, y, args.steps, args.warmup)
+        checked = validate(torch, stack, x, y, M, args.mode)
+        print(f"[bench] {name}: {checked}", file=sys.stderr, flush=True)
         nbytes, flops = algorithmic_bytes(wl, M), algorithmic_flops(wl, M)
-        res = {"wl": wl, "M": M, "ms": ms, "wall_ms": wall_ms, "bytes": nbytes, "flops": flops}
+        res = {"wl": wl, "M": M, "ms": ms, "wall_ms": wall_ms, "bytes": nbytes, "flops": flops,
+               "validated": checked}
         if with_cpu:
             print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
             res["cpu"] = cpu_baseline(wl, M, args.cpu_budget)
@@ -274,6 +318,7 @@ def main():
         "us_per_layer": round(ms * 1e3 / wl["blocks"], 4),
         "tokens_per_s_equiv": round(M / (ms * 1e-3), 1),
         "algorithmic_bytes_per_step": r["bytes"],
+        "validated": r["validated"],
         "roofline": {"bound": "hbm" if batch1 else "mfma",
                      "achieved": round(gbs if batch1 else tflops, 3),
                      "peak": HBM_PEAK_GBS if batch1 else MFMA_FP16_PEAK_TFLOPS,
@@ -294,7 +339,8 @@ def main():
                             "TFLOP/s": round(s2["flops"] / (ms2 * 1e-3) / 1e12, 3),
                             "mfma_frac": round(s2["flops"] / (ms2 * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
                             "GB/s": round(s2["bytes"] / (ms2 * 1e-3) / 1e9, 2),
-                            "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1)}
+                            "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1),
+                            "validated": s2["validated"]}
     if not args.no_init:
         print("[bench] timing initialisation from real factors", file=sys.stderr, flush=True)
         out["init"] = measure_init(torch, lbm, with_cpu=not args.no_cpu_baseline)

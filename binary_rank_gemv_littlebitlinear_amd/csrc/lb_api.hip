@@ -35,14 +35,14 @@ static lb_status fail(lb_status st, const std::string &msg) {
 
 // ------------------------------------------------------------ devices
 namespace {
+// Per-device facts and one read-only block of zero bytes (the DMA source
+// for padding).  Nothing here is written after it is set up, so layers and
+// stacks on one device share it freely; every buffer a forward call writes
+// belongs to its layer or stack.
 struct DevCtx {
   DeviceInfo info;
-  void *ws = nullptr;  // shared forward workspace of this device
-  size_t ws_bytes = 0;
-  unsigned *cnt = nullptr;  // split-K tile counters of the MFMA path (kept zero)
-  void *zero = nullptr;     // 256 zero bytes (copy source for padding)
+  void *zero = nullptr;  // 256 zero bytes
 };
-constexpr size_t kDevCounters = 4096;
 std::mutex g_mu;
 std::map<int, DevCtx> g_dev;
 
@@ -57,32 +57,12 @@ lb_status get_dev(int device, DevCtx **out) {
     if (e != hipSuccess) return fail(LB_EHIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
     c.info.cu_count = prop.multiProcessorCount;
     c.info.coop = prop.cooperativeLaunch;
-    e = hipMalloc(&c.cnt, kDevCounters * sizeof(unsigned) + 256);
-    if (e == hipSuccess) e = hipMemset(c.cnt, 0, kDevCounters * sizeof(unsigned) + 256);
-    c.zero = c.cnt + kDevCounters;
-    if (e != hipSuccess) return fail(LB_ENOMEM, std::string("counter hipMalloc: ") + hipGetErrorString(e));
+    e = hipMalloc(&c.zero, 256);
+    if (e == hipSuccess) e = hipMemset(c.zero, 0, 256);
+    if (e != hipSuccess) return fail(LB_ENOMEM, std::string("zero block hipMalloc: ") + hipGetErrorString(e));
     it = g_dev.emplace(device, c).first;
   }
   *out = &it->second;
-  return LB_OK;
-}
-
-// Grow the device workspace to at least `need` bytes (called at create
-// time only, never from a forward call).
-lb_status ensure_ws(DevCtx *c, size_t need) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (c->ws_bytes >= need) return LB_OK;
-  if (c->ws) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(c->ws);
-    c->ws = nullptr;
-    c->ws_bytes = 0;
-  }
-  void *p = nullptr;
-  hipError_t e = hipMalloc(&p, need);
-  if (e != hipSuccess) return fail(LB_ENOMEM, std::string("workspace hipMalloc: ") + hipGetErrorString(e));
-  c->ws = p;
-  c->ws_bytes = need;
   return LB_OK;
 }
 
@@ -153,15 +133,23 @@ void transpose32(uint32_t m[32]) {
 static inline DevCtx *ctx_of(const lb_layer *L) { return static_cast<DevCtx *>(L->ctx); }
 
 // --------------------------------------------------------- workspace need
+// The wave path keeps one fp32 partial latent vector per input chunk and
+// row; a layer's launches take at most wave_rows rows at a time, so these
+// partials stay within kWavePartBudget bytes (at least one row).
+constexpr size_t kWavePartBudget = (size_t)4 << 20;
+
+static int wave_rows_for(const Layer &Ly, const DeviceInfo &dev) {
+  const int nch = wave_nchunk(Ly, 1, dev);
+  const size_t per_row = wave_ws_floats(Ly, 1, nch) * sizeof(float);
+  const size_t r = kWavePartBudget / std::max<size_t>(per_row, 1);
+  return (int)std::max<size_t>(1, std::min<size_t>(63, r));
+}
+
 static size_t layer_ws_need(const Layer &Ly, const MfmaPlan *mp, const DeviceInfo &dev) {
-  size_t need = 0;
-  for (int64_t M = 1; M < 64; ++M) {
-    const int nch = wave_nchunk(Ly, M, dev);
-    const size_t b = (wave_ws_floats(Ly, M, nch) + (size_t)M * Ly.L) * sizeof(float) + 512;
-    if (b > need) need = b;
-  }
-  const size_t mf = mfma_unit_ws_bytes(mp);
-  if (mf > need) need = mf;
+  const int Mw = Ly.wave_rows;
+  const int nch = wave_nchunk(Ly, Mw, dev);
+  size_t need = (wave_ws_floats(Ly, Mw, nch) + (size_t)Mw * Ly.L) * sizeof(float) + 512;
+  need = std::max(need, mfma_unit_ws_bytes(mp));
   return need;
 }
 
@@ -216,14 +204,19 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
     const Layer *one = &Ly;
     L->mplan = mfma_plan_build(&one, 1);
   }
-  if (!L->mplan || mfma_cnt_entries(L->mplan) > kDevCounters) {
+  if (!L->mplan) {
     lb_destroy(L);
     return fail(LB_EUNSUPPORTED, "lb_create: shape not supported by the MFMA path");
   }
-  st = ensure_ws(dc, layer_ws_need(Ly, L->mplan, dc->info));
-  if (st != LB_OK) {
+  Ly.wave_rows = wave_rows_for(Ly, dc->info);
+  Ly.ws_bytes = layer_ws_need(Ly, L->mplan, dc->info);
+  const size_t ncnt = std::max<size_t>(1, mfma_cnt_entries(L->mplan));
+  hipError_t e = hipMalloc(&Ly.ws, Ly.ws_bytes);
+  if (e == hipSuccess) e = hipMalloc(&Ly.cnt, ncnt * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemset(Ly.cnt, 0, ncnt * sizeof(unsigned));
+  if (e != hipSuccess) {
     lb_destroy(L);
-    return st;
+    return fail(LB_ENOMEM, std::string("lb_create: workspace hipMalloc: ") + hipGetErrorString(e));
   }
   *out = L;
   return LB_OK;
@@ -233,7 +226,8 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   if (!L) return LB_OK;
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
-  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m};
+  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m,
+                Ly.ws, Ly.cnt};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   mfma_plan_free(L->mplan);
@@ -509,17 +503,21 @@ static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y,
   const Layer &Ly = L->ly;
   DevCtx *dc = ctx_of(L);
   if (M < 64) {
-    const int nch = wave_nchunk(Ly, M, dc->info);
-    float *part = reinterpret_cast<float *>(dc->ws);
-    float *w = part + wave_ws_floats(Ly, M, nch);
-    hipError_t e = launch_wave_stage1(Ly, x, w, M, nch, part, st);
-    if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 1: ") + hipGetErrorString(e));
-    e = launch_wave_stage2(Ly, w, y, M, st);
-    if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 2: ") + hipGetErrorString(e));
+    // rows in blocks of wave_rows, so the chunk partials fit the layer's workspace
+    for (int64_t m0 = 0; m0 < M; m0 += Ly.wave_rows) {
+      const int64_t Mc = std::min<int64_t>(Ly.wave_rows, M - m0);
+      const int nch = wave_nchunk(Ly, Mc, dc->info);
+      float *part = Ly.ws;
+      float *w = part + wave_ws_floats(Ly, Mc, nch);
+      hipError_t e = launch_wave_stage1(Ly, x + m0 * Ly.a, w, Mc, nch, part, st);
+      if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 1: ") + hipGetErrorString(e));
+      e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, st);
+      if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 2: ") + hipGetErrorString(e));
+    }
     return LB_OK;
   }
   uint16_t *ys[1] = {y};
-  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, dc->ws, dc->cnt, dc->zero,
+  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, Ly.ws, Ly.cnt, dc->zero,
                                  dc->info, st);
   if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma path: ") + hipGetErrorString(e));
   return LB_OK;
@@ -544,12 +542,12 @@ extern "C" lb_status lb_forward_stage1(const lb_layer *L, const void *x, float *
   if (st != LB_OK || M == 0) return st;
   DeviceGuard dg(Ly.device);
   DevCtx *dc = ctx_of(L);
-  // Rows in blocks of 63 so the partial buffer stays within the workspace.
-  for (int64_t m0 = 0; m0 < M; m0 += 63) {
-    const int64_t Mc = (M - m0) < 63 ? (M - m0) : 63;
+  // rows in blocks of wave_rows so the chunk partials fit the layer's workspace
+  for (int64_t m0 = 0; m0 < M; m0 += Ly.wave_rows) {
+    const int64_t Mc = std::min<int64_t>(Ly.wave_rows, M - m0);
     const int nch = wave_nchunk(Ly, Mc, dc->info);
     hipError_t e = launch_wave_stage1(Ly, (const uint16_t *)x + m0 * Ly.a, w + m0 * Ly.L, Mc, nch,
-                                      (float *)dc->ws, (hipStream_t)stream);
+                                      Ly.ws, (hipStream_t)stream);
     if (e != hipSuccess) return fail(LB_EHIP, std::string("stage 1: ") + hipGetErrorString(e));
   }
   return LB_OK;
@@ -613,8 +611,12 @@ struct lb_stack {
   int device = 0;
   int mode = 0;
   int64_t cap_M = 0;      // rows the scratch buffers hold
-  std::vector<void *> ybuf;  // per layer output scratch (cap_M x b)
+  void *ybuf = nullptr;  // the running unit's layer outputs (cap_M x unit_out_max)
   void *xbuf[2] = {nullptr, nullptr};  // unit input ping-pong (cap_M x max a)
+  int64_t unit_out_max = 0;  // max over units of (layers x b)
+  // scratch replaced by a larger reservation: kept until the stack is
+  // destroyed, since launches captured earlier may still write it
+  std::vector<void *> retired;
   int64_t max_width = 0;
   int64_t loop_rows = 4;  // automatic mode: rows run as batch-1 sweeps (see lb_stack_forward)
   PersistPlan *persist = nullptr;
@@ -624,37 +626,44 @@ struct lb_stack {
 };
 
 static void stack_free_scratch(lb_stack *S) {
-  for (void *p : S->ybuf)
-    if (p) (void)hipFree(p);
-  S->ybuf.clear();
+  if (S->ybuf) (void)hipFree(S->ybuf);
+  S->ybuf = nullptr;
   for (auto &p : S->xbuf)
     if (p) {
       (void)hipFree(p);
       p = nullptr;
     }
+  for (void *p : S->retired)
+    if (p) (void)hipFree(p);
+  S->retired.clear();
   S->cap_M = 0;
 }
 
+// Grow the scratch to at least M rows (at least doubling, so a stack that
+// grows step by step keeps few retired buffers).  The current buffers are
+// retired, not freed: nothing a forward call used is released before
+// lb_stack_destroy.  No device synchronisation.
 static lb_status stack_reserve(lb_stack *S, int64_t M) {
   if (M <= S->cap_M) return LB_OK;
-  (void)hipDeviceSynchronize();
-  stack_free_scratch(S);
-  S->ybuf.assign(S->layers.size(), nullptr);
-  for (size_t i = 0; i < S->layers.size(); ++i) {
-    hipError_t e = hipMalloc(&S->ybuf[i], (size_t)M * S->layers[i]->ly.b * 2);
-    if (e != hipSuccess) {
-      stack_free_scratch(S);
-      return fail(LB_ENOMEM, "stack scratch hipMalloc");
-    }
-  }
-  for (auto &p : S->xbuf) {
-    hipError_t e = hipMalloc(&p, (size_t)M * S->max_width * 2);
-    if (e != hipSuccess) {
-      stack_free_scratch(S);
-      return fail(LB_ENOMEM, "stack scratch hipMalloc");
-    }
-  }
-  S->cap_M = M;
+  const int64_t cap = std::max<int64_t>(M, 2 * S->cap_M);
+  void *yb = nullptr;
+  void *xb[2] = {nullptr, nullptr};
+  auto undo = [&]() {
+    if (yb) (void)hipFree(yb);
+    for (void *p : xb)
+      if (p) (void)hipFree(p);
+    return fail(LB_ENOMEM, "stack scratch hipMalloc");
+  };
+  if (hipMalloc(&yb, (size_t)cap * S->unit_out_max * 2) != hipSuccess) return undo();
+  for (auto &p : xb)
+    if (hipMalloc(&p, (size_t)cap * S->max_width * 2) != hipSuccess) return undo();
+  if (S->ybuf) S->retired.push_back(S->ybuf);
+  for (void *p : S->xbuf)
+    if (p) S->retired.push_back(p);
+  S->ybuf = yb;
+  S->xbuf[0] = xb[0];
+  S->xbuf[1] = xb[1];
+  S->cap_M = cap;
   return LB_OK;
 }
 
@@ -697,6 +706,9 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
       return fail(LB_EINVAL, "lb_stack_create: unit input width != previous unit output width");
     }
   }
+  for (int u = 0; u < n_units; ++u)
+    S->unit_out_max = std::max<int64_t>(S->unit_out_max,
+                                        (int64_t)S->unit_size[u] * layers[S->unit_begin[u]]->ly.b);
   DeviceGuard dg(S->device);
   lb_status st = stack_reserve(S, 64);
   if (st != LB_OK) {
@@ -747,7 +759,8 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
 extern "C" lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed) {
   if (!S) return fail(LB_EINVAL, "lb_stack_timeline: NULL stack");
   if (!S->persist) return fail(LB_EUNSUPPORTED, "lb_stack_timeline: no persistent plan");
-  const int64_t need = (int64_t)persist_grid(S->persist) * persist_phases(S->persist) * 4;
+  const int64_t need =
+      (int64_t)persist_grid(S->persist) * persist_phases(S->persist) * persist_stamps();
   if (needed) *needed = need;
   if (buf && capacity < need) return fail(LB_EINVAL, "lb_stack_timeline: buffer too small");
   if (((uintptr_t)buf) & 7) return fail(LB_EINVAL, "lb_stack_timeline: buffer not 8-byte aligned");
@@ -884,7 +897,7 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     std::vector<const uint16_t *> outs;
     for (int k = 0; k < nu; ++k) {
       lb_layer *Lr = S->layers[b0 + k];
-      uint16_t *o = trace ? tY[b0 + k] : (uint16_t *)S->ybuf[b0 + k];
+      uint16_t *o = trace ? tY[b0 + k] : (uint16_t *)S->ybuf + (size_t)k * M * Lr->ly.b;
       lb_status fs = forward_impl(Lr, cur, o, M, st);
       if (fs != LB_OK) return fs;
       outs.push_back(o);

@@ -78,9 +78,14 @@ struct Layer {
   uint16_t *gt = nullptr;   // T16a * P * 16
   uint32_t *sv1m = nullptr; // R1 * L words (matrix-core bit order)
   uint32_t *su2m = nullptr; // P * Wk * b16 words (matrix-core bit order)
-  // workspace: stage-1 partials / latent vectors, sized at create time
+  // The layer's own forward workspace (wave-path chunk partials and latent
+  // rows, or the matrix-core latent T and split-K partials) and split-K
+  // tile counters (zero between launches), allocated at create time and
+  // kept until destroy: forward calls on different layers share nothing.
   float *ws = nullptr;
   size_t ws_bytes = 0;
+  unsigned *cnt = nullptr;
+  int wave_rows = 1;  // rows per wave-path launch pair (the partials fit ws)
   bool ready() const {
     for (int p = 0; p < P; ++p)
       if (!signs_set[p] || !scales_set[p]) return false;

@@ -28,6 +28,7 @@ void persist_set_timeline(PersistPlan *p, uint64_t *buf);
 void persist_set_fail_test(PersistPlan *p, bool on);
 int persist_grid(const PersistPlan *p);
 int persist_phases(const PersistPlan *p);
+int persist_stamps();  // timestamps per phase and workgroup
 // Synchronise and report a device-side wait timeout of an earlier launch.
 lb_status persist_check(PersistPlan *p, std::string *msg);
 

@@ -35,22 +35,35 @@
 // HBM latency overlaps the device-wide synchronisation.
 //
 // Exchange.  Partial latent vectors (one per workgroup) are all-reduced
-// between phases: each workgroup stores its partials contiguously;
-// workgroup r sums the 8-column slice r over all workgroups in a fixed
-// order and writes it into each of kXCopies copies of the reduced vector;
-// workgroup w reads copy w % kXCopies.  Every exchanged word is a
-// 64-bit value | generation pair written and read with relaxed
-// device-coherent (sc1) atomics, so a reader knows a word is current from
-// the word itself and no flag (or store-completion wait) is needed.  A
-// launch takes its generation base from the tags the previous launch left,
-// so a launch captured into a graph and replayed stays correct.
-// Every wait is bounded: on timeout a device error word is set, all
-// workgroups leave, and lb_stack_check returns LB_ETIMEOUT.
+// between phases in three levels that follow the chip: 8 XCDs of 32 CUs,
+// each XCD with its own L2, workgroup w on XCD w % 8 (checked when the plan
+// is built).  Workgroup (x, i) = w with x = w % 8, i = w / 8 owns the
+// slice i of ceil(Lu / 32) latent columns.
+//   A  every workgroup stores its partials into its XCD's area; owner
+//      (x, i) sums slice i over the 32 workgroups of XCD x;
+//   B  owner (x, i) publishes that XCD sum device-wide and sums slice i
+//      over the 8 XCDs, in XCD order (every XCD gets the same total);
+//   C  owner (x, i) stores the total into XCD x's area, from which every
+//      workgroup of XCD x builds the next phase's tables.
+// Levels A and C never leave the XCD: their words are written with
+// workgroup-scope stores, which stay in the XCD's L2, and read with
+// device-scope loads, which skip the CU's L1 and find the line in that L2;
+// only level B's 8-way slices cross XCDs (device-scope stores and loads).
+// Every exchanged word is a 64-bit value | generation pair, so a reader
+// knows a word is current from the word itself and no flag (or
+// store-completion wait) is needed.  A launch takes its generation base
+// from the tags the previous launch left, so a launch captured into a
+// graph and replayed stays correct.  Every wait is bounded: on timeout a
+// device error word (and a host-mapped copy) is set, all workgroups leave,
+// and the next lb_stack_forward or lb_stack_check returns LB_ETIMEOUT.
 #include <hip/hip_fp16.h>
 
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "lb_persist.h"
 
@@ -67,7 +80,9 @@ constexpr int kTab2Floats = 10240;
 constexpr int kTab1Floats = 4096;
 constexpr long kSpin = 4000000;      // polls before a wait gives up
 constexpr long kSpinFailTest = 2048;  // the same in the host-requested failure test
-constexpr int kXCopies = 8;      // copies of the reduced vector; workgroup w polls copy w % 8
+constexpr int kXcd = 8;          // XCDs; workgroup w runs on XCD w % 8
+constexpr int kPerXcd = 32;      // workgroups per XCD (the grid is 256 = one per CU)
+constexpr int kSliceMax = kLuMax / kPerXcd;  // latent columns one owner sums
 
 struct alignas(16) PLayer {
   const uint32_t *su2t;
@@ -129,9 +144,13 @@ struct PArgs {
   const uint16_t *x0;
   uint16_t *y;
   uint16_t *trace;  // may be null
-  uint64_t *xpart;  // [G][kLuMax] tagged partials (value bits | generation << 32)
-  uint64_t *xT;     // [kXCopies][kLuMax] tagged reduced latent (copies of one vector)
+  // tagged words (fp32 value bits | generation << 32)
+  uint64_t *PA;  // [kXcd][kPerXcd][kLuMax] partials, in their XCD's L2
+  uint64_t *PB;  // [2][kXcd][kLuMax] XCD sums of the slices (generation parity), device-wide
+  uint64_t *PC;  // [kXcd][kLuMax] totals, in their XCD's L2
+  int xcd_local;  // 1: levels A and C stay in the XCD's L2; 0: device-scope stores throughout
   unsigned *err;
+  unsigned *herr;      // host-mapped copy of the error word (read by the next run on the host)
   uint64_t *timeline;  // optional [G][U+1][4] device timestamps (100 MHz)
   const PSeg *segs;    // [(U+1) * kMaxSeg] per-phase copy lists
   const PGroup *grp0;  // the first table group (a valid address for idle loads)
@@ -151,8 +170,11 @@ struct PersistPlan {
   PGroup *d_groups = nullptr;
   std::vector<PUnit> h_units;
   std::vector<PLayer> h_layers;
-  uint64_t *xpart = nullptr, *xT = nullptr;
+  uint64_t *PA = nullptr, *PB = nullptr, *PC = nullptr;
+  int xcd_local = 0;
   unsigned *err = nullptr;  // 64 words; word 0 is the error word
+  unsigned *herr = nullptr;      // pinned host word, set by a wait that gives up
+  unsigned *herr_dev = nullptr;  // its device address
   bool fail_test = false;  // next sweeps: unsatisfiable waits with a short bound
   bool broken = false;
   uint64_t *timeline = nullptr;
@@ -183,6 +205,17 @@ __device__ __forceinline__ void st_tag(uint64_t *p, float v, unsigned gen) {
 }
 __device__ __forceinline__ uint64_t ld_tag(uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same word for readers on this XCD only: a workgroup-scope store
+// leaves the line in this XCD's L2 (no write-through to memory), where the
+// readers' device-scope loads find it.  With local == 0 (XCD placement not
+// confirmed) it is a device-scope store.
+__device__ __forceinline__ void st_tag_xcd(uint64_t *p, float v, unsigned gen, int local) {
+  const uint64_t w = (uint64_t)__float_as_uint(v) | ((uint64_t)gen << 32);
+  if (local)
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
@@ -247,7 +280,14 @@ struct Lds {
   int *flags8;         // kWaves
   PhaseCtx *ctx;
   PSeg *segbuf;        // [2][kMaxSeg] copy lists of this and the next phase
+  uint64_t *tl;        // diagnostics: this workgroup's timestamps, or null
 };
+
+// Diagnostics: timestamp k of phase ph (100 MHz counter), thread 0 only.
+constexpr int kStamps = 8;
+__device__ __forceinline__ void stamp(const Lds &L, int ph, int k) {
+  if (L.tl && threadIdx.x == 0) L.tl[ph * kStamps + k] = __builtin_amdgcn_s_memrealtime();
+}
 
 // Stage phase ph: copy the blocks of its list (descriptors of units ph-1
 // and ph, sign bits, scales) into LDS with LDS-DMA loads (16 bytes per
@@ -400,20 +440,25 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
                              ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
         // four words per step; every read is unconditional (index clamped,
-        // result masked), so the step's reads are all in flight at once
-        // instead of waiting word by word behind branches
+        // result masked), and all 32 table reads of a step are gathered
+        // before any is summed (a tree per word), so they are in flight at
+        // once instead of each waiting for the previous one's sum
         for (int q = sub; q < Wk; q += 4 * lpt) {
           uint32_t wd[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) wd[i] = wb[min(q + i * lpt, Wk - 1) * 16];
+          float v[4][8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int qi = q + i * lpt;
-            const float *tq = tb + min(qi, Wk - 1) * 128;
-            float e = 0.f;
+            const float *tq = tb + min(q + i * lpt, Wk - 1) * 128;
 #pragma unroll
-            for (int n = 0; n < 8; ++n) e += tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
-            acc += qi < Wk ? e : 0.f;
+            for (int n = 0; n < 8; ++n) v[i][n] = tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) +
+                            ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
+            acc += q + i * lpt < Wk ? e : 0.f;
           }
         }
       }
@@ -421,6 +466,7 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       if (sub == 0 && tk < ntk) L.acc2[mp * (16 * kTMax) + r] = acc;
     }
   }
+  stamp(L, ph, 1);
   // per-layer offsets for the epilogue, loaded before the barrier
   int hoff[kMaxUnitLayers];
   int64_t trace_y[kMaxUnitLayers];
@@ -510,20 +556,34 @@ __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLay
             wd[i][0] = *(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)a;
           }
         }
+        // every table read of the step first, then the sums: the reads are
+        // all in flight together rather than pairwise behind each sum
+        float v[2][CPT][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int gi = g0 + i * lpt;
-          const uint32_t toff = kTileBytes * (uint32_t)min(gi, nt - 1);
+          const uint32_t toff = kTileBytes * (uint32_t)min(g0 + i * lpt, nt - 1);
 #pragma unroll
           for (int j = 0; j < CPT; ++j) {
             const uint32_t w = wd[i][j >> 1], tb = tq[j] + toff;
-            float e;
-            if ((j & 1) == 0)
-              e = (lds_f32(tb | nib_off<0>(w)) + lds_f32((tb | nib_off<4>(w)) + 64)) +
-                  (lds_f32((tb | nib_off<8>(w)) + 128) + lds_f32((tb | nib_off<12>(w)) + 192));
-            else
-              e = (lds_f32(tb | nib_off<16>(w)) + lds_f32((tb | nib_off<20>(w)) + 64)) +
-                  (lds_f32((tb | nib_off<24>(w)) + 128) + lds_f32((tb | nib_off<28>(w)) + 192));
+            if ((j & 1) == 0) {
+              v[i][j][0] = lds_f32(tb | nib_off<0>(w));
+              v[i][j][1] = lds_f32((tb | nib_off<4>(w)) + 64);
+              v[i][j][2] = lds_f32((tb | nib_off<8>(w)) + 128);
+              v[i][j][3] = lds_f32((tb | nib_off<12>(w)) + 192);
+            } else {
+              v[i][j][0] = lds_f32(tb | nib_off<16>(w));
+              v[i][j][1] = lds_f32((tb | nib_off<20>(w)) + 64);
+              v[i][j][2] = lds_f32((tb | nib_off<24>(w)) + 128);
+              v[i][j][3] = lds_f32((tb | nib_off<28>(w)) + 192);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int gi = g0 + i * lpt;
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) {
+            const float e = (v[i][j][0] + v[i][j][1]) + (v[i][j][2] + v[i][j][3]);
             acc[j] += gi < nt ? e : 0.f;
           }
         }
@@ -539,7 +599,7 @@ __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLay
 
 // First product of unit B over the workgroup's rows: part[col] for every
 // latent column of every layer of the unit.
-__device__ void first_product(Lds &L) {
+__device__ void first_product(Lds &L, int ph) {
   const PhaseCtx &C = *L.ctx;
   const PUnit &U = C.ub;
   const int nb = U.n, Lu = U.Lu;
@@ -575,6 +635,7 @@ __device__ void first_product(Lds &L) {
   for (int m = 0; m < kMaxUnitLayers; ++m) col0m[m] = LB[m].col0;
   const int cpt = nt == (U.cpt >> 16) ? (U.cpt & 255) : ((U.cpt >> 8) & 255);
   __syncthreads();
+  stamp(L, ph, 3);
   if (cpt == 4) s1_lookups<4>(L, C, LB, nb, Lu, nt, Pu, col0m);
   else if (cpt == 2) s1_lookups<2>(L, C, LB, nb, Lu, nt, Pu, col0m);
   else s1_lookups<1>(L, C, LB, nb, Lu, nt, Pu, col0m);
@@ -598,7 +659,7 @@ constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
 // carry gen; their values go to vals.  False on give-up or error.
 template <class Ptr, class Valid, int N>
 __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, unsigned *err,
-                                            bool fail_test, float (&vals)[N]) {
+                                            unsigned *herr, bool fail_test, float (&vals)[N]) {
   static_assert(N <= 32, "one pending bit per word");
   unsigned pend = 0;
 #pragma unroll
@@ -621,6 +682,7 @@ __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, un
       if (ld_u(err) != 0) return false;
       if (spins > kSpin || (fail_test && spins > kSpinFailTest)) {
         atomicOr(err, 1u);
+        __hip_atomic_store(herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         return false;
       }
     }
@@ -670,59 +732,66 @@ __device__ TabPlan load_tables(const PArgs &A, const Lds &L, bool live) {
   return T;
 }
 
-// First half of the exchange: this workgroup's partials, tagged.
+// First half of the exchange: this workgroup's partials, tagged, into its
+// XCD's area (level A).
 __device__ void exchange_publish(const Lds &L, int Lu, unsigned gen, const PArgs &A) {
   const int w = blockIdx.x, t = threadIdx.x;
-  const int nsl = (Lu + 7) / 8;
+  uint64_t *pa = A.PA + ((size_t)(w % kXcd) * kPerXcd + w / kXcd) * kLuMax;
   if (t < kXThreads) {
 #pragma unroll
     for (int k = 0; k < kXLoads; ++k) {
       const int c = t + k * kXThreads;
-      if (c < nsl * 8) st_tag(&A.xpart[(size_t)w * kLuMax + c], c < Lu ? L.part[c] : 0.f, gen);
+      if (c < Lu) st_tag_xcd(&pa[c], L.part[c], gen, A.xcd_local);
     }
   }
 }
 
-// Second half: the owned slices' sums, then the all-gather into the tables.
-static_assert(kXThreads == 4 * 64 && kXCopies <= 8, "the slice sum adds four waves; t < 64 stores");
-__device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp) {
-  const int G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+// Second half: levels A (owned slice over the XCD), B (over the XCDs) and C
+// (the totals, straight into the next phase's tables).
+static_assert(kXThreads == 4 * 64 && kPerXcd == 4 * 8 && kSliceMax <= 64,
+              "level A: wave v sums producers v, v + 4, ...; a lane per column");
+__device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp,
+                                 int ph) {
+  const int w = blockIdx.x, t = threadIdx.x;
+  const int x = w % kXcd, li = w / kXcd, lane = t & 63, wv = t >> 6;
   const bool xw = t < kXThreads;
-  const int nsl = (Lu + 7) / 8;
+  const int sw = (Lu + kPerXcd - 1) / kPerXcd;
+  const int c0 = li * sw, nsc = max(0, min(Lu, c0 + sw) - c0);
+  const unsigned gw = gen + A.wait_skew;
+  const bool ftest = A.wait_skew != 0;
   bool ok = true;
-  for (int r = w; r < nsl; r += G) {
-    // word k of thread t: element e = 256 k + t of the (producer, column)
-    // grid, producer e / 8, column 8 r + e % 8.  Thread t sums column t % 8
-    // over its producers in k order, shuffles (xor 32, 16, 8) sum the eight
-    // lanes of a wave that share the column, and the four waves' sums are
-    // added in wave order: a fixed order, with one barrier.
-    if (xw) {
-      float vals[kXLoads];
-      ok = ok && spin_tagged(
-          [&](int k) {
-            const int e = t + k * kXThreads;
-            return &A.xpart[(size_t)(e >> 3) * kLuMax + 8 * r + (e & 7)];
-          },
-          [&](int k) { return t + k * kXThreads < G * 8; }, gen + A.wait_skew, A.err, A.wait_skew != 0,
-          vals);
-      float v = 0.f;
+  // level A: wave wv, lane c sums column c0 + c over producers wv, wv + 4, ...
+  if (xw) {
+    float v = 0.f;
+    if (lane < nsc) {
+      float vals[8];
+      const uint64_t *pa = A.PA + (size_t)x * kPerXcd * kLuMax + c0 + lane;
+      ok = spin_tagged([&](int k) { return const_cast<uint64_t *>(pa + (size_t)(wv + 4 * k) * kLuMax); },
+                       [&](int) { return true; }, gw, A.err, A.herr, ftest, vals);
 #pragma unroll
-      for (int k = 0; k < kXLoads; ++k) v += vals[k];
-      v += __shfl_xor(v, 32, 64);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 8, 64);
-      if ((t & 63) < 8) L.red[(t >> 6) * 8 + (t & 7)] = v;
+      for (int k = 0; k < 8; ++k) v += vals[k];
     }
-    __syncthreads();
-    if (t < 8 * kXCopies) {
-      const int c = t & 7;
-      const float sum = (L.red[c] + L.red[8 + c]) + (L.red[16 + c] + L.red[24 + c]);
-      st_tag(&A.xT[(size_t)(t >> 3) * kLuMax + 8 * r + c], sum, gen);
-    }
-    if (r + G < nsl) __syncthreads();
+    L.red[wv * 64 + lane] = v;
   }
-  // all-gather, straight into the next phase's tables: w = l * t per group
-  uint64_t *xTw = A.xT + (size_t)(w % kXCopies) * kLuMax;
+  __syncthreads();
+  stamp(L, ph, 5);
+  // level B: lane c of wave 0 publishes the XCD sum of column c0 + c and sums
+  // it over the XCDs in XCD order; the total goes to this XCD's area (level C)
+  if (wv == 0 && lane < nsc && ok) {
+    const float xs = (L.red[lane] + L.red[64 + lane]) + (L.red[128 + lane] + L.red[192 + lane]);
+    uint64_t *pb = A.PB + (size_t)(gen & 1) * kXcd * kLuMax + c0 + lane;
+    st_tag(pb + (size_t)x * kLuMax, xs, gen);
+    float vals[kXcd];
+    ok = spin_tagged([&](int k) { return pb + (size_t)k * kLuMax; }, [&](int) { return true; }, gw,
+                     A.err, A.herr, ftest, vals);
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kXcd; ++k) tot += vals[k];
+    st_tag_xcd(A.PC + (size_t)x * kLuMax + c0 + lane, tot, gen, A.xcd_local);
+  }
+  stamp(L, ph, 6);
+  // level C, straight into the next phase's tables: w = l * t per group
+  uint64_t *pc = A.PC + (size_t)x * kLuMax;
   if (xw) {
     uint2 lraw[kGroupsPerThread];  // 4 fp16 l per group
 #pragma unroll
@@ -731,9 +800,9 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
     // every group's words in one wait, so a thread with several groups
     // polls them together rather than one round trip after another
     float tv[4 * kGroupsPerThread];
-    ok = ok && spin_tagged([&](int k) { return &xTw[tp.tcol[k >> 2] + (k & 3)]; },
+    ok = ok && spin_tagged([&](int k) { return &pc[tp.tcol[k >> 2] + (k & 3)]; },
                            [&](int k) { return (k >> 2) < tp.n && (k & 3) < tp.nval[k >> 2]; },
-                           gen + A.wait_skew, A.err, A.wait_skew != 0, tv);
+                           gw, A.err, A.herr, ftest, tv);
 #pragma unroll
     for (int i = 0; i < kGroupsPerThread; ++i) {
       if (i >= tp.n) break;
@@ -761,7 +830,11 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
 
 // --------------------------------------------------------------- kernel
 
-__global__ void __launch_bounds__(kThreads)
+// One 8-wave workgroup per CU (its LDS takes the CU), so two waves per
+// SIMD: telling the compiler so lets it keep many table reads in flight
+// (otherwise it may serialise them to fit a higher occupancy that can never
+// occur).
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_persist(PArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
   Lds L;
@@ -780,13 +853,14 @@ k_persist(PArgs A) {
   }
   const int w = blockIdx.x;
   const int U = A.nunits;
-  // the generation base: the tag of this workgroup's first partial word,
+  // the generation base: the tag of this workgroup's first partial word
+  // (every exchange writes column 0),
   // which the previous launch's last exchange wrote as its base + U (every
   // exchange writes it; zero after a reset), so launches, captured graph
   // replays included, continue one running count
-  const unsigned gen_base = __builtin_amdgcn_readfirstlane(
-      (unsigned)(ld_tag(&A.xpart[(size_t)w * kLuMax]) >> 32));
-  uint64_t *tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * 4 : nullptr;
+  const unsigned gen_base = __builtin_amdgcn_readfirstlane((unsigned)(
+      ld_tag(&A.PA[((size_t)(w % kXcd) * kPerXcd + w / kXcd) * kLuMax]) >> 32));
+  L.tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * kStamps : nullptr;
   // phase 0's copy list (kMaxSeg records of two 16-byte words), then its blocks
   for (int i = threadIdx.x; i < kMaxSeg * 2; i += kThreads)
     reinterpret_cast<uint4 *>(L.segbuf)[i] = reinterpret_cast<const uint4 *>(A.segs)[i];
@@ -797,7 +871,7 @@ k_persist(PArgs A) {
   }
   __syncthreads();
   for (int ph = 0; ph <= U; ++ph) {
-    if (tl && threadIdx.x == 0) tl[ph * 4 + 0] = __builtin_amdgcn_s_memrealtime();
+    stamp(L, ph, 0);
     // every context field the phase uses is read before first_product's
     // last barrier, after which waves 4-7 restage the context
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
@@ -816,11 +890,11 @@ k_persist(PArgs A) {
       __syncthreads();
     } else {
       second_product(A, ph, L);
-      if (tl && threadIdx.x == 0) tl[ph * 4 + 1] = __builtin_amdgcn_s_memrealtime();
+      stamp(L, ph, 2);
       if (ph == U) break;
     }
-    first_product(L);
-    if (tl && threadIdx.x == 0) tl[ph * 4 + 2] = __builtin_amdgcn_s_memrealtime();
+    first_product(L, ph);
+    stamp(L, ph, 4);
     const unsigned gen = gen_base + (unsigned)ph + 1u;
     exchange_publish(L, Lu, gen, A);
     // the partials, on the critical path, are issued before the next
@@ -832,13 +906,13 @@ k_persist(PArgs A) {
       stage_phase(A, ph + 1, L);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (!exchange_collect(L, Lu, gen, A, tp)) {
+    if (!exchange_collect(L, Lu, gen, A, tp, ph)) {
       // a wait gave up: let the next phase's copies into LDS land before
       // the workgroup (and its LDS) ends
       __builtin_amdgcn_s_waitcnt(0);
       return;
     }
-    if (tl && threadIdx.x == 0) tl[ph * 4 + 3] = __builtin_amdgcn_s_memrealtime();
+    stamp(L, ph, 7);
   }
 }
 
@@ -850,6 +924,46 @@ static size_t lds_bytes() {
 }
 
 int64_t persist_max_rows() { return 1; }
+
+constexpr size_t kPaBytes = sizeof(uint64_t) * kXcd * kPerXcd * kLuMax;
+constexpr size_t kPbBytes = sizeof(uint64_t) * 2 * kXcd * kLuMax;
+constexpr size_t kPcBytes = sizeof(uint64_t) * kXcd * kLuMax;
+
+__global__ void k_xcd_id(unsigned *out) {
+  if (threadIdx.x == 0) {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    out[blockIdx.x] = x & 15u;
+  }
+}
+
+// 1 when a grid of one workgroup per CU places workgroup w on XCD w % 8 (the
+// dispatcher's round robin over the XCDs), so levels A and C can stay in
+// each XCD's L2; 0 otherwise (device-scope stores throughout: correct on
+// any placement, slower); -1 on a HIP error.  Checked once per device.
+static int xcd_placement(int device) {
+  static std::mutex mu;
+  static std::map<int, int> known;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = known.find(device);
+  if (it != known.end()) return it->second;
+  const int G = kXcd * kPerXcd;
+  unsigned *d = nullptr;
+  std::vector<unsigned> h(G, 0xffffffffu);
+  int res = -1;
+  if (hipMalloc(&d, G * sizeof(unsigned)) == hipSuccess) {
+    hipLaunchKernelGGL(k_xcd_id, dim3(G), dim3(64), 0, 0, d);
+    if (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+        hipMemcpy(h.data(), d, G * sizeof(unsigned), hipMemcpyDeviceToHost) == hipSuccess) {
+      res = 1;
+      for (int w = 0; w < G; ++w)
+        if (h[w] != (unsigned)(w % kXcd)) res = 0;
+    }
+    (void)hipFree(d);
+  }
+  if (res >= 0) known[device] = res;
+  return res;
+}
 
 // Column-group width for the first product's lookups of a unit with Lu
 // columns on nt row tiles: among 1, 2, 4 (up to maxc, which divides every
@@ -890,7 +1004,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return LB_EHIP;
   const int G = prop.multiProcessorCount;
-  if (G < 1 || G > kXThreads || G % 32 != 0) return LB_EUNSUPPORTED;
+  if (G != kXcd * kPerXcd) return LB_EUNSUPPORTED;
   PersistPlan *P = new PersistPlan();
   P->device = device;
   P->G = G;
@@ -1004,9 +1118,13 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   for (int u = 0; u < P->nunits && ok; ++u) P->h_units[u].grp = P->d_groups + gfirst[u];
   ok = ok && hipMalloc(&P->d_units, sizeof(PUnit) * P->nunits) == hipSuccess &&
             hipMalloc(&P->d_layers, sizeof(PLayer) * P->nlayers) == hipSuccess &&
-            hipMalloc(&P->xpart, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess &&
-            hipMalloc(&P->xT, sizeof(uint64_t) * kXCopies * kLuMax) == hipSuccess &&
-            hipMalloc(&P->err, sizeof(unsigned) * 64) == hipSuccess;
+            hipMalloc(&P->PA, kPaBytes) == hipSuccess && hipMalloc(&P->PB, kPbBytes) == hipSuccess &&
+            hipMalloc(&P->PC, kPcBytes) == hipSuccess &&
+            hipMalloc(&P->err, sizeof(unsigned) * 64) == hipSuccess &&
+            hipHostMalloc(&P->herr, sizeof(unsigned) * 16,
+                          hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+            hipHostGetDevicePointer((void **)&P->herr_dev, P->herr, 0) == hipSuccess;
+  if (ok) *(volatile unsigned *)P->herr = 0u;
   ok = ok && hipMemcpy(P->d_units, P->h_units.data(), sizeof(PUnit) * P->nunits,
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(P->d_layers, P->h_layers.data(), sizeof(PLayer) * P->nlayers,
@@ -1060,8 +1178,13 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
   ok = ok && hipMemcpy(P->d_segs, segs.data(), sizeof(PSeg) * segs.size(), hipMemcpyHostToDevice) ==
                  hipSuccess;
   ok = ok && hipMemset(P->err, 0, sizeof(unsigned) * 64) == hipSuccess;
-  ok = ok && hipMemset(P->xpart, 0, sizeof(uint64_t) * (size_t)G * kLuMax) == hipSuccess;
-  ok = ok && hipMemset(P->xT, 0, sizeof(uint64_t) * kXCopies * kLuMax) == hipSuccess;
+  ok = ok && hipMemset(P->PA, 0, kPaBytes) == hipSuccess && hipMemset(P->PB, 0, kPbBytes) == hipSuccess &&
+       hipMemset(P->PC, 0, kPcBytes) == hipSuccess;
+  if (ok) {
+    const int xl = xcd_placement(device);
+    if (xl < 0) ok = false;
+    P->xcd_local = xl > 0;
+  }
   ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)P->lds) == hipSuccess;
   int occ = 0;
@@ -1081,21 +1204,34 @@ void persist_free(PersistPlan *p) {
   if (p->d_layers) (void)hipFree(p->d_layers);
   if (p->d_segs) (void)hipFree(p->d_segs);
   if (p->d_groups) (void)hipFree(p->d_groups);
-  if (p->xpart) (void)hipFree(p->xpart);
-  if (p->xT) (void)hipFree(p->xT);
+  if (p->PA) (void)hipFree(p->PA);
+  if (p->PB) (void)hipFree(p->PB);
+  if (p->PC) (void)hipFree(p->PC);
   if (p->err) (void)hipFree(p->err);
+  if (p->herr) (void)hipHostFree(p->herr);
   delete p;
 }
 
 lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t *trace, int64_t M,
                       hipStream_t st, std::string *msg) {
   if (M != 1) return LB_EUNSUPPORTED;
+  if (!p->broken && *(volatile unsigned *)p->herr != 0u) {
+    // a finished earlier launch gave up a wait: its output was undefined.
+    // Report it once; the next call resets and runs.
+    p->broken = true;
+    if (msg) *msg = "persistent sweep: an earlier launch gave up a device-side wait (its output is "
+                    "undefined); this call did not run, the next one resets the sweep";
+    return LB_ETIMEOUT;
+  }
   if (p->broken) {
     // a previous launch gave up a wait: clear the error word and every tag
-    if (hipMemset(p->err, 0, sizeof(unsigned) * 64) != hipSuccess ||
-        hipMemset(p->xpart, 0, sizeof(uint64_t) * (size_t)p->G * kLuMax) != hipSuccess ||
-        hipMemset(p->xT, 0, sizeof(uint64_t) * kXCopies * kLuMax) != hipSuccess)
+    // (synchronous: the launch that failed has finished before the reset)
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemset(p->err, 0, sizeof(unsigned) * 64) != hipSuccess ||
+        hipMemset(p->PA, 0, kPaBytes) != hipSuccess || hipMemset(p->PB, 0, kPbBytes) != hipSuccess ||
+        hipMemset(p->PC, 0, kPcBytes) != hipSuccess)
       return LB_EHIP;
+    *(volatile unsigned *)p->herr = 0u;
     p->broken = false;
   }
   PArgs A{};
@@ -1105,9 +1241,12 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.x0 = x0;
   A.y = y;
   A.trace = trace;
-  A.xpart = p->xpart;
-  A.xT = p->xT;
+  A.PA = p->PA;
+  A.PB = p->PB;
+  A.PC = p->PC;
+  A.xcd_local = p->xcd_local;
   A.err = p->err;
+  A.herr = p->herr_dev;
   A.timeline = p->timeline;
   A.segs = p->d_segs;
   A.grp0 = p->d_groups;
@@ -1125,6 +1264,7 @@ void persist_set_timeline(PersistPlan *p, uint64_t *buf) { p->timeline = buf; }
 void persist_set_fail_test(PersistPlan *p, bool on) { p->fail_test = on; }
 int persist_grid(const PersistPlan *p) { return p->G; }
 int persist_phases(const PersistPlan *p) { return p->nunits + 1; }
+int persist_stamps() { return kStamps; }
 
 lb_status persist_check(PersistPlan *p, std::string *msg) {
   unsigned e = 0;

@@ -235,10 +235,12 @@ lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t *elems);
  * its synchronisation words before the next sweep).  LB_OK otherwise. */
 lb_status lb_stack_check(lb_stack *S);
 
-/* Diagnostics: record, in later persistent sweeps, four device timestamps
- * (100 MHz counter) per phase and workgroup into the caller's device buffer
- * buf (uint64, layout [workgroup][phase][4]: phase start, second product
- * done, first product done, exchange done).  *needed receives the element
+/* Diagnostics: record, in later persistent sweeps, eight device timestamps
+ * (100 MHz counter) per phase and workgroup, taken by its first thread, into
+ * the caller's device buffer buf (uint64, layout [workgroup][phase][8]:
+ * phase start, second-product lookups done, second product done (epilogue
+ * and combine), first-product tables built, first product done, exchange
+ * level A done, level B done, exchange done).  *needed receives the element
  * count.  buf = NULL turns recording off.  The buffer must outlive its use. */
 lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed);
 

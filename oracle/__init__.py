@@ -43,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "unpack_signs", "pack_signs", "num_bits", "eff_bits", "rank_for_bpw",
-    "forward", "forward_path", "dense_weight", "combine", "stack_units",
+    "forward", "forward_path", "latent", "from_latent", "dense_weight", "combine", "stack_units",
     "sign_words", "rank1_magnitude", "init_from_factors", "svd_factors", "dual_svid",
     "sign_pm1", "procrustes_rotation", "itq_loss", "joint_itq_rotation", "joint_itq",
 ]
@@ -144,6 +144,42 @@ def forward(x, paths) -> np.ndarray:
     for p in paths:
         v = forward_path(x, p)
         y = v if y is None else y + v
+    return y
+
+
+def latent(x, paths) -> np.ndarray:
+    """The layer's latent vector: w_p = l_p * (S_V,p^T (g_p * x)) for each path,
+    placed path-major (columns p*s .. p*s + s - 1 belong to path p), float64.
+
+    [LB news] Sec. 2: the first binary product and the latent scale, which
+    is where a cache of factorised K/V projections would keep its entries
+    ([LB news] Sec. 4).  ``x`` is (M x a) fp16; the result is (M x P*s).
+    """
+    cols = []
+    x = _f64(x)
+    for p in paths:
+        S_V = unpack_signs(p["sv"], p["s"]).astype(np.float64)   # a x s
+        t = (x * _f64(p["g"])[None, :]) @ S_V                     # first binary product
+        cols.append(t * _f64(p["l"])[None, :])                    # latent scale
+    return np.concatenate(cols, axis=1)
+
+
+def from_latent(w, paths) -> np.ndarray:
+    """The second half of the layer: y = sum_p h_p * (S_U,p w_p) for a latent
+    ``w`` (M x P*s, path-major, any float type), float64 (M x b).
+
+    [LB news] Sec. 2: the second binary product and the row scale; the
+    paths are summed.  from_latent(latent(x)) is the forward of x.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    y = None
+    off = 0
+    for p in paths:
+        s = p["s"]
+        S_U = unpack_signs(p["su"], s).astype(np.float64)   # b x s
+        v = (w[:, off:off + s] @ S_U.T) * _f64(p["h"])[None, :]
+        y = v if y is None else y + v
+        off += s
     return y
 
 

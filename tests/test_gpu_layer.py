@@ -172,11 +172,11 @@ def test_split_stages_match_the_definition(lbm):
         lbm.lb_forward_stage1(L.handle, xd, w, M)
         lbm.lb_forward_stage2(L.handle, w, y, M)
         torch.cuda.synchronize()
-        w_ref = np.concatenate([
-            (x.astype(np.float64) * p["g"].astype(np.float64)) @ oracle.unpack_signs(p["sv"], s).astype(np.float64)
-            * p["l"].astype(np.float64) for p in paths], axis=1)
-        assert_parity(w.cpu().numpy(), w_ref, "latent w")
+        wg = w.cpu().numpy()
+        assert_parity(wg, oracle.latent(x, paths), "latent w")
         assert_parity(y.cpu().numpy(), oracle.forward(x, paths), "stage2 output")
+        # the second half alone: the oracle's product from the GPU's own latent
+        assert_parity(y.cpu().numpy(), oracle.from_latent(wg, paths), "stage2 from the GPU latent")
 
 
 def test_error_codes(lbm):

@@ -196,6 +196,28 @@ def test_persistent_sweep_parity(lbm, name, blocks):
     assert_parity(y.astype(np.float64), y1.astype(np.float64), "persistent vs per-layer")
 
 
+def test_llama70b_full_length_sweep(lbm):
+    """The measured configuration at full length: 80 blocks (240 matrices,
+    161 phases) in one launch with the trace.  Layers 0, 119 and 239 against
+    the oracle (teacher-forced) and every one of the 160 combines within one
+    fp16 ulp; an untraced sweep of the same input gives the same y bit for
+    bit, as bench.py's timed runs do."""
+    torch = lbtest.torch_dev()
+    say("[case] llama70b_mlp_stack, 80 blocks, one launch")
+    wl, S, paths = build_stack(lbm, "llama70b_mlp_stack", keep_paths=False)
+    assert len(wl["layers"]) == 240
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    check_stack(wl, paths, x0, y, tr, 1, sample=[0, 119, 239])
+    xd = lbtest.to_dev(x0)
+    y2 = torch.empty((1, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+    S.forward(xd, y2, None)
+    torch.cuda.synchronize()
+    S.check()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
+    S.close()
+
+
 def test_persistent_odd_widths(lbm):
     wl, S, paths = _odd_stack(lbm)
     say("[case] persistent odd widths")
@@ -238,8 +260,9 @@ def test_persistent_repeated_and_deterministic(lbm):
 def test_persistent_wait_failure_is_reported_and_recovers(lbm):
     """Failure path of the one-launch sweep, forced from the host: every
     device-side wait waits for words nobody writes (short bound), so the
-    kernel ends normally, lb_stack_check reports LB_ETIMEOUT, and the next
-    sweep resets the synchronisation words and is correct again."""
+    kernel ends normally; the next lb_stack_forward reports LB_ETIMEOUT
+    (and runs nothing), lb_stack_check reports it too, and the sweep after
+    that resets the synchronisation words and is correct again."""
     torch = lbtest.torch_dev()
     say("[case] persistent sweep with unsatisfiable waits")
     wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
@@ -250,10 +273,14 @@ def test_persistent_wait_failure_is_reported_and_recovers(lbm):
     lbm.lb_stack_test_wait_failure(S.handle, True)
     S.forward(xd, y2, None)
     torch.cuda.synchronize()
+    lbm.lb_stack_test_wait_failure(S.handle, False)
+    # the next forward after the failed sweep finished reports it, runs nothing
+    with pytest.raises(lbm.LBError) as ei:
+        S.forward(xd, y2, None)
+    assert ei.value.status == lbm.LB_ETIMEOUT
     with pytest.raises(lbm.LBError) as ei:
         S.check()
     assert ei.value.status == lbm.LB_ETIMEOUT
-    lbm.lb_stack_test_wait_failure(S.handle, False)
     for _ in range(3):
         S.forward(xd, y2, None)
     torch.cuda.synchronize()

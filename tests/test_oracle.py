@@ -177,6 +177,77 @@ def test_factorized_equals_brute_force_dense(a, b, s, res, M):
     assert _rel(oracle.dense_weight(paths), W_bf) <= 1e-12
 
 
+def _brute_force_latent(x, paths):
+    """w[m][p*s + k] = l_k * sum_i S_V[i, k] g_i x[m, i] by loops over Python floats."""
+    s = paths[0]["s"]
+    a = paths[0]["a"]
+    x = np.asarray(x, dtype=np.float16).astype(np.float64)
+    out = np.zeros((x.shape[0], len(paths) * s))
+    for pi, p in enumerate(paths):
+        g = [float(v) for v in p["g"]]
+        l = [float(v) for v in p["l"]]
+        for m in range(x.shape[0]):
+            for k in range(s):
+                acc = 0.0
+                for i in range(a):
+                    sv = 1.0 if _bit(p["sv"], i, k) else -1.0
+                    acc += sv * g[i] * x[m, i]
+                out[m, pi * s + k] = l[k] * acc
+    return out
+
+
+def _brute_force_from_latent(w, paths):
+    """y[m][j] = sum_p h_j sum_k S_U[j, k] w[m][p*s + k] by loops over Python floats."""
+    s, b = paths[0]["s"], paths[0]["b"]
+    y = np.zeros((w.shape[0], b))
+    for pi, p in enumerate(paths):
+        h = [float(v) for v in p["h"]]
+        for m in range(w.shape[0]):
+            for j in range(b):
+                acc = 0.0
+                for k in range(s):
+                    su = 1.0 if _bit(p["su"], j, k) else -1.0
+                    acc += su * float(w[m, pi * s + k])
+                y[m, j] += h[j] * acc
+    return y
+
+
+@pytest.mark.parametrize("a,b,s,res,M", [(5, 3, 2, False, 1), (7, 4, 33, True, 2),
+                                         (6, 9, 1, True, 3), (12, 5, 64, False, 2),
+                                         (40, 3, 65, True, 1)])
+def test_latent_and_second_half_against_loops(a, b, s, res, M):
+    """The split halves of the forward (the latent a cache would hold, and the
+    product from it) against nested loops, and their composition against the
+    brute-force dense forward."""
+    paths = lb_synth.layer_inputs(a, b, s, res, seed=a * 31 + s)
+    x = lb_synth.activations(M, a, seed=b + s)
+    w = oracle.latent(x, paths)
+    assert w.shape == (M, len(paths) * s)
+    assert _rel(w, _brute_force_latent(x, paths)) <= 1e-12
+    assert _rel(oracle.from_latent(w, paths), _brute_force_from_latent(w, paths)) <= 1e-12
+    y_bf, _ = _brute_force(x, paths)
+    assert _rel(oracle.from_latent(w, paths), y_bf) <= 1e-12
+
+
+def test_latent_path_order_and_scale():
+    """Path 1's columns follow path 0's, and the latent scale l multiplies its
+    own column only: doubling l_k of path 1 doubles column s + k alone."""
+    a, b, s = 9, 4, 5
+    paths = lb_synth.layer_inputs(a, b, s, True, seed=3)
+    x = lb_synth.activations(2, a, seed=4)
+    w = oracle.latent(x, paths)
+    assert np.array_equal(w[:, :s], oracle.latent(x, paths[:1]))
+    assert np.array_equal(w[:, s:], oracle.latent(x, paths[1:]))
+    p1 = dict(paths[1])
+    p1["l"] = p1["l"].copy()
+    p1["l"][2] = p1["l"][2] * np.float16(2)
+    w2 = oracle.latent(x, [paths[0], p1])
+    d = np.zeros_like(w, dtype=bool)
+    d[:, s + 2] = True
+    assert np.array_equal(w2[~d], w[~d])
+    assert np.array_equal(w2[:, s + 2], 2 * w[:, s + 2])
+
+
 def test_tiny_workload_dense_check():
     """The 256x256, s=32 single-path case against the dense reconstruction."""
     paths = lb_synth.layer_inputs(256, 256, 32, False, seed=0)
