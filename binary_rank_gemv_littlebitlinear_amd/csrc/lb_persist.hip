@@ -278,6 +278,7 @@ struct Lds {
   float *xs;           // 16 * kTMax input rows (fp16 values as fp32)
   float *red;          // kXThreads exchange scratch
   int *flags8;         // kWaves
+  int *xcnt;           // level-A arrivals of the exchange waves (grows by 4 a phase)
   PhaseCtx *ctx;
   PSeg *segbuf;        // [2][kMaxSeg] copy lists of this and the next phase
   uint64_t *tl;        // diagnostics: this workgroup's timestamps, or null
@@ -761,6 +762,9 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   const bool ftest = A.wait_skew != 0;
   bool ok = true;
   // level A: wave wv, lane c sums column c0 + c over producers wv, wv + 4, ...
+  // The four exchange waves meet through an LDS counter, not a workgroup
+  // barrier: waves 4-7 are still issuing the next phase's copies, and
+  // waiting for them would put that issue time on the critical path.
   if (xw) {
     float v = 0.f;
     if (lane < nsc) {
@@ -772,22 +776,35 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
       for (int k = 0; k < 8; ++k) v += vals[k];
     }
     L.red[wv * 64 + lane] = v;
+    // a wave's LDS operations complete in order: its sums land before its count
+    if (lane == 0) atomicAdd(L.xcnt, 1);
+    if (wv < 2) {
+      const int target = 4 * (ph + 1);
+      long sp = 0;
+      while (__hip_atomic_load(L.xcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target &&
+             ++sp < kSpin) {
+      }
+    }
   }
-  __syncthreads();
   stamp(L, ph, 5);
-  // level B: lane c of wave 0 publishes the XCD sum of column c0 + c and sums
-  // it over the XCDs in XCD order; the total goes to this XCD's area (level C)
-  if (wv == 0 && lane < nsc && ok) {
+  // level B, lane c: the XCD sum of column c0 + c is published by wave 1 and
+  // summed over the XCDs by wave 0 (its own XCD's term from LDS), so the
+  // polling wave never waits behind the acknowledgement of its own store;
+  // the total goes to this XCD's area (level C)
+  if (wv < 2 && lane < nsc) {
     const float xs = (L.red[lane] + L.red[64 + lane]) + (L.red[128 + lane] + L.red[192 + lane]);
     uint64_t *pb = A.PB + (size_t)(gen & 1) * kXcd * kLuMax + c0 + lane;
-    st_tag(pb + (size_t)x * kLuMax, xs, gen);
-    float vals[kXcd];
-    ok = spin_tagged([&](int k) { return pb + (size_t)k * kLuMax; }, [&](int) { return true; }, gw,
-                     A.err, A.herr, ftest, vals);
-    float tot = 0.f;
+    if (wv == 1) {
+      st_tag(pb + (size_t)x * kLuMax, xs, gen);
+    } else if (ok) {
+      float vals[kXcd];
+      ok = spin_tagged([&](int k) { return pb + (size_t)k * kLuMax; }, [&](int k) { return k != x; },
+                       gw, A.err, A.herr, ftest, vals);
+      float tot = 0.f;
 #pragma unroll
-    for (int k = 0; k < kXcd; ++k) tot += vals[k];
-    st_tag_xcd(A.PC + (size_t)x * kLuMax + c0 + lane, tot, gen, A.xcd_local);
+      for (int k = 0; k < kXcd; ++k) tot += k == x ? xs : vals[k];
+      st_tag_xcd(A.PC + (size_t)x * kLuMax + c0 + lane, tot, gen, A.xcd_local);
+    }
   }
   stamp(L, ph, 6);
   // level C, straight into the next phase's tables: w = l * t per group
@@ -850,6 +867,7 @@ k_persist(PArgs A) {
     L.xs = reinterpret_cast<float *>(p); p += 16 * kTMax * 4;
     L.red = reinterpret_cast<float *>(p); p += kXThreads * 4;
     L.flags8 = reinterpret_cast<int *>(p);
+    L.xcnt = L.flags8 + kWaves;
   }
   const int w = blockIdx.x;
   const int U = A.nunits;
@@ -862,6 +880,7 @@ k_persist(PArgs A) {
       ld_tag(&A.PA[((size_t)(w % kXcd) * kPerXcd + w / kXcd) * kLuMax]) >> 32));
   L.tl = A.timeline ? A.timeline + (size_t)w * (U + 1) * kStamps : nullptr;
   // phase 0's copy list (kMaxSeg records of two 16-byte words), then its blocks
+  if (threadIdx.x == 0) *L.xcnt = 0;
   for (int i = threadIdx.x; i < kMaxSeg * 2; i += kThreads)
     reinterpret_cast<uint4 *>(L.segbuf)[i] = reinterpret_cast<const uint4 *>(A.segs)[i];
   __syncthreads();
@@ -920,7 +939,7 @@ k_persist(PArgs A) {
 static size_t lds_bytes() {
   return kCtxBytes + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
          (size_t)(kTab2Floats + kTab1Floats + kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
-                  16 * kTMax + kXThreads + kWaves) * 4 + 64;
+                  16 * kTMax + kXThreads + kWaves + 1) * 4 + 64;
 }
 
 int64_t persist_max_rows() { return 1; }
