@@ -435,7 +435,7 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const int m = tk < ntk ? mp >> 1 : 0, p = mp & 1;
       const PLayer &Ly = C.la[m];
       const int P = Ly.P, Wk = Ly.Wk, s2o = C.s2_off[m];
-      const float *tb = L.tab2 + Ly.tb2 + p * Wk * 128;
+      const uint32_t tba = lds_addr(L.tab2) + 4u * (uint32_t)(Ly.tb2 + p * Wk * 128);
       float acc = 0.f;
       if (tk < ntk && p < P) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
@@ -451,9 +451,18 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
           float v[4][8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float *tq = tb + min(q + i * lpt, Wk - 1) * 128;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) v[i][n] = tq[n * 16 + ((wd[i] >> (4 * n)) & 15u)];
+            // the word's 8 tables are one 512-byte block: entry address =
+            // block | nibble * 4, table n at immediate offset 64 n
+            const uint32_t tq = tba + 512u * (uint32_t)min(q + i * lpt, Wk - 1);
+            const uint32_t w = wd[i];
+            v[i][0] = lds_f32(tq | nib_off<0>(w));
+            v[i][1] = lds_f32((tq | nib_off<4>(w)) + 64);
+            v[i][2] = lds_f32((tq | nib_off<8>(w)) + 128);
+            v[i][3] = lds_f32((tq | nib_off<12>(w)) + 192);
+            v[i][4] = lds_f32((tq | nib_off<16>(w)) + 256);
+            v[i][5] = lds_f32((tq | nib_off<20>(w)) + 320);
+            v[i][6] = lds_f32((tq | nib_off<24>(w)) + 384);
+            v[i][7] = lds_f32((tq | nib_off<28>(w)) + 448);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {

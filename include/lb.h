@@ -238,8 +238,8 @@ lb_status lb_stack_check(lb_stack *S);
 /* Diagnostics: record, in later persistent sweeps, eight device timestamps
  * (100 MHz counter) per phase and workgroup, taken by its first thread, into
  * the caller's device buffer buf (uint64, layout [workgroup][phase][8]:
- * phase start, second-product lookups done, second product done (epilogue
- * and combine), first-product tables built, first product done, exchange
+ * phase start, second-product lookups done (first wave), second product
+ * done (epilogue and combine), first-product tables built, first product done, exchange
  * level A done, level B done, exchange done).  *needed receives the element
  * count.  buf = NULL turns recording off.  The buffer must outlive its use. */
 lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *needed);
