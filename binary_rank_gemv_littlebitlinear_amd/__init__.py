@@ -46,6 +46,7 @@ def load_library(path: str = LIB_PATH):
         "lb_pack_signs": ([vp, i32, vp, vp], i32),
         "lb_set_scales": ([vp, i32, vp, vp, vp], i32),
         "lb_forward": ([vp, vp, vp, i64, vp], i32),
+        "lb_forward_noalloc": ([vp, vp, vp, i64, vp], i32),
         "lb_unpack_signs": ([vp, i32, vp, vp], i32),
         "lb_get_scales": ([vp, i32, vp, vp, vp], i32),
         "lb_init_from_factors": ([vp, i32, vp, vp, vp, vp], i32),
@@ -77,7 +78,8 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_unpack_signs",
+EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_forward_noalloc",
+            "lb_unpack_signs",
             "lb_get_scales", "lb_init_from_factors", "lb_joint_itq",
             "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
@@ -150,6 +152,10 @@ def lb_set_scales(layer: int, path: int, h, g, l):
 
 def lb_forward(layer: int, x, y, M: int, stream=None):
     _check(load_library().lb_forward(layer, _ptr(x), _ptr(y), int(M), _stream(stream)))
+
+
+def lb_forward_noalloc(layer: int, x, y, M: int, stream=None):
+    _check(load_library().lb_forward_noalloc(layer, _ptr(x), _ptr(y), int(M), _stream(stream)))
 
 
 def lb_forward_stage1(layer: int, x, w, M: int, stream=None):

@@ -498,38 +498,82 @@ static lb_status check_io(const Layer &Ly, const void *x, const void *y, int64_t
   return LB_OK;
 }
 
-static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
-                              hipStream_t st) {
+// The forward of one layer with the scratch it needs taken from `ws`
+// (ws_bytes) and `cnt` (cnt_entries split-K tile counters, zero on entry and
+// left zero).  Wave-path launches take as many rows as the partials of ws
+// allow (at most 63); LB_EUNSUPPORTED when not even one row, or the
+// matrix-core path, fits.
+lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
+                          hipStream_t st, void *ws, size_t ws_bytes, unsigned *cnt,
+                          size_t cnt_entries, std::string *msg) {
   const Layer &Ly = L->ly;
   DevCtx *dc = ctx_of(L);
   if (M < 64) {
-    // rows in blocks of wave_rows, so the chunk partials fit the layer's workspace
-    for (int64_t m0 = 0; m0 < M; m0 += Ly.wave_rows) {
-      const int64_t Mc = std::min<int64_t>(Ly.wave_rows, M - m0);
-      const int nch = wave_nchunk(Ly, Mc, dc->info);
-      float *part = Ly.ws;
+    const int nch = wave_nchunk(Ly, 1, dc->info);
+    const size_t per_row = (wave_ws_floats(Ly, 1, nch) + (size_t)Ly.L) * sizeof(float);
+    const int64_t rows = std::min<int64_t>(63, (int64_t)(ws_bytes / per_row));
+    if (rows < 1) {
+      if (msg) *msg = "scratch too small for one row of the wave path (needs " + std::to_string(per_row) + " bytes)";
+      return LB_EUNSUPPORTED;
+    }
+    for (int64_t m0 = 0; m0 < M; m0 += rows) {
+      const int64_t Mc = std::min<int64_t>(rows, M - m0);
+      float *part = reinterpret_cast<float *>(ws);
       float *w = part + wave_ws_floats(Ly, Mc, nch);
       hipError_t e = launch_wave_stage1(Ly, x + m0 * Ly.a, w, Mc, nch, part, st);
-      if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 1: ") + hipGetErrorString(e));
-      e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, st);
-      if (e != hipSuccess) return fail(LB_EHIP, std::string("wave stage 2: ") + hipGetErrorString(e));
+      if (e == hipSuccess) e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, st);
+      if (e != hipSuccess) {
+        if (msg) *msg = std::string("wave path: ") + hipGetErrorString(e);
+        return LB_EHIP;
+      }
     }
     return LB_OK;
   }
+  if (mfma_unit_ws_bytes(L->mplan) > ws_bytes || mfma_cnt_entries(L->mplan) > cnt_entries) {
+    if (msg)
+      *msg = "scratch too small for the matrix-core path (needs " +
+             std::to_string(mfma_unit_ws_bytes(L->mplan)) + " bytes and " +
+             std::to_string(mfma_cnt_entries(L->mplan)) + " counters)";
+    return LB_EUNSUPPORTED;
+  }
   uint16_t *ys[1] = {y};
-  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, Ly.ws, Ly.cnt, dc->zero,
-                                 dc->info, st);
-  if (e != hipSuccess) return fail(LB_EHIP, std::string("mfma path: ") + hipGetErrorString(e));
+  hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, ws, cnt, dc->zero, dc->info, st);
+  if (e != hipSuccess) {
+    if (msg) *msg = std::string("mfma path: ") + hipGetErrorString(e);
+    return LB_EHIP;
+  }
   return LB_OK;
 }
 
-extern "C" lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream) {
-  if (!L) return fail(LB_EINVAL, "lb_forward: NULL layer");
+// The layer's own workspace (sized at create time for every M).
+static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
+                              hipStream_t st) {
   const Layer &Ly = L->ly;
-  lb_status st = check_io(Ly, x, y, M, "lb_forward");
+  std::string msg;
+  const lb_status r = forward_ws(L, x, y, M, st, Ly.ws, Ly.ws_bytes, Ly.cnt,
+                                 std::max<size_t>(1, mfma_cnt_entries(L->mplan)), &msg);
+  return r == LB_OK ? r : fail(r, "lb_forward: " + msg);
+}
+
+// Checks shared by lb_forward and its allocation-free variant.
+lb_status lbi::forward_checks(const lb_layer *L, const void *x, const void *y, int64_t M,
+                              const char *who) {
+  if (!L) return fail(LB_EINVAL, std::string(who) + ": NULL layer");
+  const Layer &Ly = L->ly;
+  lb_status st = check_io(Ly, x, y, M, who);
   if (st != LB_OK || M == 0) return st;
   if (overlaps(x, (size_t)M * Ly.a * 2, y, (size_t)M * Ly.b * 2))
-    return fail(LB_EINVAL, "lb_forward: x and y overlap");
+    return fail(LB_EINVAL, std::string(who) + ": x and y overlap");
+  return LB_OK;
+}
+
+lb_status lbi::set_error(lb_status st, const std::string &msg) { return fail(st, msg); }
+const void *lbi::device_zero(const lb_layer *L) { return ctx_of(L)->zero; }
+
+extern "C" lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream) {
+  lb_status st = forward_checks(L, x, y, M, "lb_forward");
+  if (st != LB_OK || M == 0) return st;
+  const Layer &Ly = L->ly;
   DeviceGuard dg(Ly.device);
   return forward_impl(L, (const uint16_t *)x, (uint16_t *)y, M, (hipStream_t)stream);
 }

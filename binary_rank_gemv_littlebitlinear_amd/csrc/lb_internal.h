@@ -167,6 +167,14 @@ int joint_itq_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t 
 int rotate_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int64_t s,
                        const double *R, double *out, hipStream_t st, std::string *msg);
 
+// The forward of one layer with caller-chosen scratch (see lb_api.hip),
+// the argument checks of lb_forward, and the thread-local error text.
+lb_status forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M, hipStream_t st,
+                     void *ws, size_t ws_bytes, unsigned *cnt, size_t cnt_entries, std::string *msg);
+lb_status forward_checks(const lb_layer *L, const void *x, const void *y, int64_t M, const char *who);
+lb_status set_error(lb_status st, const std::string &msg);
+const void *device_zero(const lb_layer *L);
+
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,
                           int64_t elems, hipStream_t st);

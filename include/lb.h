@@ -98,6 +98,25 @@ lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t
  * unless every path has signs and scales. */
 lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
 
+/* lb_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same result as lb_forward, bit for bit, but the
+ * scratch they need lives in one fixed 32 MB device array of the library
+ * (16 KB of split-K tile counters plus 32 MB - 16 KB of workspace), held on
+ * each device the library runs on until the process ends, instead of the
+ * layer's own workspace.  Allocates nothing and makes no host
+ * synchronisation.  The first call on a device looks the array's address
+ * up (hipGetSymbolAddress) and clears its counters with a kernel on
+ * `stream`; every launch leaves them zero.  All calls on one device share
+ * the array, which keeps the last call's contents: calls that overlap on
+ * one device (other streams, concurrent host threads) race, so order them.
+ * M < 64 runs the wave path in row blocks that fit the array; M >= 64 the
+ * matrix-core path, which needs its latent (256 rows of the padded latent
+ * width) and split partials within the array.  LB_EUNSUPPORTED, with
+ * nothing launched, when a layer needs more (not even one wave-path row, or
+ * the matrix-core path, fits); the other errors as lb_forward. */
+lb_status lb_forward_noalloc(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
+
 /* Read the device signs of one path back into canonical words (padding
  * bits zero).  Bit-exact inverse of lb_pack_signs; synchronous. */
 lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, uint32_t *sv);
