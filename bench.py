@@ -32,6 +32,7 @@ import lb_synth  # noqa: E402
 METRIC = ("LittleBit linear fwd: µs/layer + achieved HBM GB/s vs 8 TB/s at batch 1; "
           "M=128 TFLOP/s")
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 
 
@@ -102,6 +103,30 @@ def measured_traffic(workload: str, kind: str, blocks):
     if t.get("kernel_source_sha256_16") != kernel_hash(kind) or t.get("blocks") != blocks:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def mall_reference(torch, nbytes: int, reps: int = 50) -> dict:
+    """Read bandwidth of a buffer of the workload's own size when it fits the
+    256 MB MALL: torch's sum over an fp16 buffer of ``nbytes``, read ``reps``
+    times after a warm-up (the first pass brings it in; later passes read it
+    from the MALL).  The reference the stack's algorithmic GB/s is set
+    against for a MALL-resident working set."""
+    n = nbytes // 2
+    buf = torch.ones(n, dtype=torch.float16, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        torch.sum(buf, dim=0, dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.sum(buf, dim=0, dtype=torch.float32, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"buffer_bytes": 2 * n, "read_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "kernel": "torch.sum over the buffer, fp16 read, fp32 accumulate",
+            "reps": reps}
 
 
 def copy_probe(torch, mib: int):
@@ -331,6 +356,11 @@ def main():
     }
     if "cpu" in r:
         out["cpu_baseline"] = r["cpu"]
+    if batch1 and r["bytes"] <= MALL_BYTES // 2:
+        # a working set that fits the MALL: also set against a measured MALL read rate
+        ref = mall_reference(torch, r["bytes"])
+        ref["stack_frac_of_mall_read"] = round(gbs / ref["read_GBs"], 4)
+        out["mall_reference"] = ref
     if args.secondary and args.secondary != args.workload:
         s2 = measure(args.secondary, None, False)
         ms2 = s2["ms"]
