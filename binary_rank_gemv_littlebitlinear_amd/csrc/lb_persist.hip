@@ -76,7 +76,20 @@ constexpr int kTMax = 8;        // 16-row tiles per workgroup and width
 constexpr int kMaxUnitLayers = 8;
 constexpr int kLuMax = 2048;    // latent columns per unit
 constexpr int kStgBytes = 56 * 1024;
-constexpr int kTab2Floats = 10240;
+constexpr int kTab2Floats = 11264;
+// Table layouts (floats).  Every table is 16 entries, 64-byte aligned, so an
+// entry address is the table address OR-ed with nibble * 4.  Blocks are
+// padded by one table so that reads of neighbouring blocks by one wave land
+// on the other half of the LDS banks instead of the same banks:
+//   second product: a word's 8 tables form a block of kWordF floats; the
+//   blocks of one (layer, path) form a set of s2_set_floats(Wk) floats,
+//   rounded so that consecutive sets start on alternating bank halves;
+//   first product: a 16-row tile's 4 tables form a block of kTileF floats;
+//   the tiles of one (layer, path) form a set of s1_set_floats(nt) floats.
+constexpr int kWordF = 8 * 16 + 16;
+constexpr int kTileF = 4 * 16 + 16;
+__host__ __device__ constexpr int s2_set_floats(int Wk) { return (Wk * kWordF + 31) / 32 * 32 + 16; }
+__host__ __device__ constexpr int s1_set_floats(int nt) { return (nt * kTileF + 31) / 32 * 32 + 16; }
 constexpr int kTab1Floats = 4096;
 constexpr long kSpin = 4000000;      // polls before a wait gives up
 constexpr long kSpinFailTest = 2048;  // the same in the host-requested failure test
@@ -89,7 +102,8 @@ struct alignas(16) PLayer {
   const uint16_t *sv16, *ht, *gt, *l;
   int a, b, s, P, L, Lp, Wk, a16, b16, s8;
   int col0;         // first latent column within the unit
-  int tb2;          // offset (floats) of the layer's path-0 second-product tables; path p at + p Wk 128
+  int tb2;          // offset (floats) of the layer's path-0 second-product tables; path p at
+                    // + p s2_set_floats(Wk)
   int64_t trace_y;  // element offset of this layer's output in the trace
 };
 
@@ -435,7 +449,7 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       const int m = tk < ntk ? mp >> 1 : 0, p = mp & 1;
       const PLayer &Ly = C.la[m];
       const int P = Ly.P, Wk = Ly.Wk, s2o = C.s2_off[m];
-      const uint32_t tba = lds_addr(L.tab2) + 4u * (uint32_t)(Ly.tb2 + p * Wk * 128);
+      const uint32_t tba = lds_addr(L.tab2) + 4u * (uint32_t)(Ly.tb2 + p * s2_set_floats(Wk));
       float acc = 0.f;
       if (tk < ntk && p < P) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
@@ -451,9 +465,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
           float v[4][8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // the word's 8 tables are one 512-byte block: entry address =
+            // the word's 8 tables are one block: entry address =
             // block | nibble * 4, table n at immediate offset 64 n
-            const uint32_t tq = tba + 512u * (uint32_t)min(q + i * lpt, Wk - 1);
+            const uint32_t tq = tba + 4u * kWordF * (uint32_t)min(q + i * lpt, Wk - 1);
             const uint32_t w = wd[i];
             v[i][0] = lds_f32(tq | nib_off<0>(w));
             v[i][1] = lds_f32((tq | nib_off<4>(w)) + 64);
@@ -532,7 +546,8 @@ __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLay
   }
   const int sub = threadIdx.x & (lpt - 1);
   const uint32_t taba = lds_addr(L.tab1), stga = lds_addr(L.stg);
-  constexpr uint32_t kTileBytes = 256u;  // tables of one pair and tile: 4 x 16 floats
+  constexpr uint32_t kTileBytes = 4u * kTileF;  // the block of one pair and tile
+  const uint32_t kPairBytes = 4u * (uint32_t)s1_set_floats(nt);
   for (int q0 = 0; q0 < ngr; q0 += kThreads >> lg) {
     const int q = q0 + ((int)threadIdx.x >> lg);
     float acc[CPT];
@@ -550,7 +565,7 @@ __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLay
       uint32_t tq[CPT];  // the column's tile-0 tables (its path's)
 #pragma unroll
       for (int j = 0; j < CPT; ++j)
-        tq[j] = taba + kTileBytes * (uint32_t)((m * Pu + (cl + j < s ? 0 : 1)) * nt);
+        tq[j] = taba + kPairBytes * (uint32_t)(m * Pu + (cl + j < s ? 0 : 1));
       for (int g0 = sub; g0 < nt; g0 += 2 * lpt) {
         uint32_t wd[2][(CPT + 1) / 2];
 #pragma unroll
@@ -621,7 +636,7 @@ __device__ void first_product(Lds &L, int ph) {
     return;
   }
   // every layer of a unit has the same path count Pu; pair j = m Pu + p
-  // (layer m, path p) has its tables at tab1 + j * quads * 16
+  // (layer m, path p) has its tile blocks at tab1 + j * s1_set_floats(nt)
   const int Pu = LB[0].P;
   // tables from z = g * x: thread t builds the table of quad t % 32 of pair t / 32
   {
@@ -635,7 +650,7 @@ __device__ void first_product(Lds &L, int ph) {
         const int r = 4 * qd + k;
         v[k] = h2f(gv[((r >> 4) * Pu + p) * 16 + (r & 15)]) * L.xs[r];
       }
-      float *tab = L.tab1 + (j * quads + qd) * 16;
+      float *tab = L.tab1 + j * s1_set_floats(nt) + (qd >> 2) * kTileF + (qd & 3) * 16;
 #pragma unroll
       for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
     }
@@ -1099,10 +1114,10 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
           // a group past s reads nothing; its l pointer is the (valid) base
           g.lp = nval > 0 ? D.l + (size_t)p * D.s8 + 4 * rem : D.l;
           g.tcol = D.col0 + p * D.s + 4 * rem;
-          g.nd = nval | ((toff + rem * 16) << 4);
+          g.nd = nval | ((toff + (rem >> 3) * kWordF + (rem & 7) * 16) << 4);
           groups.push_back(g);
         }
-        toff += D.Wk * 8 * 16;
+        toff += s2_set_floats(D.Wk);
       }
     }
     U.ngrp = (int)(groups.size() - gfirst.back());
@@ -1125,7 +1140,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
       for (int m = 0; m < U.n; ++m) {
         const PLayer &D = P->h_layers[U.first + m];
         stg += (long)D.P * ((long)D.Wk * 64 * nt + 32 * nt + 2 * D.s8);
-        tab2 += (long)D.P * D.Wk * 128;
+        tab2 += (long)D.P * s2_set_floats(D.Wk);
       }
     }
     if (ph < P->nunits) {
@@ -1133,7 +1148,7 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
       for (int m = 0; m < U.n; ++m) {
         const PLayer &D = P->h_layers[U.first + m];
         stg += (long)nt * D.Lp * 2 + (long)D.P * 32 * nt;
-        tab1 += (long)D.P * 64 * nt;
+        tab1 += (long)D.P * s1_set_floats(nt);
       }
     }
     if (stg > kStgBytes || tab2 > kTab2Floats || tab1 > kTab1Floats) return unsupported();
