@@ -313,6 +313,19 @@ def main():
         nbytes, flops = algorithmic_bytes(wl, M), algorithmic_flops(wl, M)
         res = {"wl": wl, "M": M, "ms": ms, "wall_ms": wall_ms, "bytes": nbytes, "flops": flops,
                "validated": checked}
+        if len(wl["layers"]) == 1:
+            # a single matrix: also the latency of one lb_forward call on it
+            L0 = stack.layers[0]
+            for _ in range(20):
+                L0.forward(x, y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(200):
+                L0.forward(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            res["layer_forward_us"] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
         if with_cpu:
             print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
             res["cpu"] = cpu_baseline(wl, M, args.cpu_budget)
@@ -344,6 +357,7 @@ def main():
         "tokens_per_s_equiv": round(M / (ms * 1e-3), 1),
         "algorithmic_bytes_per_step": r["bytes"],
         "validated": r["validated"],
+        **({"layer_forward_us": r["layer_forward_us"]} if "layer_forward_us" in r else {}),
         "roofline": {"bound": "hbm" if batch1 else "mfma",
                      "achieved": round(gbs if batch1 else tflops, 3),
                      "peak": HBM_PEAK_GBS if batch1 else MFMA_FP16_PEAK_TFLOPS,

@@ -42,6 +42,9 @@ namespace {
 struct DevCtx {
   DeviceInfo info;
   void *zero = nullptr;  // 256 zero bytes
+  // pinned host word set by a one-launch M = 1 forward whose wait gave up
+  // (reported by the next such lb_forward on the device), and its device address
+  unsigned *herr = nullptr, *herr_dev = nullptr;
 };
 std::mutex g_mu;
 std::map<int, DevCtx> g_dev;
@@ -59,7 +62,10 @@ lb_status get_dev(int device, DevCtx **out) {
     c.info.coop = prop.cooperativeLaunch;
     e = hipMalloc(&c.zero, 256);
     if (e == hipSuccess) e = hipMemset(c.zero, 0, 256);
-    if (e != hipSuccess) return fail(LB_ENOMEM, std::string("zero block hipMalloc: ") + hipGetErrorString(e));
+    if (e == hipSuccess) e = hipHostMalloc(&c.herr, 64, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&c.herr_dev, c.herr, 0);
+    if (e != hipSuccess) return fail(LB_ENOMEM, std::string("device context allocation: ") + hipGetErrorString(e));
+    *(volatile unsigned *)c.herr = 0u;
     it = g_dev.emplace(device, c).first;
   }
   *out = &it->second;
@@ -214,6 +220,16 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
   hipError_t e = hipMalloc(&Ly.ws, Ly.ws_bytes);
   if (e == hipSuccess) e = hipMalloc(&Ly.cnt, ncnt * sizeof(unsigned));
   if (e == hipSuccess) e = hipMemset(Ly.cnt, 0, ncnt * sizeof(unsigned));
+  {
+    Forward1Plan pl;
+    if (e == hipSuccess && forward1_plan(Ly, dc->info, &pl)) {
+      L->f1plan = new (std::nothrow) Forward1Plan(pl);
+      if (!L->f1plan) e = hipErrorOutOfMemory;
+      if (e == hipSuccess) e = hipMalloc(&Ly.f1state, pl.state_bytes);
+      if (e == hipSuccess) e = hipMemset(Ly.f1state, 0, pl.state_bytes);
+      L->f1 = e == hipSuccess;
+    }
+  }
   if (e != hipSuccess) {
     lb_destroy(L);
     return fail(LB_ENOMEM, std::string("lb_create: workspace hipMalloc: ") + hipGetErrorString(e));
@@ -227,10 +243,11 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
   void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m,
-                Ly.ws, Ly.cnt};
+                Ly.ws, Ly.cnt, Ly.f1state};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   mfma_plan_free(L->mplan);
+  delete L->f1plan;
   delete L;
   return LB_OK;
 }
@@ -545,10 +562,22 @@ lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int
   return LB_OK;
 }
 
-// The layer's own workspace (sized at create time for every M).
+// The layer's own workspace (sized at create time for every M); one row
+// takes the one-launch forward when the layer fits it.
 static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
                               hipStream_t st) {
   const Layer &Ly = L->ly;
+  if (M == 1 && L->f1) {
+    DevCtx *dc = ctx_of(L);
+    if (*(volatile unsigned *)dc->herr != 0u) {
+      *(volatile unsigned *)dc->herr = 0u;
+      return fail(LB_ETIMEOUT, "lb_forward: an earlier one-row forward on this device gave up a "
+                               "device-side wait (its output is undefined); this call did not run");
+    }
+    hipError_t e = launch_forward1(Ly, *L->f1plan, Ly.f1state, dc->herr_dev, x, y, st);
+    if (e != hipSuccess) return fail(LB_EHIP, std::string("lb_forward: one-row launch: ") + hipGetErrorString(e));
+    return LB_OK;
+  }
   std::string msg;
   const lb_status r = forward_ws(L, x, y, M, st, Ly.ws, Ly.ws_bytes, Ly.cnt,
                                  std::max<size_t>(1, mfma_cnt_entries(L->mplan)), &msg);

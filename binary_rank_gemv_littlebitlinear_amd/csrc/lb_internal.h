@@ -86,6 +86,9 @@ struct Layer {
   size_t ws_bytes = 0;
   unsigned *cnt = nullptr;
   int wave_rows = 1;  // rows per wave-path launch pair (the partials fit ws)
+  // state of the one-launch M = 1 forward (ticket, generation, tagged
+  // partials and latent), zeroed at create; null when the layer is outside it
+  void *f1state = nullptr;
   bool ready() const {
     for (int p = 0; p < P; ++p)
       if (!signs_set[p] || !scales_set[p]) return false;
@@ -94,14 +97,20 @@ struct Layer {
 };
 
 struct MfmaPlan;
+struct Forward1Plan {
+  int G = 0, N1 = 0, NR = 0, N2 = 0, wpl = 0;
+  size_t lds = 0, state_bytes = 0;
+};
 
 }  // namespace lbi
 
 // The C ABI's opaque layer handle.
 struct lb_layer {
   lbi::Layer ly;
-  void *ctx = nullptr;  // the device context (workspace owner)
+  void *ctx = nullptr;  // the device context (device facts, zero block)
   lbi::MfmaPlan *mplan = nullptr;  // the layer as a one-layer MFMA unit
+  bool f1 = false;                 // the one-launch M = 1 forward applies
+  lbi::Forward1Plan *f1plan = nullptr;
 };
 
 namespace lbi {
@@ -116,6 +125,14 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
                               int nchunk, float *ws, hipStream_t st);
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
                               hipStream_t st);
+
+// One launch for M = 1 (first product, reduction, second product by
+// workgroup role; see lb_wave.hip).  state: state_bytes of device memory,
+// zero before the first launch, owned by the layer (launches on it must be
+// stream-ordered); herr: a host-mapped word set when a wait gives up.
+bool forward1_plan(const Layer &Ly, const DeviceInfo &dev, Forward1Plan *pl);
+hipError_t launch_forward1(const Layer &Ly, const Forward1Plan &pl, void *state, unsigned *herr,
+                           const uint16_t *x, uint16_t *y, hipStream_t st);
 
 // MFMA path (used for M >= 64) over a unit: 1..kMaxUnitLayersM layers of
 // one shape that read the same input.  Rows are processed kMfmaRows at a

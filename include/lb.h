@@ -91,17 +91,25 @@ lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t
 
 /* y[M x b] = layer(x[M x a]); x, y are device fp16.  M = 0 is a no-op.
  * M < 64 runs the wave-level binary GEMV path (sign-flip identity on
- * packed bits, fp32 throughout); M >= 64 runs the fp16 matrix-core path
- * (two launches: the first product with split K, then the second), in
+ * packed bits, fp32 throughout): one launch for M = 1 (workgroups take the
+ * first product, the reduction over input chunks and the second product by
+ * an atomic ticket, each waiting only on workgroups that started before it,
+ * so it needs no co-residency and may share the device with other
+ * streams), three launches otherwise; M >= 64 runs the fp16 matrix-core
+ * path (two launches: the first product with split K, then the second), in
  * which the latent vector t is rounded once to fp16 before the second
  * product; the +-g and +-l operands are exact.  Returns LB_ENOTREADY
- * unless every path has signs and scales. */
+ * unless every path has signs and scales; LB_ETIMEOUT (running nothing)
+ * when an earlier one-row forward on the device gave up a bounded
+ * device-side wait (which does not happen while the device runs its work;
+ * the flag is then cleared). */
 lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
 
 /* lb_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
- * the same kernels and the same result as lb_forward, bit for bit, but the
- * scratch they need lives in one fixed 32 MB device array of the library
+ * for M >= 2 the same kernels and the same result as lb_forward, bit for
+ * bit (for M = 1 the wave path's three launches, where lb_forward takes one;
+ * the two agree at the parity bar), but the scratch they need lives in one fixed 32 MB device array of the library
  * (16 KB of split-K tile counters plus 32 MB - 16 KB of workspace), held on
  * each device the library runs on until the process ends, instead of the
  * layer's own workspace.  Allocates nothing and makes no host

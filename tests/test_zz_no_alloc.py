@@ -1,9 +1,12 @@
 """lb_forward_noalloc: the layer forward with its scratch in the library's
 fixed device array (for callers that cannot allocate), through the C ABI.
 
-It runs the same kernels as lb_forward, so on the same input its output is
-the same bit for bit, and both meet the oracle's bar (layer definition:
-Samsung LittleBit news page, aifrontier.co.jp, Sec. 2).  Each case makes
+For M >= 2 it runs the same kernels as lb_forward, so on the same input
+its output is the same bit for bit; for one row lb_forward takes its
+one-launch kernel (different chunking of the first product) while this
+entry point keeps the three-launch wave path, so the two agree at the
+parity bar.  Both always meet the oracle's bar (layer definition: Samsung
+LittleBit news page, aifrontier.co.jp, Sec. 2).  Each case makes
 two calls in a row, the second with a smaller input (the array keeps the
 first call's contents).
 """
@@ -32,8 +35,14 @@ def _both(lbm, torch, L, paths, xh, what):
     lbm.lb_forward(L.handle, x, y_ref, M)
     lbm.lb_forward_noalloc(L.handle, x, y_na, M)
     torch.cuda.synchronize()
-    assert torch.equal(y_na.view(torch.int16), y_ref.view(torch.int16)), f"{what}: differs from lb_forward"
-    assert_parity(y_na.cpu().numpy(), oracle.forward(xh, paths), what)
+    if M >= 2:
+        assert torch.equal(y_na.view(torch.int16), y_ref.view(torch.int16)), f"{what}: differs from lb_forward"
+    else:
+        assert_parity(y_na.cpu().numpy().astype(np.float64), y_ref.cpu().numpy().astype(np.float64),
+                      f"{what} vs lb_forward")
+    ref = oracle.forward(xh, paths)
+    assert_parity(y_na.cpu().numpy(), ref, what)
+    assert_parity(y_ref.cpu().numpy(), ref, f"{what} (lb_forward)")
 
 
 @pytest.mark.parametrize("a,b,s,res,Ms", [(4096, 11008, 133, True, (70, 5)),
