@@ -325,7 +325,23 @@ def main():
                 L0.forward(x, y)
             e1.record()
             torch.cuda.synchronize()
-            res["layer_forward_us"] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+            res["layer_forward_us_eager"] = round(e0.elapsed_time(e1) / 200 * 1e3, 3)
+            # device time per call: 100 calls captured in a graph, replayed
+            # (the eager figure can be bound by the host's launch rate)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(100):
+                    L0.forward(x, y)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res["layer_forward_us"] = round(e0.elapsed_time(e1) / 1000 * 1e3, 3)
+            del g
         if with_cpu:
             print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
             res["cpu"] = cpu_baseline(wl, M, args.cpu_budget)
@@ -357,7 +373,8 @@ def main():
         "tokens_per_s_equiv": round(M / (ms * 1e-3), 1),
         "algorithmic_bytes_per_step": r["bytes"],
         "validated": r["validated"],
-        **({"layer_forward_us": r["layer_forward_us"]} if "layer_forward_us" in r else {}),
+        **({"layer_forward_us": r["layer_forward_us"],
+            "layer_forward_us_eager": r["layer_forward_us_eager"]} if "layer_forward_us" in r else {}),
         "roofline": {"bound": "hbm" if batch1 else "mfma",
                      "achieved": round(gbs if batch1 else tflops, 3),
                      "peak": HBM_PEAK_GBS if batch1 else MFMA_FP16_PEAK_TFLOPS,

@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH):
         "lb_init_from_factors": ([vp, i32, vp, vp, vp, vp], i32),
         "lb_joint_itq": ([vp, vp, i64, i64, i64, i32, vp, vp, vp], i32),
         "lb_layer_shape": ([vp, P(i64), P(i64), P(i64), P(i32)], i32),
+        "lb_prepare": ([vp, i64], i32),
+        "lb_layer_device_bytes": ([vp, P(u64), P(u64)], i32),
         "lb_destroy": ([vp], i32),
         "lb_forward_stage1": ([vp, vp, vp, i64, vp], i32),
         "lb_forward_stage2": ([vp, vp, vp, i64, vp], i32),
@@ -81,7 +83,7 @@ def load_library(path: str = LIB_PATH):
 EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_forward_noalloc",
             "lb_unpack_signs",
             "lb_get_scales", "lb_init_from_factors", "lb_joint_itq",
-            "lb_layer_shape", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
+            "lb_layer_shape", "lb_prepare", "lb_layer_device_bytes", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
             "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
             "lb_stack_test_wait_failure",
@@ -225,6 +227,16 @@ def lb_layer_shape(layer: int):
     return a.value, b.value, s.value, bool(r.value)
 
 
+def lb_prepare(layer: int, M: int):
+    _check(load_library().lb_prepare(layer, int(M)))
+
+
+def lb_layer_device_bytes(layer: int):
+    sb, tb = C.c_uint64(), C.c_uint64()
+    _check(load_library().lb_layer_device_bytes(layer, C.byref(sb), C.byref(tb)))
+    return sb.value, tb.value
+
+
 def lb_destroy(layer: int):
     _check(load_library().lb_destroy(layer))
 
@@ -306,6 +318,13 @@ class Layer:
 
     def forward(self, x, y, M=None, stream=None):
         lb_forward(self.handle, x, y, x.shape[0] if M is None else M, stream)
+
+    def prepare(self, M: int):
+        lb_prepare(self.handle, M)
+
+    def device_bytes(self):
+        """(sign bytes, total bytes) the layer holds on the device."""
+        return lb_layer_device_bytes(self.handle)
 
     def close(self):
         if self.handle:

@@ -1,7 +1,8 @@
 """Build the HIP library in-tree: ``python -m binary_rank_gemv_littlebitlinear_amd.build``.
 
-Compiles every ``csrc/*.hip`` for gfx950 with hipcc into ``liblb.so`` next
-to this file and links rocBLAS (plain fp64 GEMMs of the Joint-ITQ rotation).
+Compiles every ``csrc/*.hip`` for gfx950 with hipcc and every host-only
+``csrc/*.cpp`` with the host C++ compiler into ``liblb.so`` next to this
+file, and links rocBLAS (plain fp64 GEMMs of the Joint-ITQ rotation).
 Packed-fp32 VALU instructions are disabled for device code.
 """
 from __future__ import annotations
@@ -17,14 +18,20 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblb.so")
 ARCH = os.environ.get("LB_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-munsafe-fp-atomics"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def host_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
@@ -34,6 +41,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in srcs:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+        if len(procs) >= jobs:
+            _drain(procs)
+    for src in host_sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [CXX, *HOST_FLAGS, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -60,7 +76,7 @@ def _drain(procs):
         out, _ = p.communicate()
         text = out.decode(errors="replace")
         if p.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{text}")
+            raise RuntimeError(f"compiler failed on {src}:\n{text}")
         if text.strip():
             sys.stderr.write(text)
 

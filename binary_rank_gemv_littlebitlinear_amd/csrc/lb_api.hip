@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "lb_internal.h"
+#include "lb_layout.h"
 #include "lb_persist.h"
 
 using namespace lbi;
@@ -85,58 +86,10 @@ struct DeviceGuard {
   }
 };
 
-// Word in the matrix-core bit order (see lb_internal.h): bits inverted and
-// permuted so that (w << (4 g + j)) & 0x80008000 holds the sign flips of
-// elements 8 g + 2 j and 8 g + 2 j + 1.
-// The permutation is bytewise: byte g of w fills its own bit positions, so
-// a table per byte position gives the word in four lookups.
-inline uint32_t mfma_bit_order_slow(uint32_t w) {
-  uint32_t o = 0;
-  for (int g = 0; g < 4; ++g)
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t flip = ((w >> (8 * g + e)) & 1u) ^ 1u;
-      const int pos = (e & 1) ? 31 - (e >> 1) - 4 * g : 15 - (e >> 1) - 4 * g;
-      o |= flip << pos;
-    }
-  return o;
-}
-
-struct MfmaOrderTable {
-  uint32_t t[4][256];
-  MfmaOrderTable() {
-    for (int g = 0; g < 4; ++g)
-      for (uint32_t v = 0; v < 256; ++v)
-        // the other bytes set to all ones contribute no flips
-        t[g][v] = mfma_bit_order_slow((0xffffffffu & ~(0xffu << (8 * g))) | (v << (8 * g)));
-  }
-};
-const MfmaOrderTable g_mfma_order;
-
-inline uint32_t mfma_bit_order(uint32_t w) {
-  return g_mfma_order.t[0][w & 0xff] | g_mfma_order.t[1][(w >> 8) & 0xff] |
-         g_mfma_order.t[2][(w >> 16) & 0xff] | g_mfma_order.t[3][w >> 24];
-}
-
-inline uint32_t tail_mask(int64_t s, int64_t q) {
-  const int64_t n = s - 32 * q;
-  return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
-}
-
-// In-place transpose of a 32 x 32 bit matrix: bit c of m[r] <-> bit r of m[c].
-void transpose32(uint32_t m[32]) {
-  uint32_t mask = 0x0000ffffu;
-  for (int j = 16; j != 0; j >>= 1, mask ^= (mask << j)) {
-    for (int k = 0; k < 32; k = ((k | j) + 1) & ~j) {
-      const uint32_t t = ((m[k] >> j) ^ m[k | j]) & mask;
-      m[k] ^= t << j;
-      m[k | j] ^= t;
-    }
-  }
-}
-
 }  // namespace
 
 static inline DevCtx *ctx_of(const lb_layer *L) { return static_cast<DevCtx *>(L->ctx); }
+static lbl::Dims dims_of(const Layer &Ly) { return lbl::dims(Ly.a, Ly.b, Ly.s, Ly.P); }
 
 // --------------------------------------------------------- workspace need
 // The wave path keeps one fp32 partial latent vector per input chunk and
@@ -176,24 +129,26 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
   if (!L) return fail(LB_ENOMEM, "lb_create: host allocation");
   Layer &Ly = L->ly;
   Ly.a = a; Ly.b = b; Ly.s = s; Ly.P = residual ? 2 : 1; Ly.device = device;
-  Ly.L = Ly.P * s; Ly.R1 = (a + 31) / 32; Ly.Wk = (s + 31) / 32;
-  Ly.T16a = (a + 15) / 16; Ly.T16b = (b + 15) / 16;
-  Ly.a16 = Ly.T16a * 16; Ly.b16 = Ly.T16b * 16; Ly.s8 = (s + 7) / 8 * 8;
-  Ly.Lp = (Ly.L + 7) / 8 * 8;
+  {
+    const lbl::Dims d = lbl::dims(a, b, s, Ly.P);
+    Ly.L = d.L; Ly.R1 = d.R1; Ly.Wk = d.Wk;
+    Ly.T16a = d.T16a; Ly.T16v = d.T16v; Ly.T16b = d.T16b;
+    Ly.a16 = d.a16; Ly.b16 = d.b16; Ly.Lp = d.Lp;
+    Ly.s8 = (s + 7) / 8 * 8;
+  }
   L->ctx = dc;
+  // the signs are held once, in the tile layouts every batch-1 and
+  // small-batch kernel reads; the matrix-core copies come with the first
+  // call that needs them (ensure_mfma_copies)
   struct Alloc { void **p; size_t n; };
   Alloc allocs[] = {
-      {(void **)&Ly.sv1, (size_t)Ly.R1 * Ly.L * 4},
-      {(void **)&Ly.su2, (size_t)Ly.P * Ly.Wk * Ly.b16 * 4},
+      {(void **)&Ly.sv16, (size_t)Ly.T16v * Ly.Lp * 2},
+      {(void **)&Ly.su2t, (size_t)Ly.T16b * Ly.P * Ly.Wk * 16 * 4},
       {(void **)&Ly.h, (size_t)Ly.P * Ly.b16 * 2},
       {(void **)&Ly.g, (size_t)Ly.P * Ly.a16 * 2},
       {(void **)&Ly.l, (size_t)Ly.P * Ly.s8 * 2},
-      {(void **)&Ly.sv16, (size_t)Ly.T16a * Ly.Lp * 2},
-      {(void **)&Ly.su2t, (size_t)Ly.T16b * Ly.P * Ly.Wk * 16 * 4},
       {(void **)&Ly.ht, (size_t)Ly.T16b * Ly.P * 16 * 2},
-      {(void **)&Ly.gt, (size_t)Ly.T16a * Ly.P * 16 * 2},
-      {(void **)&Ly.sv1m, (size_t)Ly.R1 * Ly.L * 4},
-      {(void **)&Ly.su2m, (size_t)Ly.P * Ly.Wk * Ly.b16 * 4}};
+      {(void **)&Ly.gt, (size_t)Ly.T16a * Ly.P * 16 * 2}};
   for (auto &al : allocs) {
     hipError_t e = hipMalloc(al.p, al.n);
     if (e != hipSuccess) {
@@ -242,13 +197,36 @@ extern "C" lb_status lb_destroy(lb_layer *L) {
   if (!L) return LB_OK;
   DeviceGuard g(L->ly.device);
   Layer &Ly = L->ly;
-  void *ps[] = {Ly.sv1, Ly.su2, Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m,
+  void *ps[] = {Ly.h, Ly.g, Ly.l, Ly.sv16, Ly.su2t, Ly.ht, Ly.gt, Ly.sv1m, Ly.su2m,
                 Ly.ws, Ly.cnt, Ly.f1state};
   for (void *p : ps)
     if (p) (void)hipFree(p);
   mfma_plan_free(L->mplan);
   delete L->f1plan;
   delete L;
+  return LB_OK;
+}
+
+extern "C" lb_status lb_prepare(lb_layer *L, int64_t M) {
+  if (!L || M < 0) return fail(LB_EINVAL, "lb_prepare: bad argument");
+  if (M < 64) return LB_OK;
+  DeviceGuard dg(L->ly.device);
+  return ensure_mfma_copies(L, nullptr, true, "lb_prepare");
+}
+
+extern "C" lb_status lb_layer_device_bytes(const lb_layer *L, uint64_t *sign_bytes, uint64_t *total_bytes) {
+  if (!L) return fail(LB_EINVAL, "lb_layer_device_bytes: NULL layer");
+  const Layer &Ly = L->ly;
+  const lbl::Dims d = dims_of(Ly);
+  uint64_t sb = lbl::sv16_elems(d) * 2 + lbl::su2t_elems(d) * 4;
+  if (Ly.sv1m) sb += lbl::sv1m_elems(d) * 4 + lbl::su2m_elems(d) * 4;
+  uint64_t tb = sb;
+  tb += (uint64_t)Ly.P * (Ly.b16 + Ly.a16 + Ly.s8) * 2;                    // h, g, l
+  tb += (lbl::tile16_elems(Ly.b16, Ly.P) + lbl::tile16_elems(Ly.a16, Ly.P)) * 2;  // ht, gt
+  tb += Ly.ws_bytes + std::max<size_t>(1, mfma_cnt_entries(L->mplan)) * sizeof(unsigned);
+  if (L->f1plan) tb += L->f1plan->state_bytes;
+  if (sign_bytes) *sign_bytes = sb;
+  if (total_bytes) *total_bytes = tb;
   return LB_OK;
 }
 
@@ -262,76 +240,105 @@ extern "C" lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, i
   return LB_OK;
 }
 
-// Re-lay host canonical words of one path out for the device (the caller
-// has checked the arguments and made the layer's device current).
-static lb_status pack_signs_impl(Layer &Ly, int path, const uint32_t *su, const uint32_t *sv) {
-  const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L;
-  // S_U: su2[(p*Wk + q)*b16 + j] = su[j*Wk + q] (padding masked, rows >= b zero)
-  const int64_t b16 = Ly.b16;
-  std::vector<uint32_t> u2;
-  std::vector<uint32_t> v1;
-  std::vector<uint16_t> v16;
+// Build the matrix-core copies of the signs from host tile layouts of
+// every path and upload them (allocating them on first use).
+static lb_status upload_mfma_copies(Layer &Ly, const std::vector<uint16_t> &v16,
+                                    const std::vector<uint32_t> &u2t) {
+  const lbl::Dims d = dims_of(Ly);
+  std::vector<uint32_t> v1m, u2m;
   try {
-    u2.assign((size_t)Wk * b16, 0u);
-    v1.resize((size_t)Ly.R1 * Lc);
-    v16.assign((size_t)Ly.T16a * Ly.Lp, 0);
+    v1m.resize(lbl::sv1m_elems(d));
+    u2m.resize(lbl::su2m_elems(d));
+  } catch (...) {
+    return fail(LB_ENOMEM, "matrix-core sign copies: host allocation");
+  }
+  lbl::sv1m_from_sv16(d, v16.data(), v1m.data());
+  lbl::su2m_from_su2t(d, u2t.data(), u2m.data());
+  const bool fresh = !Ly.sv1m;
+  uint32_t *pv = Ly.sv1m, *pu = Ly.su2m;
+  if (fresh) {
+    hipError_t e = hipMalloc(&pv, v1m.size() * 4);
+    if (e == hipSuccess) e = hipMalloc(&pu, u2m.size() * 4);
+    if (e != hipSuccess) {
+      if (pv) (void)hipFree(pv);
+      return fail(LB_ENOMEM, std::string("matrix-core sign copies: hipMalloc: ") + hipGetErrorString(e));
+    }
+  }
+  hipError_t e = hipMemcpy(pv, v1m.data(), v1m.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(pu, u2m.data(), u2m.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (fresh) {  // never publish copies whose contents are unknown
+      (void)hipFree(pv);
+      (void)hipFree(pu);
+    }
+    return fail(LB_EHIP, std::string("matrix-core sign copies: hipMemcpy: ") + hipGetErrorString(e));
+  }
+  Ly.sv1m = pv;
+  Ly.su2m = pu;
+  return LB_OK;
+}
+
+// Re-lay host canonical words of one path out for the device (the caller
+// has checked the arguments and made the layer's device current).  The
+// tile layouts interleave the paths, so each buffer is read back, has this
+// path's part replaced and is written whole.  Returns once the device holds
+// the new words (a later launch on any stream sees them).
+static lb_status pack_signs_impl(Layer &Ly, int path, const uint32_t *su, const uint32_t *sv) {
+  const lbl::Dims d = dims_of(Ly);
+  std::vector<uint16_t> v16;
+  std::vector<uint32_t> u2t;
+  try {
+    v16.assign(lbl::sv16_elems(d), 0);
+    u2t.assign(lbl::su2t_elems(d), 0u);
   } catch (...) {
     return fail(LB_ENOMEM, "lb_pack_signs: host allocation");
   }
-  for (int64_t q = 0; q < Wk; ++q) {
-    const uint32_t msk = tail_mask(s, q);
-    for (int64_t j = 0; j < b; ++j) u2[(size_t)q * b16 + j] = su[j * Wk + q] & msk;
+  if (Ly.P > 1) {
+    LB_HIP(hipMemcpy(v16.data(), Ly.sv16, v16.size() * 2, hipMemcpyDeviceToHost));
+    LB_HIP(hipMemcpy(u2t.data(), Ly.su2t, u2t.size() * 4, hipMemcpyDeviceToHost));
   }
-  LB_HIP(hipMemcpy(Ly.su2 + (size_t)path * Wk * b16, u2.data(), u2.size() * 4, hipMemcpyHostToDevice));
-  {
-    std::vector<uint32_t> u2m(u2.size());
-    for (size_t i = 0; i < u2.size(); ++i) u2m[i] = mfma_bit_order(u2[i]);
-    LB_HIP(hipMemcpy(Ly.su2m + (size_t)path * Wk * b16, u2m.data(), u2m.size() * 4, hipMemcpyHostToDevice));
+  lbl::put_sv16(d, path, sv, v16.data());
+  lbl::put_su2t(d, path, su, u2t.data());
+  LB_HIP(hipMemcpy(Ly.sv16, v16.data(), v16.size() * 2, hipMemcpyHostToDevice));
+  LB_HIP(hipMemcpy(Ly.su2t, u2t.data(), u2t.size() * 4, hipMemcpyHostToDevice));
+  if (Ly.sv1m) {  // already built: keep them current
+    lb_status st = upload_mfma_copies(Ly, v16, u2t);
+    if (st != LB_OK) return st;
   }
-  {
-    // tile-major: for tile tau, this path's Wk x 16 words are one 64*Wk-byte
-    // run.  The paths interleave per tile, so the whole buffer is rewritten
-    // in one contiguous copy (after reading back the other path's runs).
-    const size_t n = (size_t)Ly.T16b * Ly.P * Wk * 16;
-    std::vector<uint32_t> u2t(n, 0u);
-    if (Ly.P > 1) LB_HIP(hipMemcpy(u2t.data(), Ly.su2t, n * 4, hipMemcpyDeviceToHost));
-    for (int64_t tau = 0; tau < Ly.T16b; ++tau)
-      for (int64_t q = 0; q < Wk; ++q)
-        for (int r = 0; r < 16; ++r)
-          u2t[(((size_t)tau * Ly.P + path) * Wk + q) * 16 + r] = u2[(size_t)q * b16 + 16 * tau + r];
-    LB_HIP(hipMemcpy(Ly.su2t, u2t.data(), n * 4, hipMemcpyHostToDevice));
-  }
-  // S_V: 32 x 32 bit transposes.  Block (row group r, word q) -> columns
-  // p*s + 32q + kk of row group r.
-  {
-    // read back the other path's columns so this call only replaces its own
-    LB_HIP(hipMemcpy(v1.data(), Ly.sv1, v1.size() * 4, hipMemcpyDeviceToHost));
-    uint32_t blk[32];
-    for (int64_t r = 0; r < Ly.R1; ++r) {
-      for (int64_t q = 0; q < Wk; ++q) {
-        const uint32_t msk = tail_mask(s, q);
-        for (int e = 0; e < 32; ++e) {
-          const int64_t i = r * 32 + e;
-          blk[e] = i < a ? (sv[i * Wk + q] & msk) : 0u;
-        }
-        transpose32(blk);  // blk[kk] bit e = S_V[32r + e, 32q + kk]
-        const int64_t nk = (s - 32 * q) < 32 ? (s - 32 * q) : 32;
-        for (int64_t kk = 0; kk < nk; ++kk) v1[(size_t)r * Lc + path * s + 32 * q + kk] = blk[kk];
-      }
-    }
-    LB_HIP(hipMemcpy(Ly.sv1, v1.data(), v1.size() * 4, hipMemcpyHostToDevice));
-    {
-      std::vector<uint32_t> v1m(v1.size());
-      for (size_t i = 0; i < v1.size(); ++i) v1m[i] = mfma_bit_order(v1[i]);
-      LB_HIP(hipMemcpy(Ly.sv1m, v1m.data(), v1m.size() * 4, hipMemcpyHostToDevice));
-    }
-    // sv16[gi*Lp + c]: the 16-row halves of the sv1 words
-    for (int64_t gi = 0; gi < Ly.T16a; ++gi)
-      for (int64_t c = 0; c < Lc; ++c)
-        v16[(size_t)gi * Ly.Lp + c] = (uint16_t)(v1[(size_t)(gi / 2) * Lc + c] >> (16 * (gi % 2)));
-    LB_HIP(hipMemcpy(Ly.sv16, v16.data(), v16.size() * 2, hipMemcpyHostToDevice));
-  }
+  LB_HIP(hipDeviceSynchronize());
   Ly.signs_set[path] = true;
+  return LB_OK;
+}
+
+// The matrix-core copies of the signs, built on the first call that needs
+// them.  That call allocates and synchronises the device, so it must not be
+// captured into a graph and cannot come from lb_forward_noalloc: those
+// report LB_ENOTREADY instead (lb_prepare builds the copies ahead).
+lb_status lbi::ensure_mfma_copies(const lb_layer *L, hipStream_t st, bool may_alloc, const char *who) {
+  Layer &Ly = const_cast<lb_layer *>(L)->ly;
+  if (Ly.sv1m) return LB_OK;
+  const std::string pre = std::string(who) + ": ";
+  const std::string hint = "the matrix-core copy of the signs (M >= 64) is not built yet; call lb_prepare "
+                           "(or lb_stack_reserve) with M >= 64 first";
+  if (!may_alloc) return fail(LB_ENOTREADY, pre + hint);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  LB_HIP(hipStreamIsCapturing(st, &cs));
+  if (cs != hipStreamCaptureStatusNone) return fail(LB_ENOTREADY, pre + hint + " (the stream is capturing)");
+  if (!Ly.ready()) return fail(LB_ENOTREADY, pre + "signs/scales not set for every path");
+  const lbl::Dims d = dims_of(Ly);
+  std::vector<uint16_t> v16;
+  std::vector<uint32_t> u2t;
+  try {
+    v16.resize(lbl::sv16_elems(d));
+    u2t.resize(lbl::su2t_elems(d));
+  } catch (...) {
+    return fail(LB_ENOMEM, pre + "host allocation");
+  }
+  LB_HIP(hipMemcpy(v16.data(), Ly.sv16, v16.size() * 2, hipMemcpyDeviceToHost));
+  LB_HIP(hipMemcpy(u2t.data(), Ly.su2t, u2t.size() * 4, hipMemcpyDeviceToHost));
+  lb_status s = upload_mfma_copies(Ly, v16, u2t);
+  if (s != LB_OK) return fail(s, pre + g_last_error);
+  LB_HIP(hipDeviceSynchronize());
   return LB_OK;
 }
 
@@ -348,24 +355,19 @@ extern "C" lb_status lb_unpack_signs(const lb_layer *L, int path, uint32_t *su, 
   const Layer &Ly = L->ly;
   if (path < 0 || path >= Ly.P) return fail(LB_EINVAL, "lb_unpack_signs: path out of range");
   DeviceGuard dg(Ly.device);
-  const int64_t a = Ly.a, b = Ly.b, s = Ly.s, Wk = Ly.Wk, Lc = Ly.L;
-  std::vector<uint32_t> u2((size_t)Wk * Ly.b16), v1((size_t)Ly.R1 * Lc);
-  LB_HIP(hipMemcpy(u2.data(), Ly.su2 + (size_t)path * Wk * Ly.b16, u2.size() * 4, hipMemcpyDeviceToHost));
-  LB_HIP(hipMemcpy(v1.data(), Ly.sv1, v1.size() * 4, hipMemcpyDeviceToHost));
-  for (int64_t j = 0; j < b; ++j)
-    for (int64_t q = 0; q < Wk; ++q) su[j * Wk + q] = u2[(size_t)q * Ly.b16 + j];
-  uint32_t blk[32];
-  for (int64_t r = 0; r < Ly.R1; ++r) {
-    for (int64_t q = 0; q < Wk; ++q) {
-      const int64_t nk = (s - 32 * q) < 32 ? (s - 32 * q) : 32;
-      for (int kk = 0; kk < 32; ++kk) blk[kk] = kk < nk ? v1[(size_t)r * Lc + path * s + 32 * q + kk] : 0u;
-      transpose32(blk);  // blk[e] bit kk = S_V[32r + e, 32q + kk]
-      for (int e = 0; e < 32; ++e) {
-        const int64_t i = r * 32 + e;
-        if (i < a) sv[i * Wk + q] = blk[e];
-      }
-    }
+  const lbl::Dims d = dims_of(Ly);
+  std::vector<uint16_t> v16;
+  std::vector<uint32_t> u2t;
+  try {
+    v16.resize(lbl::sv16_elems(d));
+    u2t.resize(lbl::su2t_elems(d));
+  } catch (...) {
+    return fail(LB_ENOMEM, "lb_unpack_signs: host allocation");
   }
+  LB_HIP(hipMemcpy(v16.data(), Ly.sv16, v16.size() * 2, hipMemcpyDeviceToHost));
+  LB_HIP(hipMemcpy(u2t.data(), Ly.su2t, u2t.size() * 4, hipMemcpyDeviceToHost));
+  lbl::get_sv16(d, path, v16.data(), sv);
+  lbl::get_su2t(d, path, u2t.data(), su);
   return LB_OK;
 }
 
@@ -375,21 +377,20 @@ static lb_status set_scales_impl(Layer &Ly, int path, const uint16_t *h, const u
   LB_HIP(hipMemcpy(Ly.g + (size_t)path * Ly.a16, g, Ly.a * 2, hipMemcpyHostToDevice));
   LB_HIP(hipMemcpy(Ly.l + (size_t)path * Ly.s8, l, Ly.s * 2, hipMemcpyHostToDevice));
   {
-    // tile-major copies of h and g: 16 values per (tile, path), zero padded;
-    // the paths interleave per tile, so each buffer is rewritten whole
-    const size_t nh = (size_t)Ly.T16b * Ly.P * 16, ng = (size_t)Ly.T16a * Ly.P * 16;
+    // tile copies of h and g (the paths interleave per tile, so each buffer
+    // is read back and written whole)
+    const size_t nh = lbl::tile16_elems(Ly.b16, Ly.P), ng = lbl::tile16_elems(Ly.a16, Ly.P);
     std::vector<uint16_t> hb(nh, 0), gb(ng, 0);
     if (Ly.P > 1) {
       LB_HIP(hipMemcpy(hb.data(), Ly.ht, nh * 2, hipMemcpyDeviceToHost));
       LB_HIP(hipMemcpy(gb.data(), Ly.gt, ng * 2, hipMemcpyDeviceToHost));
     }
-    for (int64_t j = 0; j < Ly.b16; ++j)
-      hb[((size_t)(j >> 4) * Ly.P + path) * 16 + (j & 15)] = j < Ly.b ? h[j] : (uint16_t)0;
-    for (int64_t i = 0; i < Ly.a16; ++i)
-      gb[((size_t)(i >> 4) * Ly.P + path) * 16 + (i & 15)] = i < Ly.a ? g[i] : (uint16_t)0;
+    lbl::put_tile16(Ly.b, Ly.b16, Ly.P, path, h, hb.data());
+    lbl::put_tile16(Ly.a, Ly.a16, Ly.P, path, g, gb.data());
     LB_HIP(hipMemcpy(Ly.ht, hb.data(), nh * 2, hipMemcpyHostToDevice));
     LB_HIP(hipMemcpy(Ly.gt, gb.data(), ng * 2, hipMemcpyHostToDevice));
   }
+  LB_HIP(hipDeviceSynchronize());
   Ly.scales_set[path] = true;
   return LB_OK;
 }
@@ -553,6 +554,12 @@ lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int
              std::to_string(mfma_cnt_entries(L->mplan)) + " counters)";
     return LB_EUNSUPPORTED;
   }
+  // built by lb_prepare or by lb_forward's first M >= 64 call, never here:
+  // this function allocates nothing
+  if (!Ly.sv1m) {
+    if (msg) *msg = "the matrix-core copy of the signs is not built yet (lb_prepare with M >= 64)";
+    return LB_ENOTREADY;
+  }
   uint16_t *ys[1] = {y};
   hipError_t e = launch_mfma_unit(L->mplan, x, M, ys, nullptr, 1.f, true, ws, cnt, dc->zero, dc->info, st);
   if (e != hipSuccess) {
@@ -577,6 +584,10 @@ static lb_status forward_impl(const lb_layer *L, const uint16_t *x, uint16_t *y,
     hipError_t e = launch_forward1(Ly, *L->f1plan, Ly.f1state, dc->herr_dev, x, y, st);
     if (e != hipSuccess) return fail(LB_EHIP, std::string("lb_forward: one-row launch: ") + hipGetErrorString(e));
     return LB_OK;
+  }
+  if (M >= 64) {
+    lb_status es = ensure_mfma_copies(L, st, true, "lb_forward");
+    if (es != LB_OK) return es;
   }
   std::string msg;
   const lb_status r = forward_ws(L, x, y, M, st, Ly.ws, Ly.ws_bytes, Ly.cnt,
@@ -892,7 +903,13 @@ extern "C" lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t 
 extern "C" lb_status lb_stack_reserve(lb_stack *S, int64_t M) {
   if (!S || M < 0) return fail(LB_EINVAL, "lb_stack_reserve: bad argument");
   DeviceGuard dg(S->device);
-  return stack_reserve(S, M);
+  lb_status st = stack_reserve(S, M);
+  if (st != LB_OK || M < 64) return st;
+  for (lb_layer *Lr : S->layers) {
+    st = ensure_mfma_copies(Lr, nullptr, true, "lb_stack_reserve");
+    if (st != LB_OK) return st;
+  }
+  return LB_OK;
 }
 
 extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
@@ -939,6 +956,12 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
   }
   lb_status rs = stack_reserve(S, M);
   if (rs != LB_OK) return rs;
+  if (M >= 64) {
+    for (lb_layer *Lr : S->layers) {
+      lb_status es = ensure_mfma_copies(Lr, st, true, "lb_stack_forward");
+      if (es != LB_OK) return es;
+    }
+  }
   if (M >= 64 && S->mode != 1) {
     // one stage-1 and one stage-2 launch per unit; stage 2 also combines
     const uint16_t *cur = (const uint16_t *)x0;

@@ -1,43 +1,24 @@
 // Internal declarations shared by the host library and the kernels.
 //
-// Device layout of one layer (P paths, rank s, input width a, output
-// width b).  The canonical host layout packs each factor row along s; the
-// device layouts below are chosen for the kernels that read them.
+// Device storage of one layer (P paths, rank s, input width a, output
+// width b; the sign layouts are defined in lb_layout.h):
 //
 //   L   = P * s            latent columns, path-major: column c = p*s + k
-//   R1  = ceil(a / 32)     row groups of S_V
+//   R1  = ceil(a / 32)     32-row groups of S_V;  T16v = 2 R1 16-row tiles
 //   Wk  = ceil(s / 32)     words per S_U row and path
 //
-//   sv1[r * L + c]                 (uint32, R1 x L)
-//       bit (i % 32) = S_V,p[i, k] for i = 32 r + bit, c = p*s + k.
-//       Column-major bits over the input index: lane c of a wave reads
-//       its own column's word, so a wave's load of one row group is one
-//       contiguous, coalesced 4*64-byte segment.
-//   su2[(p*Wk + q) * b16 + j]      (uint32, P*Wk x b16, b16 = b rounded up to 16)
-//       bit (k % 32) = S_U,p[j, 32 q + bit].  Row j's words of one path
-//       are b16 apart, so lane j of a wave reads consecutive addresses, and
-//       the words of 16-row tiles start on 64-byte boundaries.
-//   sv16[gi * Lp + c]              (uint16, T16a x Lp, Lp = L rounded up to 8)
-//       bit (i % 16) = S_V,p[i, k] for i = 16 gi + bit, c = p*s + k: the
-//       first product's bits by 16-row groups, so a workgroup owning whole
-//       16-row tiles reads one contiguous, 16-byte aligned block.
+//   sv16, su2t     the signs, once: S_V by 16-row input tiles (column-major
+//                  over latent columns, so lane c of a wave reads column c
+//                  and a 16-row tile of all columns is one contiguous
+//                  block), S_U by 16-row output tiles (one contiguous block
+//                  of P * Wk * 16 words per tile).  Every M < 64 kernel and
+//                  the stack sweep read these.
+//   sv1m, su2m     the matrix-core copies (bits inverted and permuted for
+//                  the fp16 operand sign flips), built on the first call
+//                  with M >= 64 (null until then).
 //   h[p*b16 + j], g[p*a16 + i], l[p*s8 + k]   (fp16 bit patterns; padded
-//       per-path pitches, s8 = s rounded up to 8, zero padding)
-//
-// Tile-major copies for the persistent sweep, where a workgroup owns whole
-// 16-row tiles and stages them into LDS as one contiguous block each:
-//   su2t[((tau * P + p) * Wk + q) * 16 + r]   (uint32) = su2 word q, path p,
-//       row 16 tau + r
-//   ht[(tau * P + p) * 16 + r] = h[p*b16 + 16 tau + r]   (fp16)
-//   gt[(tau * P + p) * 16 + r] = g[p*a16 + 16 tau + r]   (fp16)
-//
-// Copies for the matrix-core path, same indexing as sv1 / su2 but with each
-// word's bits inverted (1 = sign -1) and permuted: the sign of element
-// 8 g + e (g = 0..3, e = 0..7) sits at bit 15 - e/2 - 4 g for even e and
-// 31 - (e - 1)/2 - 4 g for odd e.  Shifting the word left by 4 g + j and
-// masking 0x80008000 then gives the fp16 sign flips of elements 8 g + 2 j
-// and 8 g + 2 j + 1, one 32-bit operand register of a lane's 8 values:
-//   sv1m[r * L + c], su2m[(p*Wk + q) * b16 + j]
+//                  per-path pitches, s8 = s rounded up to 8, zero padding)
+//   ht, gt         h and g by 16-row tiles (the sweep's staging blocks)
 //
 // Padding bits and padding scales are zero, so they contribute nothing.
 #pragma once
@@ -66,18 +47,16 @@ struct Layer {
   int64_t L = 0, R1 = 0, Wk = 0;
   bool signs_set[2] = {false, false};
   bool scales_set[2] = {false, false};
-  uint32_t *sv1 = nullptr;  // R1 * L words
-  uint32_t *su2 = nullptr;  // P * Wk * b16 words
   uint16_t *h = nullptr;    // P * b16
   uint16_t *g = nullptr;    // P * a16
   uint16_t *l = nullptr;    // P * s8
-  int64_t a16 = 0, b16 = 0, s8 = 0, Lp = 0, T16a = 0, T16b = 0;
-  uint16_t *sv16 = nullptr; // T16a * Lp
+  int64_t a16 = 0, b16 = 0, s8 = 0, Lp = 0, T16a = 0, T16v = 0, T16b = 0;
+  uint16_t *sv16 = nullptr; // T16v * Lp
   uint32_t *su2t = nullptr; // T16b * P * Wk * 16
   uint16_t *ht = nullptr;   // T16b * P * 16
   uint16_t *gt = nullptr;   // T16a * P * 16
-  uint32_t *sv1m = nullptr; // R1 * L words (matrix-core bit order)
-  uint32_t *su2m = nullptr; // P * Wk * b16 words (matrix-core bit order)
+  uint32_t *sv1m = nullptr; // R1 * L words (matrix-core bit order), null until first needed
+  uint32_t *su2m = nullptr; // P * Wk * b16 words (matrix-core bit order), null until first needed
   // The layer's own forward workspace (wave-path chunk partials and latent
   // rows, or the matrix-core latent T and split-K partials) and split-K
   // tile counters (zero between launches), allocated at create time and
@@ -191,6 +170,10 @@ lb_status forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t 
 lb_status forward_checks(const lb_layer *L, const void *x, const void *y, int64_t M, const char *who);
 lb_status set_error(lb_status st, const std::string &msg);
 const void *device_zero(const lb_layer *L);
+// The matrix-core sign copies of a layer, built if missing when may_alloc
+// and the stream is not capturing (allocates, synchronises the device);
+// LB_ENOTREADY otherwise.
+lb_status ensure_mfma_copies(const lb_layer *L, hipStream_t st, bool may_alloc, const char *who);
 
 // fp16 out[M x n] = fp16(c * sum_u in_u[M x n]) for n_in inputs.
 hipError_t launch_combine(const uint16_t *const *ins, int n_in, float c, uint16_t *out,

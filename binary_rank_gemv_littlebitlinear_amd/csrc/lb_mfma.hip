@@ -126,8 +126,10 @@ struct MfmaPlan {
   int nl = 0;
   int64_t a = 0, b = 0;
   int a16 = 0, Lt = 0, ntile32 = 0, nseg = 0;
-  S1Seg seg[kMaxUnitSegs];
+  S1Seg seg[kMaxUnitSegs];  // sign pointers filled at launch (seg_layer, seg_path)
   S2Layer ly[kMaxUnitLayersM];
+  const Layer *src[kMaxUnitLayersM] = {};
+  int seg_layer[kMaxUnitSegs] = {}, seg_path[kMaxUnitSegs] = {};
 };
 
 // ----------------------------------------------------------- primitives
@@ -658,14 +660,17 @@ MfmaPlan *mfma_plan_build(const Layer *const *layers, int n) {
       delete P;
       return nullptr;
     }
+    P->src[m] = &Ly;
     S2Layer &D = P->ly[m];
-    D.su2 = Ly.su2m; D.l = Ly.l; D.h = Ly.h; D.y = nullptr;
+    D.su2 = nullptr; D.l = Ly.l; D.h = Ly.h; D.y = nullptr;
     D.b16 = (int)Ly.b16; D.s8 = (int)Ly.s8; D.Wk = (int)Ly.Wk; D.P = Ly.P;
     D.seg0[0] = D.seg0[1] = 0;
     D.pad_[0] = D.pad_[1] = 0;
     for (int p = 0; p < Ly.P; ++p) {
+      P->seg_layer[nseg] = m;
+      P->seg_path[nseg] = p;
       S1Seg &S = P->seg[nseg++];
-      S.bits = Ly.sv1m + (size_t)p * Ly.s;
+      S.bits = nullptr;
       S.g = Ly.g + (size_t)p * Ly.a16;
       S.pitch = (int)Ly.L;
       S.s = (int)Ly.s;
@@ -755,6 +760,20 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             hipStream_t st) {
   hipError_t e = set_lds_attr(dev.device);
   if (e != hipSuccess) return e;
+  // the matrix-core sign copies are built on first use, so their addresses
+  // are taken here
+  S1Seg segs[kMaxUnitSegs];
+  S2Layer lys[kMaxUnitLayersM];
+  for (int i = 0; i < kMaxUnitSegs; ++i) segs[i] = p->seg[i];
+  for (int m = 0; m < kMaxUnitLayersM; ++m) lys[m] = p->ly[m];
+  for (int m = 0; m < p->nl; ++m) {
+    if (!p->src[m]->sv1m || !p->src[m]->su2m) return hipErrorInvalidValue;
+    lys[m].su2 = p->src[m]->su2m;
+  }
+  for (int i = 0; i < p->nseg; ++i) {
+    const Layer &Ly = *p->src[p->seg_layer[i]];
+    segs[i].bits = Ly.sv1m + (size_t)p->seg_path[i] * Ly.s;
+  }
   uint16_t *T = reinterpret_cast<uint16_t *>(ws);
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
                                           round_up((int64_t)kMfmaRows * p->Lt * 2, 256));
@@ -774,7 +793,7 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A1.nsplit = s1_nsplit(*p, Mc, dev, &A1.kcps, &A1.cround);
     A1.nseg = p->nseg;
     A1.xvec = (p->a % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-    for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = p->seg[i];
+    for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = segs[i];
     dim3 g1((unsigned)(p->Lt / 128), (unsigned)((Mc + 31) / 32), (unsigned)A1.nsplit);
     const size_t lds1 = s1_lds_launch(A1.kcps, A1.cround);
     hipLaunchKernelGGL(k_unit_s1, g1, dim3(kThreads1), lds1, st, A1);
@@ -795,7 +814,7 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A2.nrounds = 0;
     for (int m = 0; m < p->nl; ++m) A2.nrounds += (p->ly[m].P * p->ly[m].Wk + A2.c2 - 1) / A2.c2;
     for (int m = 0; m < kMaxUnitLayersM; ++m) {
-      A2.ly[m] = p->ly[m];
+      A2.ly[m] = lys[m];
       A2.ly[m].y = (m < p->nl && y_layers && y_layers[m]) ? y_layers[m] + mb * p->b : nullptr;
     }
     dim3 g2((unsigned)((p->b + 64 * A2.nb - 1) / (64 * A2.nb)), (unsigned)((Mc + 31) / 32));

@@ -67,6 +67,19 @@ __device__ __forceinline__ float lut_word(const float *tab, uint32_t wd) {
   return acc;
 }
 
+// The 32-row sign word of S_V row group r, latent column col: the two
+// 16-row tiles 2 r and 2 r + 1 of the tile layout joined.
+__device__ __forceinline__ uint32_t sv_word(const uint16_t *__restrict__ sv16, int64_t Lp, int64_t r,
+                                            int64_t col) {
+  return (uint32_t)sv16[2 * r * Lp + col] | ((uint32_t)sv16[(2 * r + 1) * Lp + col] << 16);
+}
+
+// Index of word idx = p * Wk + q of S_U row j in the tile layout (nw = P Wk
+// words per row): 16-row tiles of nw * 16 words, row j % 16 innermost.
+__device__ __forceinline__ int64_t su_index(int64_t j, int nw, int idx) {
+  return (((j >> 4) * nw + idx) << 4) + (j & 15);
+}
+
 constexpr int kS1Threads = 256;
 constexpr int kS1TabFloats = 12288;  // 48 KB of stage-1 tables per batch of rows
 
@@ -81,8 +94,8 @@ static int s1_mbatch(const Layer &Ly, int G) {
 // grid.x = nchunk; chunk c covers row groups [c*G, min(c*G+G, R1)).
 // LDS: tab[mi][p][grp][16] (grp < 8 G), sz[mi][p].
 __global__ void __launch_bounds__(kS1Threads)
-k_wave_s1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
-          const uint16_t *__restrict__ x, int64_t a, int64_t a16, int64_t s, int64_t L, int P,
+k_wave_s1(const uint16_t *__restrict__ sv16, const uint16_t *__restrict__ g,
+          const uint16_t *__restrict__ x, int64_t a, int64_t a16, int64_t s, int64_t L, int64_t Lp, int P,
           int64_t R1, int M, int G, int MB, float *__restrict__ part) {
   extern __shared__ float smem[];
   const int c = blockIdx.x, t = threadIdx.x;
@@ -122,14 +135,14 @@ k_wave_s1(const uint32_t *__restrict__ sv1, const uint16_t *__restrict__ g,
       const int p = (int)((uint32_t)col / (uint32_t)s);  // col < L = P s <= 8192
       uint32_t wd[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wd[r] = (r0 + r < r1) ? sv1[(r0 + r) * L + col] : 0u;
+      for (int r = 0; r < 4; ++r) wd[r] = (r0 + r < r1) ? sv_word(sv16, Lp, r0 + r, col) : 0u;
       for (int mi = 0; mi < mn; ++mi) {
         const float *tb = tab + (size_t)(mi * P + p) * G * 8 * 16;
         float acc = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (r0 + r < r1) acc += lut_word(tb + r * 8 * 16, wd[r]);
-        for (int r = 4; r < (int)(r1 - r0); ++r) acc += lut_word(tb + r * 8 * 16, sv1[(r0 + r) * L + col]);
+        for (int r = 4; r < (int)(r1 - r0); ++r) acc += lut_word(tb + r * 8 * 16, sv_word(sv16, Lp, r0 + r, col));
         part[((int64_t)c * M + m0 + mi) * L + col] = 2.f * acc - sz[mi * P + p];
       }
     }
@@ -184,7 +197,7 @@ static int s2_mbatch(int nw, int64_t L) {
 // WPL: words per lane (>= ceil(P * Wk / 4)).
 template <int WPL>
 __global__ void __launch_bounds__(kS2Threads)
-k_wave_s2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
+k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
           const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
           int64_t Wk, int M, int MB, uint16_t *__restrict__ y) {
   extern __shared__ float smem[];
@@ -200,7 +213,7 @@ k_wave_s2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
 #pragma unroll
   for (int v = 0; v < WPL; ++v) {
     const int idx = part + kS2Lanes * v;
-    wd[v] = idx < nw ? su2[(int64_t)idx * b16 + jc] : 0u;
+    wd[v] = idx < nw ? su2t[su_index(jc, nw, idx)] : 0u;
   }
   float hv[2];
 #pragma unroll
@@ -263,7 +276,7 @@ k_wave_s2(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
 
 // Fallback for layers whose tables do not fit: one thread per output row.
 __global__ void __launch_bounds__(kS2Threads)
-k_wave_s2_bits(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
+k_wave_s2_bits(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
                const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
                int64_t Wk, int M, uint16_t *__restrict__ y) {
   extern __shared__ float smem[];
@@ -291,7 +304,7 @@ k_wave_s2_bits(const uint32_t *__restrict__ su2, const uint16_t *__restrict__ h,
         const float *wp = wl + p * s;
         float acc = 0.f;
         for (int64_t q = 0; q < Wk; ++q) {
-          const uint32_t wd = su2[(p * Wk + q) * b16 + j];
+          const uint32_t wd = su2t[su_index(j, P * (int)Wk, (int)(p * Wk + q))];
           const int64_t kb = q * 32;
           const int nb = (s - kb) < 32 ? (int)(s - kb) : 32;
           for (int bit = 0; bit < nb; ++bit) acc += ((wd >> bit) & 1u) ? wp[kb + bit] : 0.f;
@@ -326,8 +339,8 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
   if (Ly.P * G * 8 * 16 > kS1TabFloats) return hipErrorInvalidValue;  // wave_nchunk keeps G small
   const int MB = (int)std::min<int64_t>(M, s1_mbatch(Ly, G));
   const size_t lds = ((size_t)MB * Ly.P * G * 8 * 16 + (size_t)MB * Ly.P + 16) * sizeof(float);
-  hipLaunchKernelGGL(k_wave_s1, dim3(nch), dim3(kS1Threads), lds, st, Ly.sv1, Ly.g, x, Ly.a,
-                     Ly.a16, Ly.s, Ly.L, Ly.P, Ly.R1, (int)M, G, MB, ws);
+  hipLaunchKernelGGL(k_wave_s1, dim3(nch), dim3(kS1Threads), lds, st, Ly.sv16, Ly.g, x, Ly.a,
+                     Ly.a16, Ly.s, Ly.L, Ly.Lp, Ly.P, Ly.R1, (int)M, G, MB, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = M * Ly.L;
@@ -346,7 +359,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
     const dim3 grid((unsigned)((Ly.b + kS2Rows - 1) / kS2Rows));
     const int wpl = (nw + kS2Lanes - 1) / kS2Lanes;
 #define LB_S2(WPLV)                                                                       \
-  hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kS2Threads), lds, st, Ly.su2, Ly.h, w, Ly.b, \
+  hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kS2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, \
                      Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, y)
     if (wpl <= 2) LB_S2(2);
     else if (wpl <= 4) LB_S2(4);
@@ -359,7 +372,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
   const size_t lds = ((size_t)Ly.L + 2 + 16) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_wave_s2_bits, dim3((unsigned)((Ly.b + kS2Threads - 1) / kS2Threads)),
-                     dim3(kS2Threads), lds, st, Ly.su2, Ly.h, w, Ly.b, Ly.b16, Ly.s, Ly.L, Ly.P,
+                     dim3(kS2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, Ly.b16, Ly.s, Ly.L, Ly.P,
                      Ly.Wk, (int)M, y);
   return hipGetLastError();
 }
@@ -384,10 +397,11 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
 // resets the ticket for the next launch.  Every wait is bounded and sets a
 // host-mapped error word when it gives up.
 struct Forward1Args {
-  const uint32_t *sv1, *su2;
+  const uint16_t *sv16;
+  const uint32_t *su2t;
   const uint16_t *g, *h, *l, *x;
   uint16_t *y;
-  int64_t a, a16, b, b16, s, s8, L, R1, Wk;
+  int64_t a, a16, b, b16, s, s8, L, Lp, R1, Wk;
   int P, G, N1, NR, N2;
   unsigned *ctrl;  // [0] next ticket, [1] finished workgroups, [2] generation of the last launch
   uint64_t *w;     // [L] tagged latent
@@ -449,6 +463,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     const int ng = (int)(r1 - r0) * 8;
     float *tab = smem;                                  // [P][G*8][16]
     float *sz = smem + (size_t)A.P * A.G * 8 * 16;      // [P]
+    const int nr = (int)(r1 - r0);
     for (int idx = t; idx < A.P * ng; idx += kF1Threads) {
       const int p = idx / ng, gr = idx - p * ng;
       const int64_t i0 = r0 * 32 + 4 * gr;
@@ -472,7 +487,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
       const int p = (int)((uint32_t)col / (uint32_t)A.s);
       const float *tb = tab + (size_t)p * A.G * 8 * 16;
       float acc = 0.f;
-      for (int r = 0; r < (int)(r1 - r0); ++r) acc += lut_word(tb + r * 8 * 16, A.sv1[(r0 + r) * L + col]);
+      for (int r = 0; r < nr; ++r) acc += lut_word(tb + r * 8 * 16, sv_word(A.sv16, A.Lp, r0 + r, col));
       f1_put(&A.part[(size_t)c * L + col], 2.f * acc - sz[p], gen);
     }
   } else if (tk < A.N1 + A.NR) {
@@ -512,7 +527,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
 #pragma unroll
     for (int v = 0; v < WPL; ++v) {
       const int idx = part + kS2Lanes * v;
-      wd[v] = idx < nw ? A.su2[(int64_t)idx * A.b16 + jc] : 0u;
+      wd[v] = idx < nw ? A.su2t[su_index(jc, nw, idx)] : 0u;
     }
     float hv[2];
 #pragma unroll
@@ -616,8 +631,8 @@ bool forward1_plan(const Layer &Ly, const DeviceInfo &dev, Forward1Plan *pl) {
 hipError_t launch_forward1(const Layer &Ly, const Forward1Plan &pl, void *state, unsigned *herr,
                            const uint16_t *x, uint16_t *y, hipStream_t st) {
   Forward1Args A;
-  A.sv1 = Ly.sv1; A.su2 = Ly.su2; A.g = Ly.g; A.h = Ly.h; A.l = Ly.l; A.x = x; A.y = y;
-  A.a = Ly.a; A.a16 = Ly.a16; A.b = Ly.b; A.b16 = Ly.b16; A.s = Ly.s; A.s8 = Ly.s8; A.L = Ly.L;
+  A.sv16 = Ly.sv16; A.su2t = Ly.su2t; A.g = Ly.g; A.h = Ly.h; A.l = Ly.l; A.x = x; A.y = y;
+  A.a = Ly.a; A.a16 = Ly.a16; A.b = Ly.b; A.b16 = Ly.b16; A.s = Ly.s; A.s8 = Ly.s8; A.L = Ly.L; A.Lp = Ly.Lp;
   A.R1 = Ly.R1; A.Wk = Ly.Wk; A.P = Ly.P;
   A.G = pl.G; A.N1 = pl.N1; A.NR = pl.NR; A.N2 = pl.N2;
   unsigned char *base = static_cast<unsigned char *>(state);

@@ -35,17 +35,26 @@
  *   - Device pointers (x, y) are caller-owned, contiguous, row-major and
  *     16-byte aligned, and x must not overlap y.
  *   - Forward calls are asynchronous on the given hipStream_t (passed as
- *     void*, NULL = the null stream) and make no host synchronisation.
- *     lb_forward never allocates; lb_stack_forward allocates (and
- *     synchronises the device) only when M exceeds the rows reserved with
- *     lb_stack_reserve or by an earlier call.  Calls that use one layer or
- *     stack must be ordered on one stream: they share the object's device
- *     workspace.
+ *     void*, NULL = the null stream) and make no host synchronisation,
+ *     with one exception each: the first call with M >= 64 on a layer
+ *     builds the layer's matrix-core copy of the signs (allocates it and
+ *     synchronises the device; lb_prepare does this ahead of time), and
+ *     lb_stack_forward allocates (without synchronising) when M exceeds the
+ *     rows reserved with lb_stack_reserve or by an earlier call.
+ *   - Every buffer a forward call writes belongs to the layer or stack it
+ *     runs (allocated by lb_create, lb_prepare or lb_stack_reserve) or to
+ *     the caller: calls on different objects share nothing and may run on
+ *     different streams at once.  Calls that use one layer or stack must be
+ *     ordered on one stream: they share that object's workspace.  Nothing
+ *     an object allocated is freed or moved before it is destroyed (a
+ *     stack's outgrown scratch is retired, not freed).
  *   - Without a trace, lb_forward and lb_stack_forward (M within the rows
- *     already reserved) only launch kernels, so they can be captured into a
- *     HIP graph and replayed; the one-launch sweep carries its exchange
- *     generation from launch to launch on the device, so every replay is a
- *     fresh launch.
+ *     already reserved, and for M >= 64 the matrix-core copies built) only
+ *     launch kernels, so they can be captured into a HIP graph and
+ *     replayed; such a call made under capture before that preparation
+ *     returns LB_ENOTREADY instead of allocating.  The one-launch sweep
+ *     carries its exchange generation from launch to launch on the device,
+ *     so every replay is a fresh launch.
  */
 #ifndef LB_H
 #define LB_H
@@ -74,18 +83,26 @@ typedef enum {
 /* Create a layer with input width a, output width b, rank s, and one
  * path (residual = 0) or two (residual = 1), on the current HIP device.
  * [LB2 column] Ch. 1 names a, b, s and residual; [LB news] Sec. 2 the
- * structure.  a, b, s >= 1, a, b <= 2^24 and s <= 4096.  Allocates the device
- * storage for signs, scales and workspace.  *out is set on success only. */
+ * structure.  a, b, s >= 1, a, b <= 2^24 and s <= 4096.  Allocates the
+ * layer's device storage: the signs once (in 16-row tile layouts that
+ * every kernel for M < 64 reads: about P s (a + b) / 8 bytes), the scales
+ * and their tile copies, and the layer's own forward workspace (chunk
+ * partials and latent rows of up to 63 rows, the matrix-core latent and
+ * split-K partials, the one-row launch's state).  The matrix-core copy of
+ * the signs (the same count again) is added by lb_prepare or the first
+ * forward with M >= 64.  *out is set on success only. */
 lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb_layer **out);
 
 /* Set the sign factors of one path (0, or 1 when residual) from host
  * canonical words: su is b x ceil(s/32), sv is a x ceil(s/32).  The words
- * are re-laid out for the device and copied synchronously; bit-exact. */
+ * are re-laid out for the device and copied synchronously (the device is
+ * synchronised before return, so launches on any stream see them);
+ * bit-exact.  A matrix-core copy already built is rebuilt too. */
 lb_status lb_pack_signs(lb_layer *L, int path, const uint32_t *su, const uint32_t *sv);
 
 /* Set the fp16 scales of one path from host arrays: h (b values, row /
  * output scale), g (a values, column / input scale), l (s values, latent
- * scale), [LB news] Sec. 2.  Copied synchronously. */
+ * scale), [LB news] Sec. 2.  Copied synchronously (as lb_pack_signs). */
 lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t *g,
                         const uint16_t *l);
 
@@ -98,7 +115,10 @@ lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t
  * streams), three launches otherwise; M >= 64 runs the fp16 matrix-core
  * path (two launches: the first product with split K, then the second), in
  * which the latent vector t is rounded once to fp16 before the second
- * product; the +-g and +-l operands are exact.  Returns LB_ENOTREADY
+ * product; the +-g and +-l operands are exact.  The first call with
+ * M >= 64 on a layer builds its matrix-core copy of the signs (allocates,
+ * synchronises the device; LB_ENOTREADY instead when `stream` is being
+ * captured: call lb_prepare first).  Returns LB_ENOTREADY
  * unless every path has signs and scales; LB_ETIMEOUT (running nothing)
  * when an earlier one-row forward on the device gave up a bounded
  * device-side wait (which does not happen while the device runs its work;
@@ -120,7 +140,9 @@ lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void 
  * one device (other streams, concurrent host threads) race, so order them.
  * M < 64 runs the wave path in row blocks that fit the array; M >= 64 the
  * matrix-core path, which needs its latent (256 rows of the padded latent
- * width) and split partials within the array.  LB_EUNSUPPORTED, with
+ * width) and split partials within the array, and the layer's matrix-core
+ * copy of the signs built beforehand (lb_prepare, or an earlier lb_forward
+ * with M >= 64; LB_ENOTREADY, nothing launched, otherwise).  LB_EUNSUPPORTED, with
  * nothing launched, when a layer needs more (not even one wave-path row, or
  * the matrix-core path, fits); the other errors as lb_forward. */
 lb_status lb_forward_noalloc(const lb_layer *L, const void *x, void *y, int64_t M, void *stream);
@@ -188,6 +210,20 @@ lb_status lb_init_from_factors(lb_layer *L, int path, const float *U, const floa
 lb_status lb_joint_itq(const float *U, const float *V, int64_t a, int64_t b, int64_t s, int iters,
                        const double *R0, double *R, void *stream);
 
+/* Build now what forward calls of up to M rows read beyond the storage
+ * lb_create made: for M >= 64 the matrix-core copy of the signs (bits
+ * inverted and permuted for the fp16 operand sign flips; allocates and
+ * synchronises the device).  Nothing for M < 64.  Call it before capturing
+ * M >= 64 forwards into a graph or using lb_forward_noalloc with them.
+ * The signs of every path must be set (LB_ENOTREADY otherwise). */
+lb_status lb_prepare(lb_layer *L, int64_t M);
+
+/* Device bytes the layer holds: *sign_bytes for its sign words (the tile
+ * layouts, plus the matrix-core copy once built), *total_bytes for all of
+ * its storage (signs, scales, workspace, one-row state).  Either pointer
+ * may be NULL. */
+lb_status lb_layer_device_bytes(const lb_layer *L, uint64_t *sign_bytes, uint64_t *total_bytes);
+
 /* Shape queries. */
 lb_status lb_layer_shape(const lb_layer *L, int64_t *a, int64_t *b, int64_t *s, int *residual);
 
@@ -236,8 +272,12 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  * lb_stack_trace_elems).  Automatic mode:
  *   M = 1       one launch for the whole sweep: one workgroup per compute
  *               unit, the latent vector of each unit summed across
- *               workgroups through device memory with bounded waits (a
- *               wait that gives up sets a flag lb_stack_check reports);
+ *               workgroups through device memory with bounded waits.  Its
+ *               workgroups wait for one another, so all of them must be
+ *               resident at once: run it while other streams' kernels do
+ *               not hold the compute units.  A wait that gives up (e.g.
+ *               when they do) sets a flag that lb_stack_check reports and
+ *               that the next sweep returns as LB_ETIMEOUT;
  *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
  *               per unit; except that for M <= 4 (M <= 7 when the stack's
  *               mean matrix has at least 2^27 weights) without a trace the
@@ -249,9 +289,12 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
 
-/* Reserve the stack's scratch for up to M rows now (allocates and
+/* Reserve the stack's scratch for up to M rows now (allocates; for
+ * M >= 64 also builds the layers' matrix-core sign copies, which
  * synchronises the device), so that later lb_stack_forward calls with at
- * most M rows allocate nothing. */
+ * most M rows allocate nothing.  Scratch of an earlier, smaller
+ * reservation is retired, not freed (launches already queued or captured
+ * keep using it), until lb_stack_destroy. */
 lb_status lb_stack_reserve(lb_stack *S, int64_t M);
 
 /* Number of fp16 elements lb_stack_forward writes to trace for M rows. */

@@ -87,6 +87,8 @@ def test_host_argument_errors():
     assert lib.lb_joint_itq(8, 8, 4, 4, 4, -1, None, 8, None) == lbm.LB_EINVAL
     assert lib.lb_joint_itq(8, 8, 4, 4, 4, 1, None, 12, None) == lbm.LB_EINVAL
     assert lib.lb_get_scales(None, 0, None, None, None) == lbm.LB_EINVAL
+    assert lib.lb_prepare(None, 64) == lbm.LB_EINVAL
+    assert lib.lb_layer_device_bytes(None, None, None) == lbm.LB_EINVAL
     assert lib.lb_stack_create(None, 0, None, 0, 1.0, ctypes.byref(out)) == lbm.LB_EINVAL
     assert b"NULL" in lib.lb_last_error() or len(lib.lb_last_error()) > 0
     assert lib.lb_status_str(lbm.LB_ENOTREADY) == b"LB_ENOTREADY"

@@ -78,3 +78,27 @@ def test_noalloc_rejects_what_does_not_fit(lbm):
     say("[case] noalloc wave path of the same layer")
     _both(lbm, torch, L, paths, lb_synth.activations(3, a, seed=2), "noalloc wave path, s = 4096")
     L.close()
+
+
+def test_noalloc_needs_the_matrix_core_copy_built(lbm):
+    """At M >= 64 the entry point allocates nothing, so on a layer whose
+    matrix-core sign copy is not built yet it returns LB_ENOTREADY with
+    nothing launched; after lb_prepare it matches lb_forward bit for bit."""
+    torch = lbtest.torch_dev()
+    a, b, s = 1000, 600, 40
+    paths = lb_synth.layer_inputs(a, b, s, True, seed=31)
+    L = lbm.Layer.from_paths(paths)
+    say("[case] noalloc M=80 before lb_prepare")
+    x = lbtest.to_dev(lb_synth.activations(80, a, seed=3))
+    y = torch.zeros((80, b), dtype=torch.float16, device="cuda")
+    with pytest.raises(lbm.LBError) as ei:
+        lbm.lb_forward_noalloc(L.handle, x, y, 80)
+    assert ei.value.status == lbm.LB_ENOTREADY
+    assert "lb_prepare" in lbm.lb_last_error()
+    torch.cuda.synchronize()
+    assert not y.any()
+    L.prepare(80)
+    say("[case] noalloc M=80, 65 after lb_prepare")
+    for k, M in enumerate((80, 65)):
+        _both(lbm, torch, L, paths, lb_synth.activations(M, a, seed=10 + k), f"noalloc prepared M={M}")
+    L.close()
