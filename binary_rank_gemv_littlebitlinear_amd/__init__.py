@@ -66,6 +66,7 @@ def load_library(path: str = LIB_PATH):
         "lb_stack_set_mode": ([vp, i32], i32),
         "lb_stack_check": ([vp], i32),
         "lb_stack_test_wait_failure": ([vp, i32], i32),
+        "lb_stack_test_delay": ([vp, C.c_uint32, C.c_uint32], i32),
         "lb_stack_timeline": ([vp, vp, i64, P(i64)], i32),
         "lb_stack_destroy": ([vp], i32),
         "lb_status_str": ([i32], C.c_char_p),
@@ -86,7 +87,7 @@ EXPORTED = ("lb_create", "lb_pack_signs", "lb_set_scales", "lb_forward", "lb_for
             "lb_layer_shape", "lb_prepare", "lb_layer_device_bytes", "lb_destroy", "lb_forward_stage1", "lb_forward_stage2",
             "lb_eff_bits", "lb_rank_for_bpw", "lb_stack_create", "lb_stack_forward",
             "lb_stack_trace_elems", "lb_stack_reserve", "lb_stack_set_mode", "lb_stack_check",
-            "lb_stack_test_wait_failure",
+            "lb_stack_test_wait_failure", "lb_stack_test_delay",
             "lb_stack_timeline", "lb_stack_destroy", "lb_status_str", "lb_last_error", "lb_version")
 
 
@@ -283,6 +284,10 @@ def lb_stack_set_mode(stack: int, mode: int):
 
 def lb_stack_test_wait_failure(stack: int, enable: bool):
     _check(load_library().lb_stack_test_wait_failure(stack, int(bool(enable))))
+
+
+def lb_stack_test_delay(stack: int, seed: int, max_ticks: int):
+    _check(load_library().lb_stack_test_delay(stack, int(seed), int(max_ticks)))
 
 
 def lb_stack_check(stack: int):

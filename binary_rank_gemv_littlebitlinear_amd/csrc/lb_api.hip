@@ -884,6 +884,15 @@ extern "C" lb_status lb_stack_destroy(lb_stack *S) {
   return LB_OK;
 }
 
+extern "C" lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks) {
+  if (!S) return fail(LB_EINVAL, "lb_stack_test_delay: NULL stack");
+  if (max_ticks > 100000u) return fail(LB_EINVAL, "lb_stack_test_delay: max_ticks must be <= 100000 (1 ms)");
+  if (!S->persist)
+    return fail(LB_EUNSUPPORTED, "lb_stack_test_delay: the stack has no persistent sweep");
+  persist_set_delay(S->persist, seed, max_ticks);
+  return LB_OK;
+}
+
 extern "C" lb_status lb_stack_set_mode(lb_stack *S, int mode) {
   if (!S || mode < 0 || mode > 2) return fail(LB_EINVAL, "lb_stack_set_mode: bad argument");
   if (mode == 2 && !S->persist) return fail(LB_EUNSUPPORTED, "lb_stack_set_mode: no persistent plan on this device");

@@ -1,4 +1,5 @@
-// Persistent whole-stack sweep for decode-sized M (one cooperative launch).
+// Persistent whole-stack sweep for decode-sized M: one launch of one
+// workgroup per compute unit, all of which must be resident at once.
 #pragma once
 
 #include <string>
@@ -26,6 +27,9 @@ void persist_set_timeline(PersistPlan *p, uint64_t *buf);
 // Failure test: later sweeps wait for a generation nobody writes, with a
 // short bound, so every wait gives up and sets the error word.
 void persist_set_fail_test(PersistPlan *p, bool on);
+// Stress test: later sweeps delay each wave at the exchange's steps by a
+// pseudo-random time of up to max_ticks ticks of 10 ns (0 = off).
+void persist_set_delay(PersistPlan *p, unsigned seed, unsigned max_ticks);
 int persist_grid(const PersistPlan *p);
 int persist_phases(const PersistPlan *p);
 int persist_stamps();  // timestamps per phase and workgroup

@@ -171,6 +171,8 @@ struct PArgs {
   unsigned wait_skew;  // added to the generation a wait expects: 0, nonzero only in
                        // the host-requested failure test (no wait can succeed;
                        // each gives up after kSpinFailTest polls)
+  unsigned delay_seed;  // stress test: per-wave random delays at the exchange's
+  unsigned delay_max;   // steps, up to delay_max ticks of 10 ns (0 = off)
 };
 
 struct PersistPlan {
@@ -190,6 +192,7 @@ struct PersistPlan {
   unsigned *herr = nullptr;      // pinned host word, set by a wait that gives up
   unsigned *herr_dev = nullptr;  // its device address
   bool fail_test = false;  // next sweeps: unsatisfiable waits with a short bound
+  unsigned delay_seed = 0, delay_max = 0;  // next sweeps: random per-wave delays
   bool broken = false;
   uint64_t *timeline = nullptr;
 };
@@ -771,10 +774,32 @@ __device__ void exchange_publish(const Lds &L, int Lu, unsigned gen, const PArgs
   }
 }
 
+// Stress test of the exchange ordering: when the host asks for it, each
+// wave waits a pseudo-random time (a hash of the seed, the generation, the
+// workgroup, the wave and the site; zero for about half of the draws, else
+// up to delay_max ticks of the 100 MHz clock) before a step, so that
+// publishes, the LDS meeting after level A, the cross-XCD store and the
+// polls happen in orders the undisturbed sweep never shows.  The results
+// must not change: every sum has a fixed order.
+// The sweep is compiled twice: with kDelay false (every normal launch) these
+// calls are empty, so the stress hooks cost the timed kernel nothing.
+template <bool kDelay>
+__device__ __forceinline__ void test_delay(const PArgs &A, unsigned gen, int site) {
+  if (!kDelay || A.delay_max == 0u) return;
+  unsigned h = A.delay_seed ^ (gen * 0x9E3779B1u) ^ ((unsigned)blockIdx.x * 0x85EBCA77u) ^
+               ((unsigned)wave_id() * 0xC2B2AE3Du) ^ ((unsigned)site * 0x27D4EB2Fu);
+  h ^= h >> 16; h *= 0x7FEB352Du; h ^= h >> 15; h *= 0x846CA68Bu; h ^= h >> 16;
+  if (h & 1u) return;
+  const uint64_t ticks = (h >> 1) % A.delay_max;
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(1);
+}
+
 // Second half: levels A (owned slice over the XCD), B (over the XCDs) and C
 // (the totals, straight into the next phase's tables).
 static_assert(kXThreads == 4 * 64 && kPerXcd == 4 * 8 && kSliceMax <= 64,
               "level A: wave v sums producers v, v + 4, ...; a lane per column");
+template <bool kDelay>
 __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, const TabPlan &tp,
                                  int ph) {
   const int w = blockIdx.x, t = threadIdx.x;
@@ -789,6 +814,7 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   // The four exchange waves meet through an LDS counter, not a workgroup
   // barrier: waves 4-7 are still issuing the next phase's copies, and
   // waiting for them would put that issue time on the critical path.
+  test_delay<kDelay>(A, gen, 1);
   if (xw) {
     float v = 0.f;
     if (lane < nsc) {
@@ -815,6 +841,7 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   // summed over the XCDs by wave 0 (its own XCD's term from LDS), so the
   // polling wave never waits behind the acknowledgement of its own store;
   // the total goes to this XCD's area (level C)
+  test_delay<kDelay>(A, gen, 2);
   if (wv < 2 && lane < nsc) {
     const float xs = (L.red[lane] + L.red[64 + lane]) + (L.red[128 + lane] + L.red[192 + lane]);
     uint64_t *pb = A.PB + (size_t)(gen & 1) * kXcd * kLuMax + c0 + lane;
@@ -833,6 +860,7 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   stamp(L, ph, 6);
   // level C, straight into the next phase's tables: w = l * t per group
   uint64_t *pc = A.PC + (size_t)x * kLuMax;
+  test_delay<kDelay>(A, gen, 3);
   if (xw) {
     uint2 lraw[kGroupsPerThread];  // 4 fp16 l per group
 #pragma unroll
@@ -875,6 +903,7 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
 // SIMD: telling the compiler so lets it keep many table reads in flight
 // (otherwise it may serialise them to fit a higher occupancy that can never
 // occur).
+template <bool kDelay>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_persist(PArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -939,6 +968,7 @@ k_persist(PArgs A) {
     first_product(L, ph);
     stamp(L, ph, 4);
     const unsigned gen = gen_base + (unsigned)ph + 1u;
+    test_delay<kDelay>(A, gen, 0);
     exchange_publish(L, Lu, gen, A);
     // the partials, on the critical path, are issued before the next
     // phase's block copies (waves 4-7), which then overlap the waits
@@ -949,7 +979,7 @@ k_persist(PArgs A) {
       stage_phase(A, ph + 1, L);
       __builtin_amdgcn_s_setprio(0);
     }
-    if (!exchange_collect(L, Lu, gen, A, tp, ph)) {
+    if (!exchange_collect<kDelay>(L, Lu, gen, A, tp, ph)) {
       // a wait gave up: let the next phase's copies into LDS land before
       // the workgroup (and its LDS) ends
       __builtin_amdgcn_s_waitcnt(0);
@@ -1228,11 +1258,17 @@ lb_status persist_build(const std::vector<lb_layer *> &layers, const std::vector
     if (xl < 0) ok = false;
     P->xcd_local = xl > 0;
   }
-  ok = ok && hipFuncSetAttribute((const void *)k_persist, hipFuncAttributeMaxDynamicSharedMemorySize,
+  ok = ok && hipFuncSetAttribute((const void *)k_persist<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)P->lds) == hipSuccess;
+  ok = ok && hipFuncSetAttribute((const void *)k_persist<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)P->lds) == hipSuccess;
   int occ = 0;
-  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_persist, kThreads, P->lds) ==
+  int occ_d = 0;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_persist<false>, kThreads, P->lds) ==
                  hipSuccess;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_d, k_persist<true>, kThreads, P->lds) ==
+                 hipSuccess;
+  occ = std::min(occ, occ_d);
   if (!ok || occ < 1) {
     persist_free(P);
     return ok ? LB_EUNSUPPORTED : LB_EHIP;
@@ -1294,7 +1330,12 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
   A.segs = p->d_segs;
   A.grp0 = p->d_groups;
   A.wait_skew = p->fail_test ? 0x40000000u : 0u;
-  hipLaunchKernelGGL(k_persist, dim3(p->G), dim3(kThreads), p->lds, st, A);
+  A.delay_seed = p->delay_seed;
+  A.delay_max = p->delay_max;
+  if (p->delay_max)
+    hipLaunchKernelGGL(k_persist<true>, dim3(p->G), dim3(kThreads), p->lds, st, A);
+  else
+    hipLaunchKernelGGL(k_persist<false>, dim3(p->G), dim3(kThreads), p->lds, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     if (msg) *msg = std::string("persistent launch: ") + hipGetErrorString(e);
@@ -1305,6 +1346,10 @@ lb_status persist_run(PersistPlan *p, const uint16_t *x0, uint16_t *y, uint16_t 
 
 void persist_set_timeline(PersistPlan *p, uint64_t *buf) { p->timeline = buf; }
 void persist_set_fail_test(PersistPlan *p, bool on) { p->fail_test = on; }
+void persist_set_delay(PersistPlan *p, unsigned seed, unsigned max_ticks) {
+  p->delay_seed = seed;
+  p->delay_max = max_ticks;
+}
 int persist_grid(const PersistPlan *p) { return p->G; }
 int persist_phases(const PersistPlan *p) { return p->nunits + 1; }
 int persist_stamps() { return kStamps; }

@@ -322,6 +322,17 @@ lb_status lb_stack_timeline(lb_stack *S, void *buf, int64_t capacity, int64_t *n
  * LB_EUNSUPPORTED when the stack has no persistent sweep. */
 lb_status lb_stack_test_wait_failure(lb_stack *S, int enable);
 
+/* Diagnostics: stress the exchange of the one-launch sweep.  With
+ * max_ticks > 0 (at most 100000), later persistent sweeps make each wave
+ * wait, before each step of the cross-workgroup exchange (publishing its
+ * partials, the intra-XCD sum, the cross-XCD store and poll, the final
+ * poll), for a pseudo-random time drawn from seed, the sweep's generation,
+ * the workgroup, the wave and the step: zero or up to max_ticks ticks of
+ * 10 ns.  The output must not change (every sum has a fixed order), only
+ * the time.  max_ticks = 0 turns it off.  LB_EUNSUPPORTED when the stack
+ * has no persistent sweep. */
+lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
+
 /* Select the execution mode of lb_stack_forward: 0 = automatic (above),
  * 1 = every layer alone (as lb_forward) followed by a combine kernel per
  * unit, 2 = the one-launch sweep only (LB_EUNSUPPORTED unless M = 1 and

@@ -288,6 +288,44 @@ def test_persistent_wait_failure_is_reported_and_recovers(lbm):
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.view(np.uint16))
 
 
+@pytest.mark.parametrize("name,blocks", [("llama7b_mlp_stack", 3), ("llama70b_mlp_stack", 2)])
+def test_persistent_sweep_under_random_delays(lbm, name, blocks):
+    """Exchange stress: with the host-selected delay mode every wave of the
+    one-launch sweep waits a pseudo-random time before each exchange step
+    (publish, intra-XCD sum, cross-XCD store and poll, final poll), so the
+    workgroups meet in orders an undisturbed sweep never produces.  Every
+    delayed sweep, traced or not, must equal the undelayed one bit for bit
+    (fixed summation order), and no wait may give up."""
+    torch = lbtest.torch_dev()
+    say(f"[case] delayed sweeps {name} blocks={blocks}")
+    wl, S, paths = build_stack(lbm, name, blocks=blocks)
+    x0, y, tr = run_stack(lbm, wl, S, 1, mode=2)
+    S.check()
+    n = len(wl["layers"])
+    check_stack(wl, paths, x0, y, tr, 1, sample=[0, n - 1])
+    xd = lbtest.to_dev(x0)
+    yd = torch.empty((1, wl["layers"][-1]["b"]), dtype=torch.float16, device="cuda")
+    td = torch.empty(tr.size, dtype=torch.float16, device="cuda")
+    for seed, ticks in [(1, 200), (2, 2000), (3, 20000)]:
+        say(f"[case] delays seed={seed} up to {ticks} ticks")
+        lbm.lb_stack_test_delay(S.handle, seed, ticks)
+        for rep in range(3):
+            yd.zero_()
+            S.forward(xd, yd, None)
+            torch.cuda.synchronize()
+            S.check()
+            assert np.array_equal(yd.cpu().numpy().view(np.uint16), y.view(np.uint16)), (seed, rep)
+        td.zero_()
+        S.forward(xd, yd, td)
+        torch.cuda.synchronize()
+        S.check()
+        assert np.array_equal(td.cpu().numpy().view(np.uint16), tr.view(np.uint16)), f"trace, seed {seed}"
+    lbm.lb_stack_test_delay(S.handle, 0, 0)
+    with pytest.raises(lbm.LBError) as ei:
+        lbm.lb_stack_test_delay(S.handle, 1, 100001)
+    assert ei.value.status == lbm.LB_EINVAL
+
+
 @pytest.mark.parametrize("name,M", [("llama7b_mlp_stack", 2), ("llama7b_mlp_stack", 3),
                                     ("llama7b_mlp_stack", 4), ("llama70b_mlp_stack", 6),
                                     ("llama70b_mlp_stack", 7)])
