@@ -707,6 +707,7 @@ struct lb_stack {
   std::vector<MfmaPlan *> uplan;  // per unit, for M >= 64
   void *mws = nullptr;            // unit-path workspace (largest unit)
   unsigned *mcnt = nullptr;       // unit-path tile counters (kept zero)
+  MStackPlan *mstack = nullptr;   // the one-launch M >= 64 stack (null if unsupported)
 };
 
 static void stack_free_scratch(lb_stack *S) {
@@ -813,6 +814,14 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
       wsb = std::max(wsb, mfma_unit_ws_bytes(mp));
       nc = std::max(nc, mfma_cnt_entries(mp));
     }
+    {
+      std::vector<const MfmaPlan *> ups(S->uplan.begin(), S->uplan.end());
+      S->mstack = mstack_build(ups, S->kappa, ctx_of(S->layers[0])->info);
+      if (S->mstack) {
+        wsb = std::max(wsb, mstack_ws_bytes(S->mstack));
+        nc = std::max(nc, mstack_cnt_entries(S->mstack));
+      }
+    }
     hipError_t e = hipMalloc(&S->mws, wsb);
     if (e == hipSuccess) e = hipMalloc(&S->mcnt, nc * sizeof(unsigned));
     if (e == hipSuccess) e = hipMemset(S->mcnt, 0, nc * sizeof(unsigned));
@@ -832,9 +841,8 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 7 : 4;
   }
   if (st != LB_OK && st != LB_EUNSUPPORTED) {
-    stack_free_scratch(S);
-    delete S;
-    return st;
+    lb_stack_destroy(S);
+    return fail(st, std::string("lb_stack_create: one-launch sweep setup: ") + hipGetErrorString(hipGetLastError()));
   }
   *out = S;
   return LB_OK;
@@ -877,6 +885,7 @@ extern "C" lb_status lb_stack_destroy(lb_stack *S) {
   DeviceGuard dg(S->device);
   stack_free_scratch(S);
   persist_free(S->persist);
+  mstack_free(S->mstack);
   for (MfmaPlan *mp : S->uplan) mfma_plan_free(mp);
   if (S->mws) (void)hipFree(S->mws);
   if (S->mcnt) (void)hipFree(S->mcnt);
@@ -894,7 +903,9 @@ extern "C" lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t ma
 }
 
 extern "C" lb_status lb_stack_set_mode(lb_stack *S, int mode) {
-  if (!S || mode < 0 || mode > 2) return fail(LB_EINVAL, "lb_stack_set_mode: bad argument");
+  if (!S || mode < 0 || mode > 3) return fail(LB_EINVAL, "lb_stack_set_mode: bad argument");
+  if (mode == 3 && !S->mstack)
+    return fail(LB_EUNSUPPORTED, "lb_stack_set_mode: no one-launch M >= 64 plan (a width is not a multiple of 8)");
   if (mode == 2 && !S->persist) return fail(LB_EUNSUPPORTED, "lb_stack_set_mode: no persistent plan on this device");
   S->mode = mode;
   return LB_OK;
@@ -953,7 +964,7 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
   // a few rows without a trace: one batch-1 sweep per row beats the
   // per-layer kernels up to S->loop_rows rows (rows are independent, so
   // each row's result is exactly its batch-1 result)
-  if (S->persist && S->mode == 0 && !trace && M <= S->loop_rows) {
+  if (S->persist && (S->mode == 0 || S->mode == 3) && !trace && M <= S->loop_rows) {
     const int64_t a0 = S->layers[0]->ly.a, bl = S->layers.back()->ly.b;
     for (int64_t m = 0; m < M; ++m) {
       std::string msg;
@@ -970,6 +981,15 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
       lb_status es = ensure_mfma_copies(Lr, st, true, "lb_stack_forward");
       if (es != LB_OK) return es;
     }
+  }
+  if (M >= 64 && S->mode == 3 && !trace) {
+    if (!S->mstack) return fail(LB_EUNSUPPORTED, "lb_stack_forward: no one-launch M >= 64 plan for this stack");
+    std::string msg;
+    DevCtx *dc = ctx_of(S->layers[0]);
+    lb_status ms = mstack_run(S->mstack, (const uint16_t *)x0, (uint16_t *)y, M, S->mws, S->mcnt,
+                              (uint16_t *)S->xbuf[0], (uint16_t *)S->xbuf[1], dc->zero, dc->info, st, &msg);
+    if (ms != LB_OK) return fail(ms, "lb_stack_forward: " + msg);
+    return LB_OK;
   }
   if (M >= 64 && S->mode != 1) {
     // one stage-1 and one stage-2 launch per unit; stage 2 also combines

@@ -132,6 +132,25 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             void *ws, unsigned *cnt, const void *zero, const DeviceInfo &dev,
                             hipStream_t st);
 
+// The whole stack for M >= 64 in one launch per 256 rows (lb_mfma.hip):
+// the unit tiles above as work items taken by ticket, each waiting only for
+// the previous step of its own 32-row block.  Built from the stack's unit
+// plans (null when a width is not a multiple of 8 or the device cannot
+// hold the kernel).  ws and cnt as for launch_mfma_unit, sized by
+// mstack_ws_bytes and mstack_cnt_entries; xb0, xb1 hold 256 rows of the
+// widest unit width each.  Launches only once an argument set for the row
+// count and these buffers exists (built on first use outside capture;
+// LB_ENOTREADY under capture); LB_ETIMEOUT once after a launch gave up a
+// wait (the next call resets).
+struct MStackPlan;
+MStackPlan *mstack_build(const std::vector<const MfmaPlan *> &units, float kappa, const DeviceInfo &dev);
+void mstack_free(MStackPlan *p);
+size_t mstack_ws_bytes(const MStackPlan *p);
+size_t mstack_cnt_entries(const MStackPlan *p);
+lb_status mstack_run(MStackPlan *p, const uint16_t *x0, uint16_t *y, int64_t M, void *ws, unsigned *cnt,
+                     uint16_t *xb0, uint16_t *xb1, const void *zero, const DeviceInfo &dev,
+                     hipStream_t st, std::string *msg);
+
 // Initialisation of one path from real device factors U (b x s) and
 // V (a x s), fp32 row-major.  ws holds init_ws_bytes(a, b, s) bytes; the
 // results are device pointers into ws: canonical sign words su (b x Wk),

@@ -42,6 +42,10 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
+#include <map>
+#include <new>
+#include <string>
 #include <type_traits>
 #include <vector>
 
@@ -72,7 +76,7 @@ static_assert(2 * s1_lds_bytes(kS1RoundC) <= 80 * 1024, "two buffered rounds lea
 // words (two round buffers)
 constexpr int kRC2 = 32;  // a multiple of 4
 constexpr int kS2MinC = 18;            // the wave partials fit one round buffer from here
-constexpr int kS2Lds = 160 * 1024;
+constexpr int kS2Lds = 158 * 1024;  // leaves room for the static LDS of the one-launch stack
 constexpr int kRP2 = 64 + 4;           // LDS pitch (floats) of a wave's 32 x 64 partial
 static_assert(4 * 32 * kRP2 * 4 <= kS2MinC * 2048, "the reduction buffer fits one round buffer");
 // with 8 waves (nb = 2 or 4) the partials need 8 * 32 rows: they fit the
@@ -89,7 +93,7 @@ struct S1Seg {
 };
 static_assert(sizeof(S1Seg) == 40, "S1Seg layout");
 
-struct S1Args {
+struct alignas(16) S1Args {
   const uint16_t *x;
   uint16_t *T;
   float *part;
@@ -97,6 +101,9 @@ struct S1Args {
   const void *zero;  // >= 16 zero bytes (DMA source for padding)
   int64_t M;         // rows of this chunk
   int a, a16, Lt, ntile32, kcps, cround, nsplit, nseg, xvec;
+  // addressing: x row pitch (elements), T row-block pitch (8-column
+  // blocks), tiles per row block and split slots per tile of part / cnt
+  int xpitch, tp8, tstride, psplit;
   S1Seg seg[kMaxUnitSegs];
 };
 
@@ -109,7 +116,7 @@ struct S2Layer {
 };
 static_assert(sizeof(S2Layer) == 64, "S2Layer layout");
 
-struct S2Args {
+struct alignas(16) S2Args {
   const uint16_t *T;
   uint16_t *xout;  // combined output (stack) or null
   const void *zero;
@@ -119,6 +126,7 @@ struct S2Args {
   int nrounds;
   int nb;  // 64-output column pairs per block (1, 2 or 4)
   int c2;  // chunks per round
+  int tp8, opitch;  // T row-block pitch (8-column blocks), xout row pitch
   S2Layer ly[kMaxUnitLayersM];
 };
 
@@ -157,6 +165,12 @@ __device__ __forceinline__ void dma16(const void *src, void *dst) {
 __device__ __forceinline__ void dma4(const void *src, void *dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
+// The same for data another workgroup of the running launch wrote: the
+// device-scope cache policy, so no stale L2 line of this XCD is returned.
+template <bool kCoh>
+__device__ __forceinline__ void dma16c(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kCoh ? kCoherent : 0);
+}
 
 __device__ __forceinline__ half8_t as_h8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
 
@@ -189,6 +203,24 @@ __device__ __forceinline__ uint4 pack8(const float *v) {
   o.z = mf2h(v[4]) | ((uint32_t)mf2h(v[5]) << 16);
   o.w = mf2h(v[6]) | ((uint32_t)mf2h(v[7]) << 16);
   return o;
+}
+
+// 8 fp16 to [rows x n] (row pitch `pitch`) at (row, col..col+7), columns
+// >= n dropped, with device-scope stores (read by other workgroups of the
+// running launch).  rs covers the whole output.
+__device__ __forceinline__ void store8c(__amdgpu_buffer_rsrc_t rs, int n, int pitch, int64_t row, int col,
+                                        const float *v) {
+  const int off = (int)((row * pitch + col) * 2);
+  if ((n & 7) == 0 && (pitch & 7) == 0 && col + 8 <= n) {
+    const uint4 o = pack8(v);
+    u32x4 q;
+    q.x = o.x; q.y = o.y; q.z = o.z; q.w = o.w;
+    __builtin_amdgcn_raw_buffer_store_b128(q, rs, off, 0, kCoherent);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (col + e < n) __builtin_amdgcn_raw_buffer_store_b16(mf2h(v[e]), rs, off + 2 * e, 0, kCoherent);
+  }
 }
 
 // 8 fp16 to row-major [rows x n] at (row, col..col+7), columns >= n dropped.
@@ -225,14 +257,22 @@ __device__ __forceinline__ void store8(uint16_t *base, int n, int64_t row, int c
 //   g      [wave][chunk c16(C)][4 pieces of 8 fp16]
 __device__ __forceinline__ int s1_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-__global__ void __launch_bounds__(kThreads1)
-k_unit_s1(S1Args A) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_last;
+// The argument structs may be read through a constant-address-space view
+// (AT), so that uniform fields load into scalar registers.
+typedef __attribute__((address_space(4))) const S1Args CS1Args;
+typedef __attribute__((address_space(4))) const S2Args CS2Args;
+
+// Tile (bx, by, bz) of a grid with gx tiles across; kCoh: x comes from
+// and T goes to other workgroups of the running launch (device-scope
+// loads and stores).  Returns whether this block completed the tile (the
+// only split, or the last of its splits): then its T values are stored.
+template <bool kCoh, class AT>
+__device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int by, int bz,
+                                        unsigned char *smem, int *s_last) {
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int tw = w & 3, par = w >> 2;  // column tile, chunk parity
-  const int t32 = blockIdx.x * 4 + tw;
-  const int64_t tok0 = (int64_t)blockIdx.y * 32;
+  const int t32 = bx * 4 + tw;
+  const int64_t tok0 = (int64_t)by * 32;
 
   // the tile's 32 columns lie in one segment
   const bool active = t32 < A.ntile32;
@@ -254,7 +294,7 @@ k_unit_s1(S1Args A) {
     if (cval) lcol = mh2f(A.seg[e].l[k]);
   }
   const int nkc = (A.a + 31) >> 5;
-  const int kc0 = blockIdx.z * A.kcps;
+  const int kc0 = bz * A.kcps;
   const int kc1 = min(nkc, kc0 + A.kcps);
   const int C = A.cround;
   const int nr = (kc1 - kc0 + C - 1) / C;
@@ -273,8 +313,8 @@ k_unit_s1(S1Args A) {
         const int c8 = (lane & 3) ^ s1_swz(row);
         const int64_t tok = tok0 + row;
         const int i = (kcr + (u >> 1)) * 32 + c8 * 8;
-        const void *src = (tok < A.M && i < A.a) ? (const void *)(A.x + tok * A.a + i) : A.zero;
-        dma16(src, buf + u * 1024);
+        const void *src = (tok < A.M && i < A.a) ? (const void *)(xp + tok * A.xpitch + i) : A.zero;
+        dma16c<kCoh>(src, buf + u * 1024);
       }
     } else {
       for (int idx = threadIdx.x; idx < nch * 128; idx += kThreads1) {
@@ -284,7 +324,7 @@ k_unit_s1(S1Args A) {
         const int i = (kcr + kk) * 32 + c8 * 8;
         uint32_t hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hv[e] = (tok < A.M && i + e < A.a) ? A.x[tok * A.a + i + e] : 0u;
+        for (int e = 0; e < 8; ++e) hv[e] = (tok < A.M && i + e < A.a) ? xp[tok * A.xpitch + i + e] : 0u;
         uint4 o;
         o.x = hv[0] | (hv[1] << 16); o.y = hv[2] | (hv[3] << 16);
         o.z = hv[4] | (hv[5] << 16); o.w = hv[6] | (hv[7] << 16);
@@ -402,30 +442,30 @@ k_unit_s1(S1Args A) {
     __syncthreads();  // red is free again
   }
 
-  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  const int tile = by * A.tstride + bx;
   if (A.nsplit > 1) {
     // split z's partial: registers 4q..4q+3 of lane l of tile tw as one
     // 16-byte word at [(tile*nsplit + z)*1024 + (4 tw + q)*64 + l] (float4
     // units); wave (tw, par) holds q = 2 par, 2 par + 1
     const __amdgpu_buffer_rsrc_t rs =
-        coherent_rsrc(A.part + (size_t)tile * A.nsplit * 4096, (uint32_t)A.nsplit * 16384u);
+        coherent_rsrc(A.part + (size_t)tile * A.psplit * 4096, (uint32_t)A.nsplit * 16384u);
     const int l0 = ((tw * 4 + 2 * par) * 64 + lane) * 16;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       u32x4 o;
       o.x = __float_as_uint(v[4 * q]); o.y = __float_as_uint(v[4 * q + 1]);
       o.z = __float_as_uint(v[4 * q + 2]); o.w = __float_as_uint(v[4 * q + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(o, rs, blockIdx.z * 16384 + l0 + q * 1024, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, bz * 16384 + l0 + q * 1024, 0, kCoherent);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
       const unsigned old =
           __hip_atomic_fetch_add(&A.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == (unsigned)(A.nsplit - 1);
+      *s_last = old == (unsigned)(A.nsplit - 1);
     }
     __syncthreads();
-    if (!s_last) return;
+    if (!*s_last) return false;
     // the last block of the tile sums the splits in split order; every load
     // is unconditional (splits past nsplit re-read the last one) so all of
     // them are in flight at once
@@ -457,9 +497,24 @@ k_unit_s1(S1Args A) {
     tl[((col >> 3) * 32 + row) * 8 + (col & 7)] = mf2h(v[r] * lcol);
   }
   __syncthreads();
-  uint4 *dst = reinterpret_cast<uint4 *>(A.T + ((size_t)blockIdx.y * (A.Lt >> 3) + blockIdx.x * 16) * 256);
+  uint4 *dst = reinterpret_cast<uint4 *>(A.T + ((size_t)by * A.tp8 + bx * 16) * 256);
   const uint4 *srcl = reinterpret_cast<const uint4 *>(smem);
-  dst[threadIdx.x] = srcl[threadIdx.x];
+  if (kCoh) {
+    const uint4 o = srcl[threadIdx.x];
+    u32x4 q;
+    q.x = o.x; q.y = o.y; q.z = o.z; q.w = o.w;
+    __builtin_amdgcn_raw_buffer_store_b128(q, coherent_rsrc(dst, 8192u), threadIdx.x * 16, 0, kCoherent);
+  } else {
+    dst[threadIdx.x] = srcl[threadIdx.x];
+  }
+  return true;
+}
+
+__global__ void __launch_bounds__(kThreads1)
+k_unit_s1(S1Args A) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_last;
+  (void)s1_tile<false>(A, A.x, blockIdx.x, blockIdx.y, blockIdx.z, smem, &s_last);
 }
 
 // ------------------------------------------------------------- stage 2
@@ -476,19 +531,19 @@ k_unit_s1(S1Args A) {
 // [chunk][c8 4][32 rows][8 fp16], then the sign words [pair][chunk][64 outputs].
 __host__ __device__ constexpr int s2_buf_bytes(int C, int nb) { return C * 2048 + nb * C * 256; }
 
-template <int NB, int NW>
-__global__ void __launch_bounds__(NW * 64)
-k_unit_s2(S2Args A) {
-  extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
+// Tile (bx, by); kCoh: T comes from and xout goes to other workgroups of
+// the running launch (device-scope loads and stores).
+template <int NB, int NW, bool kCoh, class AT>
+__device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, unsigned char *smem) {
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int t = threadIdx.x;
   constexpr int nb = NB, nph = NW / NB;
   const int C = A.c2;
   const int cp = w % nb, phase = w / nb;
-  const int tb = blockIdx.y;
+  const int tb = by;
   const int64_t tok0 = (int64_t)tb * 32;
-  const int j0 = blockIdx.x * 64 * nb;
-  const int Lt8 = A.Lt >> 3;
+  const int j0 = bx * 64 * nb;
+  const int Lt8 = A.tp8;
   const int bufb = s2_buf_bytes(C, nb), wofs = C * 2048;
 
   // round r -> (layer m, first chunk ch0, chunk count nch); chunk ch of a
@@ -511,15 +566,15 @@ k_unit_s2(S2Args A) {
   auto issue = [&](int r) {
     int m, ch0, nch;
     round_of(r, m, ch0, nch);
-    const S2Layer &Ly = A.ly[m];
+    auto &Ly = A.ly[m];
     unsigned char *buf = smem + (r & 1) * bufb;
     const uint16_t *tsrc = A.T + ((size_t)tb * Lt8 + (Ly.seg0[0] >> 3) + ch0 * 4) * 256;
     // the blocks of a row tile all read the same T rows: each starts at its
     // own place in the list so they do not queue on the same lines
-    const int nu = nch * 2, u0 = (blockIdx.x * 4) % nu;
+    const int nu = nch * 2, u0 = (bx * 4) % nu;
     for (int i = w; i < nu; i += NW) {
       const int u = u0 + i < nu ? u0 + i : u0 + i - nu;
-      dma16(tsrc + u * 512 + lane * 8, buf + u * 1024);
+      dma16c<kCoh>(tsrc + u * 512 + lane * 8, buf + u * 1024);
     }
     // words: instruction (pair q, v) covers chunks 4 v .. 4 v + 3 of pair q
     const int nv = (nch + 3) / 4;
@@ -544,7 +599,7 @@ k_unit_s2(S2Args A) {
   issue(0);
   int r = 0;
   for (int m = 0; m < A.nl; ++m) {
-    const S2Layer &Ly = A.ly[m];
+    auto &Ly = A.ly[m];
     const int nc = Ly.P * Ly.Wk, nrm = (nc + C - 1) / C;
     // h of the wave's columns; the loads are unconditional (clamped index)
     // so no wait for them lands before the round's copies are needed
@@ -632,14 +687,25 @@ k_unit_s2(S2Args A) {
       if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + q * 64 + c_o, v);
     }
   }
-  if (t >= 256 || A.direct || !A.xout || tok0 + row_o >= A.M) return;
+  if (t >= 256 || A.direct || !xout || tok0 + row_o >= A.M) return;
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = A.c_out * ys[q][e];
-    store8(A.xout, A.b, tok0 + row_o, j0 + q * 64 + c_o, o);
+    if (kCoh)
+      store8c(coherent_rsrc(xout, (uint32_t)(A.M * A.opitch * 2)), A.b, A.opitch, tok0 + row_o,
+              j0 + q * 64 + c_o, o);
+    else
+      store8(xout, A.b, tok0 + row_o, j0 + q * 64 + c_o, o);
   }
+}
+
+template <int NB, int NW>
+__global__ void __launch_bounds__(NW * 64)
+k_unit_s2(S2Args A) {
+  extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
+  s2_tile<NB, NW, false>(A, A.xout, blockIdx.x, blockIdx.y, smem);
 }
 
 // ------------------------------------------------------------------ host
@@ -793,6 +859,10 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A1.nsplit = s1_nsplit(*p, Mc, dev, &A1.kcps, &A1.cround);
     A1.nseg = p->nseg;
     A1.xvec = (p->a % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    A1.xpitch = (int)p->a;
+    A1.tp8 = p->Lt >> 3;
+    A1.tstride = p->Lt / 128;
+    A1.psplit = A1.nsplit;
     for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = segs[i];
     dim3 g1((unsigned)(p->Lt / 128), (unsigned)((Mc + 31) / 32), (unsigned)A1.nsplit);
     const size_t lds1 = s1_lds_launch(A1.kcps, A1.cround);
@@ -811,6 +881,8 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     A2.direct = direct ? 1 : 0;
     A2.c_out = c_out;
     s2_shape(*p, Mc, dev, &A2.nb, &A2.c2);
+    A2.tp8 = p->Lt >> 3;
+    A2.opitch = (int)p->b;
     A2.nrounds = 0;
     for (int m = 0; m < p->nl; ++m) A2.nrounds += (p->ly[m].P * p->ly[m].Wk + A2.c2 - 1) / A2.c2;
     for (int m = 0; m < kMaxUnitLayersM; ++m) {
@@ -829,6 +901,377 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// ------------------------------------------------ persistent stack, M >= 64
+// The whole stack in one launch: the stage-1 and stage-2 tiles of every
+// unit above are its work items, taken in a fixed order by atomic ticket.
+// Items are ordered by chain step c (2 u for unit u's first stage, 2 u + 1
+// for its second), then by 32-row block rb, then by tile (split-major in
+// stage 1).  Rows are independent through the whole stack, so an item of
+// step c and row block rb waits only for step c - 1 of the same row block
+// (a counter of completed tiles per step and row block): the row blocks
+// pipeline, a block's next unit starting while other blocks are still in
+// the previous one, and no launch boundary separates the units.
+// A workgroup takes its next ticket when it has finished its item.  An
+// item waits only for items with smaller tickets, which running
+// workgroups hold, so the launch completes whatever number of workgroups
+// is resident at once.  Intermediate x and T rows are written and read
+// with device-scope stores and loads, each row block in its own region
+// (fixed pitches), so concurrent steps of different row blocks never
+// share memory.  The last workgroup to finish clears the counters for
+// the next launch.  Every wait is bounded: one that gives up sets the
+// error word (and its host-mapped copy) and its workgroup stops.
+struct MStackArgs {
+  const S1Args *__restrict__ s1;       // [U]; unit 0's x is x0
+  const S2Args *__restrict__ s2;       // [U]; the last unit's xout is y
+  const int *__restrict__ step_off;    // [2 U + 1] first ticket of each step
+  const int *__restrict__ step_tiles;  // [2 U] tiles of one row block that complete a step
+  int nsteps, nrb;
+  const uint16_t *x0;
+  uint16_t *y;
+  unsigned *ctrl;  // [0] next ticket, [1] finished workgroups (zero between launches)
+  unsigned *done;  // [2 U][nrb] completed tiles, kDoneStride apart (zero between launches)
+  unsigned *err;   // device error word
+  unsigned *herr;  // host-mapped error word
+};
+
+constexpr long kMSpin = 1L << 22;  // polls (each after a short sleep) before a wait gives up
+constexpr int kDoneStride = 32;    // one 128-byte line per counter: the polls of one do not queue behind another's
+
+
+__global__ void __launch_bounds__(kThreads1) k_mstack(MStackArgs A) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_last, s_ok, s_final;
+  __shared__ unsigned s_tk, s_next;
+  const int t = threadIdx.x;
+  const int total = A.step_off[A.nsteps];
+  const int U = A.nsteps >> 1;
+  if (t == 0) {
+    s_tk = __hip_atomic_fetch_add(&A.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ok = 1;
+  }
+  __syncthreads();
+  unsigned tk = __builtin_amdgcn_readfirstlane(s_tk);
+  int c = 0;  // tickets only grow, so each step search starts at the last one
+  while (tk < (unsigned)total) {
+    while ((unsigned)A.step_off[c + 1] <= tk) ++c;
+    c = __builtin_amdgcn_readfirstlane(c);
+    const int u = c >> 1;
+    const int per_rb = (A.step_off[c + 1] - A.step_off[c]) / A.nrb;
+    const int local = (int)tk - A.step_off[c];
+    const int rb = __builtin_amdgcn_readfirstlane(local / per_rb);
+    const int k = __builtin_amdgcn_readfirstlane(local - rb * per_rb);
+    if (c > 0) {
+      if (t == 0) {
+        const unsigned need = (unsigned)A.step_tiles[c - 1];
+        unsigned *d = &A.done[((size_t)(c - 1) * A.nrb + rb) * kDoneStride];
+        long sp = 0;
+        while (__hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++sp > kMSpin ||
+              __hip_atomic_load(A.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(A.herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            s_ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+    }
+    __syncthreads();  // the dependency is met (or s_ok is 0)
+    if (!s_ok) break;
+    bool completed = true;
+    if ((c & 1) == 0) {
+      CS1Args &P = *(CS1Args *)(A.s1 + u);  // uniform: scalar loads
+      const int gx = P.Lt / 128;
+      completed = s1_tile<true>(P, u == 0 ? A.x0 : P.x, k % gx, rb, k / gx, smem, &s_last);
+    } else {
+      CS2Args &P = *(CS2Args *)(A.s2 + u);
+      uint16_t *xo = u == U - 1 ? A.y : P.xout;
+      if (P.nb == 4)
+        s2_tile<4, 8, true>(P, xo, k, rb, smem);
+      else if (P.nb == 2)
+        s2_tile<2, 8, true>(P, xo, k, rb, smem);
+      else
+        s2_tile<1, 8, true>(P, xo, k, rb, smem);
+    }
+    // every wave's device-scope stores have completed before the tile is
+    // counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0) {
+      if (completed)
+        __hip_atomic_fetch_add(&A.done[((size_t)c * A.nrb + rb) * kDoneStride], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      // the next ticket only now: a ticket taken ahead would hold its item
+      // back behind this one, and every item of its step waits for it
+      s_next = __hip_atomic_fetch_add(&A.ctrl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // LDS free for the next item; s_next visible
+    tk = __builtin_amdgcn_readfirstlane(s_next);
+  }
+  if (t == 0) {
+    const unsigned f = __hip_atomic_fetch_add(&A.ctrl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_final = f == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_final) return;
+  // every other workgroup has finished: clear the counters for the next launch
+  for (int i = t; i < A.nsteps * A.nrb; i += kThreads1)
+    __hip_atomic_store(&A.done[(size_t)i * kDoneStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) {
+    __hip_atomic_store(&A.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&A.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+struct MStackArgSet {
+  S1Args *s1 = nullptr;
+  S2Args *s2 = nullptr;
+  int *steps = nullptr;  // step_off [2U + 1] then step_tiles [2U]
+  size_t lds = 0;
+};
+
+struct MStackPlan {
+  std::vector<const MfmaPlan *> units;
+  int device = 0;
+  int64_t a0 = 0, b_last = 0, max_width = 0;
+  float kappa = 1.f;
+  int G = 0;
+  int Ltmax = 0, gxmax = 0;
+  unsigned *ctrl = nullptr;  // ctrl[2], err at ctrl[2]
+  unsigned *done = nullptr;
+  unsigned *herr = nullptr, *herr_dev = nullptr;
+  bool broken = false;
+  // argument sets by (rows, scratch addresses); kept until the plan is freed
+  std::map<std::vector<uintptr_t>, MStackArgSet> sets;
+};
+
+static void mstack_free_sets(MStackPlan *p) {
+  for (auto &kv : p->sets) {
+    if (kv.second.s1) (void)hipFree(kv.second.s1);
+    if (kv.second.s2) (void)hipFree(kv.second.s2);
+    if (kv.second.steps) (void)hipFree(kv.second.steps);
+  }
+  p->sets.clear();
+}
+
+void mstack_free(MStackPlan *p) {
+  if (!p) return;
+  mstack_free_sets(p);
+  if (p->ctrl) (void)hipFree(p->ctrl);
+  if (p->done) (void)hipFree(p->done);
+  if (p->herr) (void)hipHostFree(p->herr);
+  delete p;
+}
+
+MStackPlan *mstack_build(const std::vector<const MfmaPlan *> &units, float kappa, const DeviceInfo &dev) {
+  if (units.empty()) return nullptr;
+  MStackPlan *P = new (std::nothrow) MStackPlan();
+  if (!P) return nullptr;
+  P->units = units;
+  P->device = dev.device;
+  P->kappa = kappa;
+  P->a0 = units.front()->a;
+  P->b_last = units.back()->b;
+  for (const MfmaPlan *u : units) {
+    // 16-byte rows throughout (the x copies are LDS-DMA of 8 fp16)
+    if (u->a % 8 != 0 || u->b % 8 != 0) {
+      delete P;
+      return nullptr;
+    }
+    P->max_width = std::max<int64_t>(P->max_width, std::max(u->a, u->b));
+    P->Ltmax = std::max(P->Ltmax, u->Lt);
+  }
+  P->gxmax = P->Ltmax / 128;
+  const int U = (int)units.size();
+  const int nrb = kMfmaRows / 32;
+  bool ok = hipMalloc(&P->ctrl, 64) == hipSuccess && hipMemset(P->ctrl, 0, 64) == hipSuccess;
+  const size_t done_bytes = sizeof(unsigned) * 2 * U * nrb * kDoneStride;
+  ok = ok && hipMalloc(&P->done, done_bytes) == hipSuccess && hipMemset(P->done, 0, done_bytes) == hipSuccess;
+  ok = ok && hipHostMalloc(&P->herr, 64, hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+       hipHostGetDevicePointer((void **)&P->herr_dev, P->herr, 0) == hipSuccess;
+  if (ok) *(volatile unsigned *)P->herr = 0u;
+  const size_t lds_max = std::max(kS1Lds, (size_t)kS2Lds);
+  ok = ok && hipFuncSetAttribute((const void *)k_mstack, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds_max) == hipSuccess;
+  int occ = 0;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_mstack, kThreads1, lds_max) == hipSuccess;
+  if (!ok || occ < 1) {
+    (void)hipGetLastError();  // not an error of the caller's next call
+    mstack_free(P);
+    return nullptr;
+  }
+  P->G = (dev.cu_count > 0 ? dev.cu_count : 256) * occ;
+  return P;
+}
+
+size_t mstack_ws_bytes(const MStackPlan *p) {
+  return (size_t)round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256) +
+         (size_t)(kMfmaRows / 32) * p->gxmax * kMaxSplit * 4096 * sizeof(float);
+}
+size_t mstack_cnt_entries(const MStackPlan *p) { return (size_t)(kMfmaRows / 32) * p->gxmax; }
+
+// The device argument set for Mc rows and these scratch buffers, built on
+// first use (allocates and copies synchronously).
+static lb_status mstack_args(MStackPlan *p, int64_t Mc, void *ws, unsigned *cnt, uint16_t *xb0,
+                             uint16_t *xb1, const void *zero, const DeviceInfo &dev, hipStream_t st,
+                             MStackArgSet **out, std::string *msg) {
+  const std::vector<uintptr_t> key = {(uintptr_t)Mc, (uintptr_t)ws, (uintptr_t)cnt, (uintptr_t)xb0,
+                                      (uintptr_t)xb1};
+  auto it = p->sets.find(key);
+  if (it != p->sets.end()) {
+    *out = &it->second;
+    return LB_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    if (msg) *msg = "the persistent M >= 64 launch for this row count is not set up yet (run this M once "
+                    "outside capture first)";
+    return LB_ENOTREADY;
+  }
+  const int U = (int)p->units.size();
+  const int nrb = (int)((Mc + 31) / 32);
+  std::vector<S1Args> h1(U);
+  std::vector<S2Args> h2(U);
+  std::vector<int> steps(4 * U + 1, 0);
+  uint16_t *T = reinterpret_cast<uint16_t *>(ws);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
+                                          round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256));
+  size_t lds = 16384;
+  int off = 0;
+  for (int u = 0; u < U; ++u) {
+    const MfmaPlan &P = *p->units[u];
+    for (int m = 0; m < P.nl; ++m)
+      if (!P.src[m]->sv1m || !P.src[m]->su2m) {
+        if (msg) *msg = "matrix-core sign copies missing";
+        return LB_ENOTREADY;
+      }
+    S1Args &A1 = h1[u];
+    A1.x = u == 0 ? nullptr : (((u - 1) & 1) ? xb1 : xb0);
+    A1.T = T;
+    A1.part = part;
+    A1.cnt = cnt;
+    A1.zero = zero;
+    A1.M = Mc;
+    A1.a = (int)P.a;
+    A1.a16 = P.a16;
+    A1.Lt = P.Lt;
+    A1.ntile32 = P.ntile32;
+    A1.nsplit = s1_nsplit(P, Mc, dev, &A1.kcps, &A1.cround);
+    A1.nseg = P.nseg;
+    A1.xvec = 1;
+    A1.xpitch = u == 0 ? (int)p->a0 : (int)p->max_width;
+    A1.tp8 = p->Ltmax >> 3;
+    A1.tstride = p->gxmax;
+    A1.psplit = kMaxSplit;
+    for (int i = 0; i < kMaxUnitSegs; ++i) A1.seg[i] = P.seg[i];
+    for (int i = 0; i < P.nseg; ++i) {
+      const Layer &Ly = *P.src[P.seg_layer[i]];
+      A1.seg[i].bits = Ly.sv1m + (size_t)P.seg_path[i] * Ly.s;
+    }
+    lds = std::max(lds, s1_lds_launch(A1.kcps, A1.cround));
+    S2Args &A2 = h2[u];
+    A2.T = T;
+    A2.xout = u == U - 1 ? nullptr : ((u & 1) ? xb1 : xb0);
+    A2.zero = zero;
+    A2.M = Mc;
+    A2.b = (int)P.b;
+    A2.Lt = P.Lt;
+    A2.nl = P.nl;
+    A2.direct = 0;
+    A2.c_out = p->kappa / std::sqrt((float)P.nl);
+    s2_shape(P, Mc, dev, &A2.nb, &A2.c2);
+    A2.tp8 = p->Ltmax >> 3;
+    A2.opitch = u == U - 1 ? (int)p->b_last : (int)p->max_width;
+    A2.nrounds = 0;
+    for (int m = 0; m < P.nl; ++m) A2.nrounds += (P.ly[m].P * P.ly[m].Wk + A2.c2 - 1) / A2.c2;
+    for (int m = 0; m < kMaxUnitLayersM; ++m) {
+      A2.ly[m] = P.ly[m];
+      A2.ly[m].su2 = m < P.nl ? P.src[m]->su2m : nullptr;
+      A2.ly[m].y = nullptr;
+    }
+    lds = std::max(lds, (size_t)2 * s2_buf_bytes(A2.c2, A2.nb));
+    const int gx = P.Lt / 128;
+    const int njx = (int)((P.b + 64 * A2.nb - 1) / (64 * A2.nb));
+    steps[2 * u] = off;
+    off += nrb * gx * A1.nsplit;
+    steps[2 * u + 1] = off;
+    off += nrb * njx;
+    steps[2 * U + 1 + 2 * u] = gx;
+    steps[2 * U + 1 + 2 * u + 1] = njx;
+  }
+  steps[2 * U] = off;
+  MStackArgSet set;
+  set.lds = lds;
+  hipError_t e = hipMalloc(&set.s1, sizeof(S1Args) * U);
+  if (e == hipSuccess) e = hipMalloc(&set.s2, sizeof(S2Args) * U);
+  if (e == hipSuccess) e = hipMalloc(&set.steps, sizeof(int) * steps.size());
+  if (e == hipSuccess) e = hipMemcpy(set.s1, h1.data(), sizeof(S1Args) * U, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(set.s2, h2.data(), sizeof(S2Args) * U, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(set.steps, steps.data(), sizeof(int) * steps.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    if (set.s1) (void)hipFree(set.s1);
+    if (set.s2) (void)hipFree(set.s2);
+    if (set.steps) (void)hipFree(set.steps);
+    if (msg) *msg = std::string("persistent M >= 64 setup: ") + hipGetErrorString(e);
+    return LB_EHIP;
+  }
+  *out = &(p->sets[key] = set);
+  return LB_OK;
+}
+
+lb_status mstack_run(MStackPlan *p, const uint16_t *x0, uint16_t *y, int64_t M, void *ws, unsigned *cnt,
+                     uint16_t *xb0, uint16_t *xb1, const void *zero, const DeviceInfo &dev,
+                     hipStream_t st, std::string *msg) {
+  if (!p->broken && *(volatile unsigned *)p->herr != 0u) {
+    p->broken = true;
+    if (msg) *msg = "persistent M >= 64 stack: an earlier launch gave up a device-side wait (its output "
+                    "is undefined); this call did not run, the next one resets";
+    return LB_ETIMEOUT;
+  }
+  if (p->broken) {
+    if (hipDeviceSynchronize() != hipSuccess || hipMemset(p->ctrl, 0, 64) != hipSuccess ||
+        hipMemset(p->done, 0, sizeof(unsigned) * 2 * p->units.size() * (kMfmaRows / 32) * kDoneStride) !=
+            hipSuccess ||
+        hipMemset(cnt, 0, sizeof(unsigned) * mstack_cnt_entries(p)) != hipSuccess)
+      return LB_EHIP;
+    *(volatile unsigned *)p->herr = 0u;
+    p->broken = false;
+  }
+  if (((uintptr_t)x0 & 15) || ((uintptr_t)y & 15)) {
+    if (msg) *msg = "x0 and y must be 16-byte aligned";
+    return LB_EINVAL;
+  }
+  const int U = (int)p->units.size();
+  for (int64_t mb = 0; mb < M; mb += kMfmaRows) {
+    const int64_t Mc = std::min<int64_t>(kMfmaRows, M - mb);
+    MStackArgSet *set = nullptr;
+    lb_status s = mstack_args(p, Mc, ws, cnt, xb0, xb1, zero, dev, st, &set, msg);
+    if (s != LB_OK) return s;
+    MStackArgs A;
+    A.s1 = set->s1;
+    A.s2 = set->s2;
+    A.step_off = set->steps;
+    A.step_tiles = set->steps + 2 * U + 1;
+    A.nsteps = 2 * U;
+    A.nrb = (int)((Mc + 31) / 32);
+    A.x0 = x0 + mb * p->a0;
+    A.y = y + mb * p->b_last;
+    A.ctrl = p->ctrl;
+    A.done = p->done;
+    A.err = p->ctrl + 2;
+    A.herr = p->herr_dev;
+    hipLaunchKernelGGL(k_mstack, dim3(p->G), dim3(kThreads1), set->lds, st, A);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      if (msg) *msg = std::string("persistent M >= 64 launch: ") + hipGetErrorString(e);
+      return LB_EHIP;
+    }
+  }
+  return LB_OK;
 }
 
 }  // namespace lbi

@@ -284,7 +284,7 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               one-launch sweep runs once per row (faster at these M; each
  *               row's output is exactly its M = 1 output);
  *   M >= 64     two matrix-core launches per unit, the combine fused into
- *               the second.
+ *               the second (see mode 3 for the one-launch alternative).
  * x0, y and trace must be 16-byte aligned; y must not overlap x0. */
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
@@ -336,7 +336,18 @@ lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
 /* Select the execution mode of lb_stack_forward: 0 = automatic (above),
  * 1 = every layer alone (as lb_forward) followed by a combine kernel per
  * unit, 2 = the one-launch sweep only (LB_EUNSUPPORTED unless M = 1 and
- * the device can hold one workgroup per compute unit). */
+ * the device can hold one workgroup per compute unit), 3 = automatic
+ * except that M >= 64 without a trace runs the whole stack in one launch
+ * per 256 rows: the same matrix-core tiles as mode 0, in the same order
+ * (identical results), as work items taken by an atomic ticket, each
+ * waiting only for the previous step of its own 32-row block, so row
+ * blocks pipeline through the units and no co-residency is needed; its
+ * bounded waits report a give-up as LB_ETIMEOUT from the next call, and
+ * the first call for a row count sets up its launch arguments (allocates,
+ * synchronises; LB_ENOTREADY under capture).  Measured slower than mode 0
+ * on MI355X at M = 64 .. 512 (the tiles, not the launches, bound the
+ * time).  Mode 3 needs every width to be a multiple of 8
+ * (LB_EUNSUPPORTED otherwise). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);
 
 lb_status lb_stack_destroy(lb_stack *S);
