@@ -697,6 +697,11 @@ struct lb_stack {
   int64_t cap_M = 0;      // rows the scratch buffers hold
   void *ybuf = nullptr;  // the running unit's layer outputs (cap_M x unit_out_max)
   void *xbuf[2] = {nullptr, nullptr};  // unit input ping-pong (cap_M x max a)
+  // wave-path scratch of the stack's layers (chunk partials and latent rows
+  // of up to min(cap_M, 63) rows; the layers run one after another), so a
+  // small batch takes one launch pair per layer however large the layer
+  void *wws = nullptr;
+  size_t wws_bytes = 0;
   int64_t unit_out_max = 0;  // max over units of (layers x b)
   // scratch replaced by a larger reservation: kept until the stack is
   // destroyed, since launches captured earlier may still write it
@@ -718,6 +723,9 @@ static void stack_free_scratch(lb_stack *S) {
       (void)hipFree(p);
       p = nullptr;
     }
+  if (S->wws) (void)hipFree(S->wws);
+  S->wws = nullptr;
+  S->wws_bytes = 0;
   for (void *p : S->retired)
     if (p) (void)hipFree(p);
   S->retired.clear();
@@ -742,12 +750,26 @@ static lb_status stack_reserve(lb_stack *S, int64_t M) {
   if (hipMalloc(&yb, (size_t)cap * S->unit_out_max * 2) != hipSuccess) return undo();
   for (auto &p : xb)
     if (hipMalloc(&p, (size_t)cap * S->max_width * 2) != hipSuccess) return undo();
+  const int64_t R = std::min<int64_t>(cap, 63);
+  size_t wneed = 0;
+  for (const lb_layer *Lr : S->layers) {
+    const Layer &Ly = Lr->ly;
+    const int nch = wave_nchunk(Ly, 1, ctx_of(Lr)->info);
+    wneed = std::max(wneed, (wave_ws_floats(Ly, R, nch) + (size_t)R * Ly.L) * sizeof(float) + 512);
+  }
+  void *wb = nullptr;
+  if (wneed > S->wws_bytes && hipMalloc(&wb, wneed) != hipSuccess) return undo();
   if (S->ybuf) S->retired.push_back(S->ybuf);
   for (void *p : S->xbuf)
     if (p) S->retired.push_back(p);
   S->ybuf = yb;
   S->xbuf[0] = xb[0];
   S->xbuf[1] = xb[1];
+  if (wb) {
+    if (S->wws) S->retired.push_back(S->wws);
+    S->wws = wb;
+    S->wws_bytes = wneed;
+  }
   S->cap_M = cap;
   return LB_OK;
 }
@@ -1023,8 +1045,16 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     for (int k = 0; k < nu; ++k) {
       lb_layer *Lr = S->layers[b0 + k];
       uint16_t *o = trace ? tY[b0 + k] : (uint16_t *)S->ybuf + (size_t)k * M * Lr->ly.b;
-      lb_status fs = forward_impl(Lr, cur, o, M, st);
-      if (fs != LB_OK) return fs;
+      lb_status fs;
+      if (M > 1 && M < 64) {
+        // the wave path with the stack's scratch: all rows in one launch pair
+        std::string msg;
+        fs = forward_ws(Lr, cur, o, M, st, S->wws, S->wws_bytes, Lr->ly.cnt, 1, &msg);
+        if (fs != LB_OK) return fail(fs, "lb_stack_forward: " + msg);
+      } else {
+        fs = forward_impl(Lr, cur, o, M, st);
+        if (fs != LB_OK) return fs;
+      }
       outs.push_back(o);
     }
     uint16_t *next;

@@ -67,6 +67,20 @@ __device__ __forceinline__ float lut_word(const float *tab, uint32_t wd) {
   return acc;
 }
 
+// Sum of the totals (entry 15) of the first n tables, n a multiple of 8,
+// added in table order; the reads go out eight at a time.
+__device__ __forceinline__ float sum_totals(const float *tab, int n) {
+  float acc = 0.f;
+  for (int g0 = 0; g0 < n; g0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tab[(g0 + e) * 16 + 15];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += v[e];
+  }
+  return acc;
+}
+
 // The 32-row sign word of S_V row group r, latent column col: the two
 // 16-row tiles 2 r and 2 r + 1 of the tile layout joined.
 __device__ __forceinline__ uint32_t sv_word(const uint16_t *__restrict__ sv16, int64_t Lp, int64_t r,
@@ -93,7 +107,11 @@ static int s1_mbatch(const Layer &Ly, int G) {
 
 // grid.x = nchunk; chunk c covers row groups [c*G, min(c*G+G, R1)).
 // LDS: tab[mi][p][grp][16] (grp < 8 G), sz[mi][p].
-__global__ void __launch_bounds__(kS1Threads)
+// At most two workgroups share a CU (nchunk <= 2 x CUs, wave_nchunk), so
+// the compiler may use the registers of two waves per SIMD: with the
+// default occupancy target it reuses one register for all eight table
+// reads of a word and waits for each in turn.
+__global__ void __launch_bounds__(kS1Threads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 k_wave_s1(const uint16_t *__restrict__ sv16, const uint16_t *__restrict__ g,
           const uint16_t *__restrict__ x, int64_t a, int64_t a16, int64_t s, int64_t L, int64_t Lp, int P,
           int64_t R1, int M, int G, int MB, float *__restrict__ part) {
@@ -114,20 +132,24 @@ k_wave_s1(const uint16_t *__restrict__ sv16, const uint16_t *__restrict__ g,
       const int rem = idx - mi * P * ng;
       const int p = rem / ng, gr = rem - p * ng;
       const int64_t i0 = r0 * 32 + 4 * gr;
+      const uint16_t *gp = g + p * a16, *xp = x + (int64_t)(m0 + mi) * a;
+      // the eight loads go out together: indices past the input read its
+      // last element and the product is replaced by 0
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t i = i0 + e;
-        v[e] = i < a ? h2f(g[p * a16 + i]) * h2f(x[(int64_t)(m0 + mi) * a + i]) : 0.f;
+        const int64_t i = i0 + e < a ? i0 + e : a - 1;
+        v[e] = h2f(gp[i]) * h2f(xp[i]);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e >= a) v[e] = 0.f;
       build_table(tab + ((size_t)(mi * P + p) * G * 8 + gr) * 16, v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
     for (int idx = t; idx < mn * P; idx += kS1Threads) {
       const float *tb = tab + (size_t)idx * G * 8 * 16;
-      float acc = 0.f;
-      for (int gr = 0; gr < ng; ++gr) acc += tb[gr * 16 + 15];
-      sz[idx] = acc;
+      sz[idx] = sum_totals(tb, ng);
     }
     __syncthreads();
     // a thread per column: its words are loaded once, before the rows
@@ -244,9 +266,7 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
     if (t < mn * P) {
       const int mi = t / P, p = t - mi * P;
       const float *tb = tab + ((size_t)mi * nw + (size_t)p * Wk) * 128;
-      float acc = 0.f;
-      for (int gi = 0; gi < (int)Wk * 8; ++gi) acc += tb[gi * 16 + 15];
-      ws[mi * 2 + p] = acc;
+      ws[mi * 2 + p] = sum_totals(tb, (int)Wk * 8);
     }
     __syncthreads();
     for (int mi = 0; mi < mn; ++mi) {
@@ -467,20 +487,21 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     for (int idx = t; idx < A.P * ng; idx += kF1Threads) {
       const int p = idx / ng, gr = idx - p * ng;
       const int64_t i0 = r0 * 32 + 4 * gr;
-      float v[4];
+      const uint16_t *gp = A.g + p * A.a16;
+      float v[4];  // loads issued together, as in k_wave_s1
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t i = i0 + e;
-        v[e] = i < A.a ? h2f(A.g[p * A.a16 + i]) * h2f(A.x[i]) : 0.f;
+        const int64_t i = i0 + e < A.a ? i0 + e : A.a - 1;
+        v[e] = h2f(gp[i]) * h2f(A.x[i]);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e >= A.a) v[e] = 0.f;
       build_table(tab + ((size_t)p * A.G * 8 + gr) * 16, v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
     if (t < A.P) {
-      const float *tb = tab + (size_t)t * A.G * 8 * 16;
-      float acc = 0.f;
-      for (int gr = 0; gr < ng; ++gr) acc += tb[gr * 16 + 15];
-      sz[t] = acc;
+      sz[t] = sum_totals(tab + (size_t)t * A.G * 8 * 16, ng);
     }
     __syncthreads();
     for (int64_t col = t; col < L; col += kF1Threads) {
@@ -567,10 +588,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     }
     __syncthreads();
     if (t < A.P) {
-      const float *tb = tab + (size_t)t * A.Wk * 128;
-      float acc = 0.f;
-      for (int gi = 0; gi < (int)A.Wk * 8; ++gi) acc += tb[gi * 16 + 15];
-      wsum[t] = acc;
+      wsum[t] = sum_totals(tab + (size_t)t * A.Wk * 128, (int)A.Wk * 8);
     }
     __syncthreads();
     float acc[2] = {0.f, 0.f};
