@@ -129,6 +129,108 @@ def mall_reference(torch, nbytes: int, reps: int = 50) -> dict:
             "reps": reps}
 
 
+def _time_eager(torch, fn, reps: int) -> float:
+    """ms per call of fn, events on torch's current stream after warm-up."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def dense_fp16_reference(torch, wl: dict, M: int, ours_ms: float, max_gib: float = 16.0,
+                         reps: int = 10) -> dict:
+    """The FP16 baseline of the pages' speed-up figure, on this GPU: the same
+    stack wiring with dense fp16 weights (b x a per matrix, random: timing
+    only) through torch's linear (the platform's GEMV/GEMM library).  Only the
+    first blocks that fit max_gib are built; each is distinct, and a block's
+    time is bound by streaming its weights, so their mean per-block time
+    stands for the whole stack.  Context, not a target."""
+    F = torch.nn.functional
+    per = wl["per_block"]
+    ub = wl["units"][:len(wl["units"]) // wl["blocks"]]
+    blk_bytes = sum(2 * sp["a"] * sp["b"] for sp in wl["layers"][:per])
+    nb = max(1, min(wl["blocks"], int(max_gib * (1 << 30)) // blk_bytes))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl["seed"])
+    W = [torch.empty((sp["b"], sp["a"]), dtype=torch.float16, device="cuda").normal_(
+        0.0, sp["a"] ** -0.5, generator=gen) for sp in wl["layers"][:per * nb]]
+    x = torch.randn((M, wl["layers"][0]["a"]), dtype=torch.float16, device="cuda", generator=gen)
+    kap = lb_synth.kappa(2 if wl["layers"][0]["residual"] else 1)
+
+    def fwd():
+        h, li = x, 0
+        for _ in range(nb):
+            for n in ub:
+                acc = F.linear(h, W[li])
+                for k in range(1, n):
+                    acc = acc + F.linear(h, W[li + k])
+                li += n
+                h = acc * (kap / math.sqrt(n))
+        return h
+
+    ms = _time_eager(torch, fwd, reps)
+    del W
+    torch.cuda.empty_cache()
+    per_block = ms / nb
+    ours_block = ours_ms / wl["blocks"]
+    return {"what": "same wiring, dense fp16 weights, torch.nn.functional.linear; random weights, timing only",
+            "blocks_timed": nb, "us_per_block": round(per_block * 1e3, 2),
+            "weight_GBs": round(blk_bytes / (per_block * 1e-3) / 1e9, 1),
+            "littlebit_us_per_block": round(ours_block * 1e3, 3),
+            "speedup_of_littlebit": round(per_block / ours_block, 2)}
+
+
+def factored_library_reference(torch, wl: dict, M: int, ours_ms: float, reps: int = 5) -> dict:
+    """The LittleBit contractions of the matrix-core path with their operands
+    materialised in fp16 and run through torch.matmul (the platform's GEMM
+    library): per unit T = x . B1 (the unit's +-g l columns side by side),
+    per layer y = T[:, its columns] . B2 (its +-h rows of both paths stacked),
+    the unit's outputs summed and scaled into the next input.  Random operands,
+    timing only.  Context for the bit-expanding kernels, not a target."""
+    ub = wl["units"][:len(wl["units"]) // wl["blocks"]]
+    P = 2 if wl["layers"][0]["residual"] else 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl["seed"])
+
+    def rnd(r, c):
+        return torch.empty((r, c), dtype=torch.float16, device="cuda").normal_(0.0, r ** -0.5, generator=gen)
+
+    ops, li = [], 0
+    for _ in range(wl["blocks"]):
+        for n in ub:
+            lay = wl["layers"][li:li + n]
+            li += n
+            ks = [P * sp["s"] for sp in lay]
+            ops.append((rnd(lay[0]["a"], sum(ks)), [rnd(k, sp["b"]) for k, sp in zip(ks, lay)], ks))
+    x = torch.randn((M, wl["layers"][0]["a"]), dtype=torch.float16, device="cuda", generator=gen)
+    kap = lb_synth.kappa(P)
+
+    def fwd():
+        h = x
+        for B1, B2, ks in ops:
+            T = torch.matmul(h, B1)
+            c0, acc = 0, None
+            for B, k in zip(B2, ks):
+                y = torch.matmul(T[:, c0:c0 + k], B)
+                acc = y if acc is None else acc + y
+                c0 += k
+            h = acc * (kap / math.sqrt(len(ks)))
+        return h
+
+    ms = _time_eager(torch, fwd, reps)
+    del ops
+    torch.cuda.empty_cache()
+    return {"what": "same contractions, operands materialised in fp16, torch.matmul; random operands, timing only",
+            "ms_per_step": round(ms, 4), "littlebit_ms_per_step": round(ours_ms, 4),
+            "speedup_of_littlebit": round(ms / ours_ms, 2)}
+
+
 def copy_probe(torch, mib: int):
     """An elementwise kernel of known size (reads and writes MIB MiB each;
     calibrates the HBM byte counters)."""
@@ -297,6 +399,8 @@ def main():
                     help="extra workload measured in the same run ('' to skip)")
     ap.add_argument("--no-init", action="store_true",
                     help="skip timing the initialisation from real factors")
+    ap.add_argument("--no-fp16-reference", action="store_true",
+                    help="skip the dense fp16 / library references (torch on random weights)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -402,6 +506,9 @@ def main():
     }
     if "cpu" in r:
         out["cpu_baseline"] = r["cpu"]
+    if not args.no_fp16_reference:
+        print("[bench] timing the dense fp16 reference", file=sys.stderr, flush=True)
+        out["dense_fp16_reference"] = dense_fp16_reference(torch, wl, M, ms)
     if batch1 and r["bytes"] <= MALL_BYTES // 2:
         # a working set that fits the MALL: also set against a measured MALL read rate
         ref = mall_reference(torch, r["bytes"])
@@ -417,6 +524,11 @@ def main():
                             "GB/s": round(s2["bytes"] / (ms2 * 1e-3) / 1e9, 2),
                             "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1),
                             "validated": s2["validated"]}
+        if not args.no_fp16_reference:
+            print("[bench] timing the fp16 references of the secondary workload", file=sys.stderr, flush=True)
+            out["secondary"]["dense_fp16_reference"] = dense_fp16_reference(torch, s2["wl"], s2["M"], ms2)
+            out["secondary"]["factored_library_reference"] = factored_library_reference(
+                torch, s2["wl"], s2["M"], ms2)
     if not args.no_init:
         print("[bench] timing initialisation from real factors", file=sys.stderr, flush=True)
         out["init"] = measure_init(torch, lbm, with_cpu=not args.no_cpu_baseline)
