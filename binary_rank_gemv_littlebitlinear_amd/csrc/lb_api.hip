@@ -177,7 +177,7 @@ extern "C" lb_status lb_create(int64_t a, int64_t b, int64_t s, int residual, lb
   if (e == hipSuccess) e = hipMemset(Ly.cnt, 0, ncnt * sizeof(unsigned));
   {
     Forward1Plan pl;
-    if (e == hipSuccess && forward1_plan(Ly, dc->info, &pl)) {
+    if (e == hipSuccess && forward1_plan(Ly, &pl)) {
       L->f1plan = new (std::nothrow) Forward1Plan(pl);
       if (!L->f1plan) e = hipErrorOutOfMemory;
       if (e == hipSuccess) e = hipMalloc(&Ly.f1state, pl.state_bytes);

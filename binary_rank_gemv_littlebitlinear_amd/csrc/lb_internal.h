@@ -77,7 +77,7 @@ struct Layer {
 
 struct MfmaPlan;
 struct Forward1Plan {
-  int G = 0, N1 = 0, NR = 0, N2 = 0, wpl = 0;
+  int G = 0, N1 = 0, N2 = 0, wpl = 0;
   size_t lds = 0, state_bytes = 0;
 };
 
@@ -105,11 +105,12 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
                               hipStream_t st);
 
-// One launch for M = 1 (first product, reduction, second product by
-// workgroup role; see lb_wave.hip).  state: state_bytes of device memory,
+// One launch for M = 1 on small layers (a <= 4096 input rows, at most 256
+// latent columns: first product, reduction and second product by workgroup
+// role; see lb_wave.hip).  state: state_bytes of device memory,
 // zero before the first launch, owned by the layer (launches on it must be
 // stream-ordered); herr: a host-mapped word set when a wait gives up.
-bool forward1_plan(const Layer &Ly, const DeviceInfo &dev, Forward1Plan *pl);
+bool forward1_plan(const Layer &Ly, Forward1Plan *pl);
 hipError_t launch_forward1(const Layer &Ly, const Forward1Plan &pl, void *state, unsigned *herr,
                            const uint16_t *x, uint16_t *y, hipStream_t st);
 

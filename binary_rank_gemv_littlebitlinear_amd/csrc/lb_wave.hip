@@ -398,17 +398,20 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
 }
 
 // --------------------------------------------------------- one launch, M = 1
-// The three steps above in one launch for a single row.  Workgroups take
-// roles by ticket (an atomic counter taken as each workgroup starts):
-//   [0, N1)            first product of input chunk c (as k_wave_s1), the
-//                      chunk partial of every latent column stored tagged;
-//   [N1, N1 + NR)      reducer of 16 latent columns (as k_wave_reduce): waits
-//                      for the N1 partials, stores w = l * t tagged;
-//   [N1 + NR, .. + N2) 64 output rows (as k_wave_s2): waits for all of w.
-// Small layers (at most 16 chunks and 256 latent columns) have no reducers:
-// each output block sums the chunk partials itself, a thread per column, in
-// the same order (16 chunk ranges, then a fixed pairwise tree), one exchange
-// fewer on the way.
+// The three steps above in one launch for a single row of a small layer
+// (at most 16 input chunks and 256 latent columns; the 4096^2 projections).
+// Workgroups take roles by ticket (an atomic counter taken as each
+// workgroup starts):
+//   [0, N1)        first product of input chunk c (as k_wave_s1), the chunk
+//                  partial of every latent column stored tagged;
+//   [N1, N1 + N2)  64 output rows (as k_wave_s2): each sums the N1 <= 16
+//                  partials of every column itself, a thread per column, in
+//                  the reduction's order (16 chunk ranges, then a fixed
+//                  pairwise tree), applies l and goes on as k_wave_s2.
+// Larger layers take the three launches: with hundreds of workgroups in
+// one launch the waiting output blocks hold CU slots that the roles they
+// wait for need (some start tens of us late), and the separate launches
+// are faster (17 against 27 us for 8192 -> 28672, s = 302).
 // A role waits only for lower tickets, held by workgroups that have already
 // started, so the launch completes however many workgroups are resident (no
 // co-residency needed; another stream's kernels can share the device).
@@ -422,17 +425,15 @@ struct Forward1Args {
   const uint16_t *g, *h, *l, *x;
   uint16_t *y;
   int64_t a, a16, b, b16, s, s8, L, Lp, R1, Wk;
-  int P, G, N1, NR, N2;
+  int P, G, N1, N2;
   unsigned *ctrl;  // [0] next ticket, [1] finished workgroups, [2] generation of the last launch
-  uint64_t *w;     // [L] tagged latent
   uint64_t *part;  // [N1][L] tagged chunk partials
   unsigned *herr;  // host-mapped: set when a wait gives up
 };
 
 constexpr int kF1Threads = 256;
 constexpr long kF1Spin = 1L << 24;
-constexpr int kF1MaxRange = 32;    // chunk partials one reducer thread sums (N1 <= 512)
-constexpr int kF1MaxWCols = 3072;  // latent columns L = P s the output blocks wait for
+constexpr int kF1MaxChunks = 16;  // first-product chunks (one partial each per column)
 
 // Up to N words at p(k), k < n, polled together (every pending word read in
 // each round), values into v[k].
@@ -511,38 +512,13 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
       for (int r = 0; r < nr; ++r) acc += lut_word(tb + r * 8 * 16, sv_word(A.sv16, A.Lp, r0 + r, col));
       f1_put(&A.part[(size_t)c * L + col], 2.f * acc - sz[p], gen);
     }
-  } else if (tk < A.N1 + A.NR) {
-    // 16 columns; thread group grp sums chunk range grp in order, then a
-    // fixed pairwise tree over the 16 ranges
-    __shared__ float red[16][16];
-    const int cl = t & 15, grp = t >> 4;
-    const int64_t col = (int64_t)(tk - A.N1) * 16 + cl;
-    const int q = (A.N1 + 15) / 16;  // <= kF1MaxRange (checked by the plan)
-    const int c0 = grp * q, c1 = min(c0 + q, A.N1);
-    float acc = 0.f;
-    if (col < L) {
-      float v[kF1MaxRange];
-      f1_wait_n([&](int k) { return &A.part[(size_t)(c0 + k) * L + col]; }, c1 - c0, gen, v, A.herr);
-#pragma unroll
-      for (int k = 0; k < kF1MaxRange; ++k) acc += v[k];
-    }
-    red[grp][cl] = acc;
-    __syncthreads();
-    for (int o = 8; o >= 1; o >>= 1) {
-      if (grp < o) red[grp][cl] += red[grp + o][cl];
-      __syncthreads();
-    }
-    if (grp == 0 && col < L) {
-      const int64_t p = (uint32_t)col / (uint32_t)A.s;
-      f1_put(&A.w[col], h2f(A.l[p * A.s8 + (col - p * A.s)]) * red[0][cl], gen);
-    }
   } else {
     // output rows [64 j, 64 j + 64): four lanes per row split its words
     const int part = t & (kS2Lanes - 1), nw = A.P * (int)A.Wk;
     float *tab = smem;                         // [nw][8][16]
     float *wsum = smem + (size_t)nw * 128;     // [2]
     float *wl = wsum + 2;                      // [L]
-    const int64_t j = (int64_t)(tk - A.N1 - A.NR) * kS2Rows + (t >> 2);
+    const int64_t j = (int64_t)(tk - A.N1) * kS2Rows + (t >> 2);
     const int64_t jc = j < A.b ? j : A.b - 1;
     uint32_t wd[WPL];
 #pragma unroll
@@ -553,27 +529,17 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     float hv[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) hv[p] = p < A.P ? h2f(A.h[p * A.b16 + jc]) : 0.f;
-    if (A.NR == 0) {
-      // no reducers: thread t sums column t over the N1 <= 16 chunks as
-      // ranges of one chunk and the pairwise tree, then applies l
-      if (t < L) {
-        float v[16];
-        f1_wait_n([&](int k) { return &A.part[(size_t)k * L + t]; }, A.N1, gen, v, A.herr);
+    // thread t sums column t over the N1 <= 16 chunks as ranges of one
+    // chunk and the pairwise tree, then applies l
+    if (t < L) {
+      float v[kF1MaxChunks];
+      f1_wait_n([&](int k) { return &A.part[(size_t)k * L + t]; }, A.N1, gen, v, A.herr);
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1)
+      for (int o = kF1MaxChunks / 2; o >= 1; o >>= 1)
 #pragma unroll
-          for (int g = 0; g < o; ++g) v[g] += v[g + o];
-        const int p = (int)((uint32_t)t / (uint32_t)A.s);
-        wl[t] = h2f(A.l[p * A.s8 + (t - p * A.s)]) * v[0];
-      }
-    } else {
-      // L <= kF1MaxWCols (checked by the plan): every thread's words together
-      float v[kF1MaxWCols / kF1Threads];
-      const int n = (int)((L - t + kF1Threads - 1) / kF1Threads);
-      f1_wait_n([&](int k) { return &A.w[t + (int64_t)k * kF1Threads]; }, max(n, 0), gen, v, A.herr);
-#pragma unroll
-      for (int k = 0; k < kF1MaxWCols / kF1Threads; ++k)
-        if (k < n) wl[t + k * kF1Threads] = v[k];
+        for (int g = 0; g < o; ++g) v[g] += v[g + o];
+      const int p = (int)((uint32_t)t / (uint32_t)A.s);
+      wl[t] = h2f(A.l[p * A.s8 + (t - p * A.s)]) * v[0];
     }
     __syncthreads();
     for (int gi = t; gi < nw * 8; gi += kF1Threads) {
@@ -614,7 +580,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
   // the last workgroup to finish resets the ticket and publishes the generation
   __syncthreads();
   if (t == 0) {
-    const unsigned total = (unsigned)(A.N1 + A.NR + A.N2);
+    const unsigned total = (unsigned)(A.N1 + A.N2);
     if (atomicAdd(&A.ctrl[1], 1u) == total - 1u) {
       __hip_atomic_store(&A.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&A.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -624,25 +590,21 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
 }
 
 // Sizes of the one-launch forward, or false when the layer is outside it
-// (second-product tables or first-product tables beyond the LDS it takes).
-bool forward1_plan(const Layer &Ly, const DeviceInfo &dev, Forward1Plan *pl) {
+// (more than 16 chunks or 256 latent columns, or tables beyond its LDS).
+bool forward1_plan(const Layer &Ly, Forward1Plan *pl) {
   const int nw = Ly.P * (int)Ly.Wk;
-  if (nw > kS2MaxWords || Ly.L > kF1MaxWCols) return false;
-  // small layers: at most 16 chunks (of at most 8 row groups), no reducers
-  const bool direct = Ly.L <= kF1Threads && (Ly.R1 + 15) / 16 <= 8;
-  const int nch = direct ? (int)std::min<int64_t>(16, Ly.R1) : wave_nchunk(Ly, 1, dev);
+  // small layers only: at most 16 chunks of at most 8 row groups, L <= 256
+  if (nw > kS2MaxWords || Ly.L > kF1Threads || (Ly.R1 + kF1MaxChunks - 1) / kF1MaxChunks > 8) return false;
+  const int nch = (int)std::min<int64_t>(kF1MaxChunks, Ly.R1);
   const int G = (int)((Ly.R1 + nch - 1) / nch);
-  if (Ly.P * G * 8 * 16 > kS1TabFloats) return false;
   pl->G = G;
   pl->N1 = (int)((Ly.R1 + G - 1) / G);
-  pl->NR = direct ? 0 : (int)((Ly.L + 15) / 16);
-  if ((pl->N1 + 15) / 16 > kF1MaxRange) return false;
   pl->N2 = (int)((Ly.b + kS2Rows - 1) / kS2Rows);
   pl->wpl = (nw + kS2Lanes - 1) / kS2Lanes;
   const size_t l1 = ((size_t)Ly.P * G * 8 * 16 + Ly.P + 16) * sizeof(float);
   const size_t l2 = ((size_t)nw * 128 + 2 + Ly.L + 16) * sizeof(float);
   pl->lds = std::max(l1, l2);
-  pl->state_bytes = 256 + ((size_t)Ly.L * 8 + 255) / 256 * 256 + (size_t)pl->N1 * Ly.L * 8;
+  pl->state_bytes = 256 + (size_t)pl->N1 * Ly.L * 8;
   return pl->lds <= 64 * 1024;
 }
 
@@ -652,13 +614,12 @@ hipError_t launch_forward1(const Layer &Ly, const Forward1Plan &pl, void *state,
   A.sv16 = Ly.sv16; A.su2t = Ly.su2t; A.g = Ly.g; A.h = Ly.h; A.l = Ly.l; A.x = x; A.y = y;
   A.a = Ly.a; A.a16 = Ly.a16; A.b = Ly.b; A.b16 = Ly.b16; A.s = Ly.s; A.s8 = Ly.s8; A.L = Ly.L; A.Lp = Ly.Lp;
   A.R1 = Ly.R1; A.Wk = Ly.Wk; A.P = Ly.P;
-  A.G = pl.G; A.N1 = pl.N1; A.NR = pl.NR; A.N2 = pl.N2;
+  A.G = pl.G; A.N1 = pl.N1; A.N2 = pl.N2;
   unsigned char *base = static_cast<unsigned char *>(state);
   A.ctrl = reinterpret_cast<unsigned *>(base);
-  A.w = reinterpret_cast<uint64_t *>(base + 256);
-  A.part = reinterpret_cast<uint64_t *>(base + 256 + ((size_t)Ly.L * 8 + 255) / 256 * 256);
+  A.part = reinterpret_cast<uint64_t *>(base + 256);
   A.herr = herr;
-  const dim3 grid((unsigned)(pl.N1 + pl.NR + pl.N2));
+  const dim3 grid((unsigned)(pl.N1 + pl.N2));
 #define LB_F1(WPLV) hipLaunchKernelGGL(k_forward1<WPLV>, grid, dim3(kF1Threads), pl.lds, st, A)
   if (pl.wpl <= 2) LB_F1(2);
   else if (pl.wpl <= 4) LB_F1(4);

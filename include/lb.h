@@ -108,11 +108,13 @@ lb_status lb_set_scales(lb_layer *L, int path, const uint16_t *h, const uint16_t
 
 /* y[M x b] = layer(x[M x a]); x, y are device fp16.  M = 0 is a no-op.
  * M < 64 runs the wave-level binary GEMV path (sign-flip identity on
- * packed bits, fp32 throughout): one launch for M = 1 (workgroups take the
- * first product, the reduction over input chunks and the second product by
- * an atomic ticket, each waiting only on workgroups that started before it,
- * so it needs no co-residency and may share the device with other
- * streams), three launches otherwise; M >= 64 runs the fp16 matrix-core
+ * packed bits, fp32 throughout): one launch for M = 1 on small layers
+ * (a <= 4096 and P s <= 256, e.g. the 4096^2 projections at 0.1 bits per
+ * weight; workgroups take the first product, the reduction over input
+ * chunks and the second product by an atomic ticket, each waiting only on
+ * workgroups that started before it, so it needs no co-residency and may
+ * share the device with other streams), three launches otherwise (faster
+ * for larger layers); M >= 64 runs the fp16 matrix-core
  * path (two launches: the first product with split K, then the second), in
  * which the latent vector t is rounded once to fp16 before the second
  * product; the +-g and +-l operands are exact.  The first call with
@@ -128,7 +130,8 @@ lb_status lb_forward(const lb_layer *L, const void *x, void *y, int64_t M, void 
 /* lb_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * for M >= 2 the same kernels and the same result as lb_forward, bit for
- * bit (for M = 1 the wave path's three launches, where lb_forward takes one;
+ * bit (for M = 1 on a small layer the wave path's three launches, where
+ * lb_forward takes one;
  * the two agree at the parity bar), but the scratch they need lives in one fixed 32 MB device array of the library
  * (16 KB of split-K tile counters plus 32 MB - 16 KB of workspace), held on
  * each device the library runs on until the process ends, instead of the

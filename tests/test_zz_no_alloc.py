@@ -2,8 +2,8 @@
 fixed device array (for callers that cannot allocate), through the C ABI.
 
 For M >= 2 it runs the same kernels as lb_forward, so on the same input
-its output is the same bit for bit; for one row lb_forward takes its
-one-launch kernel (different chunking of the first product) while this
+its output is the same bit for bit; for one row of a small layer (a <=
+4096, P s <= 256) lb_forward takes its one-launch kernel (different chunking of the first product) while this
 entry point keeps the three-launch wave path, so the two agree at the
 parity bar.  Both always meet the oracle's bar (layer definition: Samsung
 LittleBit news page, aifrontier.co.jp, Sec. 2).  Each case makes
