@@ -539,7 +539,7 @@ lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int
       float *part = reinterpret_cast<float *>(ws);
       float *w = part + wave_ws_floats(Ly, Mc, nch);
       hipError_t e = launch_wave_stage1(Ly, x + m0 * Ly.a, w, Mc, nch, part, st);
-      if (e == hipSuccess) e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, st);
+      if (e == hipSuccess) e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, dc->info, st);
       if (e != hipSuccess) {
         if (msg) *msg = std::string("wave path: ") + hipGetErrorString(e);
         return LB_EHIP;
@@ -647,7 +647,7 @@ extern "C" lb_status lb_forward_stage2(const lb_layer *L, const float *w, void *
   for (int64_t m0 = 0; m0 < M; m0 += 63) {
     const int64_t Mc = (M - m0) < 63 ? (M - m0) : 63;
     hipError_t e = launch_wave_stage2(Ly, w + m0 * Ly.L, (uint16_t *)y + m0 * Ly.b, Mc,
-                                      (hipStream_t)stream);
+                                      ctx_of(L)->info, (hipStream_t)stream);
     if (e != hipSuccess) return fail(LB_EHIP, std::string("stage 2: ") + hipGetErrorString(e));
   }
   return LB_OK;

@@ -103,7 +103,7 @@ int wave_nchunk(const Layer &Ly, int64_t M, const DeviceInfo &dev);
 hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, int64_t M,
                               int nchunk, float *ws, hipStream_t st);
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
-                              hipStream_t st);
+                              const DeviceInfo &dev, hipStream_t st);
 
 // One launch for M = 1 on small layers (a <= 4096 input rows, at most 256
 // latent columns: first product, reduction and second product by workgroup

@@ -27,6 +27,7 @@
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "lb_internal.h"
 
@@ -205,29 +206,28 @@ constexpr int kS2Threads = 256;
 constexpr int kS2Lanes = 4;                        // lanes per output row
 constexpr int kS2Rows = kS2Threads / kS2Lanes;     // output rows per workgroup
 constexpr int kS2MaxWords = 96;                    // P * Wk with tables (48 KB per row m)
-constexpr int kS2TabFloats = 12288;                // 48 KB of tables per batch of rows m
-constexpr int kS2MaxBatch = 16;
+constexpr int kS2TabFloats = 12288;                // 48 KB: the least LDS a workgroup is given
+constexpr int kS2MaxBatch = 32;
+constexpr int kS2LdsCU = 160 * 1024;               // LDS of one CU
+constexpr int kS2LdsMax = 150 * 1024;              // the most one workgroup takes
 
-// Rows m whose tables (and w rows) share one build.
-static int s2_mbatch(int nw, int64_t L) {
-  const int64_t mb = kS2TabFloats / ((int64_t)nw * 128 + L);
-  return mb < 1 ? 1 : (mb > kS2MaxBatch ? kS2MaxBatch : (int)mb);
-}
-
-// LDS: tab[mi][p*Wk + q][8][16] for a batch of MB rows, ws[mi][P], and the
-// batch's w rows wl[mi][L] (one coalesced copy, so the table build reads LDS).
+// LDS: tab[mi][p*Wk + q][8][16] for a batch of MB rows, ws[mi][P], and w
+// rows wl[.][L]: every row's, copied once at the start (wall), or the
+// batch's, copied per batch; the copies are coalesced, so the table build
+// reads LDS.  Each batch then costs a table build and three barriers, so
+// the launcher gives a workgroup as much LDS as its CU can spare.
 // WPL: words per lane (>= ceil(P * Wk / 4)).
 template <int WPL>
 __global__ void __launch_bounds__(kS2Threads)
 k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
           const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
-          int64_t Wk, int M, int MB, uint16_t *__restrict__ y) {
+          int64_t Wk, int M, int MB, int wall, uint16_t *__restrict__ y) {
   extern __shared__ float smem[];
   const int t = threadIdx.x, part = t & (kS2Lanes - 1);
   const int nw = P * (int)Wk;
   float *tab = smem;                               // [MB][nw][8][16]
   float *ws = smem + (size_t)MB * nw * 128;        // [MB][2]
-  float *wl = ws + (size_t)MB * 2;                 // [MB][L]
+  float *wl = ws + (size_t)MB * 2;                 // [wall ? M : MB][L]
   const int64_t j = (int64_t)blockIdx.x * kS2Rows + (t >> 2);
   const int64_t jc = j < b ? j : b - 1;
   // this lane's words (the same for every row m): idx = part + 4 v
@@ -240,22 +240,28 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
   float hv[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) hv[p] = p < P ? h2f(h[p * b16 + jc]) : 0.f;
+  if (wall) {
+    const int64_t n = (int64_t)M * L;
+#pragma unroll 4
+    for (int64_t i = t; i < n; i += kS2Threads) wl[i] = w[i];
+  }
   for (int m0 = 0; m0 < M; m0 += MB) {
     const int mn = (M - m0) < MB ? (M - m0) : MB;
-    __syncthreads();  // the previous batch's lookups are done
-    {
+    __syncthreads();  // the previous batch's lookups are done (and the copy of every row landed)
+    if (!wall) {
       const float *src = w + (int64_t)m0 * L;
       const int64_t n = (int64_t)mn * L;
 #pragma unroll 4
       for (int64_t i = t; i < n; i += kS2Threads) wl[i] = src[i];
+      __syncthreads();
     }
-    __syncthreads();
+    const float *wb = wl + (wall ? (int64_t)m0 * L : 0);  // the batch's first row
     for (int gi = t; gi < mn * nw * 8; gi += kS2Threads) {
       const int mi = gi / (nw * 8), rem = gi - mi * nw * 8;
       const int idx = rem >> 3, gg = rem & 7;
       const int p = idx / (int)Wk, q = idx - p * (int)Wk;
       const int64_t k0 = (int64_t)q * 32 + 4 * gg;
-      const float *wm = wl + (int64_t)mi * L + p * s;
+      const float *wm = wb + (int64_t)mi * L + p * s;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (k0 + e < s) ? wm[k0 + e] : 0.f;
@@ -369,18 +375,60 @@ hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, 
   return hipGetLastError();
 }
 
+// Stage-2 batching: the LDS a workgroup may take (its CU's share when the
+// grid needs several workgroups per CU at once), then rows per batch, with
+// every row's w copied once when that costs no extra batch.
+static void s2_shape(int nw, int64_t L, int64_t M, int64_t grid, int cus, int *MB, int *wall,
+                     size_t *lds) {
+  const int64_t per_cu = (grid + cus - 1) / cus;
+  const int64_t budget = std::max<int64_t>(kS2TabFloats * 4 + 2048,
+                                           std::min<int64_t>(kS2LdsMax, kS2LdsCU / per_cu - 2048));
+  const int64_t fl = budget / 4, tab = (int64_t)nw * 128 + 2;
+  const int64_t cap = std::min<int64_t>(M, kS2MaxBatch);
+  const int64_t mb_b = std::max<int64_t>(1, std::min<int64_t>(cap, fl / (tab + L)));  // per-batch copies
+  const int64_t mb_a = std::min<int64_t>(cap, (fl - M * L) / tab);                   // every row once
+  if (mb_a >= 1 && (M + mb_a - 1) / mb_a <= (M + mb_b - 1) / mb_b) {
+    *MB = (int)mb_a;
+    *wall = 1;
+    *lds = ((size_t)mb_a * tab + (size_t)M * L) * sizeof(float);
+  } else {
+    *MB = (int)mb_b;
+    *wall = 0;
+    *lds = ((size_t)mb_b * (tab + L)) * sizeof(float);
+  }
+}
+
+// Stage-2 workgroups may take more than 64 KB of LDS: allowed once per
+// device for every instance.
+static hipError_t s2_lds_attr(int device) {
+  static std::atomic<uint64_t> done{0};
+  const uint64_t bit = device >= 0 && device < 64 ? (1ull << device) : 0;
+  if (bit && (done.load() & bit)) return hipSuccess;
+  const void *k[5] = {(const void *)k_wave_s2<2>, (const void *)k_wave_s2<4>, (const void *)k_wave_s2<8>,
+                      (const void *)k_wave_s2<12>, (const void *)k_wave_s2<24>};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 5 && e == hipSuccess; ++i)
+    e = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, kS2LdsMax);
+  if (e == hipSuccess && bit) done.fetch_or(bit);
+  return e;
+}
+
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
-                              hipStream_t st) {
+                              const DeviceInfo &dev, hipStream_t st) {
   const int nw = (int)(Ly.P * Ly.Wk);
   if (nw <= kS2MaxWords) {
-    const int MB = (int)std::min<int64_t>(M, s2_mbatch(nw, Ly.L));
-    const size_t lds = ((size_t)MB * nw * 128 + (size_t)MB * 2 + (size_t)MB * Ly.L) * sizeof(float);
-    if (lds > 64 * 1024) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((Ly.b + kS2Rows - 1) / kS2Rows));
+    hipError_t ea = s2_lds_attr(dev.device);
+    if (ea != hipSuccess) return ea;
+    const int64_t nblk = (Ly.b + kS2Rows - 1) / kS2Rows;
+    int MB = 1, wall = 0;
+    size_t lds = 0;
+    s2_shape(nw, Ly.L, M, nblk, dev.cu_count > 0 ? dev.cu_count : 256, &MB, &wall, &lds);
+    if (lds > (size_t)kS2LdsMax) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nblk);
     const int wpl = (nw + kS2Lanes - 1) / kS2Lanes;
 #define LB_S2(WPLV)                                                                       \
   hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kS2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, \
-                     Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, y)
+                     Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, wall, y)
     if (wpl <= 2) LB_S2(2);
     else if (wpl <= 4) LB_S2(4);
     else if (wpl <= 8) LB_S2(8);
