@@ -129,6 +129,39 @@ def mall_reference(torch, nbytes: int, reps: int = 50) -> dict:
             "reps": reps}
 
 
+TIMELINE_PARTS = ("second-product lookups", "second-product epilogue and combine", "first-product tables",
+                  "first-product lookups", "publish + level A (XCD-local sum)", "level B (across XCDs)",
+                  "level C + next tables")
+
+
+def sweep_timeline(torch, lbm, stack, x, y, nunits: int) -> dict:
+    """Where a phase of the one-launch sweep spends its time: one sweep with
+    lb_stack_timeline's device timestamps (eight per phase and workgroup,
+    100 MHz), medians over workgroups and over the phases of each kind
+    (odd phases carry the gate/up second product and the down first product,
+    even ones the reverse)."""
+    need = lbm.lb_stack_timeline(stack.handle, None, 0)
+    buf = torch.zeros(need, dtype=torch.int64, device="cuda")
+    lbm.lb_stack_timeline(stack.handle, buf, need)
+    stack.forward(x, y)
+    torch.cuda.synchronize()
+    lbm.lb_stack_timeline(stack.handle, None, 0)
+    stack.check()
+    G = need // ((nunits + 1) * 8)
+    t = buf.cpu().numpy().reshape(G, nunits + 1, 8).astype(np.int64)
+    out = {"workgroups": int(G), "phases": nunits + 1}
+    for kind, sel in (("heavy", list(range(1, nunits, 2))), ("light", list(range(2, nunits, 2)))):
+        if not sel:
+            continue
+        parts = {n: round(float(np.median(t[:, sel, k + 1] - t[:, sel, k])) / 100.0, 3)
+                 for k, n in enumerate(TIMELINE_PARTS)}
+        period = float(np.median(np.diff(t[:, :, 0], axis=1)[:, sel])) / 100.0  # start to next start
+        out[kind + "_phase_us"] = parts
+        out[kind + "_exchange_us"] = round(sum(parts[n] for n in TIMELINE_PARTS[4:]), 3)
+        out[kind + "_period_us"] = round(period, 3)
+    return out
+
+
 def _time_eager(torch, fn, reps: int) -> float:
     """ms per call of fn, events on torch's current stream after warm-up."""
     for _ in range(3):
@@ -399,6 +432,8 @@ def main():
                     help="extra workload measured in the same run ('' to skip)")
     ap.add_argument("--no-init", action="store_true",
                     help="skip timing the initialisation from real factors")
+    ap.add_argument("--timeline", action="store_true",
+                    help="also record one batch-1 sweep's per-phase device timestamps (timeline object)")
     ap.add_argument("--no-fp16-reference", action="store_true",
                     help="skip the dense fp16 / library references (torch on random weights)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -461,6 +496,9 @@ def main():
             torch.cuda.synchronize()
             res["layer_forward_us"] = round(e0.elapsed_time(e1) / 1000 * 1e3, 3)
             del g
+        if args.timeline and M == 1 and args.mode != 1:
+            print("[bench] one sweep with device timestamps", file=sys.stderr, flush=True)
+            res["timeline"] = sweep_timeline(torch, lbm, stack, x, y, len(wl["units"]))
         if with_cpu:
             print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
             res["cpu"] = cpu_baseline(wl, M, args.cpu_budget)
@@ -506,6 +544,8 @@ def main():
     }
     if "cpu" in r:
         out["cpu_baseline"] = r["cpu"]
+    if "timeline" in r:
+        out["timeline"] = r["timeline"]
     if not args.no_fp16_reference:
         print("[bench] timing the dense fp16 reference", file=sys.stderr, flush=True)
         out["dense_fp16_reference"] = dense_fp16_reference(torch, wl, M, ms)
