@@ -187,9 +187,19 @@ __global__ void __launch_bounds__(256) k_wave_reduce(const float *__restrict__ p
   const int64_t col = live ? idx - (int64_t)m * L : 0;
   const int q = (nchunk + 15) / 16;
   const int c0 = grp * q, c1 = (c0 + q) < nchunk ? (c0 + q) : nchunk;
+  // the range's partials are loaded 16 at a time, then added in chunk order
+  // (one load waited for at a time would make each add a memory round trip)
+  constexpr int kBatch = 16;
   float acc = 0.f;
   if (live)
-    for (int c = c0; c < c1; ++c) acc += part[((int64_t)c * M + m) * L + col];
+    for (int cb = c0; cb < c1; cb += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) v[k] = cb + k < c1 ? part[((int64_t)(cb + k) * M + m) * L + col] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (cb + k < c1) acc += v[k];
+    }
   red[grp][cl] = acc;
   __syncthreads();
   for (int o = 8; o >= 1; o >>= 1) {
