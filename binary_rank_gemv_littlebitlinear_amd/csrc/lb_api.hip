@@ -860,7 +860,7 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     // and 7 for 8192 x 28672 ones, so the limit follows the mean size
     double elems = 0;
     for (const lb_layer *L : S->layers) elems += (double)L->ly.a * (double)L->ly.b;
-    S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 7 : 3;
+    S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 5 : 3;
   }
   if (st != LB_OK && st != LB_EUNSUPPORTED) {
     lb_stack_destroy(S);
