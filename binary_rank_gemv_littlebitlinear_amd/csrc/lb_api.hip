@@ -523,7 +523,7 @@ static lb_status check_io(const Layer &Ly, const void *x, const void *y, int64_t
 // matrix-core path, fits.
 lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M,
                           hipStream_t st, void *ws, size_t ws_bytes, unsigned *cnt,
-                          size_t cnt_entries, std::string *msg) {
+                          size_t cnt_entries, std::string *msg, const CombineReq *comb) {
   const Layer &Ly = L->ly;
   DevCtx *dc = ctx_of(L);
   if (M < 64) {
@@ -539,13 +539,24 @@ lb_status lbi::forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int
       float *part = reinterpret_cast<float *>(ws);
       float *w = part + wave_ws_floats(Ly, Mc, nch);
       hipError_t e = launch_wave_stage1(Ly, x + m0 * Ly.a, w, Mc, nch, part, st);
-      if (e == hipSuccess) e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, dc->info, st);
+      if (e == hipSuccess && comb) {
+        const uint16_t *cin[7];
+        for (int u = 0; u < comb->n && u < 7; ++u) cin[u] = comb->in[u] + m0 * Ly.b;
+        e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, dc->info, st, cin, comb->n, comb->c,
+                               comb->out + m0 * Ly.b);
+      } else if (e == hipSuccess) {
+        e = launch_wave_stage2(Ly, w, y + m0 * Ly.b, Mc, dc->info, st);
+      }
       if (e != hipSuccess) {
         if (msg) *msg = std::string("wave path: ") + hipGetErrorString(e);
         return LB_EHIP;
       }
     }
     return LB_OK;
+  }
+  if (comb) {
+    if (msg) *msg = "a fused combine is for the wave path only";
+    return LB_EINVAL;
   }
   if (mfma_unit_ws_bytes(L->mplan) > ws_bytes || mfma_cnt_entries(L->mplan) > cnt_entries) {
     if (msg)
@@ -1041,30 +1052,40 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
   }
   for (int u = 0; u < U; ++u) {
     const int b0 = S->unit_begin[u], nu = S->unit_size[u];
+    uint16_t *next;
+    if (u == U - 1)
+      next = (uint16_t *)y;
+    else
+      next = trace ? tX[u + 1] : (uint16_t *)S->xbuf[u & 1];
+    const float c = S->kappa / std::sqrt((float)nu);
     std::vector<const uint16_t *> outs;
+    bool combined = false;
     for (int k = 0; k < nu; ++k) {
       lb_layer *Lr = S->layers[b0 + k];
       uint16_t *o = trace ? tY[b0 + k] : (uint16_t *)S->ybuf + (size_t)k * M * Lr->ly.b;
       lb_status fs;
       if (M > 1 && M < 64) {
-        // the wave path with the stack's scratch: all rows in one launch pair
+        // the wave path with the stack's scratch: all rows in one launch
+        // pair; up to 16 rows the unit's last layer also forms the combine
+        // in its second product when its kernel can (one launch fewer; with
+        // more rows the separate combine kernel was faster)
         std::string msg;
-        fs = forward_ws(Lr, cur, o, M, st, S->wws, S->wws_bytes, Lr->ly.cnt, 1, &msg);
+        const bool fuse = k == nu - 1 && M <= 16 && wave_stage2_combines(Lr->ly);
+        const CombineReq cr{outs.data(), k, c, next};
+        fs = forward_ws(Lr, cur, o, M, st, S->wws, S->wws_bytes, Lr->ly.cnt, 1, &msg, fuse ? &cr : nullptr);
         if (fs != LB_OK) return fail(fs, "lb_stack_forward: " + msg);
+        combined = fuse;
       } else {
         fs = forward_impl(Lr, cur, o, M, st);
         if (fs != LB_OK) return fs;
       }
       outs.push_back(o);
     }
-    uint16_t *next;
-    if (u == U - 1)
-      next = (uint16_t *)y;
-    else
-      next = trace ? tX[u + 1] : (uint16_t *)S->xbuf[u & 1];
-    const int64_t elems = M * S->layers[b0]->ly.b;
-    hipError_t e = launch_combine(outs.data(), nu, S->kappa / std::sqrt((float)nu), next, elems, st);
-    if (e != hipSuccess) return fail(LB_EHIP, std::string("combine: ") + hipGetErrorString(e));
+    if (!combined) {
+      const int64_t elems = M * S->layers[b0]->ly.b;
+      hipError_t e = launch_combine(outs.data(), nu, c, next, elems, st);
+      if (e != hipSuccess) return fail(LB_EHIP, std::string("combine: ") + hipGetErrorString(e));
+    }
     cur = next;
   }
   return LB_OK;

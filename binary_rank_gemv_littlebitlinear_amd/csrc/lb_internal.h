@@ -102,8 +102,12 @@ size_t wave_ws_floats(const Layer &Ly, int64_t M, int nchunk);
 int wave_nchunk(const Layer &Ly, int64_t M, const DeviceInfo &dev);
 hipError_t launch_wave_stage1(const Layer &Ly, const uint16_t *x, float *w_out, int64_t M,
                               int nchunk, float *ws, hipStream_t st);
+// With cout: also cout = fp16(c * (cin[0] + .. + cin[ncin - 1] + y)), the
+// unit's combine (ncin <= 7), when wave_stage2_combines(Ly).
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
-                              const DeviceInfo &dev, hipStream_t st);
+                              const DeviceInfo &dev, hipStream_t st, const uint16_t *const *cin = nullptr,
+                              int ncin = 0, float c = 0.f, uint16_t *cout = nullptr);
+bool wave_stage2_combines(const Layer &Ly);
 
 // One launch for M = 1 on small layers (a <= 4096 input rows, at most 256
 // latent columns: first product, reduction and second product by workgroup
@@ -185,8 +189,16 @@ int rotate_factors_dev(const float *U, const float *V, int64_t a, int64_t b, int
 
 // The forward of one layer with caller-chosen scratch (see lb_api.hip),
 // the argument checks of lb_forward, and the thread-local error text.
+// A unit's combine for the wave path's second product (see launch_wave_stage2).
+struct CombineReq {
+  const uint16_t *const *in;  // the unit's earlier layers' outputs, M x b each
+  int n;
+  float c;
+  uint16_t *out;
+};
 lb_status forward_ws(const lb_layer *L, const uint16_t *x, uint16_t *y, int64_t M, hipStream_t st,
-                     void *ws, size_t ws_bytes, unsigned *cnt, size_t cnt_entries, std::string *msg);
+                     void *ws, size_t ws_bytes, unsigned *cnt, size_t cnt_entries, std::string *msg,
+                     const CombineReq *comb = nullptr);
 lb_status forward_checks(const lb_layer *L, const void *x, const void *y, int64_t M, const char *who);
 lb_status set_error(lb_status st, const std::string &msg);
 const void *device_zero(const lb_layer *L);

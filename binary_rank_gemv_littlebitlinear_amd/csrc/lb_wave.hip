@@ -212,6 +212,15 @@ __global__ void __launch_bounds__(256) k_wave_reduce(const float *__restrict__ p
   }
 }
 
+// The combine of a unit's outputs fused into its last layer's second
+// product (k_wave_s2 only): out = fp16(c * (sum of in[u], then this layer)).
+struct WaveCombine {
+  const uint16_t *in[7];  // the unit's earlier layers' outputs, M x b each
+  int n;
+  float c;
+  uint16_t *out;  // null: no combine
+};
+
 constexpr int kS2Threads = 256;
 constexpr int kS2Lanes = 4;                        // lanes per output row
 constexpr int kS2Rows = kS2Threads / kS2Lanes;     // output rows per workgroup
@@ -231,7 +240,7 @@ template <int WPL>
 __global__ void __launch_bounds__(kS2Threads)
 k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
           const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
-          int64_t Wk, int M, int MB, int wall, uint16_t *__restrict__ y) {
+          int64_t Wk, int M, int MB, int wall, uint16_t *__restrict__ y, WaveCombine cb) {
   extern __shared__ float smem[];
   const int t = threadIdx.x, part = t & (kS2Lanes - 1);
   const int nw = P * (int)Wk;
@@ -304,7 +313,17 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       if (part == 0 && j < b) {
         float out = 0.f;
         for (int p = 0; p < P; ++p) out += hv[p] * (2.f * acc[p] - ws[mi * 2 + p]);
-        y[(int64_t)(m0 + mi) * b + j] = f2h(out);
+        const int64_t o = (int64_t)(m0 + mi) * b + j;
+        const uint16_t yv = f2h(out);
+        y[o] = yv;
+        if (cb.out) {
+          // the unit's combine, as k_combine: the fp16 outputs of its layers
+          // summed in layer order in fp32, this layer's last, one rounding
+          float acc2 = 0.f;
+          for (int u = 0; u < cb.n; ++u) acc2 += h2f(cb.in[u][o]);
+          acc2 += h2f(yv);
+          cb.out[o] = f2h(cb.c * acc2);
+        }
       }
     }
   }
@@ -423,8 +442,11 @@ static hipError_t s2_lds_attr(int device) {
   return e;
 }
 
+bool wave_stage2_combines(const Layer &Ly) { return Ly.P * Ly.Wk <= kS2MaxWords; }
+
 hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int64_t M,
-                              const DeviceInfo &dev, hipStream_t st) {
+                              const DeviceInfo &dev, hipStream_t st, const uint16_t *const *cin,
+                              int ncin, float c, uint16_t *cout) {
   const int nw = (int)(Ly.P * Ly.Wk);
   if (nw <= kS2MaxWords) {
     hipError_t ea = s2_lds_attr(dev.device);
@@ -436,9 +458,17 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
     if (lds > (size_t)kS2LdsMax) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nblk);
     const int wpl = (nw + kS2Lanes - 1) / kS2Lanes;
+    WaveCombine cb{};
+    if (cout) {
+      if (ncin < 0 || ncin > 7) return hipErrorInvalidValue;
+      for (int u = 0; u < ncin; ++u) cb.in[u] = cin[u];
+      cb.n = ncin;
+      cb.c = c;
+      cb.out = cout;
+    }
 #define LB_S2(WPLV)                                                                       \
   hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kS2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, \
-                     Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, wall, y)
+                     Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, wall, y, cb)
     if (wpl <= 2) LB_S2(2);
     else if (wpl <= 4) LB_S2(4);
     else if (wpl <= 8) LB_S2(8);
@@ -447,6 +477,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
 #undef LB_S2
     return hipGetLastError();
   }
+  if (cout) return hipErrorInvalidValue;  // see wave_stage2_combines
   const size_t lds = ((size_t)Ly.L + 2 + 16) * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_wave_s2_bits, dim3((unsigned)((Ly.b + kS2Threads - 1) / kS2Threads)),
