@@ -68,6 +68,26 @@ __device__ __forceinline__ float lut_word(const float *tab, uint32_t wd) {
   return acc;
 }
 
+// Entries 4 h .. 4 h + 3 of build_table's table: entry k sums the v_e with
+// bit e of k set, added in index order with the first taken as is (the
+// same additions as build_table, so the same values bit for bit).
+__device__ __forceinline__ float4 table_quarter(float v0, float v1, float v2, float v3, int h) {
+  const float lo[4] = {0.f, v0, v1, v0 + v1};  // entries 0-3: the subsets of (v0, v1)
+  float o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float acc = lo[j];
+    bool any = j != 0;
+    if (h & 1) {
+      acc = any ? acc + v2 : v2;
+      any = true;
+    }
+    if (h & 2) acc = any ? acc + v3 : v3;
+    o[j] = acc;
+  }
+  return make_float4(o[0], o[1], o[2], o[3]);
+}
+
 // Sum of the totals (entry 15) of the first n tables, n a multiple of 8,
 // added in table order; the reads go out eight at a time.
 __device__ __forceinline__ float sum_totals(const float *tab, int n) {
@@ -227,6 +247,8 @@ constexpr int kS2Rows = kS2Threads / kS2Lanes;     // output rows per workgroup
 constexpr int kS2MaxWords = 96;                    // P * Wk with tables (48 KB per row m)
 constexpr int kS2TabFloats = 12288;                // 48 KB: the least LDS a workgroup is given
 constexpr int kS2MaxBatch = 32;
+constexpr int kS2WordF = 8 * 16 + 16;  // a word's 8 tables plus a pad, so neighbouring words' tables
+                                       // sit on different bank halves
 constexpr int kS2LdsCU = 160 * 1024;               // LDS of one CU
 constexpr int kS2LdsMax = 150 * 1024;              // the most one workgroup takes
 
@@ -244,8 +266,8 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
   extern __shared__ float smem[];
   const int t = threadIdx.x, part = t & (kS2Lanes - 1);
   const int nw = P * (int)Wk;
-  float *tab = smem;                               // [MB][nw][8][16]
-  float *ws = smem + (size_t)MB * nw * 128;        // [MB][2]
+  float *tab = smem;                               // [MB][nw][kS2WordF]: a word's 8 tables, padded
+  float *ws = smem + (size_t)MB * nw * kS2WordF;   // [MB][2]
   float *wl = ws + (size_t)MB * 2;                 // [wall ? M : MB][L]
   const int64_t j = (int64_t)blockIdx.x * kS2Rows + (t >> 2);
   const int64_t jc = j < b ? j : b - 1;
@@ -275,7 +297,11 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       __syncthreads();
     }
     const float *wb = wl + (wall ? (int64_t)m0 * L : 0);  // the batch's first row
-    for (int gi = t; gi < mn * nw * 8; gi += kS2Threads) {
+    // four threads per table, each storing four entries at once: a wave's
+    // stores are 1 KB contiguous (one thread per table put 64 lanes' stores
+    // 64 bytes apart, on the same banks)
+    for (int gq = t; gq < mn * nw * 8 * 4; gq += kS2Threads) {
+      const int gi = gq >> 2, hq = gq & 3;
       const int mi = gi / (nw * 8), rem = gi - mi * nw * 8;
       const int idx = rem >> 3, gg = rem & 7;
       const int p = idx / (int)Wk, q = idx - p * (int)Wk;
@@ -284,24 +310,34 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (k0 + e < s) ? wm[k0 + e] : 0.f;
-      build_table(tab + (size_t)gi * 16, v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4 *>(tab + ((size_t)mi * nw + idx) * kS2WordF + gg * 16 + 4 * hq) =
+          table_quarter(v[0], v[1], v[2], v[3], hq);
     }
     __syncthreads();
     // sum_k w_p[k] of each row: the group totals (entry 15) in order
     if (t < mn * P) {
       const int mi = t / P, p = t - mi * P;
-      const float *tb = tab + ((size_t)mi * nw + (size_t)p * Wk) * 128;
-      ws[mi * 2 + p] = sum_totals(tb, (int)Wk * 8);
+      const float *tb = tab + ((size_t)mi * nw + (size_t)p * Wk) * kS2WordF;
+      float acc = 0.f;  // one running sum over every table, in order (as sum_totals)
+      for (int q = 0; q < (int)Wk; ++q) {
+        const float *tq = tb + (size_t)q * kS2WordF;
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = tq[e * 16 + 15];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += v8[e];
+      }
+      ws[mi * 2 + p] = acc;
     }
     __syncthreads();
     for (int mi = 0; mi < mn; ++mi) {
-      const float *tb = tab + (size_t)mi * nw * 128;
+      const float *tb = tab + (size_t)mi * nw * kS2WordF;
       float acc[2] = {0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < WPL; ++v) {
         const int idx = part + kS2Lanes * v;
         if (idx < nw) {
-          const float sum = lut_word(tb + (size_t)idx * 128, wd[v]);
+          const float sum = lut_word(tb + (size_t)idx * kS2WordF, wd[v]);
           if (idx < (int)Wk) acc[0] += sum; else acc[1] += sum;
         }
       }
@@ -412,7 +448,7 @@ static void s2_shape(int nw, int64_t L, int64_t M, int64_t grid, int cus, int *M
   const int64_t per_cu = (grid + cus - 1) / cus;
   const int64_t budget = std::max<int64_t>(kS2TabFloats * 4 + 2048,
                                            std::min<int64_t>(kS2LdsMax, kS2LdsCU / per_cu - 2048));
-  const int64_t fl = budget / 4, tab = (int64_t)nw * 128 + 2;
+  const int64_t fl = budget / 4, tab = (int64_t)nw * kS2WordF + 2;
   const int64_t cap = std::min<int64_t>(M, kS2MaxBatch);
   const int64_t mb_b = std::max<int64_t>(1, std::min<int64_t>(cap, fl / (tab + L)));  // per-batch copies
   const int64_t mb_a = std::min<int64_t>(cap, (fl - M * L) / tab);                   // every row once
