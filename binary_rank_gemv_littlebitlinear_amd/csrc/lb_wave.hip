@@ -17,9 +17,9 @@
 // Reduce (k_wave_reduce): w = l * sum of the chunk partials, 16 fixed
 //   chunk ranges per column combined by a fixed pairwise tree.
 // Stage 2 (k_wave_s2): tables of w_p for a batch of rows m (as many as fit
-//   in 48 KB, so one build and three barriers serve several rows); four
-//   lanes per output row j split its words (kept in registers for every
-//   row) and are summed by a fixed shuffle tree:
+//   the LDS the workgroup's CU can spare, so one build and three barriers
+//   serve several rows); eight lanes per output row j split its words
+//   (kept in registers for every row) and are summed by a fixed shuffle tree:
 //   y[m][j] = fp16(sum_p h_p[j] (2 * sum_{bit} w_p - sum_k w_p[k])).
 //   Layers whose tables would not fit (P * ceil(s/32) > 96) use
 //   k_wave_s2_bits, one thread per row testing bits one by one.
@@ -244,6 +244,10 @@ struct WaveCombine {
 constexpr int kS2Threads = 256;
 constexpr int kS2Lanes = 4;                        // lanes per output row
 constexpr int kS2Rows = kS2Threads / kS2Lanes;     // output rows per workgroup
+// k_wave_s2 itself: 8 waves, eight lanes per output row (two waves per
+// SIMD hide each other's table-read latency; with four waves and four
+// lanes per row the kernel was 7-12% slower on the MLP stacks).
+constexpr int kW2Threads = 512, kW2Lanes = 8;
 constexpr int kS2MaxWords = 96;                    // P * Wk with tables (48 KB per row m)
 constexpr int kS2TabFloats = 12288;                // 48 KB: the least LDS a workgroup is given
 constexpr int kS2MaxBatch = 32;
@@ -259,23 +263,23 @@ constexpr int kS2LdsMax = 150 * 1024;              // the most one workgroup tak
 // the launcher gives a workgroup as much LDS as its CU can spare.
 // WPL: words per lane (>= ceil(P * Wk / 4)).
 template <int WPL>
-__global__ void __launch_bounds__(kS2Threads)
+__global__ void __launch_bounds__(kW2Threads)
 k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
           const float *__restrict__ w, int64_t b, int64_t b16, int64_t s, int64_t L, int P,
           int64_t Wk, int M, int MB, int wall, uint16_t *__restrict__ y, WaveCombine cb) {
   extern __shared__ float smem[];
-  const int t = threadIdx.x, part = t & (kS2Lanes - 1);
+  const int t = threadIdx.x, part = t & (kW2Lanes - 1);
   const int nw = P * (int)Wk;
   float *tab = smem;                               // [MB][nw][kS2WordF]: a word's 8 tables, padded
   float *ws = smem + (size_t)MB * nw * kS2WordF;   // [MB][2]
   float *wl = ws + (size_t)MB * 2;                 // [wall ? M : MB][L]
-  const int64_t j = (int64_t)blockIdx.x * kS2Rows + (t >> 2);
+  const int64_t j = (int64_t)blockIdx.x * kS2Rows + (t >> 3);
   const int64_t jc = j < b ? j : b - 1;
   // this lane's words (the same for every row m): idx = part + 4 v
   uint32_t wd[WPL];
 #pragma unroll
   for (int v = 0; v < WPL; ++v) {
-    const int idx = part + kS2Lanes * v;
+    const int idx = part + kW2Lanes * v;
     wd[v] = idx < nw ? su2t[su_index(jc, nw, idx)] : 0u;
   }
   float hv[2];
@@ -284,7 +288,7 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
   if (wall) {
     const int64_t n = (int64_t)M * L;
 #pragma unroll 4
-    for (int64_t i = t; i < n; i += kS2Threads) wl[i] = w[i];
+    for (int64_t i = t; i < n; i += kW2Threads) wl[i] = w[i];
   }
   for (int m0 = 0; m0 < M; m0 += MB) {
     const int mn = (M - m0) < MB ? (M - m0) : MB;
@@ -293,14 +297,14 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       const float *src = w + (int64_t)m0 * L;
       const int64_t n = (int64_t)mn * L;
 #pragma unroll 4
-      for (int64_t i = t; i < n; i += kS2Threads) wl[i] = src[i];
+      for (int64_t i = t; i < n; i += kW2Threads) wl[i] = src[i];
       __syncthreads();
     }
     const float *wb = wl + (wall ? (int64_t)m0 * L : 0);  // the batch's first row
     // four threads per table, each storing four entries at once: a wave's
     // stores are 1 KB contiguous (one thread per table put 64 lanes' stores
     // 64 bytes apart, on the same banks)
-    for (int gq = t; gq < mn * nw * 8 * 4; gq += kS2Threads) {
+    for (int gq = t; gq < mn * nw * 8 * 4; gq += kW2Threads) {
       const int gi = gq >> 2, hq = gq & 3;
       const int mi = gi / (nw * 8), rem = gi - mi * nw * 8;
       const int idx = rem >> 3, gg = rem & 7;
@@ -335,7 +339,7 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       float acc[2] = {0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < WPL; ++v) {
-        const int idx = part + kS2Lanes * v;
+        const int idx = part + kW2Lanes * v;
         if (idx < nw) {
           const float sum = lut_word(tb + (size_t)idx * kS2WordF, wd[v]);
           if (idx < (int)Wk) acc[0] += sum; else acc[1] += sum;
@@ -345,6 +349,7 @@ k_wave_s2(const uint32_t *__restrict__ su2t, const uint16_t *__restrict__ h,
       for (int p = 0; p < 2; ++p) {
         acc[p] += __shfl_xor(acc[p], 1, 64);
         acc[p] += __shfl_xor(acc[p], 2, 64);
+        acc[p] += __shfl_xor(acc[p], 4, 64);
       }
       if (part == 0 && j < b) {
         float out = 0.f;
@@ -493,7 +498,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
     s2_shape(nw, Ly.L, M, nblk, dev.cu_count > 0 ? dev.cu_count : 256, &MB, &wall, &lds);
     if (lds > (size_t)kS2LdsMax) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nblk);
-    const int wpl = (nw + kS2Lanes - 1) / kS2Lanes;
+    const int wpl = (nw + kW2Lanes - 1) / kW2Lanes;
     WaveCombine cb{};
     if (cout) {
       if (ncin < 0 || ncin > 7) return hipErrorInvalidValue;
@@ -503,7 +508,7 @@ hipError_t launch_wave_stage2(const Layer &Ly, const float *w, uint16_t *y, int6
       cb.out = cout;
     }
 #define LB_S2(WPLV)                                                                       \
-  hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kS2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, \
+  hipLaunchKernelGGL(k_wave_s2<WPLV>, grid, dim3(kW2Threads), lds, st, Ly.su2t, Ly.h, w, Ly.b, \
                      Ly.b16, Ly.s, Ly.L, Ly.P, Ly.Wk, (int)M, MB, wall, y, cb)
     if (wpl <= 2) LB_S2(2);
     else if (wpl <= 4) LB_S2(4);
