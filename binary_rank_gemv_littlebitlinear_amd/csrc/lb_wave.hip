@@ -11,9 +11,10 @@
 // table at a time (one group), so the reads are bank-conflict free.
 //
 // Stage 1 (k_wave_s1): one workgroup per chunk of input rows builds the
-//   tables of z = g_p * x for its rows, then each thread takes latent
-//   columns c = p*s + k: part[chunk][m][c] = 2 * sum_{bit} z - sum z over
-//   the chunk (its words read once for all rows m).
+//   tables of z = g_p * x for its rows, then each thread takes items of one
+//   latent column c = p*s + k and four rows m:
+//   part[chunk][m][c] = 2 * sum_{bit} z - sum z over the chunk (the
+//   column's words read once per item).
 // Reduce (k_wave_reduce): w = l * sum of the chunk partials, 16 fixed
 //   chunk ranges per column combined by a fixed pairwise tree.
 // Stage 2 (k_wave_s2): tables of w_p for a batch of rows m (as many as fit
@@ -115,7 +116,8 @@ __device__ __forceinline__ int64_t su_index(int64_t j, int nw, int idx) {
   return (((j >> 4) * nw + idx) << 4) + (j & 15);
 }
 
-constexpr int kS1Threads = 256;
+constexpr int kS1Threads = 512;
+constexpr int kS1RowBlock = 4;  // rows m one lookup item covers (its column's words reused)
 constexpr int kS1TabFloats = 12288;  // 48 KB of stage-1 tables per batch of rows
 
 // Rows m processed together by one stage-1 workgroup (tables of every such
@@ -128,11 +130,11 @@ static int s1_mbatch(const Layer &Ly, int G) {
 
 // grid.x = nchunk; chunk c covers row groups [c*G, min(c*G+G, R1)).
 // LDS: tab[mi][p][grp][16] (grp < 8 G), sz[mi][p].
-// At most two workgroups share a CU (nchunk <= 2 x CUs, wave_nchunk), so
-// the compiler may use the registers of two waves per SIMD: with the
-// default occupancy target it reuses one register for all eight table
-// reads of a word and waits for each in turn.
-__global__ void __launch_bounds__(kS1Threads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+// At most two workgroups of eight waves share a CU (nchunk <= 2 x CUs,
+// wave_nchunk), so the compiler may use the registers of four waves per
+// SIMD: with the default occupancy target it reused one register for all
+// eight table reads of a word and waited for each in turn.
+__global__ void __launch_bounds__(kS1Threads) __attribute__((amdgpu_waves_per_eu(1, 4)))
 k_wave_s1(const uint16_t *__restrict__ sv16, const uint16_t *__restrict__ g,
           const uint16_t *__restrict__ x, int64_t a, int64_t a16, int64_t s, int64_t L, int64_t Lp, int P,
           int64_t R1, int M, int G, int MB, float *__restrict__ part) {
@@ -173,13 +175,19 @@ k_wave_s1(const uint16_t *__restrict__ sv16, const uint16_t *__restrict__ g,
       sz[idx] = sum_totals(tb, ng);
     }
     __syncthreads();
-    // a thread per column: its words are loaded once, before the rows
-    for (int64_t col = t; col < L; col += kS1Threads) {
+    // a thread per (column, block of kS1RowBlock rows) item, columns
+    // innermost (coalesced stores); the column's words are loaded once per
+    // item, before its rows
+    const int nrb = (mn + kS1RowBlock - 1) / kS1RowBlock;
+    for (int64_t it = t; it < (int64_t)nrb * L; it += kS1Threads) {
+      const int rb = (int)((uint64_t)it / (uint64_t)L);
+      const int64_t col = it - (int64_t)rb * L;
       const int p = (int)((uint32_t)col / (uint32_t)s);  // col < L = P s <= 8192
       uint32_t wd[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) wd[r] = (r0 + r < r1) ? sv_word(sv16, Lp, r0 + r, col) : 0u;
-      for (int mi = 0; mi < mn; ++mi) {
+      const int mi1 = min(mn, (rb + 1) * kS1RowBlock);
+      for (int mi = rb * kS1RowBlock; mi < mi1; ++mi) {
         const float *tb = tab + (size_t)(mi * P + p) * G * 8 * 16;
         float acc = 0.f;
 #pragma unroll
