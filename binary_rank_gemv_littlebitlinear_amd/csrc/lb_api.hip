@@ -718,7 +718,7 @@ struct lb_stack {
   // destroyed, since launches captured earlier may still write it
   std::vector<void *> retired;
   int64_t max_width = 0;
-  int64_t loop_rows = 3;  // automatic mode: rows run as batch-1 sweeps (see lb_stack_forward)
+  int64_t loop_rows = 2;  // automatic mode: rows run as batch-1 sweeps (see lb_stack_forward)
   PersistPlan *persist = nullptr;
   std::vector<MfmaPlan *> uplan;  // per unit, for M >= 64
   void *mws = nullptr;            // unit-path workspace (largest unit)
@@ -871,7 +871,7 @@ extern "C" lb_status lb_stack_create(lb_layer *const *layers, int n_layers, cons
     // and 7 for 8192 x 28672 ones, so the limit follows the mean size
     double elems = 0;
     for (const lb_layer *L : S->layers) elems += (double)L->ly.a * (double)L->ly.b;
-    S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 5 : 3;
+    S->loop_rows = elems / (double)S->layers.size() >= (double)(1 << 27) ? 3 : 2;
   }
   if (st != LB_OK && st != LB_EUNSUPPORTED) {
     lb_stack_destroy(S);

@@ -282,7 +282,7 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               when they do) sets a flag that lb_stack_check reports and
  *               that the next sweep returns as LB_ETIMEOUT;
  *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
- *               per unit; except that for M <= 3 (M <= 5 when the stack's
+ *               per unit; except that for M <= 2 (M <= 3 when the stack's
  *               mean matrix has at least 2^27 weights) without a trace the
  *               one-launch sweep runs once per row (faster at these M; each
  *               row's output is exactly its M = 1 output);
