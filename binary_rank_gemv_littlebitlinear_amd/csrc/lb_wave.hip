@@ -569,7 +569,9 @@ struct Forward1Args {
   unsigned *herr;  // host-mapped: set when a wait gives up
 };
 
-constexpr int kF1Threads = 256;
+constexpr int kF1Threads = 512;  // eight waves: two per SIMD
+constexpr int kF1MaxL = 256;      // latent columns (one thread pair each in the first product)
+constexpr int kF1Lanes = 8;       // lanes per output row
 constexpr long kF1Spin = 1L << 24;
 constexpr int kF1MaxChunks = 16;  // first-product chunks (one partial each per column)
 
@@ -622,8 +624,11 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     const int ng = (int)(r1 - r0) * 8;
     float *tab = smem;                                  // [P][G*8][16]
     float *sz = smem + (size_t)A.P * A.G * 8 * 16;      // [P]
+    float *half1 = sz + 16;                             // [kF1MaxL]
     const int nr = (int)(r1 - r0);
-    for (int idx = t; idx < A.P * ng; idx += kF1Threads) {
+    // four threads per table, four entries each (one 16-byte store)
+    for (int gq = t; gq < A.P * ng * 4; gq += kF1Threads) {
+      const int idx = gq >> 2, hq = gq & 3;
       const int p = idx / ng, gr = idx - p * ng;
       const int64_t i0 = r0 * 32 + 4 * gr;
       const uint16_t *gp = A.g + p * A.a16;
@@ -636,32 +641,40 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (i0 + e >= A.a) v[e] = 0.f;
-      build_table(tab + ((size_t)p * A.G * 8 + gr) * 16, v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4 *>(tab + ((size_t)p * A.G * 8 + gr) * 16 + 4 * hq) =
+          table_quarter(v[0], v[1], v[2], v[3], hq);
     }
     __syncthreads();
     if (t < A.P) {
       sz[t] = sum_totals(tab + (size_t)t * A.G * 8 * 16, ng);
     }
     __syncthreads();
-    for (int64_t col = t; col < L; col += kF1Threads) {
-      const int p = (int)((uint32_t)col / (uint32_t)A.s);
+    // two threads per column (L <= kF1MaxL), each on half of the chunk's row
+    // groups; the second half's sum is added to the first's
+    const int col = t & (kF1MaxL - 1), hf = t / kF1MaxL, rh = (nr + 1) / 2;
+    const int ra = hf * rh, rb = min(nr, ra + rh);
+    float acc = 0.f;
+    int p = 0;
+    if (col < L) {
+      p = (int)((uint32_t)col / (uint32_t)A.s);
       const float *tb = tab + (size_t)p * A.G * 8 * 16;
-      float acc = 0.f;
-      for (int r = 0; r < nr; ++r) acc += lut_word(tb + r * 8 * 16, sv_word(A.sv16, A.Lp, r0 + r, col));
-      f1_put(&A.part[(size_t)c * L + col], 2.f * acc - sz[p], gen);
+      for (int r = ra; r < rb; ++r) acc += lut_word(tb + r * 8 * 16, sv_word(A.sv16, A.Lp, r0 + r, col));
+      if (hf) half1[col] = acc;
     }
+    __syncthreads();
+    if (hf == 0 && col < L) f1_put(&A.part[(size_t)c * L + col], 2.f * (acc + half1[col]) - sz[p], gen);
   } else {
-    // output rows [64 j, 64 j + 64): four lanes per row split its words
-    const int part = t & (kS2Lanes - 1), nw = A.P * (int)A.Wk;
+    // output rows [64 j, 64 j + 64): eight lanes per row split its words
+    const int part = t & (kF1Lanes - 1), nw = A.P * (int)A.Wk;
     float *tab = smem;                         // [nw][8][16]
     float *wsum = smem + (size_t)nw * 128;     // [2]
     float *wl = wsum + 2;                      // [L]
-    const int64_t j = (int64_t)(tk - A.N1) * kS2Rows + (t >> 2);
+    const int64_t j = (int64_t)(tk - A.N1) * kS2Rows + (t >> 3);
     const int64_t jc = j < A.b ? j : A.b - 1;
     uint32_t wd[WPL];
 #pragma unroll
     for (int v = 0; v < WPL; ++v) {
-      const int idx = part + kS2Lanes * v;
+      const int idx = part + kF1Lanes * v;
       wd[v] = idx < nw ? A.su2t[su_index(jc, nw, idx)] : 0u;
     }
     float hv[2];
@@ -680,7 +693,8 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
       wl[t] = h2f(A.l[p * A.s8 + (t - p * A.s)]) * v[0];
     }
     __syncthreads();
-    for (int gi = t; gi < nw * 8; gi += kF1Threads) {
+    for (int gq = t; gq < nw * 8 * 4; gq += kF1Threads) {
+      const int gi = gq >> 2, hq = gq & 3;
       const int idx = gi >> 3, gg = gi & 7;
       const int p = idx / (int)A.Wk, qq = idx - p * (int)A.Wk;
       const int64_t k0 = (int64_t)qq * 32 + 4 * gg;
@@ -688,7 +702,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (k0 + e < A.s) ? wm[k0 + e] : 0.f;
-      build_table(tab + (size_t)gi * 16, v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4 *>(tab + (size_t)gi * 16 + 4 * hq) = table_quarter(v[0], v[1], v[2], v[3], hq);
     }
     __syncthreads();
     if (t < A.P) {
@@ -698,7 +712,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     float acc[2] = {0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < WPL; ++v) {
-      const int idx = part + kS2Lanes * v;
+      const int idx = part + kF1Lanes * v;
       if (idx < nw) {
         const float sum = lut_word(tab + (size_t)idx * 128, wd[v]);
         if (idx < (int)A.Wk) acc[0] += sum; else acc[1] += sum;
@@ -708,6 +722,7 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
     for (int p = 0; p < 2; ++p) {
       acc[p] += __shfl_xor(acc[p], 1, 64);
       acc[p] += __shfl_xor(acc[p], 2, 64);
+      acc[p] += __shfl_xor(acc[p], 4, 64);
     }
     if (part == 0 && j < A.b) {
       float out = 0.f;
@@ -732,14 +747,14 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
 bool forward1_plan(const Layer &Ly, Forward1Plan *pl) {
   const int nw = Ly.P * (int)Ly.Wk;
   // small layers only: at most 16 chunks of at most 8 row groups, L <= 256
-  if (nw > kS2MaxWords || Ly.L > kF1Threads || (Ly.R1 + kF1MaxChunks - 1) / kF1MaxChunks > 8) return false;
+  if (nw > kS2MaxWords || Ly.L > kF1MaxL || (Ly.R1 + kF1MaxChunks - 1) / kF1MaxChunks > 8) return false;
   const int nch = (int)std::min<int64_t>(kF1MaxChunks, Ly.R1);
   const int G = (int)((Ly.R1 + nch - 1) / nch);
   pl->G = G;
   pl->N1 = (int)((Ly.R1 + G - 1) / G);
   pl->N2 = (int)((Ly.b + kS2Rows - 1) / kS2Rows);
-  pl->wpl = (nw + kS2Lanes - 1) / kS2Lanes;
-  const size_t l1 = ((size_t)Ly.P * G * 8 * 16 + Ly.P + 16) * sizeof(float);
+  pl->wpl = (nw + kF1Lanes - 1) / kF1Lanes;
+  const size_t l1 = ((size_t)Ly.P * G * 8 * 16 + 16 + kF1MaxL + 16) * sizeof(float);
   const size_t l2 = ((size_t)nw * 128 + 2 + Ly.L + 16) * sizeof(float);
   pl->lds = std::max(l1, l2);
   pl->state_bytes = 256 + (size_t)pl->N1 * Ly.L * 8;
@@ -762,8 +777,7 @@ hipError_t launch_forward1(const Layer &Ly, const Forward1Plan &pl, void *state,
   if (pl.wpl <= 2) LB_F1(2);
   else if (pl.wpl <= 4) LB_F1(4);
   else if (pl.wpl <= 8) LB_F1(8);
-  else if (pl.wpl <= 12) LB_F1(12);
-  else LB_F1(24);
+  else LB_F1(12);  // nw <= kS2MaxWords = 96
 #undef LB_F1
   return hipGetLastError();
 }
