@@ -564,7 +564,7 @@ struct Forward1Args {
   uint16_t *y;
   int64_t a, a16, b, b16, s, s8, L, Lp, R1, Wk;
   int P, G, N1, N2;
-  unsigned *ctrl;  // [0] next ticket, [1] finished workgroups, [2] generation of the last launch
+  unsigned *ctrl;  // one 64-bit word: the launch's generation (high half), the next ticket (low half)
   uint64_t *part;  // [N1][L] tagged chunk partials
   unsigned *herr;  // host-mapped: set when a wait gives up
 };
@@ -609,9 +609,18 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
   extern __shared__ float smem[];
   __shared__ unsigned s_tk, s_gen;
   const int t = threadIdx.x;
+  // the workgroup that draws the last ticket moves the word to the next
+  // generation with the count at 0: every workgroup of this launch has
+  // drawn by then, and the next launch (stream-ordered) starts from there,
+  // so no workgroup has to count finishers at the end
   if (t == 0) {
-    s_tk = atomicAdd(&A.ctrl[0], 1u);
-    s_gen = __hip_atomic_load(&A.ctrl[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    unsigned long long *tw = reinterpret_cast<unsigned long long *>(A.ctrl);
+    const unsigned long long old = __hip_atomic_fetch_add(tw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tk = (unsigned)old, g = (unsigned)(old >> 32);
+    if (tk == (unsigned)(A.N1 + A.N2) - 1u)
+      __hip_atomic_store(tw, (unsigned long long)(g + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tk = tk;
+    s_gen = g + 1u;
   }
   __syncthreads();
   const int tk = (int)s_tk;
@@ -728,16 +737,6 @@ __global__ void __launch_bounds__(kF1Threads) k_forward1(Forward1Args A) {
       float out = 0.f;
       for (int p = 0; p < A.P; ++p) out += hv[p] * (2.f * acc[p] - wsum[p]);
       A.y[j] = f2h(out);
-    }
-  }
-  // the last workgroup to finish resets the ticket and publishes the generation
-  __syncthreads();
-  if (t == 0) {
-    const unsigned total = (unsigned)(A.N1 + A.N2);
-    if (atomicAdd(&A.ctrl[1], 1u) == total - 1u) {
-      __hip_atomic_store(&A.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&A.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&A.ctrl[2], gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
