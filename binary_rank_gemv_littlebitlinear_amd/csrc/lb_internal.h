@@ -65,8 +65,9 @@ struct Layer {
   size_t ws_bytes = 0;
   unsigned *cnt = nullptr;
   int wave_rows = 1;  // rows per wave-path launch pair (the partials fit ws)
-  // state of the one-launch M = 1 forward (ticket, generation, tagged
-  // partials and latent), zeroed at create; null when the layer is outside it
+  // state of the one-launch M = 1 forward (one 64-bit ticket-and-generation
+  // word, then the tagged chunk partials), zeroed at create; null when the
+  // layer is outside it
   void *f1state = nullptr;
   bool ready() const {
     for (int p = 0; p < P; ++p)
