@@ -139,7 +139,7 @@ hipError_t launch_mfma_unit(const MfmaPlan *p, const uint16_t *x, int64_t M,
                             hipStream_t st);
 
 // The whole stack for M >= 64 in one launch per 256 rows (lb_mfma.hip):
-// the unit tiles above as work items taken by ticket, each waiting only for
+// the unit tiles above as work items dealt round robin, each waiting only for
 // the previous step of its own 32-row block.  Built from the stack's unit
 // plans (null when a width is not a multiple of 8 or the device cannot
 // hold the kernel).  ws and cnt as for launch_mfma_unit, sized by

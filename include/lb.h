@@ -342,10 +342,11 @@ lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
  * the device can hold one workgroup per compute unit), 3 = automatic
  * except that M >= 64 without a trace runs the whole stack in one launch
  * per 256 rows: the same matrix-core tiles as mode 0, in the same order
- * (identical results), as work items taken by an atomic ticket, each
- * waiting only for the previous step of its own 32-row block, so row
- * blocks pipeline through the units and no co-residency is needed; its
- * bounded waits report a give-up as LB_ETIMEOUT from the next call, and
+ * (identical results), as work items dealt round robin to a grid of the
+ * device's resident capacity, each waiting only for the previous step of
+ * its own 32-row block, so row blocks pipeline through the units (kernels
+ * on other streams that hold compute units delay it until they finish);
+ * its bounded waits report a give-up as LB_ETIMEOUT from the next call, and
  * the first call for a row count sets up its launch arguments (allocates,
  * synchronises; LB_ENOTREADY under capture).  Measured slower than mode 0
  * on MI355X at M = 64 .. 512 (the tiles, not the launches, bound the
