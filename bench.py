@@ -64,6 +64,18 @@ def build(lbm, wl):
     return stack, time.time() - t0
 
 
+def kernel_desc(M: int, mode: int) -> str:
+    """The kernels lb_stack_forward runs for M rows in this mode (no trace)."""
+    if M <= 1 and mode != 1:
+        return "k_persist: one launch per step, timed with events on its stream"
+    if (M >= 128 and mode == 0) or (M >= 64 and mode == 3):
+        return "k_mstack: one launch per 256 rows, timed with events on its stream"
+    if M >= 64:
+        return "k_unit_s1 + k_unit_s2 per unit, timed together with events on their stream"
+    return ("wave-path kernels per layer (or the M = 1 sweep once per row for a few rows), "
+            "timed together with events on their stream")
+
+
 def time_steps(torch, stack, x, y, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -538,9 +550,7 @@ def main():
                      "unit": "GB/s" if batch1 else "TFLOP/s",
                      "frac": round((gbs / HBM_PEAK_GBS) if batch1 else (tflops / MFMA_FP16_PEAK_TFLOPS), 4),
                      "traffic": traffic,
-                     "kernel": ("k_persist: one launch per step, timed with events on its stream"
-                                if kind == "persistent" else
-                                "k_unit_s1 + k_unit_s2 per unit, timed together with events on their stream")},
+                     "kernel": kernel_desc(M, args.mode)},
     }
     if "cpu" in r:
         out["cpu_baseline"] = r["cpu"]
@@ -563,6 +573,7 @@ def main():
                             "mfma_frac": round(s2["flops"] / (ms2 * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
                             "GB/s": round(s2["bytes"] / (ms2 * 1e-3) / 1e9, 2),
                             "tokens_per_s_equiv": round(s2["M"] / (ms2 * 1e-3), 1),
+                            "kernel": kernel_desc(s2["M"], args.mode),
                             "validated": s2["validated"]}
         if not args.no_fp16_reference:
             print("[bench] timing the fp16 references of the secondary workload", file=sys.stderr, flush=True)

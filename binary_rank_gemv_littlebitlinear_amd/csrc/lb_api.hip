@@ -1015,7 +1015,20 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
       if (es != LB_OK) return es;
     }
   }
-  if (M >= 64 && S->mode == 3 && !trace) {
+  // from 128 rows (four 32-row blocks that pipeline through the units) the
+  // automatic mode runs the one-launch stack too, unless it is not set up
+  // for this M yet while the stream is being captured (then the unit
+  // launches below, the same tiles in the same order)
+  bool one_launch = M >= 64 && S->mode == 3 && !trace;
+  if (M >= 128 && S->mode == 0 && !trace && S->mstack) {
+    one_launch = true;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return fail(LB_EHIP, "lb_stack_forward: hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone &&
+        !mstack_ready(S->mstack, M, S->mws, S->mcnt, (uint16_t *)S->xbuf[0], (uint16_t *)S->xbuf[1]))
+      one_launch = false;
+  }
+  if (one_launch) {
     if (!S->mstack) return fail(LB_EUNSUPPORTED, "lb_stack_forward: no one-launch M >= 64 plan for this stack");
     std::string msg;
     DevCtx *dc = ctx_of(S->layers[0]);

@@ -153,6 +153,9 @@ MStackPlan *mstack_build(const std::vector<const MfmaPlan *> &units, float kappa
 void mstack_free(MStackPlan *p);
 size_t mstack_ws_bytes(const MStackPlan *p);
 size_t mstack_cnt_entries(const MStackPlan *p);
+// Whether the argument sets of every 256-row chunk of M exist for these
+// buffers (no side effects).
+bool mstack_ready(const MStackPlan *p, int64_t M, void *ws, unsigned *cnt, uint16_t *xb0, uint16_t *xb1);
 lb_status mstack_run(MStackPlan *p, const uint16_t *x0, uint16_t *y, int64_t M, void *ws, unsigned *cnt,
                      uint16_t *xb0, uint16_t *xb1, const void *zero, const DeviceInfo &dev,
                      hipStream_t st, std::string *msg);

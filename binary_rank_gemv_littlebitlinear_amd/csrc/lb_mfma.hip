@@ -775,13 +775,20 @@ static int s1_nsplit(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *
 }
 
 // Stage-2 block width: the widest (nb column pairs) that still gives about
-// 0.6 blocks per CU, so wide outputs do not re-read T from many blocks;
-// c2 = chunks per round, as many as two buffers allow.
+// 0.6 blocks per CU (one per CU from four 32-row blocks on), so wide
+// outputs do not re-read T from many blocks; c2 = chunks per round, as
+// many as two buffers allow.  The unit launches and the one-launch stack
+// share the rule, so they run the same tiles in the same order.
 static void s2_shape(const MfmaPlan &P, int64_t Mc, const DeviceInfo &dev, int *nb, int *c2) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int64_t rt = (Mc + 31) / 32;
   int n = 4;
-  while (n > 1 && (P.b + 64 * n - 1) / (64 * n) * rt < cus * 6 / 10) n /= 2;
+  // with four or more row blocks the one-launch stack pipelines them and
+  // is faster with the narrower blocks (M = 128: 2.80 against 2.90 ms; the
+  // unit launches then take 3.03 against 2.91 ms, and are no longer the
+  // automatic choice there)
+  const int64_t fill10 = rt >= 4 ? 10 : 6;
+  while (n > 1 && (P.b + 64 * n - 1) / (64 * n) * rt < cus * fill10 / 10) n /= 2;
   *nb = n;
   // a multiple of 4: one word instruction covers 4 chunks of a pair, and
   // must not spill into the next pair's words
@@ -1244,6 +1251,16 @@ static lb_status mstack_args(MStackPlan *p, int64_t Mc, void *ws, unsigned *cnt,
   }
   *out = &(p->sets[key] = set);
   return LB_OK;
+}
+
+bool mstack_ready(const MStackPlan *p, int64_t M, void *ws, unsigned *cnt, uint16_t *xb0, uint16_t *xb1) {
+  for (int64_t mb = 0; mb < M; mb += kMfmaRows) {
+    const int64_t Mc = std::min<int64_t>(kMfmaRows, M - mb);
+    const std::vector<uintptr_t> key = {(uintptr_t)Mc, (uintptr_t)ws, (uintptr_t)cnt, (uintptr_t)xb0,
+                                        (uintptr_t)xb1};
+    if (p->sets.find(key) == p->sets.end()) return false;
+  }
+  return true;
 }
 
 lb_status mstack_run(MStackPlan *p, const uint16_t *x0, uint16_t *y, int64_t M, void *ws, unsigned *cnt,

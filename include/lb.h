@@ -40,7 +40,9 @@
  *     builds the layer's matrix-core copy of the signs (allocates it and
  *     synchronises the device; lb_prepare does this ahead of time), and
  *     lb_stack_forward allocates (without synchronising) when M exceeds the
- *     rows reserved with lb_stack_reserve or by an earlier call.
+ *     rows reserved with lb_stack_reserve or by an earlier call, and sets
+ *     up its one-launch M >= 128 path on the first call for a row count
+ *     (allocates and synchronises; see lb_stack_forward).
  *   - Every buffer a forward call writes belongs to the layer or stack it
  *     runs (allocated by lb_create, lb_prepare or lb_stack_reserve) or to
  *     the caller: calls on different objects share nothing and may run on
@@ -286,8 +288,15 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               mean matrix has at least 2^27 weights) without a trace the
  *               one-launch sweep runs once per row (faster at these M; each
  *               row's output is exactly its M = 1 output);
- *   M >= 64     two matrix-core launches per unit, the combine fused into
- *               the second (see mode 3 for the one-launch alternative).
+ *   64 <= M < 128, or any M >= 64 with a trace: two matrix-core
+ *               launches per unit, the combine fused into the second;
+ *   M >= 128    without a trace: the whole stack in one launch per 256 rows
+ *               (as mode 3: the same tiles in the same order, so the same
+ *               output bit for bit; measured faster from four 32-row blocks
+ *               on).  The first call for a row count sets up that launch's
+ *               arguments (allocates, synchronises the device); while the
+ *               stream is being captured before that, the two launches per
+ *               unit run instead.
  * x0, y and trace must be 16-byte aligned; y must not overlap x0. */
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
@@ -348,10 +357,11 @@ lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
  * on other streams that hold compute units delay it until they finish);
  * its bounded waits report a give-up as LB_ETIMEOUT from the next call, and
  * the first call for a row count sets up its launch arguments (allocates,
- * synchronises; LB_ENOTREADY under capture).  Measured slower than mode 0
- * on MI355X at M = 64 .. 512 (the tiles, not the launches, bound the
- * time).  Mode 3 needs every width to be a multiple of 8
- * (LB_EUNSUPPORTED otherwise). */
+ * synchronises; LB_ENOTREADY under capture).  Mode 0 takes the same
+ * launch from M = 128 on; at M = 64 .. 127 the two launches per unit
+ * measured faster.  Mode 3 needs every width to be a multiple of 8
+ * (LB_EUNSUPPORTED otherwise; mode 0 then keeps the two launches per
+ * unit). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);
 
 lb_status lb_stack_destroy(lb_stack *S);

@@ -1,8 +1,9 @@
 """The one-launch M >= 64 stack (include/lb.h, lb_stack_set_mode 3): every
 unit's matrix-core tiles as work items of one launch, pipelined by 32-row
-block.  It runs the same tiles, with the same splits and summation order,
-as the two launches per unit of mode 0 (traced or not), so its output must
-equal theirs bit for bit; the traced call's layers and combines
+block (mode 3 from M = 64; the automatic mode takes it from M = 128).  It
+runs the same tiles, with the same splits and summation order, as the two
+launches per unit (a traced call, or automatic mode below 128 rows), so its
+output must equal theirs bit for bit; the traced call's layers and combines
 are checked against the float64 oracle (layer definition: [LB news]
 Sec. 2), and the untraced result against the oracle's chain on sampled
 rows."""
@@ -106,4 +107,42 @@ def test_one_launch_graph_replays(lbm):
         torch.cuda.synchronize()
         assert torch.equal(y, ref), f"replay {k}"
     S.check()
+    S.close()
+
+
+def test_automatic_mode_capture_before_setup_runs_unit_launches(lbm):
+    """Automatic mode from M = 128 takes the one-launch stack, whose launch
+    arguments are set up on the first eager call for a row count.  Captured
+    before that, the call runs the two launches per unit instead; both
+    graphs and the eager call must give the same output bit for bit (the
+    same tiles in the same order)."""
+    torch = lbtest.torch_dev()
+    say("[case] automatic M=128: capture before and after the one-launch setup")
+    wl, S, paths = build_stack(lbm, "llama7b_full_stack_M128", blocks=1)
+    M = 128
+    S.reserve(M)  # scratch and matrix-core sign copies, so the capture allocates nothing
+    xd = lbtest.to_dev(lb_synth.activations(M, wl["layers"][0]["a"], seed=6))
+    b_last = wl["layers"][-1]["b"]
+    y = torch.empty((M, b_last), dtype=torch.float16, device="cuda")
+
+    def captured():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            S.forward(xd, y, None)
+        torch.cuda.synchronize()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return y.clone()
+
+    y_units = captured()                  # not set up yet: two launches per unit
+    S.forward(xd, y, None)                # eager: sets up and runs the one launch
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    y_one = captured()                    # set up: the one launch
+    S.check()
+    assert torch.isfinite(y_eager.float()).all()
+    assert torch.equal(y_units, y_eager), "captured unit launches differ from the eager one-launch call"
+    assert torch.equal(y_one, y_eager), "captured one-launch call differs from the eager call"
     S.close()
