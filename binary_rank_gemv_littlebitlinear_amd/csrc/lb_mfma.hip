@@ -264,11 +264,14 @@ typedef __attribute__((address_space(4))) const S2Args CS2Args;
 
 // Tile (bx, by, bz) of a grid with gx tiles across; kCoh: x comes from
 // and T goes to other workgroups of the running launch (device-scope
-// loads and stores).  Returns whether this block completed the tile (the
-// only split, or the last of its splits): then its T values are stored.
-template <bool kCoh, class AT>
-__device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int by, int bz,
-                                        unsigned char *smem, int *s_last) {
+// loads and stores).  dep() is a workgroup-wide call, true once x may be
+// read; with kCoh the first round's sign words and g are requested before
+// it (M = 128 stack 2.79 -> 2.72 ms), its x rows after it.  Returns 1 when this block completed the tile (the only
+// split, or the last of its splits: then its T values are stored), 0 when
+// another split completes it, -1 when dep() returned false.
+template <bool kCoh, class AT, class Dep>
+__device__ __forceinline__ int s1_tile(AT &A, const uint16_t *xp, int bx, int by, int bz,
+                                       unsigned char *smem, int *s_last, Dep &&dep) {
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int tw = w & 3, par = w >> 2;  // column tile, chunk parity
   const int t32 = bx * 4 + tw;
@@ -302,9 +305,7 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
 
   // round r: chunks [kc0 + r C, +nch) of x rows (all waves), and of the
   // tile's sign words and g (waves 0-3, one tile each)
-  auto issue = [&](int r) {
-    unsigned char *buf = smem + (r & 1) * s1_lds_bytes(C);
-    const int kcr = kc0 + r * C, nch = min(C, kc1 - kcr);
+  auto issue_x = [&](unsigned char *buf, int kcr, int nch) {
     if (A.xvec) {
       // instruction u: chunk u / 2, rows 16 (u & 1) + lane / 4
       const int rw = lane >> 2;
@@ -331,6 +332,8 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
         *reinterpret_cast<uint4 *>(buf + idx * 16) = o;
       }
     }
+  };
+  auto issue_w = [&](unsigned char *buf, int kcr, int nch) {
     if (active && par == 0) {
       // words: lanes 0-31 chunk 2 v, lanes 32-63 chunk 2 v + 1 (C is even)
       for (int v = 0; v < (nch + 1) / 2; ++v) {
@@ -346,6 +349,12 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
       }
     }
   };
+  auto issue = [&](int r) {
+    unsigned char *buf = smem + (r & 1) * s1_lds_bytes(C);
+    const int kcr = kc0 + r * C, nch = min(C, kc1 - kcr);
+    issue_x(buf, kcr, nch);
+    issue_w(buf, kcr, nch);
+  };
 
   // chunks of the wave's parity alternate between two accumulators, so two
   // independent MFMA chains interleave
@@ -354,7 +363,19 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
   const int xo0 = lr * 4 + (lh ^ s1_swz(lr)), xo1 = lr * 4 + ((2 + lh) ^ s1_swz(lr));
   const int bstride = s1_lds_bytes(C);  // rounds alternate between two buffers when there are several
-  issue(0);
+  if constexpr (kCoh) {
+    const int nch0 = min(C, kc1 - kc0);
+    issue_w(smem, kc0, nch0);
+    if (!dep()) {
+      __builtin_amdgcn_s_waitcnt(0);  // the copies land before the LDS is left
+      return -1;
+    }
+    issue_x(smem, kc0, nch0);
+  } else {
+    // a launch of its own: x first (measured faster there)
+    if (!dep()) return -1;
+    issue(0);
+  }
   for (int r = 0; r < nr; ++r) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of round r landed
     __syncthreads();                // ... and every other wave's
@@ -465,7 +486,7 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
       *s_last = old == (unsigned)(A.nsplit - 1);
     }
     __syncthreads();
-    if (!*s_last) return false;
+    if (!*s_last) return 0;
     // the last block of the tile sums the splits in split order; every load
     // is unconditional (splits past nsplit re-read the last one) so all of
     // them are in flight at once
@@ -507,14 +528,14 @@ __device__ __forceinline__ bool s1_tile(AT &A, const uint16_t *xp, int bx, int b
   } else {
     dst[threadIdx.x] = srcl[threadIdx.x];
   }
-  return true;
+  return 1;
 }
 
 __global__ void __launch_bounds__(kThreads1)
 k_unit_s1(S1Args A) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_last;
-  (void)s1_tile<false>(A, A.x, blockIdx.x, blockIdx.y, blockIdx.z, smem, &s_last);
+  (void)s1_tile<false>(A, A.x, blockIdx.x, blockIdx.y, blockIdx.z, smem, &s_last, [] { return true; });
 }
 
 // ------------------------------------------------------------- stage 2
@@ -532,9 +553,13 @@ k_unit_s1(S1Args A) {
 __host__ __device__ constexpr int s2_buf_bytes(int C, int nb) { return C * 2048 + nb * C * 256; }
 
 // Tile (bx, by); kCoh: T comes from and xout goes to other workgroups of
-// the running launch (device-scope loads and stores).
-template <int NB, int NW, bool kCoh, class AT>
-__device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, unsigned char *smem) {
+// the running launch (device-scope loads and stores).  dep() is a
+// workgroup-wide call, true once T may be read; with kCoh the first round's
+// sign words are requested before it, its T rows after it.  False when
+// dep() returned false.
+template <int NB, int NW, bool kCoh, class AT, class Dep>
+__device__ __forceinline__ bool s2_tile(AT &A, uint16_t *xout, int bx, int by, unsigned char *smem,
+                                        Dep &&dep) {
   const int w = wave_id(), lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
   const int t = threadIdx.x;
   constexpr int nb = NB, nph = NW / NB;
@@ -563,9 +588,7 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
       ++m;
     }
   };
-  auto issue = [&](int r) {
-    int m, ch0, nch;
-    round_of(r, m, ch0, nch);
+  auto issue_t = [&](int r, int m, int ch0, int nch) {
     auto &Ly = A.ly[m];
     unsigned char *buf = smem + (r & 1) * bufb;
     const uint16_t *tsrc = A.T + ((size_t)tb * Lt8 + (Ly.seg0[0] >> 3) + ch0 * 4) * 256;
@@ -576,6 +599,10 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
       const int u = u0 + i < nu ? u0 + i : u0 + i - nu;
       dma16c<kCoh>(tsrc + u * 512 + lane * 8, buf + u * 1024);
     }
+  };
+  auto issue_w = [&](int r, int m, int ch0, int nch) {
+    auto &Ly = A.ly[m];
+    unsigned char *buf = smem + (r & 1) * bufb;
     // words: instruction (pair q, v) covers chunks 4 v .. 4 v + 3 of pair q
     const int nv = (nch + 3) / 4;
     for (int iv = w; iv < nb * nv; iv += NW) {
@@ -588,6 +615,12 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
       dma16(src, buf + wofs + (q * C + 4 * v) * 256);
     }
   };
+  auto issue = [&](int r) {
+    int m, ch0, nch;
+    round_of(r, m, ch0, nch);
+    issue_t(r, m, ch0, nch);
+    issue_w(r, m, ch0, nch);
+  };
 
   // outputs of thread t: row t / 8, columns q * 64 + 8 (t % 8) .. + 7 of each pair q
   float ys[NB][8];
@@ -596,7 +629,20 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
 #pragma unroll
     for (int e = 0; e < 8; ++e) ys[q][e] = 0.f;
   const int row_o = t >> 3, c_o = 8 * (t & 7);
-  issue(0);
+  if constexpr (kCoh) {
+    int m0, ch00, nch0;
+    round_of(0, m0, ch00, nch0);
+    issue_w(0, m0, ch00, nch0);
+    if (!dep()) {
+      __builtin_amdgcn_s_waitcnt(0);  // the copies land before the LDS is left
+      return false;
+    }
+    issue_t(0, m0, ch00, nch0);
+  } else {
+    // a launch of its own: T first (measured faster there)
+    if (!dep()) return false;
+    issue(0);
+  }
   int r = 0;
   for (int m = 0; m < A.nl; ++m) {
     auto &Ly = A.ly[m];
@@ -687,7 +733,7 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
       if (Ly.y && tok0 + row_o < A.M) store8(Ly.y, A.b, tok0 + row_o, j0 + q * 64 + c_o, v);
     }
   }
-  if (t >= 256 || A.direct || !xout || tok0 + row_o >= A.M) return;
+  if (t >= 256 || A.direct || !xout || tok0 + row_o >= A.M) return true;
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     float o[8];
@@ -699,13 +745,14 @@ __device__ __forceinline__ void s2_tile(AT &A, uint16_t *xout, int bx, int by, u
     else
       store8(xout, A.b, tok0 + row_o, j0 + q * 64 + c_o, o);
   }
+  return true;
 }
 
 template <int NB, int NW>
 __global__ void __launch_bounds__(NW * 64)
 k_unit_s2(S2Args A) {
   extern __shared__ __align__(16) unsigned char smem[];  // 2 round buffers
-  s2_tile<NB, NW, false>(A, A.xout, blockIdx.x, blockIdx.y, smem);
+  (void)s2_tile<NB, NW, false>(A, A.xout, blockIdx.x, blockIdx.y, smem, [] { return true; });
 }
 
 // ------------------------------------------------------------------ host
@@ -979,54 +1026,61 @@ __global__ void __launch_bounds__(kThreads1) k_mstack(MStackArgs A) {
     const int local = (int)tk - A.step_off[c];
     const int rb = __builtin_amdgcn_readfirstlane(local / per_rb);
     const int k = __builtin_amdgcn_readfirstlane(local - rb * per_rb);
-    if (c > 0 && t < 64) {
-      // wave 0: lane i polls flags i, i + 64, ... of step c - 1 and this row
-      // block until every one carries this launch's generation
-      const int need = A.step_tiles[c - 1];
-      const unsigned *f = A.done + ((size_t)(c - 1) * A.nrb + rb) * A.fstride;
-      long sp = 0;
-      bool ok = true;
-      for (int b0 = 0; b0 < need && ok; b0 += 64) {
-        const int i = b0 + t;
-        while (true) {
-          const unsigned v = i < need ? __hip_atomic_load(const_cast<unsigned *>(f + i), __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT)
-                                      : gen;
-          if (__all(v == gen)) break;
-          const unsigned ev = __builtin_amdgcn_readfirstlane(
-              __hip_atomic_load(A.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          if (++sp > kMSpin || ev != 0u) {
-            if (t == 0) {
-              __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(A.herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-              s_ok = 0;
+    // the dependency, waited for inside the tile once its weights are
+    // requested: wave 0, lane i polls flags i, i + 64, ... of step c - 1 and
+    // this row block until every one carries this launch's generation
+    auto dep = [&]() -> bool {
+      if (c > 0 && t < 64) {
+        const int need = A.step_tiles[c - 1];
+        const unsigned *f = A.done + ((size_t)(c - 1) * A.nrb + rb) * A.fstride;
+        long sp = 0;
+        bool ok = true;
+        for (int b0 = 0; b0 < need && ok; b0 += 64) {
+          const int i = b0 + t;
+          while (true) {
+            const unsigned v = i < need ? __hip_atomic_load(const_cast<unsigned *>(f + i), __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : gen;
+            if (__all(v == gen)) break;
+            const unsigned ev = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(A.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (++sp > kMSpin || ev != 0u) {
+              if (t == 0) {
+                __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(A.herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                s_ok = 0;
+              }
+              ok = false;
+              break;
             }
-            ok = false;
-            break;
+            __builtin_amdgcn_s_sleep(4);
           }
-          __builtin_amdgcn_s_sleep(4);
         }
       }
-    }
-    __syncthreads();  // the dependency is met (or s_ok is 0)
-    if (!s_ok) break;
-    bool completed = true;
+      __syncthreads();  // the dependency is met (or s_ok is 0)
+      return s_ok != 0;
+    };
+    int res;
     int slot = k;  // the tile's place among its step's tiles of this row block
     if ((c & 1) == 0) {
       CS1Args &P = *(CS1Args *)(A.s1 + u);  // uniform: scalar loads
       const int gx = P.Lt / 128;
       slot = k % gx;
-      completed = s1_tile<true>(P, u == 0 ? A.x0 : P.x, k % gx, rb, k / gx, smem, &s_last);
+      res = s1_tile<true>(P, u == 0 ? A.x0 : P.x, k % gx, rb, k / gx, smem, &s_last, dep);
     } else {
       CS2Args &P = *(CS2Args *)(A.s2 + u);
       uint16_t *xo = u == U - 1 ? A.y : P.xout;
+      bool ok2;
       if (P.nb == 4)
-        s2_tile<4, 8, true>(P, xo, k, rb, smem);
+        ok2 = s2_tile<4, 8, true>(P, xo, k, rb, smem, dep);
       else if (P.nb == 2)
-        s2_tile<2, 8, true>(P, xo, k, rb, smem);
+        ok2 = s2_tile<2, 8, true>(P, xo, k, rb, smem, dep);
       else
-        s2_tile<1, 8, true>(P, xo, k, rb, smem);
+        ok2 = s2_tile<1, 8, true>(P, xo, k, rb, smem, dep);
+      res = ok2 ? 1 : -1;
     }
+    if (res < 0) break;
+    const bool completed = res == 1;
     // every wave's device-scope stores have completed before the tile is
     // counted
     __builtin_amdgcn_s_waitcnt(0);
