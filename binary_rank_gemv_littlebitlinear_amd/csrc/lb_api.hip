@@ -1015,12 +1015,12 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
       if (es != LB_OK) return es;
     }
   }
-  // from 128 rows (four 32-row blocks that pipeline through the units) the
-  // automatic mode runs the one-launch stack too, unless it is not set up
-  // for this M yet while the stream is being captured (then the unit
-  // launches below, the same tiles in the same order)
+  // the automatic mode runs the one-launch stack too (its row blocks
+  // pipeline through the units; measured faster from 64 rows), unless it
+  // is not set up for this M yet while the stream is being captured (then
+  // the unit launches below, the same tiles in the same order)
   bool one_launch = M >= 64 && S->mode == 3 && !trace;
-  if (M >= 128 && S->mode == 0 && !trace && S->mstack) {
+  if (M >= 64 && S->mode == 0 && !trace && S->mstack) {
     one_launch = true;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess) return fail(LB_EHIP, "lb_stack_forward: hipStreamIsCapturing");

@@ -41,7 +41,7 @@
  *     synchronises the device; lb_prepare does this ahead of time), and
  *     lb_stack_forward allocates (without synchronising) when M exceeds the
  *     rows reserved with lb_stack_reserve or by an earlier call, and sets
- *     up its one-launch M >= 128 path on the first call for a row count
+ *     up its one-launch M >= 64 path on the first call for a row count
  *     (allocates and synchronises; see lb_stack_forward).
  *   - Every buffer a forward call writes belongs to the layer or stack it
  *     runs (allocated by lb_create, lb_prepare or lb_stack_reserve) or to
@@ -288,15 +288,15 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               mean matrix has at least 2^27 weights) without a trace the
  *               one-launch sweep runs once per row (faster at these M; each
  *               row's output is exactly its M = 1 output);
- *   64 <= M < 128, or any M >= 64 with a trace: two matrix-core
- *               launches per unit, the combine fused into the second;
- *   M >= 128    without a trace: the whole stack in one launch per 256 rows
- *               (as mode 3: the same tiles in the same order, so the same
- *               output bit for bit; measured faster from four 32-row blocks
- *               on).  The first call for a row count sets up that launch's
- *               arguments (allocates, synchronises the device); while the
- *               stream is being captured before that, the two launches per
- *               unit run instead.
+ *   M >= 64     without a trace: the whole stack in one launch per 256 rows
+ *               (as mode 3: the same tiles in the same order as the two
+ *               launches per unit, so the same output bit for bit; measured
+ *               faster).  The first call for a row count sets up that
+ *               launch's arguments (allocates, synchronises the device);
+ *               while the stream is being captured before that, two
+ *               matrix-core launches per unit run instead, the combine fused
+ *               into the second, as they do for any M >= 64 with a trace
+ *               (and when a width is not a multiple of 8).
  * x0, y and trace must be 16-byte aligned; y must not overlap x0. */
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
@@ -358,8 +358,8 @@ lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
  * its bounded waits report a give-up as LB_ETIMEOUT from the next call, and
  * the first call for a row count sets up its launch arguments (allocates,
  * synchronises; LB_ENOTREADY under capture).  Mode 0 takes the same
- * launch from M = 128 on; at M = 64 .. 127 the two launches per unit
- * measured faster.  Mode 3 needs every width to be a multiple of 8
+ * launch, except under capture before that setup (then the two launches
+ * per unit).  Mode 3 needs every width to be a multiple of 8
  * (LB_EUNSUPPORTED otherwise; mode 0 then keeps the two launches per
  * unit). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);

@@ -1,9 +1,9 @@
 """The one-launch M >= 64 stack (include/lb.h, lb_stack_set_mode 3): every
 unit's matrix-core tiles as work items of one launch, pipelined by 32-row
-block (mode 3 from M = 64; the automatic mode takes it from M = 128).  It
+block (mode 3, and the automatic mode without a trace, from M = 64).  It
 runs the same tiles, with the same splits and summation order, as the two
-launches per unit (a traced call, or automatic mode below 128 rows), so its
-output must equal theirs bit for bit; the traced call's layers and combines
+launches per unit (which a traced call runs), so its output must equal
+theirs bit for bit; the traced call's layers and combines
 are checked against the float64 oracle (layer definition: [LB news]
 Sec. 2), and the untraced result against the oracle's chain on sampled
 rows."""
@@ -51,7 +51,7 @@ def test_one_launch_equals_unit_launches(lbm, name, blocks, M):
     xd = lbtest.to_dev(x0)
     b_last = wl["layers"][-1]["b"]
     y0 = _untraced(torch, S, xd, b_last, M, 0)
-    assert np.array_equal(y0.view(np.uint16), yt.view(np.uint16)), "unit launches: traced != untraced"
+    assert np.array_equal(y0.view(np.uint16), yt.view(np.uint16)), "automatic mode: untraced != traced"
     for rep in range(3):
         y3 = _untraced(torch, S, xd, b_last, M, 3)
         S.check()
@@ -111,7 +111,7 @@ def test_one_launch_graph_replays(lbm):
 
 
 def test_automatic_mode_capture_before_setup_runs_unit_launches(lbm):
-    """Automatic mode from M = 128 takes the one-launch stack, whose launch
+    """Automatic mode from M = 64 takes the one-launch stack, whose launch
     arguments are set up on the first eager call for a row count.  Captured
     before that, the call runs the two launches per unit instead; both
     graphs and the eager call must give the same output bit for bit (the
