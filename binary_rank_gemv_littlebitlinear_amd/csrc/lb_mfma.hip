@@ -1029,14 +1029,26 @@ __global__ void __launch_bounds__(kThreads1) k_mstack(MStackArgs A) {
     // the dependency, waited for inside the tile once its weights are
     // requested: wave 0, lane i polls flags i, i + 64, ... of step c - 1 and
     // this row block until every one carries this launch's generation
+    // flags [f0, f1) of step c - 1: every tile of it, except that a stage-1
+    // split needs only the stage-2 column blocks that hold its x columns
+    int f0 = 0, f1 = c > 0 ? A.step_tiles[c - 1] : 0;
+    if (c > 0 && (c & 1) == 0) {
+      CS1Args &P = *(CS1Args *)(A.s1 + u);
+      const int nkc = (P.a + 31) >> 5, kc0 = (k / (P.Lt / 128)) * P.kcps, kc1 = min(nkc, kc0 + P.kcps);
+      const int wcb = 64 * ((CS2Args *)(A.s2 + u - 1))->nb;  // columns per stage-2 tile of unit u - 1
+      f0 = (32 * kc0) / wcb;
+      f1 = min(f1, (min(32 * kc1, P.a) - 1) / wcb + 1);
+    }
+    f0 = __builtin_amdgcn_readfirstlane(f0);
+    f1 = __builtin_amdgcn_readfirstlane(f1);
     auto dep = [&]() -> bool {
       if (c > 0 && t < 64) {
-        const int need = A.step_tiles[c - 1];
         const unsigned *f = A.done + ((size_t)(c - 1) * A.nrb + rb) * A.fstride;
         long sp = 0;
         bool ok = true;
-        for (int b0 = 0; b0 < need && ok; b0 += 64) {
+        for (int b0 = f0; b0 < f1 && ok; b0 += 64) {
           const int i = b0 + t;
+          const int need = f1;
           while (true) {
             const unsigned v = i < need ? __hip_atomic_load(const_cast<unsigned *>(f + i), __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT)
@@ -1192,7 +1204,7 @@ MStackPlan *mstack_build(const std::vector<const MfmaPlan *> &units, float kappa
 }
 
 size_t mstack_ws_bytes(const MStackPlan *p) {
-  return (size_t)round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256) +
+  return 2 * (size_t)round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256) +
          (size_t)(kMfmaRows / 32) * p->gxmax * kMaxSplit * 4096 * sizeof(float);
 }
 size_t mstack_cnt_entries(const MStackPlan *p) { return (size_t)(kMfmaRows / 32) * p->gxmax; }
@@ -1220,9 +1232,14 @@ static lb_status mstack_args(MStackPlan *p, int64_t Mc, void *ws, unsigned *cnt,
   std::vector<S1Args> h1(U);
   std::vector<S2Args> h2(U);
   std::vector<int> steps(4 * U + 1, 0);
-  uint16_t *T = reinterpret_cast<uint16_t *>(ws);
-  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
-                                          round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256));
+  // T alternates between two regions by unit parity: a stage-1 split of
+  // unit u + 1 waits only for the stage-2 tiles of unit u that produce its
+  // x columns, so it may run while other stage-2 tiles of unit u still read
+  // unit u's T
+  const size_t tbytes = (size_t)round_up((int64_t)kMfmaRows * p->Ltmax * 2, 256);
+  uint16_t *Tr[2] = {reinterpret_cast<uint16_t *>(ws),
+                     reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(ws) + tbytes)};
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + 2 * tbytes);
   size_t lds = 16384;
   int off = 0;
   for (int u = 0; u < U; ++u) {
@@ -1234,7 +1251,7 @@ static lb_status mstack_args(MStackPlan *p, int64_t Mc, void *ws, unsigned *cnt,
       }
     S1Args &A1 = h1[u];
     A1.x = u == 0 ? nullptr : (((u - 1) & 1) ? xb1 : xb0);
-    A1.T = T;
+    A1.T = Tr[u & 1];
     A1.part = part;
     A1.cnt = cnt;
     A1.zero = zero;
@@ -1257,7 +1274,7 @@ static lb_status mstack_args(MStackPlan *p, int64_t Mc, void *ws, unsigned *cnt,
     }
     lds = std::max(lds, s1_lds_launch(A1.kcps, A1.cround));
     S2Args &A2 = h2[u];
-    A2.T = T;
+    A2.T = Tr[u & 1];
     A2.xout = u == U - 1 ? nullptr : ((u & 1) ? xb1 : xb0);
     A2.zero = zero;
     A2.M = Mc;
