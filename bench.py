@@ -68,12 +68,13 @@ def kernel_desc(M: int, mode: int) -> str:
     """The kernels lb_stack_forward runs for M rows in this mode (no trace)."""
     if M <= 1 and mode != 1:
         return "k_persist: one launch per step, timed with events on its stream"
-    if M >= 64 and mode in (0, 3):
+    if M == 2 and mode in (0, 3):
+        return "k_persist once per row, timed with events on its stream"
+    if M >= 3 and mode in (0, 3):
         return "k_mstack: one launch per 256 rows, timed with events on its stream"
     if M >= 64:
         return "k_unit_s1 + k_unit_s2 per unit, timed together with events on their stream"
-    return ("wave-path kernels per layer (or the M = 1 sweep once per row for a few rows), "
-            "timed together with events on their stream")
+    return "wave-path kernels per layer, timed together with events on their stream"
 
 
 def time_steps(torch, stack, x, y, steps, warmup):

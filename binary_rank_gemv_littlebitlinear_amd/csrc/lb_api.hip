@@ -953,11 +953,22 @@ extern "C" lb_status lb_stack_trace_elems(const lb_stack *S, int64_t M, int64_t 
   return LB_OK;
 }
 
+// Rows that the automatic mode runs as one batch-1 sweep each (no trace).
+static int64_t sweep_rows(const lb_stack *S) {
+  if (!S->persist) return 0;
+  return S->mstack ? std::min<int64_t>(S->loop_rows, 2) : S->loop_rows;
+}
+// Whether a call of M rows without a trace runs the one-launch stack (in
+// the automatic mode and in mode 3): every M past the per-row sweeps.
+static bool one_launch_rows(const lb_stack *S, int64_t M) {
+  return S->mstack && M >= 2 && M > sweep_rows(S);
+}
+
 extern "C" lb_status lb_stack_reserve(lb_stack *S, int64_t M) {
   if (!S || M < 0) return fail(LB_EINVAL, "lb_stack_reserve: bad argument");
   DeviceGuard dg(S->device);
   lb_status st = stack_reserve(S, M);
-  if (st != LB_OK || M < 64) return st;
+  if (st != LB_OK || (M < 64 && !one_launch_rows(S, M))) return st;
   for (lb_layer *Lr : S->layers) {
     st = ensure_mfma_copies(Lr, nullptr, true, "lb_stack_reserve");
     if (st != LB_OK) return st;
@@ -994,10 +1005,11 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
     if (ps != LB_OK) return fail(ps, msg);
     return LB_OK;
   }
-  // a few rows without a trace: one batch-1 sweep per row beats the
-  // per-layer kernels up to S->loop_rows rows (rows are independent, so
-  // each row's result is exactly its batch-1 result)
-  if (S->persist && (S->mode == 0 || S->mode == 3) && !trace && M <= S->loop_rows) {
+  // a few rows without a trace: one batch-1 sweep per row (rows are
+  // independent, so each row's result is exactly its batch-1 result); it
+  // beats the per-layer kernels up to S->loop_rows rows, and the one-launch
+  // stack up to 2
+  if (S->persist && (S->mode == 0 || S->mode == 3) && !trace && M <= sweep_rows(S)) {
     const int64_t a0 = S->layers[0]->ly.a, bl = S->layers.back()->ly.b;
     for (int64_t m = 0; m < M; ++m) {
       std::string msg;
@@ -1009,27 +1021,32 @@ extern "C" lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void
   }
   lb_status rs = stack_reserve(S, M);
   if (rs != LB_OK) return rs;
-  if (M >= 64) {
+  // past the per-row sweeps, without a trace: the one-launch stack (row
+  // blocks pipeline through the units; measured faster than the per-layer
+  // kernels from 3 rows, where the wave path has become ALU-bound).  In the
+  // automatic mode, while the stream is being captured before the layers'
+  // matrix-core sign copies or the launch's setup for this M exist, the
+  // per-layer kernels below run instead (for M >= 64 the unit launches:
+  // the same tiles in the same order)
+  bool one_launch = (S->mode == 0 || S->mode == 3) && !trace && one_launch_rows(S, M);
+  if (one_launch && S->mode == 0) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return fail(LB_EHIP, "lb_stack_forward: hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone) {
+      bool copies = true;
+      for (const lb_layer *Lr : S->layers) copies = copies && Lr->ly.sv1m && Lr->ly.su2m;
+      if (!copies ||
+          !mstack_ready(S->mstack, M, S->mws, S->mcnt, (uint16_t *)S->xbuf[0], (uint16_t *)S->xbuf[1]))
+        one_launch = false;
+    }
+  }
+  if (M >= 64 || one_launch) {
     for (lb_layer *Lr : S->layers) {
       lb_status es = ensure_mfma_copies(Lr, st, true, "lb_stack_forward");
       if (es != LB_OK) return es;
     }
   }
-  // the automatic mode runs the one-launch stack too (its row blocks
-  // pipeline through the units; measured faster from 64 rows), unless it
-  // is not set up for this M yet while the stream is being captured (then
-  // the unit launches below, the same tiles in the same order)
-  bool one_launch = M >= 64 && S->mode == 3 && !trace;
-  if (M >= 64 && S->mode == 0 && !trace && S->mstack) {
-    one_launch = true;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return fail(LB_EHIP, "lb_stack_forward: hipStreamIsCapturing");
-    if (cs != hipStreamCaptureStatusNone &&
-        !mstack_ready(S->mstack, M, S->mws, S->mcnt, (uint16_t *)S->xbuf[0], (uint16_t *)S->xbuf[1]))
-      one_launch = false;
-  }
   if (one_launch) {
-    if (!S->mstack) return fail(LB_EUNSUPPORTED, "lb_stack_forward: no one-launch M >= 64 plan for this stack");
     std::string msg;
     DevCtx *dc = ctx_of(S->layers[0]);
     lb_status ms = mstack_run(S->mstack, (const uint16_t *)x0, (uint16_t *)y, M, S->mws, S->mcnt,

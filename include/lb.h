@@ -283,28 +283,37 @@ lb_status lb_stack_create(lb_layer *const *layers, int n_layers, const int32_t *
  *               not hold the compute units.  A wait that gives up (e.g.
  *               when they do) sets a flag that lb_stack_check reports and
  *               that the next sweep returns as LB_ETIMEOUT;
- *   2 <= M < 64 the wave-path kernels of each layer, then a combine kernel
- *               per unit; except that for M <= 2 (M <= 3 when the stack's
- *               mean matrix has at least 2^27 weights) without a trace the
- *               one-launch sweep runs once per row (faster at these M; each
+ *   M = 2       without a trace: the one-launch sweep once per row (each
  *               row's output is exactly its M = 1 output);
- *   M >= 64     without a trace: the whole stack in one launch per 256 rows
- *               (as mode 3: the same tiles in the same order as the two
- *               launches per unit, so the same output bit for bit; measured
- *               faster).  The first call for a row count sets up that
- *               launch's arguments (allocates, synchronises the device);
- *               while the stream is being captured before that, two
- *               matrix-core launches per unit run instead, the combine fused
- *               into the second, as they do for any M >= 64 with a trace
- *               (and when a width is not a multiple of 8).
+ *   M >= 3      without a trace (M >= 2 when the device cannot hold the
+ *               sweep): the whole stack in one launch per 256 rows on the
+ *               matrix cores, its 32-row blocks pipelined through the units
+ *               (as mode 3; measured faster than the per-layer kernels from
+ *               3 rows, where the wave path has become ALU-bound).  The
+ *               first such call builds the layers' matrix-core sign copies
+ *               (lb_prepare, or lb_stack_reserve, does it ahead), and the
+ *               first call for a row count sets up the launch's arguments
+ *               (both allocate and synchronise the device).  While the
+ *               stream is being captured before either exists, the
+ *               per-layer kernels below run instead;
+ *   otherwise   (a trace, a width that is not a multiple of 8, or that
+ *               capture): for M < 64 the wave-path kernels of each layer,
+ *               then a combine kernel per unit (fused into the unit's last
+ *               layer up to 16 rows), or the sweep once per row for M <= 2
+ *               (M <= 3 when the stack's mean matrix has at least 2^27
+ *               weights) without a trace; for M >= 64 two matrix-core
+ *               launches per unit, the combine fused into the second (the
+ *               same tiles in the same order as the one launch, so the same
+ *               output bit for bit).
  * x0, y and trace must be 16-byte aligned; y must not overlap x0. */
 lb_status lb_stack_forward(lb_stack *S, const void *x0, void *y, void *trace, int64_t M,
                            void *stream);
 
 /* Reserve the stack's scratch for up to M rows now (allocates; for
- * M >= 64 also builds the layers' matrix-core sign copies, which
- * synchronises the device), so that later lb_stack_forward calls with at
- * most M rows allocate nothing.  Scratch of an earlier, smaller
+ * M >= 3, when the stack has a one-launch plan, or M >= 64, also builds
+ * the layers' matrix-core sign copies, which synchronises the device), so
+ * that later lb_stack_forward calls with at most M rows allocate nothing
+ * except the one-launch setup of a new row count.  Scratch of an earlier, smaller
  * reservation is retired, not freed (launches already queued or captured
  * keep using it), until lb_stack_destroy. */
 lb_status lb_stack_reserve(lb_stack *S, int64_t M);
@@ -349,19 +358,18 @@ lb_status lb_stack_test_delay(lb_stack *S, uint32_t seed, uint32_t max_ticks);
  * 1 = every layer alone (as lb_forward) followed by a combine kernel per
  * unit, 2 = the one-launch sweep only (LB_EUNSUPPORTED unless M = 1 and
  * the device can hold one workgroup per compute unit), 3 = automatic
- * except that M >= 64 without a trace runs the whole stack in one launch
- * per 256 rows: the same matrix-core tiles as mode 0, in the same order
+ * (where it takes the one launch, from 3 rows without a trace) without the
+ * capture fallback.  The one launch runs the whole stack per 256 rows: the
+ * matrix-core tiles of the two launches per unit, in the same order
  * (identical results), as work items dealt round robin to a grid of the
  * device's resident capacity, each waiting only for the previous step of
  * its own 32-row block, so row blocks pipeline through the units (kernels
  * on other streams that hold compute units delay it until they finish);
  * its bounded waits report a give-up as LB_ETIMEOUT from the next call, and
  * the first call for a row count sets up its launch arguments (allocates,
- * synchronises; LB_ENOTREADY under capture).  Mode 0 takes the same
- * launch, except under capture before that setup (then the two launches
- * per unit).  Mode 3 needs every width to be a multiple of 8
- * (LB_EUNSUPPORTED otherwise; mode 0 then keeps the two launches per
- * unit). */
+ * synchronises; LB_ENOTREADY under capture, where mode 0 falls back to
+ * the per-layer kernels).  Mode 3 needs every width to be a multiple of 8
+ * (LB_EUNSUPPORTED otherwise; mode 0 then keeps the per-layer kernels). */
 lb_status lb_stack_set_mode(lb_stack *S, int mode);
 
 lb_status lb_stack_destroy(lb_stack *S);

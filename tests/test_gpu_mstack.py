@@ -27,6 +27,20 @@ def lbm():
     return lbtest.ensure_built()
 
 
+def _oracle_chain(wl, paths, x0, rows):
+    """The oracle's own chain on the given rows: every layer and combine in
+    float64 from the previous unit's fp16-rounded combine (the rounding the
+    stack performs); residual layers (kappa for two paths)."""
+    kap = lb_synth.kappa(2)
+    x = x0[rows].astype(np.float64)
+    b0 = 0
+    for nu in wl["units"]:
+        ys = [oracle.forward(x.astype(np.float16), paths[b0 + k]).astype(np.float16) for k in range(nu)]
+        x = (kap / math.sqrt(nu)) * np.sum([v.astype(np.float64) for v in ys], axis=0)
+        b0 += nu
+    return x
+
+
 def _untraced(torch, S, xd, b_last, M, mode):
     y = torch.full((M, b_last), float("nan"), dtype=torch.float16, device="cuda")
     S.set_mode(mode)
@@ -59,25 +73,18 @@ def test_one_launch_equals_unit_launches(lbm, name, blocks, M):
     S.close()
 
 
-def test_one_launch_rows_follow_the_oracle_chain(lbm):
+@pytest.mark.parametrize("M", [5, 70])
+def test_one_launch_rows_follow_the_oracle_chain(lbm, M):
     """Untraced one-launch output on sampled rows against the oracle's own
     chain: every layer and combine computed in float64 from the previous
     unit's fp16-rounded combine (the rounding the stack performs)."""
     torch = lbtest.torch_dev()
-    say("[case] one-launch M=70 vs the oracle chain")
+    say(f"[case] one-launch M={M} vs the oracle chain")
     wl, S, paths = build_stack(lbm, "llama7b_full_stack_M128", blocks=1)
-    M = 70
     x0 = lb_synth.activations(M, wl["layers"][0]["a"], seed=wl["seed"])
     y = _untraced(torch, S, lbtest.to_dev(x0), wl["layers"][-1]["b"], M, 3)
-    kap = lb_synth.kappa(2)
-    rows = [0, 33, 69]
-    x = x0[rows].astype(np.float64)
-    b0 = 0
-    for nu in wl["units"]:
-        ys = [oracle.forward(x.astype(np.float16), paths[b0 + k]).astype(np.float16) for k in range(nu)]
-        x = (kap / math.sqrt(nu)) * np.sum([v.astype(np.float64) for v in ys], axis=0)
-        b0 += nu
-    assert_parity(y[rows], x, "one-launch stack vs oracle chain")
+    rows = sorted({0, M // 2, M - 1})
+    assert_parity(y[rows], _oracle_chain(wl, paths, x0, rows), "one-launch stack vs oracle chain")
     S.close()
 
 
@@ -145,4 +152,32 @@ def test_automatic_mode_capture_before_setup_runs_unit_launches(lbm):
     assert torch.isfinite(y_eager.float()).all()
     assert torch.equal(y_units, y_eager), "captured unit launches differ from the eager one-launch call"
     assert torch.equal(y_one, y_eager), "captured one-launch call differs from the eager call"
+    S.close()
+
+
+@pytest.mark.parametrize("name,blocks,M", [("llama7b_mlp_stack", 3, 3), ("llama7b_mlp_stack", 2, 16),
+                                           ("llama70b_mlp_stack", 2, 3), ("llama7b_full_stack_M128", 1, 40)])
+def test_small_batch_runs_one_launch(lbm, name, blocks, M):
+    """From 3 rows without a trace the automatic mode runs the one-launch
+    stack: its output equals mode 3's bit for bit, repeated calls agree,
+    and sampled rows meet the parity bar against the oracle's own chain.
+    The traced call runs the wave-path kernels of each layer instead, each
+    layer and combine checked against the oracle (teacher-forced)."""
+    torch = lbtest.torch_dev()
+    say(f"[case] small batch one launch {name} blocks={blocks} M={M}")
+    wl, S, paths = build_stack(lbm, name, blocks=blocks)
+    x0, yt, tr = run_stack(lbm, wl, S, M)  # traced: the wave path
+    n = len(wl["layers"])
+    check_stack(wl, paths, x0, yt, tr, M, sample=[0, n // 2, n - 1])
+    xd = lbtest.to_dev(x0)
+    b_last = wl["layers"][-1]["b"]
+    y0 = _untraced(torch, S, xd, b_last, M, 0)
+    S.check()
+    y3 = _untraced(torch, S, xd, b_last, M, 3)
+    y0b = _untraced(torch, S, xd, b_last, M, 0)
+    S.check()
+    assert np.array_equal(y0.view(np.uint16), y3.view(np.uint16)), "automatic mode != mode 3"
+    assert np.array_equal(y0.view(np.uint16), y0b.view(np.uint16)), "repeated calls differ"
+    rows = sorted({0, M // 2, M - 1})
+    assert_parity(y0[rows], _oracle_chain(wl, paths, x0, rows), f"one launch vs oracle chain M={M}")
     S.close()
