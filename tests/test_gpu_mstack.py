@@ -181,3 +181,38 @@ def test_small_batch_runs_one_launch(lbm, name, blocks, M):
     rows = sorted({0, M // 2, M - 1})
     assert_parity(y0[rows], _oracle_chain(wl, paths, x0, rows), f"one launch vs oracle chain M={M}")
     S.close()
+
+
+def test_small_batch_capture_before_setup_runs_wave_path(lbm):
+    """Captured before the one launch is set up for its row count, an M = 8
+    stack call runs the wave-path kernels instead (nothing is allocated
+    under capture).  Its replays and the later eager one-launch call each
+    meet the parity bar against the oracle's chain on sampled rows, and they
+    are different kernels (fp16 latent on the matrix cores, fp32 in the
+    wave path), so the replay differs from the eager output."""
+    torch = lbtest.torch_dev()
+    say("[case] automatic M=8: capture before the one-launch setup")
+    wl, S, paths = build_stack(lbm, "llama7b_mlp_stack", blocks=2)
+    M = 8
+    S.reserve(M)  # scratch and matrix-core sign copies; the launch setup is per row count
+    x0 = lb_synth.activations(M, wl["layers"][0]["a"], seed=8)
+    xd = lbtest.to_dev(x0)
+    b_last = wl["layers"][-1]["b"]
+    y = torch.empty((M, b_last), dtype=torch.float16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        S.forward(xd, y, None)
+    torch.cuda.synchronize()
+    y.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    y_wave = y.cpu().numpy()
+    y_one = _untraced(torch, S, xd, b_last, M, 0)
+    S.check()
+    rows = [0, 3, 7]
+    ref = _oracle_chain(wl, paths, x0, rows)
+    assert_parity(y_wave[rows], ref, "captured wave path vs oracle chain")
+    assert_parity(y_one[rows], ref, "eager one launch vs oracle chain")
+    assert not np.array_equal(y_wave.view(np.uint16), y_one.view(np.uint16)), "the fallback did not run"
+    S.close()
