@@ -142,9 +142,9 @@ def mall_reference(torch, nbytes: int, reps: int = 50) -> dict:
             "reps": reps}
 
 
-TIMELINE_PARTS = ("second-product lookups", "second-product epilogue and combine", "first-product tables",
-                  "first-product lookups", "publish + level A (XCD-local sum)", "level B (across XCDs)",
-                  "level C + next tables")
+TIMELINE_PARTS = ("second-product lookups", "second-product epilogue, combine and next tables",
+                  "first-product set-up", "first-product lookups and publish",
+                  "barrier + level A (XCD-local sum)", "level B (across XCDs)", "level C + next tables")
 
 
 def sweep_timeline(torch, lbm, stack, x, y, nunits: int) -> dict:

@@ -234,6 +234,26 @@ __device__ __forceinline__ void st_tag_xcd(uint64_t *p, float v, unsigned gen, i
   else
     __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// N adjacent tagged words (N = 1, 2 or 4, the first one 8 N bytes
+// aligned) for readers on this XCD: with local, plain stores of 8 N bytes
+// (as the workgroup-scope store above; an aligned 8-byte word within one
+// vector store is never torn), else one device-scope store per word.
+template <int N>
+__device__ __forceinline__ void st_tags_xcd(uint64_t *p, const float (&v)[N], unsigned gen,
+                                            int local) {
+  uint64_t w[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) w[k] = (uint64_t)__float_as_uint(v[k]) | ((uint64_t)gen << 32);
+  if (local && N == 4) {
+    reinterpret_cast<ulonglong2 *>(p)[0] = make_ulonglong2(w[0], w[1]);
+    reinterpret_cast<ulonglong2 *>(p)[1] = make_ulonglong2(w[2], w[3]);
+  } else if (local && N == 2) {
+    reinterpret_cast<ulonglong2 *>(p)[0] = make_ulonglong2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) st_tag_xcd(p + k, v[k], gen, local);
+  }
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // 16-row tiles [t0, t1) owned by workgroup w out of `tiles`.
@@ -290,7 +310,6 @@ struct Lds {
   unsigned char *stg;  // kStgBytes staged bits and scales of the phase
   float *tab2;         // kTab2Floats second-product tables
   float *tab1;         // kTab1Floats first-product tables
-  float *part;         // kLuMax
   float *acc2;         // kMaxUnitLayers * 2 * 16 * kTMax
   float *xs;           // 16 * kTMax input rows (fp16 values as fp32)
   float *red;          // kXThreads exchange scratch
@@ -397,6 +416,13 @@ __device__ __forceinline__ void table_quad(float *tab, float v0, float v1, float
   *reinterpret_cast<float4 *>(tab + 4 * hi) = e;
 }
 
+// The value of lane i of this lane's quad (lanes 4k .. 4k + 3), by a DPP
+// lane move; every lane of the quad must be active.
+template <int i>
+__device__ __forceinline__ float quad_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), i * 0x55, 0xf, 0xf, false));
+}
+
 // ceil(2^32 / n) for 1 <= n <= kTMax (the division for larger n).
 __device__ __forceinline__ uint64_t ceil_recip32(int n) {
   static_assert(kTMax == 8, "constants for n <= 8");
@@ -420,8 +446,8 @@ __device__ __forceinline__ uint64_t ceil_recip32(int n) {
 // of dependent LDS reads costs ~0.1 us per link.
 
 // Second product of unit A over the workgroup's rows: every layer's fp16
-// outputs (trace), their combine into xs, and the output rows on the last
-// phase.
+// outputs (trace), their combine, and the output rows on the last phase or
+// else the first-product tables of unit B over the combined rows.
 __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   const PhaseCtx &C = *L.ctx;
   const PUnit &U = C.ua;
@@ -505,28 +531,54 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   const float c_out = U.c_out;
   const int64_t trace_x = C.ub.trace_x;
   __syncthreads();
-  // epilogue: y per layer, combine, output
-  for (int r = threadIdx.x; r < rows; r += kThreads) {
-    const int j = 16 * t0 + r;
-    float ys = 0.f;
+  // epilogue, a thread per row r: y per layer, the combine and the output
+  // row.  The combined rows are the next unit's input, so the same threads
+  // build its first product's tables from them: the four lanes of rows
+  // 4 qd .. 4 qd + 3 (one quad of a wave) share their z = g * x values by
+  // lane moves, and lane k writes entries 4 k .. 4 k + 3 of each pair's
+  // table of that quad.
+  {
+    const bool next = ph < A.nunits;
+    const PLayer *LB = C.la + na;
+    const int Pu = next ? LB[0].P : 1;
+    const int npairs = next ? C.ub.n * Pu : 0;
+    int goff[kMaxUnitLayers];
 #pragma unroll
-    for (int m = 0; m < kMaxUnitLayers; ++m) {
-      if (m >= na) break;
-      const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + hoff[m]);
-      const int P = Pm[m];
-      float yv = h2f(hv[((r >> 4) * P) * 16 + (r & 15)]) * L.acc2[(m * 2) * (16 * kTMax) + r];
-      if (P > 1) yv += h2f(hv[((r >> 4) * P + 1) * 16 + (r & 15)]) * L.acc2[(m * 2 + 1) * (16 * kTMax) + r];
-      const uint16_t y16 = f2h(yv);
-      if (j < ub && A.trace) A.trace[trace_y[m] + j] = y16;
-      ys += h2f(y16);
-    }
-    const uint16_t xv = f2h(c_out * ys);
-    L.xs[r] = j < ub ? h2f(xv) : 0.f;
-    if (j < ub) {
-      if (ph == A.nunits)
-        A.y[j] = xv;
-      else if (A.trace)
-        A.trace[trace_x + j] = xv;
+    for (int m = 0; m < kMaxUnitLayers; ++m) goff[m] = C.g_off[m];
+    const int r = threadIdx.x;
+    if (r < rows) {
+      const int j = 16 * t0 + r;
+      float ys = 0.f;
+#pragma unroll
+      for (int m = 0; m < kMaxUnitLayers; ++m) {
+        if (m >= na) break;
+        const uint16_t *hv = reinterpret_cast<const uint16_t *>(L.stg + hoff[m]);
+        const int P = Pm[m];
+        float yv = h2f(hv[((r >> 4) * P) * 16 + (r & 15)]) * L.acc2[(m * 2) * (16 * kTMax) + r];
+        if (P > 1) yv += h2f(hv[((r >> 4) * P + 1) * 16 + (r & 15)]) * L.acc2[(m * 2 + 1) * (16 * kTMax) + r];
+        const uint16_t y16 = f2h(yv);
+        if (j < ub && A.trace) A.trace[trace_y[m] + j] = y16;
+        ys += h2f(y16);
+      }
+      const uint16_t xv = f2h(c_out * ys);
+      const float xr = j < ub ? h2f(xv) : 0.f;
+      if (j < ub) {
+        if (!next)
+          A.y[j] = xv;
+        else if (A.trace)
+          A.trace[trace_x + j] = xv;
+      }
+      // rows is a multiple of 16, so every quad of lanes is whole here
+      const int qd = r >> 2, hi = r & 3;
+      for (int jt = 0; jt < npairs; ++jt) {
+        const int m = Pu == 2 ? jt >> 1 : jt, p = jt - m * Pu;
+        const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + goff[m]);
+        const float v = h2f(gv[((r >> 4) * Pu + p) * 16 + (r & 15)]) * xr;
+        const float v0 = quad_lane<0>(v), v1 = quad_lane<1>(v), v2 = quad_lane<2>(v),
+                    v3 = quad_lane<3>(v);
+        table_quad(L.tab1 + jt * s1_set_floats(nt) + (qd >> 2) * kTileF + (qd & 3) * 16, v0, v1,
+                   v2, v3, hi);
+      }
     }
   }
   __syncthreads();
@@ -537,10 +589,13 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
 // two layers), and lpt lanes split the group's nt 16-row words; one LDS
 // read gives a tile's bits of all CPT columns.  Per column and tile the four
 // entries are summed as ((q0 + q1) + (q2 + q3)) and added in tile order.
+// The column's partial goes straight from the register to the workgroup's
+// slot of its XCD's exchange area (level A of the exchange), tagged.
 template <int CPT>
 __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLayer *LB, int nb,
                                            int Lu, int nt, int Pu,
-                                           const int (&col0m)[kMaxUnitLayers]) {
+                                           const int (&col0m)[kMaxUnitLayers], uint64_t *pa,
+                                           unsigned gen, int xcd_local) {
   const int ngr = Lu / CPT;
   int lpt = 1, lg = 0;
   while (lpt < 64 && lpt < nt && ngr * lpt * 2 <= kThreads) {
@@ -620,29 +675,33 @@ __device__ __forceinline__ void s1_lookups(Lds &L, const PhaseCtx &C, const PLay
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       for (int o = 1; o < lpt; o <<= 1) acc[j] += __shfl_xor(acc[j], o, 64);
-      if (sub == 0 && q < ngr) L.part[q * CPT + j] = acc[j];
     }
+    if (sub == 0 && q < ngr) st_tags_xcd<CPT>(&pa[q * CPT], acc, gen, xcd_local);
   }
 }
 
-// First product of unit B over the workgroup's rows: part[col] for every
-// latent column of every layer of the unit.
-__device__ void first_product(Lds &L, int ph) {
+// First product of unit B over the workgroup's rows: the partial of every
+// latent column of every layer of the unit, published tagged into this
+// workgroup's slot of its XCD's exchange area.  In phase 0 the tables are
+// built here from the input rows (xs); later phases find them built by the
+// second product's epilogue.
+__device__ void first_product(const PArgs &A, Lds &L, int ph, unsigned gen) {
   const PhaseCtx &C = *L.ctx;
   const PUnit &U = C.ub;
   const int nb = U.n, Lu = U.Lu;
   const PLayer *LB = C.la + (C.has_a ? C.ua.n : 0);
   const int nt = C.t1 - C.t0, quads = 4 * nt;
+  const int w = blockIdx.x;
+  uint64_t *pa = A.PA + ((size_t)(w % kXcd) * kPerXcd + w / kXcd) * kLuMax;
   if (nt == 0) {
-    for (int c = threadIdx.x; c < Lu; c += kThreads) L.part[c] = 0.f;
-    __syncthreads();
+    for (int c = threadIdx.x; c < Lu; c += kThreads) st_tag_xcd(&pa[c], 0.f, gen, A.xcd_local);
     return;
   }
   // every layer of a unit has the same path count Pu; pair j = m Pu + p
   // (layer m, path p) has its tile blocks at tab1 + j * s1_set_floats(nt)
   const int Pu = LB[0].P;
-  // tables from z = g * x: thread t builds the table of quad t % 32 of pair t / 32
-  {
+  if (ph == 0) {
+    // tables from z = g * x: thread t builds the table of quad t % 32 of pair t / 32
     const int j = (int)threadIdx.x >> 5, qd = (int)threadIdx.x & 31;
     const int m = Pu == 2 ? j >> 1 : j, p = j - m * Pu;
     if (m < nb && qd < quads) {
@@ -657,31 +716,25 @@ __device__ void first_product(Lds &L, int ph) {
 #pragma unroll
       for (int hi = 0; hi < 4; ++hi) table_quad(tab, v[0], v[1], v[2], v[3], hi);
     }
+    __syncthreads();
   }
   int col0m[kMaxUnitLayers];
 #pragma unroll
   for (int m = 0; m < kMaxUnitLayers; ++m) col0m[m] = LB[m].col0;
   const int cpt = nt == (U.cpt >> 16) ? (U.cpt & 255) : ((U.cpt >> 8) & 255);
-  __syncthreads();
   stamp(L, ph, 3);
-  if (cpt == 4) s1_lookups<4>(L, C, LB, nb, Lu, nt, Pu, col0m);
-  else if (cpt == 2) s1_lookups<2>(L, C, LB, nb, Lu, nt, Pu, col0m);
-  else s1_lookups<1>(L, C, LB, nb, Lu, nt, Pu, col0m);
-  __syncthreads();
+  if (cpt == 4) s1_lookups<4>(L, C, LB, nb, Lu, nt, Pu, col0m, pa, gen, A.xcd_local);
+  else if (cpt == 2) s1_lookups<2>(L, C, LB, nb, Lu, nt, Pu, col0m, pa, gen, A.xcd_local);
+  else s1_lookups<1>(L, C, LB, nb, Lu, nt, Pu, col0m, pa, gen, A.xcd_local);
 }
 
 // -------------------------------------------------------- the exchange
-// part (LDS, Lu floats) of every workgroup -> T (LDS) = their sum.
-// Reduce-scatter then all-gather through device memory with tagged words
-// and no separate flags: workgroup w stores its partials tagged with this
-// phase's generation; the owner of slice r (8 columns) spins on the 8 G
-// words of its slice until every one carries the generation, sums them in
-// a fixed order and stores the 8 sums tagged into every copy; a
-// workgroup spins on the Lu tagged sums of its copy.  Each level costs one
-// store and one read (plus re-reads
-// while words are missing).  Only threads < kXThreads touch memory; every
-// spin is bounded and checks the error word every 64 rounds.
-constexpr int kXLoads = kLuMax / kXThreads;  // per-thread words of one step
+// The partials every workgroup published (first_product) -> the next
+// phase's second-product tables over their sum, in the three levels
+// described at the top of this file.  Each level costs one store and one
+// read (plus re-reads while words are missing).  Past the publish only
+// threads < kXThreads touch exchange memory; every spin is bounded and
+// checks the error word every 64 rounds.
 
 // Wait (per thread) until the words at p(k), k < N with valid(k),
 // carry gen; their values go to vals.  False on give-up or error.
@@ -758,20 +811,6 @@ __device__ TabPlan load_tables(const PArgs &A, const Lds &L, bool live) {
     if (v) T.n = i + 1;
   }
   return T;
-}
-
-// First half of the exchange: this workgroup's partials, tagged, into its
-// XCD's area (level A).
-__device__ void exchange_publish(const Lds &L, int Lu, unsigned gen, const PArgs &A) {
-  const int w = blockIdx.x, t = threadIdx.x;
-  uint64_t *pa = A.PA + ((size_t)(w % kXcd) * kPerXcd + w / kXcd) * kLuMax;
-  if (t < kXThreads) {
-#pragma unroll
-    for (int k = 0; k < kXLoads; ++k) {
-      const int c = t + k * kXThreads;
-      if (c < Lu) st_tag_xcd(&pa[c], L.part[c], gen, A.xcd_local);
-    }
-  }
 }
 
 // Stress test of the exchange ordering: when the host asks for it, each
@@ -915,7 +954,6 @@ k_persist(PArgs A) {
     L.stg = p; p += kStgBytes;
     L.tab2 = reinterpret_cast<float *>(p); p += kTab2Floats * 4;
     L.tab1 = reinterpret_cast<float *>(p); p += kTab1Floats * 4;
-    L.part = reinterpret_cast<float *>(p); p += kLuMax * 4;
     L.acc2 = reinterpret_cast<float *>(p); p += kMaxUnitLayers * 2 * 16 * kTMax * 4;
     L.xs = reinterpret_cast<float *>(p); p += 16 * kTMax * 4;
     L.red = reinterpret_cast<float *>(p); p += kXThreads * 4;
@@ -944,8 +982,8 @@ k_persist(PArgs A) {
   __syncthreads();
   for (int ph = 0; ph <= U; ++ph) {
     stamp(L, ph, 0);
-    // every context field the phase uses is read before first_product's
-    // last barrier, after which waves 4-7 restage the context
+    // every context field the phase uses is read before the barrier that
+    // follows the first product, after which waves 4-7 restage the context
     const int t0 = L.ctx->t0, t1 = L.ctx->t1;
     const int Lu = L.ctx->ub.Lu;
     // this thread's share of the next phase's tables (built in the
@@ -965,13 +1003,14 @@ k_persist(PArgs A) {
       stamp(L, ph, 2);
       if (ph == U) break;
     }
-    first_product(L, ph);
-    stamp(L, ph, 4);
     const unsigned gen = gen_base + (unsigned)ph + 1u;
     test_delay<kDelay>(A, gen, 0);
-    exchange_publish(L, Lu, gen, A);
-    // the partials, on the critical path, are issued before the next
-    // phase's block copies (waves 4-7), which then overlap the waits
+    // the partials, on the critical path, are stored by the lookup threads
+    // as they finish, before the next phase's block copies (waves 4-7),
+    // which then overlap the waits; the barrier keeps the copies off the
+    // LDS the lookups still read
+    first_product(A, L, ph, gen);
+    stamp(L, ph, 4);
     __syncthreads();
     if (wave_id() >= 4) {
       // the copy issue gets the SIMDs first while waves 0-3 only poll
@@ -992,7 +1031,7 @@ k_persist(PArgs A) {
 // ------------------------------------------------------------------ host
 static size_t lds_bytes() {
   return kCtxBytes + 2 * kMaxSeg * sizeof(PSeg) + (size_t)kStgBytes +
-         (size_t)(kTab2Floats + kTab1Floats + kLuMax + kMaxUnitLayers * 2 * 16 * kTMax +
+         (size_t)(kTab2Floats + kTab1Floats + kMaxUnitLayers * 2 * 16 * kTMax +
                   16 * kTMax + kXThreads + kWaves + 1) * 4 + 64;
 }
 
