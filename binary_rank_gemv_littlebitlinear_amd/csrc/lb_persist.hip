@@ -445,6 +445,46 @@ __device__ __forceinline__ uint64_t ceil_recip32(int n) {
 // they are in flight together) and only then branches on them; a chain
 // of dependent LDS reads costs ~0.1 us per link.
 
+// The second product's lookups of one task: its words q = sub, sub + lpt,
+// ... below Wk, R words per step.  Every read is unconditional (index
+// clamped, result masked), and all 8 R table reads of a step are gathered
+// before any is summed (a tree per word), so they are in flight at once
+// instead of each waiting for the previous one's sum; the words are added
+// to the total in order.
+template <int R>
+__device__ __forceinline__ float s2_words(const uint32_t *wb, uint32_t tba, int sub, int lpt,
+                                          int Wk) {
+  float acc = 0.f;
+  for (int q = sub; q < Wk; q += R * lpt) {
+    uint32_t wd[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) wd[i] = wb[min(q + i * lpt, Wk - 1) * 16];
+    float v[R][8];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      // the word's 8 tables are one block: entry address =
+      // block | nibble * 4, table n at immediate offset 64 n
+      const uint32_t tq = tba + 4u * kWordF * (uint32_t)min(q + i * lpt, Wk - 1);
+      const uint32_t w = wd[i];
+      v[i][0] = lds_f32(tq | nib_off<0>(w));
+      v[i][1] = lds_f32((tq | nib_off<4>(w)) + 64);
+      v[i][2] = lds_f32((tq | nib_off<8>(w)) + 128);
+      v[i][3] = lds_f32((tq | nib_off<12>(w)) + 192);
+      v[i][4] = lds_f32((tq | nib_off<16>(w)) + 256);
+      v[i][5] = lds_f32((tq | nib_off<20>(w)) + 320);
+      v[i][6] = lds_f32((tq | nib_off<24>(w)) + 384);
+      v[i][7] = lds_f32((tq | nib_off<28>(w)) + 448);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float e = ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) +
+                      ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
+      acc += q + i * lpt < Wk ? e : 0.f;
+    }
+  }
+  return acc;
+}
+
 // Second product of unit A over the workgroup's rows: every layer's fp16
 // outputs (trace), their combine, and the output rows on the last phase or
 // else the first-product tables of unit B over the combined rows.
@@ -483,37 +523,14 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       if (tk < ntk && p < P) {
         const uint32_t *wb = reinterpret_cast<const uint32_t *>(L.stg + s2o) +
                              ((size_t)((r >> 4) * P + p) * Wk) * 16 + (r & 15);
-        // four words per step; every read is unconditional (index clamped,
-        // result masked), and all 32 table reads of a step are gathered
-        // before any is summed (a tree per word), so they are in flight at
-        // once instead of each waiting for the previous one's sum
-        for (int q = sub; q < Wk; q += 4 * lpt) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) wd[i] = wb[min(q + i * lpt, Wk - 1) * 16];
-          float v[4][8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // the word's 8 tables are one block: entry address =
-            // block | nibble * 4, table n at immediate offset 64 n
-            const uint32_t tq = tba + 4u * kWordF * (uint32_t)min(q + i * lpt, Wk - 1);
-            const uint32_t w = wd[i];
-            v[i][0] = lds_f32(tq | nib_off<0>(w));
-            v[i][1] = lds_f32((tq | nib_off<4>(w)) + 64);
-            v[i][2] = lds_f32((tq | nib_off<8>(w)) + 128);
-            v[i][3] = lds_f32((tq | nib_off<12>(w)) + 192);
-            v[i][4] = lds_f32((tq | nib_off<16>(w)) + 256);
-            v[i][5] = lds_f32((tq | nib_off<20>(w)) + 320);
-            v[i][6] = lds_f32((tq | nib_off<24>(w)) + 384);
-            v[i][7] = lds_f32((tq | nib_off<28>(w)) + 448);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) +
-                            ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
-            acc += q + i * lpt < Wk ? e : 0.f;
-          }
-        }
+        // R words per step: 4, or 5 where that takes fewer steps for the
+        // task's first lane (the same choice for every lane of a task; the
+        // sum order does not depend on it)
+        const int wpt = (Wk + lpt - 1) >> lg;
+        if ((wpt + 4) / 5 < (wpt + 3) / 4)
+          acc = s2_words<5>(wb, tba, sub, lpt, Wk);
+        else
+          acc = s2_words<4>(wb, tba, sub, lpt, Wk);
       }
       for (int o = 1; o < lpt; o <<= 1) acc += __shfl_xor(acc, o, 64);
       if (sub == 0 && tk < ntk) L.acc2[mp * (16 * kTMax) + r] = acc;
