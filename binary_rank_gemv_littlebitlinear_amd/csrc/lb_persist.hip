@@ -548,12 +548,13 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
   const float c_out = U.c_out;
   const int64_t trace_x = C.ub.trace_x;
   __syncthreads();
-  // epilogue, a thread per row r: y per layer, the combine and the output
-  // row.  The combined rows are the next unit's input, so the same threads
-  // build its first product's tables from them: the four lanes of rows
-  // 4 qd .. 4 qd + 3 (one quad of a wave) share their z = g * x values by
-  // lane moves, and lane k writes entries 4 k .. 4 k + 3 of each pair's
-  // table of that quad.
+  // epilogue, a thread per row r in each of four groups of 128 threads: y
+  // per layer, the combine and (group 0) the output row.  The combined rows
+  // are the next unit's input, so the same threads build its first
+  // product's tables from them, group jg taking pairs jg, jg + 4, ...: the
+  // four lanes of rows 4 qd .. 4 qd + 3 (one quad of a wave) share their
+  // z = g * x values by lane moves, and lane k writes entries 4 k .. 4 k + 3
+  // of the pair's table of that quad.
   {
     const bool next = ph < A.nunits;
     const PLayer *LB = C.la + na;
@@ -562,8 +563,9 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
     int goff[kMaxUnitLayers];
 #pragma unroll
     for (int m = 0; m < kMaxUnitLayers; ++m) goff[m] = C.g_off[m];
-    const int r = threadIdx.x;
-    if (r < rows) {
+    static_assert(16 * kTMax <= kThreads / 4, "a group of threads per 128 rows");
+    const int r = threadIdx.x & (kThreads / 4 - 1), jg = threadIdx.x / (kThreads / 4);
+    if (r < rows && (jg == 0 || jg < npairs)) {
       const int j = 16 * t0 + r;
       float ys = 0.f;
 #pragma unroll
@@ -574,12 +576,12 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
         float yv = h2f(hv[((r >> 4) * P) * 16 + (r & 15)]) * L.acc2[(m * 2) * (16 * kTMax) + r];
         if (P > 1) yv += h2f(hv[((r >> 4) * P + 1) * 16 + (r & 15)]) * L.acc2[(m * 2 + 1) * (16 * kTMax) + r];
         const uint16_t y16 = f2h(yv);
-        if (j < ub && A.trace) A.trace[trace_y[m] + j] = y16;
+        if (jg == 0 && j < ub && A.trace) A.trace[trace_y[m] + j] = y16;
         ys += h2f(y16);
       }
       const uint16_t xv = f2h(c_out * ys);
       const float xr = j < ub ? h2f(xv) : 0.f;
-      if (j < ub) {
+      if (jg == 0 && j < ub) {
         if (!next)
           A.y[j] = xv;
         else if (A.trace)
@@ -587,7 +589,7 @@ __device__ void second_product(const PArgs &A, int ph, Lds &L) {
       }
       // rows is a multiple of 16, so every quad of lanes is whole here
       const int qd = r >> 2, hi = r & 3;
-      for (int jt = 0; jt < npairs; ++jt) {
+      for (int jt = jg; jt < npairs; jt += kThreads / (kThreads / 4)) {
         const int m = Pu == 2 ? jt >> 1 : jt, p = jt - m * Pu;
         const uint16_t *gv = reinterpret_cast<const uint16_t *>(L.stg + goff[m]);
         const float v = h2f(gv[((r >> 4) * Pu + p) * 16 + (r & 15)]) * xr;
