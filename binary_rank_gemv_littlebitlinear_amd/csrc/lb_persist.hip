@@ -751,9 +751,9 @@ __device__ void first_product(const PArgs &A, Lds &L, int ph, unsigned gen) {
 // The partials every workgroup published (first_product) -> the next
 // phase's second-product tables over their sum, in the three levels
 // described at the top of this file.  Each level costs one store and one
-// read (plus re-reads while words are missing).  Past the publish only
-// threads < kXThreads touch exchange memory; every spin is bounded and
-// checks the error word every 64 rounds.
+// read (plus re-reads while words are missing).  Levels A and B run on
+// the first kXThreads threads, level C on all of them; every spin is
+// bounded and checks the error word every 64 rounds.
 
 // Wait (per thread) until the words at p(k), k < N with valid(k),
 // carry gen; their values go to vals.  False on give-up or error.
@@ -791,11 +791,12 @@ __device__ __forceinline__ bool spin_tagged(Ptr p, Valid valid, unsigned gen, un
 }
 
 // The second product's tables of the next phase (unit B of this phase):
-// group g (4 latent columns of one layer and path) is built by exchange
-// thread g % 256 from the reduced latent words and l.  The groups are
+// group g (4 latent columns of one layer and path) is built by thread
+// g % 512 from the reduced latent words and l (every wave takes part in
+// level C, so a thread has at most one group up to 512 groups).  The groups are
 // listed on the host; a thread loads its own at the start of the phase, so
 // the loads are long done when the exchange needs them.
-constexpr int kGroupsPerThread = (kTab2Floats / 16 + kXThreads - 1) / kXThreads;
+constexpr int kGroupsPerThread = (kTab2Floats / 16 + kThreads - 1) / kThreads;
 struct TabPlan {
   int n;                                 // groups of this thread
   int tcol[kGroupsPerThread];            // latent column of the group's first word
@@ -819,8 +820,8 @@ __device__ TabPlan load_tables(const PArgs &A, const Lds &L, bool live) {
   T.n = 0;
 #pragma unroll
   for (int i = 0; i < kGroupsPerThread; ++i) {
-    const int g = (int)threadIdx.x + i * kXThreads;
-    const bool v = (int)threadIdx.x < kXThreads && g < ng;
+    const int g = (int)threadIdx.x + i * kThreads;
+    const bool v = g < ng;
     const u4v rv = gg[min(g, gmax)];
     const uint4 raw = v ? make_uint4(rv.x, rv.y, rv.z, rv.w) : make_uint4(0u, 0u, 0u, 0u);
     T.lp[i] = reinterpret_cast<const uint16_t *>((uint64_t)raw.x | ((uint64_t)raw.y << 32));
@@ -919,7 +920,7 @@ __device__ bool exchange_collect(Lds &L, int Lu, unsigned gen, const PArgs &A, c
   // level C, straight into the next phase's tables: w = l * t per group
   uint64_t *pc = A.PC + (size_t)x * kLuMax;
   test_delay<kDelay>(A, gen, 3);
-  if (xw) {
+  {
     uint2 lraw[kGroupsPerThread];  // 4 fp16 l per group
 #pragma unroll
     for (int i = 0; i < kGroupsPerThread; ++i)
